@@ -1,0 +1,42 @@
+"""CPU oracle for the normalization hot path -- TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow, obviously correct reference that the HIP
+kernels are checked against. It is not part of the product: only the test
+suite, the smoke check of the package entry point and the CPU-baseline leg of
+the benchmark may import it. The product library never calls it and has no CPU
+fallback.
+
+Everything is computed in float64 from the exact bf16 input values and rounded
+once to bf16 (round to nearest, ties to even) at the end:
+
+* ``rmsnorm_fwd``       -- row-wise RMSNorm, y = x / sqrt(mean(x^2) + eps) * w
+  ("[Inductor] Codegen Gluon", section 3.1, the RMSNorm reference workload:
+  an x*x accumulation, then x * rstd * weight).
+* ``qk_norm_rope_fwd``  -- per-head RMSNorm with q/k weights followed by
+  rotate-half (NeoX) rotary embedding on the q and k heads of a packed QKV
+  tensor, in place, v heads untouched ("[pretuned] Optimize fused_qk_norm_rope
+  on B200", Summary).
+
+The oracle shares no code with the HIP path. It takes raw bf16 bit patterns
+(numpy ``uint16``) and returns raw bf16 bit patterns.
+"""
+
+from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+from .rmsnorm import rmsnorm_fwd, rmsnorm_fwd_f64
+from .qk_norm_rope import (
+    qk_norm_rope_fwd,
+    qk_norm_rope_fwd_f64,
+    rope_inv_freq,
+    rope_rotate_neox,
+)
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "f64_to_bf16_bits",
+    "rmsnorm_fwd",
+    "rmsnorm_fwd_f64",
+    "qk_norm_rope_fwd",
+    "qk_norm_rope_fwd_f64",
+    "rope_inv_freq",
+    "rope_rotate_neox",
+]
