@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the normalization hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+  1. rmsnorm_fwd on x[16384, 16384] bf16 (N(0,1), w ~ U(0.5, 1.5), eps 1e-6),
+     the shape the RMSNorm bandwidth table of "[Inductor] Codegen Gluon"
+     (section 3.1) peaks at;
+  2. qk_norm_rope_fwd on qkv[256, (32+8+8)*128] bf16 (full-rotary fused
+     QK-norm + RoPE, "[pretuned] Optimize fused_qk_norm_rope on B200").
+Each launch is bracketed by HIP events on the stream it runs on; `value` is the
+RMSNorm's achieved HBM bandwidth, algorithmic bytes (2*M*N*2 + 2*N) divided by
+its mean event-timed duration, in GB/s (1e9 B/s). Prints one JSON line.
+
+The CPU baseline is the fp64 oracle run on the host over the same RMSNorm
+workload (row blocks of 1024), single-threaded.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+RMS_WORKLOAD = "rms_16384x16384"
+QK_WORKLOAD = "qk_256"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_16384x16384_hbm_traffic.txt")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "memory_bound_normalization_amd", "csrc", f)
+    for f in ("rmsnorm.hip", "device.h")
+]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(algorithmic_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    src = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    tot = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not tot or src.group(1) != kernel_source_hash():
+        return None
+    return float(tot.group(1))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(x_bits, w_bits, eps, n: int, budget_s: float):
+    """Time the oracle on row blocks of the workload until `budget_s` is used."""
+    from oracle import rmsnorm_fwd as oracle_rmsnorm
+
+    rows_done = 0
+    block = 1024
+    t0 = time.perf_counter()
+    while rows_done < x_bits.shape[0]:
+        oracle_rmsnorm(x_bits[rows_done : rows_done + block], w_bits, eps)
+        rows_done += min(block, x_bits.shape[0] - rows_done)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = 2 * rows_done * n * 2 + 2 * n
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{rows_done} of {x_bits.shape[0]} rows of x[16384, 16384] in 1024-row blocks, "
+        f"numpy fp64, one thread, {dt:.1f} s on {cpu_model()} ({os.cpu_count()} logical CPUs)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(
+            "bench.py measures one GPU only: the kernels run on one MI355X's share of the "
+            "rows; multi-GPU runs are not part of this build.",
+            file=sys.stderr,
+        )
+        return 2
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+    from workloads import QK_WORKLOADS, RMS_WORKLOADS, make_qk_inputs, make_rms_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    mbn.lib()  # fail loudly if the HIP library is missing
+
+    dev = torch.device("cuda:0")
+    wl = RMS_WORKLOADS[RMS_WORKLOAD]
+    qwl = QK_WORKLOADS[QK_WORKLOAD]
+    x_bits, w_bits, eps = make_rms_inputs(wl)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = to_dev(x_bits)
+    w = to_dev(w_bits)
+    y = torch.empty_like(x)
+    qkv_bits, qw_bits, kw_bits, pos, qeps, theta = make_qk_inputs(qwl)
+    qkv0 = to_dev(qkv_bits)
+    qkv = qkv0.clone()
+    q_w, k_w = to_dev(qw_bits), to_dev(kw_bits)
+    positions = torch.from_numpy(pos).to(dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mbn.rmsnorm_fwd(x, w, y, eps=eps)
+        if ev is not None:
+            ev[1].record(stream)
+        mbn.qk_norm_rope_fwd(qkv, q_w, k_w, positions, qwl.n_q_heads, qwl.n_kv_heads,
+                             qwl.head_dim, eps=qeps, theta=theta)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    rms_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    qk_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    rms_mean_s = sum(rms_ms) / len(rms_ms) / 1e3
+    qk_mean_s = sum(qk_ms) / len(qk_ms) / 1e3
+    rms_bytes = wl.algorithmic_bytes
+    achieved = rms_bytes / rms_mean_s / 1e9
+
+    traffic = measured_traffic(rms_bytes)
+    out = {
+        "metric": "achieved HBM GB/s and % of 8 TB/s peak, bf16 RMSNorm M=N=16384",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy, see workloads/)",
+        "config": {
+            "workload": "bf16 RMSNorm x[16384,16384] + fused QK-norm+RoPE qkv[256,48*128]",
+            "io_dtype": "bf16",
+            "rmsnorm": {"M": wl.M, "N": wl.N, "eps": wl.eps},
+            "qk_norm_rope": {"T": qwl.T, "n_q_heads": qwl.n_q_heads, "n_kv_heads": qwl.n_kv_heads,
+                             "head_dim": qwl.head_dim, "theta": qwl.theta, "eps": qwl.eps},
+        },
+        "pct_of_peak": round(100.0 * achieved / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "rmsnorm_fwd",
+            "algorithmic_bytes_per_launch": rms_bytes,
+            "mean_us": round(rms_mean_s * 1e6, 2),
+            "best_us": round(min(rms_ms) * 1e3, 2),
+        },
+        "qk_norm_rope": {
+            "mean_us": round(qk_mean_s * 1e6, 2),
+            "best_us": round(min(qk_ms) * 1e3, 2),
+            "algorithmic_bytes_per_launch": qwl.algorithmic_bytes,
+            "GBps": round(qwl.algorithmic_bytes / qk_mean_s / 1e9, 1),
+            "note": "2.5 MiB in place; stays in L2/MALL across steps; launch-latency bound",
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x_bits, w_bits, eps, wl.N, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,120 @@
+/*
+ * mbn.h -- C interface of the memory-bound normalization library (libmbn.so),
+ * MI355X / gfx950.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are raw device pointers owned by the caller. bf16 means the raw
+ *     16-bit IEEE bfloat16 bit pattern. Arrays are row-major and contiguous.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *     is enqueued on it asynchronously; the library never synchronizes and
+ *     never allocates device or host memory.
+ *   - Every argument is validated on the host before any HIP call. A non-zero
+ *     status means nothing was launched (except MBN_EHIP, which reports that
+ *     the launch itself failed; the HIP error state is read and cleared with
+ *     hipGetLastError).
+ *   - The library is stateless and may be called from several host threads.
+ *   - Results are deterministic: a fixed reduction order, no atomics.
+ */
+#ifndef MBN_H
+#define MBN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MBN_API __attribute__((visibility("default")))
+
+/* Status codes returned by every entry point. */
+#define MBN_OK 0           /* success (also for empty inputs: nothing launched) */
+#define MBN_EINVAL 1       /* an argument is invalid: null pointer, negative size,
+                              eps negative / NaN / infinite, odd head_dim,
+                              overlapping input and output ranges */
+#define MBN_EUNSUPPORTED 2 /* valid but outside what the kernels handle: row
+                              width not a multiple of 8, wider than
+                              MBN_RMSNORM_MAX_N, pointer not 16-byte aligned,
+                              head_dim other than MBN_QK_HEAD_DIM */
+#define MBN_EHIP 3         /* the kernel launch failed */
+
+/* Widest RMSNorm row: one row is staged whole in LDS (2 bytes per element). */
+#define MBN_RMSNORM_MAX_N 65536
+/* Head size handled by qk_norm_rope_fwd. */
+#define MBN_QK_HEAD_DIM 128
+
+/*
+ * rmsnorm_fwd -- row-wise RMSNorm forward in bf16.
+ *
+ * Defined by "[Inductor] Codegen Gluon", section 3.1 (the RMSNorm reference
+ * workload: x is read for the x*x accumulation and again for x * rstd *
+ * weight). For every row i of x:
+ *     rstd_i = 1 / sqrt( (1/N) * sum_j x[i,j]^2 + eps )
+ *     y[i,j] = bf16( x[i,j] * rstd_i * w[j] )
+ * Each row is read from HBM once and staged in LDS as bf16; both the sum of
+ * squares and the scaling read the staged copy and widen to fp32 there. The
+ * sum of squares and the products are fp32; the output is rounded to nearest
+ * even.
+ *
+ *   x      device, bf16 [M, N], read only (unless y == x)
+ *   w      device, bf16 [N], read only
+ *   y      device, bf16 [M, N], written. y == x (exact alias, in place) is
+ *          allowed; any other overlap of y with x or w is MBN_EINVAL.
+ *   M      rows, >= 0 (M == 0 returns MBN_OK, pointers may then be NULL);
+ *          at most 2^31 - 1
+ *   N      row width, 1 <= N <= MBN_RMSNORM_MAX_N, N % 8 == 0
+ *   eps    finite, >= 0 (added inside the square root)
+ *   stream hipStream_t or NULL
+ * x, w and y must be 16-byte aligned.
+ * IEEE behaviour: a NaN in a row makes the row NaN; an infinite element makes
+ * the finite elements of its row 0 and itself NaN; a zero row gives 0 when
+ * eps > 0 and NaN when eps == 0. Rows whose sum of squares overflows fp32
+ * (|x| above about 1.8e19) behave like rows holding an infinity.
+ */
+MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                        float eps, void* stream);
+
+/*
+ * qk_norm_rope_fwd -- fused per-head RMSNorm + rotary embedding on the q and
+ * k heads of a packed QKV tensor, in place.
+ *
+ * Defined by "[pretuned] Optimize fused_qk_norm_rope on B200", Summary (full
+ * rotary case: the two rotary halves of each head are loaded once, the RMS is
+ * taken over the whole head, the Q/K weight and the rotary embedding are
+ * applied without a round trip through memory, and each half is stored once).
+ * For token t, with D = head_dim and each q head (weight q_w) or k head
+ * (weight k_w) holding x[0..D):
+ *     rstd  = 1 / sqrt( mean_d x[d]^2 + eps ),   u[d] = x[d] * rstd * w[d]
+ *     phi_i = positions[t] * theta^(-2i/D)        for i in [0, D/2)
+ *     out[i]       = u[i]       * cos(phi_i) - u[i+D/2] * sin(phi_i)
+ *     out[i+D/2]   = u[i+D/2]   * cos(phi_i) + u[i]     * sin(phi_i)
+ * (rotate-half pairing, as in NeoX-style rotary embeddings). The angles and
+ * their sine / cosine are computed in fp64, the rest in fp32, with one
+ * rounding to bf16 at the store.
+ *
+ *   qkv        device, bf16 [T, (n_q_heads + 2*n_kv_heads) * head_dim], read
+ *              and written in place. Per token: n_q_heads q heads, then
+ *              n_kv_heads k heads, then n_kv_heads v heads; v is never read
+ *              or written.
+ *   q_w, k_w   device, bf16 [head_dim] each, shared by all q (k) heads
+ *   positions  device, int64 [T] (|position| < 2^53)
+ *   T          tokens, >= 0 (T == 0 returns MBN_OK); at most 2^31 - 1
+ *   n_q_heads, n_kv_heads  >= 0
+ *   head_dim   must equal MBN_QK_HEAD_DIM (odd values are MBN_EINVAL)
+ *   eps        finite, >= 0;  theta  finite, > 0
+ *   stream     hipStream_t or NULL
+ * qkv, q_w and k_w must be 16-byte aligned, positions 8-byte aligned; q_w,
+ * k_w and positions must not overlap the q/k part of qkv.
+ */
+MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,
+                             const int64_t* positions, int64_t T, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
+                             void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+MBN_API const char* mbn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBN_H */

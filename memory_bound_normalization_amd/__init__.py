@@ -1,0 +1,161 @@
+"""Python binding of libmbn.so: bf16 RMSNorm and fused QK-norm + rotary on MI355X.
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels. PyTorch supplies device memory and streams. There is no CPU
+fallback; importing works without a GPU, but any call raises if the library is
+not built or the tensors are not on the GPU.
+
+Functions with the C names take torch tensors:
+
+* ``rmsnorm_fwd(x, w, y=None, eps=1e-6, stream=None)`` -- x [..., N] bf16,
+  w [N] bf16; returns y (allocated like x when not given; ``y is x`` runs in
+  place).
+* ``qk_norm_rope_fwd(qkv, q_w, k_w, positions, n_q_heads, n_kv_heads,
+  head_dim=128, eps=1e-6, theta=1e6, stream=None)`` -- modifies qkv in place
+  and returns it.
+* ``mbn_strerror(status)``.
+
+``lib()`` returns the raw ctypes handle (C signatures of include/mbn.h).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MBN_OK",
+    "MBN_EINVAL",
+    "MBN_EUNSUPPORTED",
+    "MBN_EHIP",
+    "MBN_RMSNORM_MAX_N",
+    "MBN_QK_HEAD_DIM",
+    "MbnError",
+    "lib",
+    "lib_path",
+    "mbn_strerror",
+    "qk_norm_rope_fwd",
+    "rmsnorm_fwd",
+]
+
+MBN_OK = 0
+MBN_EINVAL = 1
+MBN_EUNSUPPORTED = 2
+MBN_EHIP = 3
+MBN_RMSNORM_MAX_N = 65536
+MBN_QK_HEAD_DIM = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libmbn.so")
+
+
+class MbnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({mbn_strerror(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmbn.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m memory_bound_normalization_amd.build`"
+            )
+        h = ctypes.CDLL(path)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        h.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, vp]
+        h.rmsnorm_fwd.restype = ctypes.c_int
+        h.qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, f32, vp]
+        h.qk_norm_rope_fwd.restype = ctypes.c_int
+        h.mbn_strerror.argtypes = [ctypes.c_int]
+        h.mbn_strerror.restype = ctypes.c_char_p
+        _LIB = h
+    return _LIB
+
+
+def mbn_strerror(status: int) -> str:
+    try:
+        return lib().mbn_strerror(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check_bf16_cuda(name, t):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def rmsnorm_fwd(x, w, y=None, eps: float = 1e-6, stream=None):
+    """y = x * rsqrt(mean(x^2, -1) + eps) * w over the last dim of bf16 x."""
+    import torch
+
+    _check_bf16_cuda("x", x)
+    _check_bf16_cuda("w", w)
+    n = x.shape[-1] if x.dim() > 0 else 0
+    if w.dim() != 1 or w.shape[0] != n:
+        raise ValueError(f"w must have shape [{n}], got {tuple(w.shape)}")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _check_bf16_cuda("y", y)
+        if y.shape != x.shape:
+            raise ValueError("y must have the shape of x")
+    m = x.numel() // n if n else 0
+    rc = lib().rmsnorm_fwd(
+        x.data_ptr(), w.data_ptr(), y.data_ptr(), m, n, float(eps), _stream_handle(stream, x.device)
+    )
+    if rc != MBN_OK:
+        raise MbnError(rc, "rmsnorm_fwd")
+    return y
+
+
+def qk_norm_rope_fwd(
+    qkv, q_w, k_w, positions, n_q_heads: int, n_kv_heads: int, head_dim: int = MBN_QK_HEAD_DIM,
+    eps: float = 1e-6, theta: float = 1e6, stream=None,
+):
+    """In-place per-head RMSNorm (q_w / k_w) + rotate-half RoPE on qkv [T, (Hq+2Hkv)*D]."""
+    import torch
+
+    _check_bf16_cuda("qkv", qkv)
+    _check_bf16_cuda("q_w", q_w)
+    _check_bf16_cuda("k_w", k_w)
+    if positions.dtype != torch.int64 or not positions.is_cuda or not positions.is_contiguous():
+        raise TypeError("positions must be a contiguous int64 GPU tensor")
+    t = qkv.shape[0] if qkv.dim() else 0
+    if qkv.dim() != 2 or qkv.shape[1] != (n_q_heads + 2 * n_kv_heads) * head_dim:
+        raise ValueError("qkv must have shape [T, (n_q_heads + 2 * n_kv_heads) * head_dim]")
+    if positions.numel() != t:
+        raise ValueError("positions must have T entries")
+    rc = lib().qk_norm_rope_fwd(
+        qkv.data_ptr(), q_w.data_ptr(), k_w.data_ptr(), positions.data_ptr(), t,
+        int(n_q_heads), int(n_kv_heads), int(head_dim), float(eps), float(theta),
+        _stream_handle(stream, qkv.device),
+    )
+    if rc != MBN_OK:
+        raise MbnError(rc, "qk_norm_rope_fwd")
+    return qkv

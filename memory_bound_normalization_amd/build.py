@@ -1,0 +1,71 @@
+"""Build libmbn.so (the HIP kernels and the C entry points) for gfx950, in tree.
+
+    python -m memory_bound_normalization_amd.build
+
+Compiles every ``csrc/*.hip`` file with hipcc into one shared library next to
+this file. No fast-math: the kernels rely on IEEE fp32/fp64 behaviour.
+"""
+
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libmbn.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmbn.so)")
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def compile_command(out: str, extra: list[str] | None = None) -> list[str]:
+    return [
+        hipcc(),
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        "-fvisibility=hidden",
+        "-Wall",
+        # packed fp32 VALU ops stay off (device pass; the host pass ignores it)
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE,
+        *(extra or []),
+        "-o", out,
+        *sources(),
+    ]
+
+
+def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = None) -> str:
+    """Compile the library; always rebuilds. Returns the path of the .so."""
+    tmp = out + ".tmp"
+    cmd = compile_command(tmp, extra)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

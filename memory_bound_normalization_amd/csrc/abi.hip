@@ -1,0 +1,81 @@
+// C entry points of libmbn.so: argument validation (host only, before any HIP
+// call) and dispatch to the kernel launchers. The contract of every function
+// is documented in include/mbn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mbn.h"
+#include "kernels.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+bool valid_eps(float eps) { return isfinite(eps) && eps >= 0.0f; }
+
+}  // namespace
+
+extern "C" {
+
+MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps,
+                        void* stream) {
+  if (M < 0 || N <= 0 || !valid_eps(eps)) return MBN_EINVAL;
+  if (M == 0) return MBN_OK;
+  if (!x || !w || !y) return MBN_EINVAL;
+  if (N % 8 != 0 || N > MBN_RMSNORM_MAX_N || M > 0x7fffffffLL) return MBN_EUNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return MBN_EUNSUPPORTED;
+  const int64_t bytes = M * N * 2;
+  if (y != x && overlap(x, bytes, y, bytes)) return MBN_EINVAL;
+  if (overlap(w, N * 2, y, bytes)) return MBN_EINVAL;
+  const hipError_t err =
+      mbn::launch_rmsnorm(x, w, y, M, N, eps, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MBN_OK : MBN_EHIP;
+}
+
+MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,
+                             const int64_t* positions, int64_t T, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
+                             void* stream) {
+  if (T < 0 || n_q_heads < 0 || n_kv_heads < 0 || head_dim <= 0 || (head_dim & 1))
+    return MBN_EINVAL;
+  if (!valid_eps(eps) || !isfinite(theta) || !(theta > 0.0f)) return MBN_EINVAL;
+  if (head_dim != MBN_QK_HEAD_DIM) return MBN_EUNSUPPORTED;
+  const int64_t heads = (int64_t)n_q_heads + n_kv_heads;
+  if (T == 0 || heads == 0) return MBN_OK;
+  if (!qkv || !positions || (n_q_heads > 0 && !q_w) || (n_kv_heads > 0 && !k_w))
+    return MBN_EINVAL;
+  if (T > 0x7fffffffLL || heads > (1 << 20)) return MBN_EUNSUPPORTED;
+  if (!aligned(qkv, 16) || (q_w && !aligned(q_w, 16)) || (k_w && !aligned(k_w, 16)) ||
+      !aligned(positions, 8))
+    return MBN_EUNSUPPORTED;
+  // The q/k part of the last token ends before its v heads; any read-only input
+  // inside the span [qkv, end of the last token's k heads) is rejected.
+  const int64_t row_bytes = ((int64_t)n_q_heads + 2 * (int64_t)n_kv_heads) * head_dim * 2;
+  const int64_t span = (T - 1) * row_bytes + heads * head_dim * 2;
+  const int64_t wbytes = (int64_t)head_dim * 2;
+  if ((n_q_heads > 0 && overlap(q_w, wbytes, qkv, span)) ||
+      (n_kv_heads > 0 && overlap(k_w, wbytes, qkv, span)) || overlap(positions, T * 8, qkv, span))
+    return MBN_EINVAL;
+  const hipError_t err = mbn::launch_qk_norm_rope(qkv, q_w, k_w, positions, T, n_q_heads,
+                                                  n_kv_heads, eps, theta,
+                                                  static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MBN_OK : MBN_EHIP;
+}
+
+MBN_API const char* mbn_strerror(int status) {
+  switch (status) {
+    case MBN_OK: return "success";
+    case MBN_EINVAL: return "invalid argument";
+    case MBN_EUNSUPPORTED: return "unsupported shape, alignment or head size";
+    case MBN_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

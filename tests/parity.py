@@ -1,0 +1,65 @@
+"""Helpers shared by the GPU parity tests: bit transfer and the tolerance check.
+
+Tolerance (elementwise, on every compared output): with y_ref the oracle's
+bf16 value widened to float64,
+
+    |y_gpu - y_ref| <= 2^-7 * |y_ref| + 1e-6
+
+i.e. one bf16 ulp relative plus an absolute floor for outputs near zero. NaN
+positions must match exactly; infinities must match exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import bf16_bits_to_f64
+
+REL_TOL = 2.0**-7
+ABS_TOL = 1e-6
+
+
+def to_gpu_bf16(bits: np.ndarray, device="cuda"):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def from_gpu_bf16(t) -> np.ndarray:
+    import torch
+
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def tolerance_violations(got_bits, ref_bits):
+    """Return a boolean mask of outputs outside the tolerance (NaN/inf aware)."""
+    g = bf16_bits_to_f64(got_bits)
+    r = bf16_bits_to_f64(ref_bits)
+    nan_r, nan_g = np.isnan(r), np.isnan(g)
+    with np.errstate(invalid="ignore"):
+        ok = (np.abs(g - r) <= REL_TOL * np.abs(r) + ABS_TOL) | (g == r)
+    ok = np.where(nan_r | nan_g, nan_r & nan_g, ok)
+    return ~ok
+
+
+def assert_parity(got_bits, ref_bits, what: str = ""):
+    got_bits = np.asarray(got_bits)
+    ref_bits = np.asarray(ref_bits)
+    assert got_bits.shape == ref_bits.shape, (got_bits.shape, ref_bits.shape)
+    bad = tolerance_violations(got_bits, ref_bits)
+    n = int(np.count_nonzero(bad))
+    if n:
+        idx = np.argwhere(bad)[:8]
+        g = bf16_bits_to_f64(got_bits)
+        r = bf16_bits_to_f64(ref_bits)
+        rows = [f"  at {tuple(int(v) for v in i)}: gpu {g[tuple(i)]!r} oracle {r[tuple(i)]!r}" for i in idx]
+        raise AssertionError(f"{what}: {n} of {bad.size} outputs outside tolerance\n" + "\n".join(rows))
+
+
+def ulp_stats(got_bits, ref_bits) -> dict:
+    """How far the GPU is from the oracle, in bf16 ulps of the oracle value (finite only)."""
+    g = bf16_bits_to_f64(got_bits)
+    r = bf16_bits_to_f64(ref_bits)
+    fin = np.isfinite(r) & np.isfinite(g)
+    same = int(np.count_nonzero((got_bits == ref_bits) & fin))
+    return {"compared": int(fin.sum()), "bit_equal": same, "frac_bit_equal": same / max(1, int(fin.sum()))}

@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library builds, loads, exports every
+symbol include/mbn.h declares, and rejects invalid arguments on the host before
+any HIP call (every case below is invalid by construction, so no kernel is ever
+launched and no pointer is dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bound_normalization_amd as mbn
+from memory_bound_normalization_amd import build as mbn_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mbn.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mbn.lib_path()):
+        mbn_build.build()
+    return mbn.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MBN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def _header_constants():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(MBN_\w+)\s+(\d+)", text)}
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared_functions()) == {"rmsnorm_fwd", "qk_norm_rope_fwd", "mbn_strerror"}
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_python_constants_match_header():
+    c = _header_constants()
+    for name in ("MBN_OK", "MBN_EINVAL", "MBN_EUNSUPPORTED", "MBN_EHIP", "MBN_RMSNORM_MAX_N", "MBN_QK_HEAD_DIM"):
+        assert getattr(mbn, name) == c[name], name
+
+
+def test_strerror(lib):
+    for s in range(5):
+        assert isinstance(mbn.mbn_strerror(s), str) and mbn.mbn_strerror(s)
+    assert mbn.mbn_strerror(0) == "success"
+
+
+def test_build_command_targets_gfx950_without_fast_math():
+    cmd = mbn_build.compile_command("/tmp/x.so")
+    assert "--offload-arch=gfx950" in cmd
+    assert "-packed-fp32-ops" in cmd
+    assert not any("fast-math" in a or a == "-ffast-math" for a in cmd)
+
+
+def rms(lib, x=FAKE, w=FAKE + 0x10000000, y=FAKE + 0x20000000, M=4, N=64, eps=1e-6):
+    return lib.rmsnorm_fwd(x, w, y, M, N, eps, None)
+
+
+@pytest.mark.parametrize(
+    "kw, status",
+    [
+        (dict(M=-1), mbn.MBN_EINVAL),
+        (dict(N=0), mbn.MBN_EINVAL),
+        (dict(N=-8), mbn.MBN_EINVAL),
+        (dict(eps=-1e-6), mbn.MBN_EINVAL),
+        (dict(eps=float("nan")), mbn.MBN_EINVAL),
+        (dict(eps=float("inf")), mbn.MBN_EINVAL),
+        (dict(x=None), mbn.MBN_EINVAL),
+        (dict(w=None), mbn.MBN_EINVAL),
+        (dict(y=None), mbn.MBN_EINVAL),
+        (dict(N=12), mbn.MBN_EUNSUPPORTED),
+        (dict(N=1), mbn.MBN_EUNSUPPORTED),
+        (dict(N=65544), mbn.MBN_EUNSUPPORTED),
+        (dict(M=1 << 31), mbn.MBN_EUNSUPPORTED),
+        (dict(x=FAKE + 2), mbn.MBN_EUNSUPPORTED),
+        (dict(w=FAKE + 0x10000008), mbn.MBN_EUNSUPPORTED),
+        (dict(y=FAKE + 0x20000004), mbn.MBN_EUNSUPPORTED),
+        (dict(y=FAKE + 16), mbn.MBN_EINVAL),  # partial overlap of y with x
+        (dict(w=FAKE + 0x20000000 + 64), mbn.MBN_EINVAL),  # w inside y
+    ],
+)
+def test_rmsnorm_rejects(lib, kw, status):
+    assert rms(lib, **kw) == status
+
+
+def test_rmsnorm_empty_is_a_noop(lib):
+    assert lib.rmsnorm_fwd(None, None, None, 0, 64, 1e-6, None) == mbn.MBN_OK
+
+
+def qk(lib, qkv=FAKE, q_w=FAKE + 0x10000000, k_w=FAKE + 0x10001000, pos=FAKE + 0x10002000,
+       T=4, hq=4, hk=2, d=128, eps=1e-6, theta=1e6):
+    return lib.qk_norm_rope_fwd(qkv, q_w, k_w, pos, T, hq, hk, d, eps, theta, None)
+
+
+@pytest.mark.parametrize(
+    "kw, status",
+    [
+        (dict(T=-1), mbn.MBN_EINVAL),
+        (dict(hq=-1), mbn.MBN_EINVAL),
+        (dict(hk=-2), mbn.MBN_EINVAL),
+        (dict(d=0), mbn.MBN_EINVAL),
+        (dict(d=127), mbn.MBN_EINVAL),
+        (dict(eps=-1.0), mbn.MBN_EINVAL),
+        (dict(eps=float("nan")), mbn.MBN_EINVAL),
+        (dict(theta=0.0), mbn.MBN_EINVAL),
+        (dict(theta=-10.0), mbn.MBN_EINVAL),
+        (dict(theta=float("inf")), mbn.MBN_EINVAL),
+        (dict(qkv=None), mbn.MBN_EINVAL),
+        (dict(pos=None), mbn.MBN_EINVAL),
+        (dict(q_w=None), mbn.MBN_EINVAL),
+        (dict(k_w=None), mbn.MBN_EINVAL),
+        (dict(d=64), mbn.MBN_EUNSUPPORTED),
+        (dict(d=256), mbn.MBN_EUNSUPPORTED),
+        (dict(qkv=FAKE + 8), mbn.MBN_EUNSUPPORTED),
+        (dict(q_w=FAKE + 0x10000002), mbn.MBN_EUNSUPPORTED),
+        (dict(pos=FAKE + 0x10002004), mbn.MBN_EUNSUPPORTED),
+        (dict(q_w=FAKE + 256), mbn.MBN_EINVAL),  # weight inside the q/k span
+        (dict(pos=FAKE + 1024), mbn.MBN_EINVAL),
+    ],
+)
+def test_qk_rejects(lib, kw, status):
+    assert qk(lib, **kw) == status
+
+
+def test_qk_empty_is_a_noop(lib):
+    assert qk(lib, qkv=None, q_w=None, k_w=None, pos=None, T=0) == mbn.MBN_OK
+    assert qk(lib, hq=0, hk=0) == mbn.MBN_OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    w = torch.ones(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        mbn.rmsnorm_fwd(x, w)
+    with pytest.raises(TypeError):
+        mbn.rmsnorm_fwd(x.float(), w)
