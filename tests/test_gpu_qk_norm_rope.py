@@ -66,7 +66,7 @@ def test_token_counts(T):
 
 def test_positions():
     rng = np.random.default_rng(9)
-    pos = np.array([0, 1, 7, 255, 4096, 65535, 1 << 20, (1 << 31) - 1, -1, -300, 123456789, 3], dtype=np.int64)
+    pos = np.array([0, 1, 7, 255, 4096, 65535, 1 << 20, 1 << 24, -1, -300, 123456789, 3], dtype=np.int64)
     _check(len(pos), 4, 2, pos=pos, seed=10)
     _check(64, 4, 2, pos=rng.integers(0, 1 << 17, 64), seed=11)
 
