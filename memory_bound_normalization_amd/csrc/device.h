@@ -61,11 +61,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// 16-byte load from global memory straight into LDS (global_load_lds_dwordx4).
-// Lane l of the wave writes bytes [16 l, 16 l + 16) after the wave-uniform LDS
-// address `lds_wave_base`. Completion is tracked by vmcnt.
+// 16-byte load from global memory straight into LDS (global_load_lds_dwordx4),
+// marked non-temporal (the data is read once). Lane l of the wave writes bytes
+// [16 l, 16 l + 16) after the wave-uniform LDS address `lds_wave_base`.
+// Completion is tracked by vmcnt.
+constexpr int kCachePolicyNT = 2;
 __device__ __forceinline__ void load_lds_16(const void* gptr, lds_void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gptr, lds_wave_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gptr, lds_wave_base, 16, 0, kCachePolicyNT);
 }
 
 // Wait until every vector-memory load of this wave has landed (LDS included).

@@ -24,20 +24,36 @@
 namespace mbn {
 namespace {
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b mod 8). With xcd_group = G > 0, XCD x is given runs of G consecutive
+// row blocks instead of every 8th one, which changes how the concurrent HBM
+// traffic of the XCDs interleaves; G = 0 keeps the identity. The remap is a
+// bijection on the leading blocks that fill whole groups of 8*G; the rest keep
+// their own index.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nblocks, int group) {
+  if (group <= 0) return b;
+  const int64_t span = 8 * (int64_t)group;
+  if (b >= (nblocks / span) * span) return b;
+  const int64_t xcd = b & 7, i = b >> 3;
+  return (i / group) * span + xcd * group + (i % group);
+}
+
 // FULL: the row is exactly MAXC chunks per lane (the power-of-two widths), so
 // no chunk needs a bounds predicate.
 template <int WPR, int ROWS, int MAXC, bool FULL>
 __global__ void __launch_bounds__(64 * WPR * ROWS)
 rmsnorm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-               uint16_t* __restrict__ y, int64_t M, int nchunk, float inv_n, float eps) {
+               uint16_t* __restrict__ y, int64_t M, int nchunk, float inv_n, float eps,
+               int xcd_group) {
   constexpr int TPR = 64 * WPR;  // lanes per row
-  extern __shared__ u32x4 lds_rows[];  // ROWS * nchunk chunks of 16 bytes
+  extern __shared__ u32x4 lds_rows[];  // ROWS * nchunk chunks of 16 bytes (or more, see launcher)
 
   const int tid = threadIdx.x;
   const int slot = tid / TPR;
   const int t = tid - slot * TPR;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t row = (int64_t)blockIdx.x * ROWS + slot;
+  const int64_t block = xcd_remap(blockIdx.x, gridDim.x, xcd_group);
+  const int64_t row = block * ROWS + slot;
   const bool live = row < M;
 
   u32x4* buf = lds_rows + (size_t)slot * nchunk;
@@ -116,36 +132,56 @@ rmsnorm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   }
 }
 
-typedef void (*RmsKernel)(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, float, float);
+typedef void (*RmsKernel)(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, float, float,
+                          int);
+
+// LDS of one CU on gfx950; a workgroup may use all of it.
+constexpr size_t kLdsPerCU = 160 * 1024;
 
 struct RmsCfg {
-  int max_nchunk;  // widest row (in 16-byte chunks) this entry serves
+  int max_nchunk;    // widest row (in 16-byte chunks) this entry serves
   int wpr, rows, maxc;
+  int wgs_per_cu;    // occupancy cap (0 = as many as LDS and waves allow)
+  int xcd_group;     // row blocks per XCD run (0 = dispatch order)
   RmsKernel ragged;  // any width up to max_nchunk
   RmsKernel full;    // width exactly max_nchunk
 };
 
-#define MBN_RMS_CFG(WPR, ROWS, MAXC)                                               \
-  RmsCfg {                                                                         \
-    64 * (WPR) * (MAXC), WPR, ROWS, MAXC, &rmsnorm_kernel<WPR, ROWS, MAXC, false>, \
-        &rmsnorm_kernel<WPR, ROWS, MAXC, true>                                     \
+#define MBN_RMS_CFG(WPR, ROWS, MAXC, CAP, GROUP)                                        \
+  RmsCfg {                                                                              \
+    64 * (WPR) * (MAXC), WPR, ROWS, MAXC, CAP, GROUP,                                   \
+        &rmsnorm_kernel<WPR, ROWS, MAXC, false>, &rmsnorm_kernel<WPR, ROWS, MAXC, true> \
   }
 
 // Per-width launch table, narrowest first: the first entry whose max_nchunk
 // covers the row is used. Every entry with WPR > 1 starts where the previous
 // entry ends, at or above 64 * WPR chunks, which the parked partial sums need.
+// Entries for N = 4096 ... 32768 were chosen by timing every shape / cap /
+// group combination on MI355X at M*N = 2^26 ... 2^28 (median of 7 repeats);
+// the narrower and wider bands are untuned.
 const RmsCfg kRmsTable[] = {
-    MBN_RMS_CFG(1, 4, 1),   // N <= 512
-    MBN_RMS_CFG(1, 4, 2),   // N <= 1024
-    MBN_RMS_CFG(1, 4, 4),   // N <= 2048
-    MBN_RMS_CFG(4, 1, 2),   // N <= 4096
-    MBN_RMS_CFG(4, 1, 4),   // N <= 8192
-    MBN_RMS_CFG(4, 1, 8),   // N <= 16384
-    MBN_RMS_CFG(8, 1, 8),   // N <= 32768
-    MBN_RMS_CFG(16, 1, 8),  // N <= 65536
+    MBN_RMS_CFG(1, 4, 1, 0, 0),    // N <= 512
+    MBN_RMS_CFG(1, 4, 2, 0, 0),    // N <= 1024
+    MBN_RMS_CFG(1, 4, 4, 0, 0),    // N <= 2048
+    MBN_RMS_CFG(4, 2, 2, 0, 8),    // N <= 4096:  512 threads, 2 rows
+    MBN_RMS_CFG(8, 1, 2, 0, 0),    // N <= 8192:  512 threads
+    MBN_RMS_CFG(2, 2, 16, 2, 4),   // N <= 16384: 256 threads, 2 rows, 2 WGs/CU
+    MBN_RMS_CFG(16, 1, 4, 0, 0),   // N <= 32768: 1024 threads
+    MBN_RMS_CFG(16, 1, 8, 0, 0),   // N <= 65536: 1024 threads
 };
 
 }  // namespace
+
+// Dynamic LDS of a launch: the staged rows, raised to kLdsPerCU / cap when an
+// occupancy cap asks for fewer resident workgroups per CU than LDS would allow.
+size_t rmsnorm_lds_bytes(int rows, int64_t N, int wgs_per_cu) {
+  size_t lds = (size_t)rows * (size_t)N * 2;
+  if (wgs_per_cu > 0) {
+    const size_t cap = (kLdsPerCU / (size_t)wgs_per_cu) & ~(size_t)511;
+    if (cap > lds) lds = cap;
+  }
+  return lds;
+}
 
 hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps,
                           hipStream_t stream) {
@@ -156,12 +192,12 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t M, int6
   if (!cfg) return hipErrorInvalidValue;
   if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant
   const int64_t blocks = (M + cfg->rows - 1) / cfg->rows;
-  const size_t lds = (size_t)cfg->rows * (size_t)N * 2;
+  const size_t lds = rmsnorm_lds_bytes(cfg->rows, N, cfg->wgs_per_cu);
   const float inv_n = 1.0f / (float)N;
   const RmsKernel kernel = (nchunk == cfg->max_nchunk) ? cfg->full : cfg->ragged;
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * cfg->wpr * cfg->rows), lds,
                      stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
-                     static_cast<uint16_t*>(y), M, nchunk, inv_n, eps);
+                     static_cast<uint16_t*>(y), M, nchunk, inv_n, eps, cfg->xcd_group);
   return hipGetLastError();
 }
 
