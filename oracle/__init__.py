@@ -12,6 +12,8 @@ once to bf16 (round to nearest, ties to even) at the end:
 * ``rmsnorm_fwd``       -- row-wise RMSNorm, y = x / sqrt(mean(x^2) + eps) * w
   ("[Inductor] Codegen Gluon", section 3.1, the RMSNorm reference workload:
   an x*x accumulation, then x * rstd * weight).
+* ``add_rmsnorm_fwd``, ``layernorm_fwd``, ``l2norm_fwd`` -- the rest of the
+  reused-input norm family (see ``oracle/norms.py`` for sources and readings).
 * ``qk_norm_rope_fwd``  -- per-head RMSNorm with q/k weights followed by
   rotate-half (NeoX) rotary embedding on the q and k heads of a packed QKV
   tensor, in place, v heads untouched ("[pretuned] Optimize fused_qk_norm_rope
@@ -23,6 +25,7 @@ The oracle shares no code with the HIP path. It takes raw bf16 bit patterns
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
 from .rmsnorm import rmsnorm_fwd, rmsnorm_fwd_f64
+from .norms import add_rmsnorm_fwd, l2norm_fwd, l2norm_fwd_f64, layernorm_fwd, layernorm_fwd_f64
 from .qk_norm_rope import (
     qk_norm_rope_fwd,
     qk_norm_rope_fwd_f64,
@@ -35,6 +38,11 @@ __all__ = [
     "f64_to_bf16_bits",
     "rmsnorm_fwd",
     "rmsnorm_fwd_f64",
+    "add_rmsnorm_fwd",
+    "layernorm_fwd",
+    "layernorm_fwd_f64",
+    "l2norm_fwd",
+    "l2norm_fwd_f64",
     "qk_norm_rope_fwd",
     "qk_norm_rope_fwd_f64",
     "rope_inv_freq",

@@ -120,3 +120,32 @@ def exact_rmsnorm_row(xs, ws, eps) -> list:
             d = decimal.Decimal(num.numerator) / decimal.Decimal(num.denominator) / root
             out.append(Fraction(d))
     return out
+
+
+def _dec(q: Fraction) -> decimal.Decimal:
+    return decimal.Decimal(q.numerator) / decimal.Decimal(q.denominator)
+
+
+def exact_layernorm_row(xs, ws, bs, eps) -> list:
+    """LayerNorm of one row of exact values: exact mean and variance, 70-digit root."""
+    n = len(xs)
+    mu = sum(xs, Fraction(0)) / n
+    var = sum(((x - mu) ** 2 for x in xs), Fraction(0)) / n
+    root = dec_sqrt(var + Fraction(eps))
+    out = []
+    with decimal.localcontext() as ctx:
+        ctx.prec = PREC
+        for x, w, b in zip(xs, ws, bs):
+            out.append(Fraction(_dec((x - mu) * w) / root) + b)
+    return out
+
+
+def exact_l2norm_row(xs, eps) -> list:
+    """x / max(||x||_2, eps) for one row of exact values, 70-digit root."""
+    ss = sum((x * x for x in xs), Fraction(0))
+    root = dec_sqrt(ss)
+    e = decimal.Decimal(Fraction(eps).numerator) / decimal.Decimal(Fraction(eps).denominator)
+    with decimal.localcontext() as ctx:
+        ctx.prec = PREC
+        d = max(root, e)
+        return [Fraction(_dec(x) / d) for x in xs]
