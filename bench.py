@@ -37,7 +37,7 @@ QK_WORKLOAD = "qk_256"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_16384x16384_hbm_traffic.txt")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "memory_bound_normalization_amd", "csrc", f)
-    for f in ("rmsnorm.hip", "device.h")
+    for f in ("rownorm.hip", "device.h")
 ]
 
 
@@ -142,6 +142,32 @@ def suite(steps: int, warmup: int) -> int:
                           "median_us": round(med, 2), "best_us": round(best, 2), "GBps_median": round(b / med / 1e3, 1),
                           "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2)}), flush=True)
         del xs, ys, x0
+        torch.cuda.empty_cache()
+    from workloads import make_norm_family_inputs
+
+    for name in ("rms_8192x8192", "rms_16384x16384"):
+        wl = RMS_WORKLOADS[name]
+        x_bits, w_bits, r_bits, b_bits, eps = make_norm_family_inputs(wl)
+        x, w, r, bb = to_dev(x_bits), to_dev(w_bits), to_dev(r_bits), to_dev(b_bits)
+        mn, n = wl.M * wl.N, wl.N
+        nrot = max(1, -(-(1 << 30) // (2 * mn * 2)))
+        xs = [x] + [x.clone() for _ in range(nrot - 1)]
+        rs = [r] + [r.clone() for _ in range(nrot - 1)]
+        hs = [torch.empty_like(x) for _ in range(nrot)]
+        ys = [torch.empty_like(x) for _ in range(nrot)]
+        cases = [
+            ("add_rmsnorm_fwd", 8 * mn + 2 * n,
+             lambda i: mbn.add_rmsnorm_fwd(xs[i], rs[i], w, h=hs[i], y=ys[i], eps=eps)),
+            ("layernorm_fwd", 4 * mn + 4 * n, lambda i: mbn.layernorm_fwd(xs[i], w, bb, y=ys[i], eps=eps)),
+            ("l2norm_fwd", 4 * mn, lambda i: mbn.l2norm_fwd(xs[i], y=ys[i], eps=1e-12)),
+        ]
+        for kname, b, fn in cases:
+            med, best = timed(fn, nrot)
+            print(json.dumps({"workload": name.replace("rms_", "family_"), "kernel": kname, "M": wl.M, "N": wl.N,
+                              "rotating_sets": nrot, "algorithmic_bytes": b, "median_us": round(med, 2),
+                              "best_us": round(best, 2), "GBps_median": round(b / med / 1e3, 1),
+                              "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2)}), flush=True)
+        del xs, rs, hs, ys, x, r
         torch.cuda.empty_cache()
     for name, wl in QK_WORKLOADS.items():
         qkv_bits, qw_bits, kw_bits, pos, eps, theta = make_qk_inputs(wl)

@@ -74,6 +74,60 @@ MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_
                         float eps, void* stream);
 
 /*
+ * add_rmsnorm_fwd -- residual add fused with RMSNorm (bf16).
+ *
+ * The residual add + norm fusion of "TorchInductor: from ATen IR to Triton
+ * kernel", sections 14.25 and 14.27, on the staged-row kernel of
+ * "[Inductor] Codegen Gluon", section 3.1. The residual stream is bf16, so
+ * the sum is rounded and the norm is taken of what is stored:
+ *     h[i,j] = bf16( x[i,j] + r[i,j] )
+ *     y[i,j] = bf16( h[i,j] / sqrt( (1/N) sum_j h[i,j]^2 + eps ) * w[j] )
+ *
+ *   x, r   device, bf16 [M, N], read only (unless aliased by h or y)
+ *   w      device, bf16 [N]
+ *   h      device, bf16 [M, N], written (the updated residual stream)
+ *   y      device, bf16 [M, N], written
+ *   M, N, eps, stream: as for rmsnorm_fwd.
+ * h and y may each coincide exactly with x or with r (in place); h and y must
+ * not overlap each other, and no other overlap is allowed (MBN_EINVAL). All
+ * five pointers must be 16-byte aligned.
+ */
+MBN_API int add_rmsnorm_fwd(const void* x, const void* r, const void* w, void* h, void* y,
+                            int64_t M, int64_t N, float eps, void* stream);
+
+/*
+ * layernorm_fwd -- row-wise LayerNorm forward (bf16).
+ *
+ * The decomposition of "TorchInductor: from ATen IR to Triton kernel",
+ * section 14.12.2 (var_mean, add eps, rsqrt, subtract, multiply, weight,
+ * bias), and the LayerNorm entry of "[Inductor] Codegen Gluon", section 3.2
+ * (the input is reused by the mean / variance reduction and by the affine
+ * pass). Biased variance:
+ *     mu  = (1/N) sum_j x[i,j],  var = (1/N) sum_j (x[i,j] - mu)^2
+ *     y[i,j] = bf16( (x[i,j] - mu) / sqrt(var + eps) * w[j] + b[j] )
+ * Both moments are taken from the LDS-staged row in fp32 (two passes).
+ *
+ *   x      device, bf16 [M, N];  w, b  device, bf16 [N];  y  device, bf16 [M, N]
+ *   M, N, eps, stream: as for rmsnorm_fwd. y == x allowed; w and b must not
+ *   overlap y. All pointers 16-byte aligned.
+ */
+MBN_API int layernorm_fwd(const void* x, const void* w, const void* b, void* y, int64_t M,
+                          int64_t N, float eps, void* stream);
+
+/*
+ * l2norm_fwd -- row-wise L2 normalization (bf16).
+ *
+ * The L2Norm entry of "[Inductor] Codegen Gluon", section 3.2 (one reduction,
+ * then a scale by the inverse norm), with the usual eps guard:
+ *     y[i,j] = bf16( x[i,j] / max( sqrt( sum_j x[i,j]^2 ), eps ) )
+ * A NaN anywhere in a row makes the row NaN; eps = 0 and a zero row give NaN.
+ *
+ *   x, y   device, bf16 [M, N] (y == x allowed), 16-byte aligned
+ *   M, N, eps, stream: as for rmsnorm_fwd.
+ */
+MBN_API int l2norm_fwd(const void* x, void* y, int64_t M, int64_t N, float eps, void* stream);
+
+/*
  * qk_norm_rope_fwd -- fused per-head RMSNorm + rotary embedding on the q and
  * k heads of a packed QKV tensor, in place.
  *
@@ -87,9 +141,9 @@ MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_
  *     phi_i = positions[t] * theta^(-2i/D)        for i in [0, D/2)
  *     out[i]       = u[i]       * cos(phi_i) - u[i+D/2] * sin(phi_i)
  *     out[i+D/2]   = u[i+D/2]   * cos(phi_i) + u[i]     * sin(phi_i)
- * (rotate-half pairing, as in NeoX-style rotary embeddings). The angles and
- * their sine / cosine are computed in fp64, the rest in fp32, with one
- * rounding to bf16 at the store.
+ * (rotate-half pairing, as in NeoX-style rotary embeddings). The angles, their
+ * sine / cosine and the rotation's products are computed in fp64, the head's
+ * sum of squares and rstd in fp32, with one rounding to bf16 at the store.
  *
  *   qkv        device, bf16 [T, (n_q_heads + 2*n_kv_heads) * head_dim], read
  *              and written in place. Per token: n_q_heads q heads, then

@@ -10,6 +10,10 @@ Functions with the C names take torch tensors:
 * ``rmsnorm_fwd(x, w, y=None, eps=1e-6, stream=None)`` -- x [..., N] bf16,
   w [N] bf16; returns y (allocated like x when not given; ``y is x`` runs in
   place).
+* ``add_rmsnorm_fwd(x, r, w, h=None, y=None, eps=1e-6, stream=None)`` --
+  h = x + r (bf16), y = RMSNorm(h) * w; returns (h, y).
+* ``layernorm_fwd(x, w, b, y=None, eps=1e-5, stream=None)``.
+* ``l2norm_fwd(x, y=None, eps=1e-12, stream=None)``.
 * ``qk_norm_rope_fwd(qkv, q_w, k_w, positions, n_q_heads, n_kv_heads,
   head_dim=128, eps=1e-6, theta=1e6, stream=None)`` -- modifies qkv in place
   and returns it.
@@ -31,6 +35,9 @@ __all__ = [
     "MBN_RMSNORM_MAX_N",
     "MBN_QK_HEAD_DIM",
     "MbnError",
+    "add_rmsnorm_fwd",
+    "l2norm_fwd",
+    "layernorm_fwd",
     "lib",
     "lib_path",
     "mbn_strerror",
@@ -72,6 +79,12 @@ def lib() -> ctypes.CDLL:
         vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
         h.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, vp]
         h.rmsnorm_fwd.restype = ctypes.c_int
+        h.add_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, vp]
+        h.add_rmsnorm_fwd.restype = ctypes.c_int
+        h.layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
+        h.layernorm_fwd.restype = ctypes.c_int
+        h.l2norm_fwd.argtypes = [vp, vp, i64, i64, f32, vp]
+        h.l2norm_fwd.restype = ctypes.c_int
         h.qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, f32, vp]
         h.qk_norm_rope_fwd.restype = ctypes.c_int
         h.mbn_strerror.argtypes = [ctypes.c_int]
@@ -131,6 +144,70 @@ def rmsnorm_fwd(x, w, y=None, eps: float = 1e-6, stream=None):
     )
     if rc != MBN_OK:
         raise MbnError(rc, "rmsnorm_fwd")
+    return y
+
+
+def _rows_of(x, what="x"):
+    n = x.shape[-1] if x.dim() > 0 else 0
+    return (x.numel() // n if n else 0), n
+
+
+def _out_like(x, y, name):
+    import torch
+
+    if y is None:
+        return torch.empty_like(x)
+    _check_bf16_cuda(name, y)
+    if y.shape != x.shape:
+        raise ValueError(f"{name} must have the shape of x")
+    return y
+
+
+def _check_vec(name, v, n):
+    _check_bf16_cuda(name, v)
+    if v.dim() != 1 or v.shape[0] != n:
+        raise ValueError(f"{name} must have shape [{n}], got {tuple(v.shape)}")
+
+
+def add_rmsnorm_fwd(x, r, w, h=None, y=None, eps: float = 1e-6, stream=None):
+    """h = bf16(x + r); y = h * rsqrt(mean(h^2, -1) + eps) * w. Returns (h, y)."""
+    _check_bf16_cuda("x", x)
+    _check_bf16_cuda("r", r)
+    if r.shape != x.shape:
+        raise ValueError("r must have the shape of x")
+    m, n = _rows_of(x)
+    _check_vec("w", w, n)
+    h = _out_like(x, h, "h")
+    y = _out_like(x, y, "y")
+    rc = lib().add_rmsnorm_fwd(x.data_ptr(), r.data_ptr(), w.data_ptr(), h.data_ptr(), y.data_ptr(),
+                               m, n, float(eps), _stream_handle(stream, x.device))
+    if rc != MBN_OK:
+        raise MbnError(rc, "add_rmsnorm_fwd")
+    return h, y
+
+
+def layernorm_fwd(x, w, b, y=None, eps: float = 1e-5, stream=None):
+    """y = (x - mean) * rsqrt(var + eps) * w + b over the last dim of bf16 x."""
+    _check_bf16_cuda("x", x)
+    m, n = _rows_of(x)
+    _check_vec("w", w, n)
+    _check_vec("b", b, n)
+    y = _out_like(x, y, "y")
+    rc = lib().layernorm_fwd(x.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(), m, n,
+                             float(eps), _stream_handle(stream, x.device))
+    if rc != MBN_OK:
+        raise MbnError(rc, "layernorm_fwd")
+    return y
+
+
+def l2norm_fwd(x, y=None, eps: float = 1e-12, stream=None):
+    """y = x / max(||x||_2, eps) over the last dim of bf16 x."""
+    _check_bf16_cuda("x", x)
+    m, n = _rows_of(x)
+    y = _out_like(x, y, "y")
+    rc = lib().l2norm_fwd(x.data_ptr(), y.data_ptr(), m, n, float(eps), _stream_handle(stream, x.device))
+    if rc != MBN_OK:
+        raise MbnError(rc, "l2norm_fwd")
     return y
 
 

@@ -19,23 +19,93 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 bool valid_eps(float eps) { return isfinite(eps) && eps >= 0.0f; }
 
+// Checks shared by the row norms: sizes, eps, and the widths and row counts
+// the kernels handle. Returns MBN_OK when a launch should follow, -1 for an
+// empty input (nothing to do), or a status.
+int check_rows(int64_t M, int64_t N, float eps) {
+  if (M < 0 || N <= 0 || !valid_eps(eps)) return MBN_EINVAL;
+  if (M == 0) return -1;
+  if (N % 8 != 0 || N > MBN_RMSNORM_MAX_N || M > 0x7fffffffLL) return MBN_EUNSUPPORTED;
+  return MBN_OK;
+}
+
+// An output may coincide exactly with an input of the same shape (in place);
+// any other overlap is invalid.
+bool bad_alias(const void* out, const void* in, int64_t bytes) {
+  return out != in && overlap(out, bytes, in, bytes);
+}
+
+int launch(mbn::Norm mode, mbn::RowNormArgs a, void* stream) {
+  const hipError_t err = mbn::launch_rownorm(mode, a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MBN_OK : MBN_EHIP;
+}
+
+mbn::RowNormArgs row_args(const void* x, const void* r, const void* w, const void* b,
+                                 void* h, void* y, int64_t M, int64_t N, float eps) {
+  mbn::RowNormArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.r = static_cast<const uint16_t*>(r);
+  a.w = static_cast<const uint16_t*>(w);
+  a.b = static_cast<const uint16_t*>(b);
+  a.h = static_cast<uint16_t*>(h);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.nchunk = (int)(N / 8);
+  a.eps = eps;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
 
 MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps,
                         void* stream) {
-  if (M < 0 || N <= 0 || !valid_eps(eps)) return MBN_EINVAL;
-  if (M == 0) return MBN_OK;
+  const int st = check_rows(M, N, eps);
+  if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !w || !y) return MBN_EINVAL;
-  if (N % 8 != 0 || N > MBN_RMSNORM_MAX_N || M > 0x7fffffffLL) return MBN_EUNSUPPORTED;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return MBN_EUNSUPPORTED;
   const int64_t bytes = M * N * 2;
-  if (y != x && overlap(x, bytes, y, bytes)) return MBN_EINVAL;
-  if (overlap(w, N * 2, y, bytes)) return MBN_EINVAL;
-  const hipError_t err =
-      mbn::launch_rmsnorm(x, w, y, M, N, eps, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? MBN_OK : MBN_EHIP;
+  if (bad_alias(y, x, bytes) || overlap(w, N * 2, y, bytes)) return MBN_EINVAL;
+  return launch(mbn::Norm::kRms, row_args(x, nullptr, w, nullptr, nullptr, y, M, N, eps), stream);
+}
+
+MBN_API int add_rmsnorm_fwd(const void* x, const void* r, const void* w, void* h, void* y,
+                            int64_t M, int64_t N, float eps, void* stream) {
+  const int st = check_rows(M, N, eps);
+  if (st != MBN_OK) return st < 0 ? MBN_OK : st;
+  if (!x || !r || !w || !h || !y) return MBN_EINVAL;
+  if (!aligned(x, 16) || !aligned(r, 16) || !aligned(w, 16) || !aligned(h, 16) || !aligned(y, 16))
+    return MBN_EUNSUPPORTED;
+  const int64_t bytes = M * N * 2;
+  if (overlap(h, bytes, y, bytes) || bad_alias(h, x, bytes) || bad_alias(h, r, bytes) ||
+      bad_alias(y, x, bytes) || bad_alias(y, r, bytes) || overlap(w, N * 2, h, bytes) ||
+      overlap(w, N * 2, y, bytes))
+    return MBN_EINVAL;
+  return launch(mbn::Norm::kAddRms, row_args(x, r, w, nullptr, h, y, M, N, eps), stream);
+}
+
+MBN_API int layernorm_fwd(const void* x, const void* w, const void* b, void* y, int64_t M,
+                          int64_t N, float eps, void* stream) {
+  const int st = check_rows(M, N, eps);
+  if (st != MBN_OK) return st < 0 ? MBN_OK : st;
+  if (!x || !w || !b || !y) return MBN_EINVAL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(b, 16) || !aligned(y, 16))
+    return MBN_EUNSUPPORTED;
+  const int64_t bytes = M * N * 2;
+  if (bad_alias(y, x, bytes) || overlap(w, N * 2, y, bytes) || overlap(b, N * 2, y, bytes))
+    return MBN_EINVAL;
+  return launch(mbn::Norm::kLayer, row_args(x, nullptr, w, b, nullptr, y, M, N, eps), stream);
+}
+
+MBN_API int l2norm_fwd(const void* x, void* y, int64_t M, int64_t N, float eps, void* stream) {
+  const int st = check_rows(M, N, eps);
+  if (st != MBN_OK) return st < 0 ? MBN_OK : st;
+  if (!x || !y) return MBN_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return MBN_EUNSUPPORTED;
+  if (bad_alias(y, x, M * N * 2)) return MBN_EINVAL;
+  return launch(mbn::Norm::kL2, row_args(x, nullptr, nullptr, nullptr, nullptr, y, M, N, eps),
+                stream);
 }
 
 MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,

@@ -8,8 +8,28 @@
 
 namespace mbn {
 
-hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps,
-                          hipStream_t stream);
+// Row-wise norms served by one kernel template (rownorm.hip).
+enum class Norm : int { kRms = 0, kAddRms = 1, kLayer = 2, kL2 = 3 };
+
+// Kernel arguments of every row norm; unused pointers are null.
+struct RowNormArgs {
+  const uint16_t* x;  // [M, N] bf16 input
+  const uint16_t* r;  // [M, N] bf16 residual (kAddRms)
+  const uint16_t* w;  // [N] bf16 weight (all but kL2)
+  const uint16_t* b;  // [N] bf16 bias (kLayer)
+  uint16_t* h;        // [M, N] bf16 x + r (kAddRms)
+  uint16_t* y;        // [M, N] bf16 output
+  int64_t M;
+  int nchunk;         // N / 8
+  float inv_n;        // 1 / N, set by the launcher
+  float eps;
+  int xcd_group;      // set by the launcher
+};
+
+hipError_t launch_rownorm(Norm mode, RowNormArgs args, hipStream_t stream);
+
+// Dynamic LDS bytes a row-norm launch requests (exposed for tuning tools).
+size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu);
 
 hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
                                const int64_t* positions, int64_t T, int n_q_heads,

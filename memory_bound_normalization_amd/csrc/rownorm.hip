@@ -1,0 +1,314 @@
+// Row-wise norms for gfx950 with each row staged in LDS: RMSNorm, residual add
+// + RMSNorm, LayerNorm and L2Norm.
+//
+// The method ("[Inductor] Codegen Gluon", section 3.1, RMSNorm as the reference
+// workload; section 3.2 for the rest of the family): the input row is needed
+// by the reduction and again by the normalize pass, so each row is read from
+// HBM once into on-chip memory, kept narrow (bf16) there, and widened to fp32
+// only where it is computed on. On gfx950 the row copy is a burst of
+// global_load_lds_dwordx4 (HBM -> LDS without passing through VGPRs), issued
+// for the whole row before the first wait, so a workgroup keeps its entire row
+// in flight.
+//
+// Work decomposition: a workgroup holds ROWS row slots; each row is served by
+// WPR waves (64 * WPR lanes). Lane t of a row owns the 16-byte chunks
+// k = j * (64 * WPR) + t, j < MAXC, and reads back only the chunks it loaded,
+// so the LDS passes need no barrier; the only barriers are the cross-wave
+// steps of the reductions. Those need one float per wave of LDS; rather than
+// allocate it beside the row (LDS is allocated in coarse granules, and 16
+// extra bytes on a 32 KiB row would cost one resident workgroup per CU), each
+// lane keeps its first chunk in VGPRs after the first pass and the wave parks
+// its partial sums in that chunk's LDS slot, which nothing reads afterwards.
+// The LDS footprint is exactly ROWS * N * 2 bytes.
+//
+// Modes (compile time):
+//   kRms     y = x * rstd * w,            rstd = 1/sqrt(mean(x^2) + eps)
+//   kAddRms  h = bf16(x + r) is stored, and replaces x in the LDS row;
+//            y = h * rstd(h) * w          (r is read into VGPRs, used once)
+//   kLayer   y = (x - mu) * rstd * w + b, mu = mean(x), rstd = 1/sqrt(var + eps),
+//            var = mean((x - mu)^2): a second reduction over the staged row
+//   kL2      y = x / max(||x||_2, eps)
+#include "device.h"
+#include "kernels.h"
+
+namespace mbn {
+namespace {
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b mod 8). With xcd_group = G > 0, XCD x is given runs of G consecutive
+// row blocks instead of every 8th one, which changes how the concurrent HBM
+// traffic of the XCDs interleaves; G = 0 keeps the identity. The remap is a
+// bijection on the leading blocks that fill whole groups of 8*G; the rest keep
+// their own index.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nblocks, int group) {
+  if (group <= 0) return b;
+  const int64_t span = 8 * (int64_t)group;
+  if (b >= (nblocks / span) * span) return b;
+  const int64_t xcd = b & 7, i = b >> 3;
+  return (i / group) * span + xcd * group + (i % group);
+}
+
+// Sum of v over the WPR waves of one row. The wave total is parked in float
+// `which` of the wave's first chunk (see the header comment).
+template <int WPR>
+__device__ __forceinline__ float row_sum(float v, u32x4* buf, int t, int wave, int which) {
+  float s = wave_sum(v);
+  if constexpr (WPR > 1) {
+    float* parked = reinterpret_cast<float*>(buf);
+    if ((t & 63) == 0) parked[wave * 256 + which] = s;  // 256 floats = 64 chunks
+    __syncthreads();
+    s = 0.f;
+#pragma unroll
+    for (int i = 0; i < WPR; ++i) s += parked[i * 256 + which];
+  }
+  return s;
+}
+
+// FULL: the row is exactly MAXC chunks per lane (the power-of-two widths), so
+// no chunk needs a bounds predicate.
+template <Norm MODE, int WPR, int ROWS, int MAXC, bool FULL>
+__global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a) {
+  constexpr int TPR = 64 * WPR;  // lanes per row
+  constexpr bool kHasW = MODE != Norm::kL2;
+  constexpr bool kHasB = MODE == Norm::kLayer;
+  constexpr bool kHasR = MODE == Norm::kAddRms;
+  extern __shared__ u32x4 lds_rows[];  // ROWS * nchunk chunks of 16 bytes (or more, see launcher)
+
+  const int nchunk = a.nchunk;
+  const int tid = threadIdx.x;
+  const int slot = tid / TPR;
+  const int t = tid - slot * TPR;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t block = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group);
+  const int64_t row = block * ROWS + slot;
+  const bool live = row < a.M;
+
+  u32x4* buf = lds_rows + (size_t)slot * nchunk;
+  const int64_t row_off = row * nchunk;  // in chunks
+
+  // HBM -> LDS: the whole row, all chunks in flight before any wait.
+  if (live) {
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + row_off;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * TPR + t;
+      if (FULL || k < nchunk) load_lds_16(xrow + k, (lds_void*)(buf + j * TPR + wave * 64));
+    }
+  }
+  // Residual chunks go to VGPRs (consumed once); weights and bias to VGPRs
+  // (L2 hits after the first rows), all overlapping the row copy.
+  u32x4 rreg[kHasR ? MAXC : 1], wreg[kHasW ? MAXC : 1], breg[kHasB ? MAXC : 1];
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * TPR + t;
+    const bool in = FULL || k < nchunk;
+    if constexpr (kHasR)
+      rreg[j] = (live && in) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r) + row_off + k)
+                             : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kHasW) wreg[j] = in ? reinterpret_cast<const u32x4*>(a.w)[k] : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kHasB) breg[j] = in ? reinterpret_cast<const u32x4*>(a.b)[k] : u32x4{0u, 0u, 0u, 0u};
+  }
+  wait_vmem();
+
+  // Pass 1 (from LDS): sum of squares, or sum for LayerNorm. For the residual
+  // add, h = bf16(x + r) is formed here, written back over x in LDS and
+  // stored; the norm is taken of the rounded h.
+  float acc0 = 0.f, acc1 = 0.f;
+  u32x4 first = {0u, 0u, 0u, 0u};  // chunk j = 0, kept for the later passes
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * TPR + t;
+    if (FULL || k < nchunk) {
+      u32x4 v = buf[k];
+      if constexpr (kHasR) {
+        u32x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hv[e] = pack_bf16x2(bf16_lo(v[e]) + bf16_lo(rreg[j][e]), bf16_hi(v[e]) + bf16_hi(rreg[j][e]));
+        v = hv;
+        buf[k] = hv;
+        if (live) store_nt_16(reinterpret_cast<u32x4*>(a.h) + row_off + k, hv);
+      }
+      if (j == 0) first = v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = bf16_lo(v[e]);
+        const float q = bf16_hi(v[e]);
+        if constexpr (MODE == Norm::kLayer) {
+          acc0 += p;
+          acc1 += q;
+        } else {
+          acc0 = __builtin_fmaf(p, p, acc0);
+          acc1 = __builtin_fmaf(q, q, acc1);
+        }
+      }
+    }
+  }
+  // Chunk wave * 64 (lane 0's first chunk) is in VGPRs now and is not read
+  // from LDS again; the launch tables guarantee nchunk >= 64 * WPR, so every
+  // wave owns such a chunk to park its partial sums in.
+  const float s1 = row_sum<WPR>(acc0 + acc1, buf, t, wave, 0);
+
+  float mu = 0.f, scale;
+  if constexpr (MODE == Norm::kLayer) {
+    // Pass 1b (from LDS): centred second moment.
+    mu = s1 * a.inv_n;
+    acc0 = acc1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * TPR + t;
+      if (FULL || k < nchunk) {
+        const u32x4 v = (j == 0) ? first : buf[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = bf16_lo(v[e]) - mu;
+          const float q = bf16_hi(v[e]) - mu;
+          acc0 = __builtin_fmaf(p, p, acc0);
+          acc1 = __builtin_fmaf(q, q, acc1);
+        }
+      }
+    }
+    const float var = row_sum<WPR>(acc0 + acc1, buf, t, wave, 1) * a.inv_n;
+    scale = __builtin_amdgcn_rsqf(var + a.eps);
+  } else if constexpr (MODE == Norm::kL2) {
+    const float nrm = __builtin_sqrtf(s1);
+    scale = 1.0f / ((nrm < a.eps) ? a.eps : nrm);  // NaN norms stay NaN
+  } else {
+    scale = __builtin_amdgcn_rsqf(__builtin_fmaf(s1, a.inv_n, a.eps));
+  }
+
+  // Pass 2 (from LDS): normalize, weight, round to bf16, streaming stores.
+  if (live) {
+    u32x4* yrow = reinterpret_cast<u32x4*>(a.y) + row_off;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * TPR + t;
+      if (FULL || k < nchunk) {
+        const u32x4 v = (j == 0) ? first : buf[k];
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float p = bf16_lo(v[e]), q = bf16_hi(v[e]);
+          if constexpr (MODE == Norm::kLayer) {
+            p = __builtin_fmaf((p - mu) * scale, bf16_lo(wreg[j][e]), bf16_lo(breg[j][e]));
+            q = __builtin_fmaf((q - mu) * scale, bf16_hi(wreg[j][e]), bf16_hi(breg[j][e]));
+          } else if constexpr (MODE == Norm::kL2) {
+            p *= scale;
+            q *= scale;
+          } else {
+            p = (p * scale) * bf16_lo(wreg[j][e]);
+            q = (q * scale) * bf16_hi(wreg[j][e]);
+          }
+          o[e] = pack_bf16x2(p, q);
+        }
+        store_nt_16(yrow + k, o);
+      }
+    }
+  }
+}
+
+typedef void (*RowNormKernel)(RowNormArgs);
+
+// LDS of one CU on gfx950; a workgroup may use all of it.
+constexpr size_t kLdsPerCU = 160 * 1024;
+
+struct RowNormCfg {
+  int max_nchunk;    // widest row (in 16-byte chunks) this entry serves
+  int wpr, rows, maxc;
+  int wgs_per_cu;    // occupancy cap (0 = as many as LDS, waves and VGPRs allow)
+  int xcd_group;     // row blocks per XCD run (0 = dispatch order)
+  RowNormKernel ragged;  // any width up to max_nchunk
+  RowNormKernel full;    // width exactly max_nchunk
+};
+
+#define MBN_CFG(MODE, WPR, ROWS, MAXC, CAP, GROUP)                                   \
+  RowNormCfg {                                                                       \
+    64 * (WPR) * (MAXC), WPR, ROWS, MAXC, CAP, GROUP,                                \
+        &rownorm_kernel<MODE, WPR, ROWS, MAXC, false>,                               \
+        &rownorm_kernel<MODE, WPR, ROWS, MAXC, true>                                 \
+  }
+
+// Per-width launch tables, narrowest first: the first entry whose max_nchunk
+// covers the row is used. Every entry with WPR > 1 starts where the previous
+// entry ends, at or above 64 * WPR chunks, which the parked partial sums need.
+//
+// RMSNorm entries for N = 4096 ... 32768 were chosen by timing every shape /
+// cap / group combination on MI355X at M*N = 2^26 ... 2^28 (median of 7
+// repeats); the other bands and the other modes start from the same shapes,
+// with the 16-chunk entry replaced where its extra weight / residual registers
+// would not fit as well.
+#define MBN_NARROW_BANDS(MODE)                                                     \
+  MBN_CFG(MODE, 1, 4, 1, 0, 0), /* N <= 512 */                                     \
+      MBN_CFG(MODE, 1, 4, 2, 0, 0), /* N <= 1024 */                                \
+      MBN_CFG(MODE, 1, 4, 4, 0, 0), /* N <= 2048 */                                \
+      MBN_CFG(MODE, 4, 2, 2, 0, 8), /* N <= 4096:  512 threads, 2 rows */          \
+      MBN_CFG(MODE, 8, 1, 2, 0, 0)  /* N <= 8192:  512 threads */
+
+#define MBN_WIDE_BANDS(MODE)                                                       \
+  MBN_CFG(MODE, 16, 1, 4, 0, 0),  /* N <= 32768: 1024 threads */                   \
+      MBN_CFG(MODE, 16, 1, 8, 0, 0) /* N <= 65536: 1024 threads */
+
+const RowNormCfg kRmsTable[] = {
+    MBN_NARROW_BANDS(Norm::kRms),
+    MBN_CFG(Norm::kRms, 2, 2, 16, 2, 4),  // N <= 16384: 256 threads, 2 rows, 2 WGs/CU
+    MBN_WIDE_BANDS(Norm::kRms),
+};
+const RowNormCfg kAddRmsTable[] = {
+    MBN_NARROW_BANDS(Norm::kAddRms),
+    MBN_CFG(Norm::kAddRms, 4, 1, 8, 3, 4),  // N <= 16384: 256 threads, 3 WGs/CU
+    MBN_WIDE_BANDS(Norm::kAddRms),
+};
+const RowNormCfg kLayerTable[] = {
+    MBN_NARROW_BANDS(Norm::kLayer),
+    MBN_CFG(Norm::kLayer, 4, 1, 8, 3, 4),  // N <= 16384: 256 threads, 3 WGs/CU
+    MBN_WIDE_BANDS(Norm::kLayer),
+};
+const RowNormCfg kL2Table[] = {
+    MBN_NARROW_BANDS(Norm::kL2),
+    MBN_CFG(Norm::kL2, 2, 2, 16, 2, 4),  // N <= 16384
+    MBN_WIDE_BANDS(Norm::kL2),
+};
+
+template <size_t K>
+const RowNormCfg* pick(const RowNormCfg (&table)[K], int nchunk) {
+  for (const RowNormCfg& c : table)
+    if (nchunk <= c.max_nchunk) return &c;
+  return nullptr;
+}
+
+}  // namespace
+
+// Dynamic LDS of a launch: the staged rows, raised to kLdsPerCU / cap when an
+// occupancy cap asks for fewer resident workgroups per CU than LDS would allow.
+size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu) {
+  size_t lds = (size_t)rows * (size_t)N * 2;
+  if (wgs_per_cu > 0) {
+    const size_t cap = (kLdsPerCU / (size_t)wgs_per_cu) & ~(size_t)511;
+    if (cap > lds) lds = cap;
+  }
+  return lds;
+}
+
+hipError_t launch_rownorm(Norm mode, RowNormArgs args, hipStream_t stream) {
+  const int nchunk = args.nchunk;
+  const RowNormCfg* cfg = nullptr;
+  switch (mode) {
+    case Norm::kRms: cfg = pick(kRmsTable, nchunk); break;
+    case Norm::kAddRms: cfg = pick(kAddRmsTable, nchunk); break;
+    case Norm::kLayer: cfg = pick(kLayerTable, nchunk); break;
+    case Norm::kL2: cfg = pick(kL2Table, nchunk); break;
+  }
+  if (!cfg) return hipErrorInvalidValue;
+  if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant
+  const int64_t blocks = (args.M + cfg->rows - 1) / cfg->rows;
+  const int64_t N = (int64_t)nchunk * 8;
+  const size_t lds = rownorm_lds_bytes(cfg->rows, N, cfg->wgs_per_cu);
+  args.inv_n = 1.0f / (float)N;
+  const RowNormKernel kernel = (nchunk == cfg->max_nchunk) ? cfg->full : cfg->ragged;
+  args.xcd_group = cfg->xcd_group;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * cfg->wpr * cfg->rows), lds, stream,
+                     args);
+  return hipGetLastError();
+}
+
+}  // namespace mbn

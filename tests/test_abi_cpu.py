@@ -36,7 +36,8 @@ def _header_constants():
 
 
 def test_header_declares_the_entry_points():
-    assert set(_declared_functions()) == {"rmsnorm_fwd", "qk_norm_rope_fwd", "mbn_strerror"}
+    assert set(_declared_functions()) == {
+        "rmsnorm_fwd", "add_rmsnorm_fwd", "layernorm_fwd", "l2norm_fwd", "qk_norm_rope_fwd", "mbn_strerror"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -148,3 +149,70 @@ def test_python_binding_refuses_cpu_tensors():
         mbn.rmsnorm_fwd(x, w)
     with pytest.raises(TypeError):
         mbn.rmsnorm_fwd(x.float(), w)
+
+
+B = 0x10000000  # spacing of the fake buffers below
+
+
+@pytest.mark.parametrize(
+    "kw, status",
+    [
+        (dict(M=-1), mbn.MBN_EINVAL),
+        (dict(eps=float("nan")), mbn.MBN_EINVAL),
+        (dict(r=None), mbn.MBN_EINVAL),
+        (dict(h=None), mbn.MBN_EINVAL),
+        (dict(N=20), mbn.MBN_EUNSUPPORTED),
+        (dict(r=FAKE + 1 * B + 8), mbn.MBN_EUNSUPPORTED),
+        (dict(h=FAKE + 4 * B), mbn.MBN_EINVAL),  # h == y
+        (dict(h=FAKE + 4 * B + 64), mbn.MBN_EINVAL),  # h overlaps y
+        (dict(y=FAKE + 16), mbn.MBN_EINVAL),  # y overlaps x partially
+        (dict(h=FAKE + 1 * B + 32), mbn.MBN_EINVAL),  # h overlaps r partially
+        (dict(w=FAKE + 3 * B + 16), mbn.MBN_EINVAL),  # w inside h
+    ],
+)
+def test_add_rmsnorm_rejects(lib, kw, status):
+    a = dict(x=FAKE, r=FAKE + 1 * B, w=FAKE + 2 * B, h=FAKE + 3 * B, y=FAKE + 4 * B, M=4, N=64, eps=1e-6)
+    a.update(kw)
+    assert lib.add_rmsnorm_fwd(a["x"], a["r"], a["w"], a["h"], a["y"], a["M"], a["N"], a["eps"], None) == status
+
+
+@pytest.mark.parametrize(
+    "kw, status",
+    [
+        (dict(N=0), mbn.MBN_EINVAL),
+        (dict(eps=-1.0), mbn.MBN_EINVAL),
+        (dict(b=None), mbn.MBN_EINVAL),
+        (dict(w=None), mbn.MBN_EINVAL),
+        (dict(N=65544), mbn.MBN_EUNSUPPORTED),
+        (dict(b=FAKE + 2 * B + 4), mbn.MBN_EUNSUPPORTED),
+        (dict(b=FAKE + 3 * B + 32), mbn.MBN_EINVAL),  # b inside y
+        (dict(y=FAKE + 496), mbn.MBN_EINVAL),  # y overlaps the tail of x
+    ],
+)
+def test_layernorm_rejects(lib, kw, status):
+    a = dict(x=FAKE, w=FAKE + 1 * B, b=FAKE + 2 * B, y=FAKE + 3 * B, M=4, N=64, eps=1e-5)
+    a.update(kw)
+    assert lib.layernorm_fwd(a["x"], a["w"], a["b"], a["y"], a["M"], a["N"], a["eps"], None) == status
+
+
+@pytest.mark.parametrize(
+    "kw, status",
+    [
+        (dict(M=-3), mbn.MBN_EINVAL),
+        (dict(x=None), mbn.MBN_EINVAL),
+        (dict(eps=float("inf")), mbn.MBN_EINVAL),
+        (dict(N=4), mbn.MBN_EUNSUPPORTED),
+        (dict(y=FAKE + 1 * B + 2), mbn.MBN_EUNSUPPORTED),
+        (dict(y=FAKE + 256), mbn.MBN_EINVAL),
+    ],
+)
+def test_l2norm_rejects(lib, kw, status):
+    a = dict(x=FAKE, y=FAKE + 1 * B, M=4, N=64, eps=1e-12)
+    a.update(kw)
+    assert lib.l2norm_fwd(a["x"], a["y"], a["M"], a["N"], a["eps"], None) == status
+
+
+def test_new_entry_points_empty_is_a_noop(lib):
+    assert lib.add_rmsnorm_fwd(None, None, None, None, None, 0, 64, 1e-6, None) == mbn.MBN_OK
+    assert lib.layernorm_fwd(None, None, None, None, 0, 64, 1e-5, None) == mbn.MBN_OK
+    assert lib.l2norm_fwd(None, None, 0, 64, 1e-12, None) == mbn.MBN_OK

@@ -19,6 +19,9 @@ operator of "[pretuned] Optimize fused_qk_norm_rope on B200", Summary):
   100 in float32 before rounding, w ~ U(0.5, 1.5), eps 1e-6
 * ``rms_16384x16384`` x[16384, 16384] ~ N(0, 1), w ~ U(0.5, 1.5), eps 1e-6
 * ``rms_4096x32768``  x[4096, 32768] ~ 0.5 * N(0, 1), w ~ U(0.5, 1.5), eps 1e-5
+* residual add + RMSNorm, LayerNorm, L2Norm: x and w of an RMSNorm workload,
+  then (same generator, drawn after w) r ~ N(0, 1) [M, N] for the residual
+  add, or b ~ U(-0.5, 0.5) [N] for the LayerNorm bias
 * ``qk_256``          qkv[256, (32 + 8 + 8) * 128] ~ N(0, 1) (v heads too),
   q_w then k_w [128] ~ U(0.5, 1.5), positions 0..255 (int64), eps 1e-6,
   theta 1e6
@@ -37,6 +40,7 @@ __all__ = [
     "QkWorkload",
     "f32_to_bf16_bits",
     "make_rms_inputs",
+    "make_norm_family_inputs",
     "make_qk_inputs",
     "random_bf16_bits",
 ]
@@ -134,6 +138,29 @@ def make_rms_inputs(wl: RmsWorkload, rows: int | None = None):
     if rows is not None:
         x = x[:rows]
     return f32_to_bf16_bits(x), f32_to_bf16_bits(w), wl.eps
+
+
+def make_norm_family_inputs(wl: RmsWorkload, rows: int | None = None):
+    """Inputs for the other row norms on an RMSNorm workload's shape.
+
+    Returns (x_bits, w_bits, r_bits, b_bits, eps): x and w exactly as
+    make_rms_inputs (outlier rows included), then r ~ N(0, 1) [M, N] and
+    b ~ U(-0.5, 0.5) [N] from the same generator.
+    """
+    rng = np.random.default_rng(wl.seed)
+    x = rng.standard_normal((wl.M, wl.N), dtype=np.float32)
+    if wl.x_scale != 1.0:
+        x *= np.float32(wl.x_scale)
+    w = _uniform_f32(rng, wl.N, 0.5, 1.5)
+    if wl.outlier_frac > 0.0:
+        k = int(wl.M * wl.outlier_frac)
+        idx = rng.choice(wl.M, size=k, replace=False)
+        x[idx] *= np.float32(wl.outlier_scale)
+    r = rng.standard_normal((wl.M, wl.N), dtype=np.float32)
+    b = _uniform_f32(rng, wl.N, -0.5, 0.5)
+    if rows is not None:
+        x, r = x[:rows], r[:rows]
+    return f32_to_bf16_bits(x), f32_to_bf16_bits(w), f32_to_bf16_bits(r), f32_to_bf16_bits(b), wl.eps
 
 
 def outlier_rows(wl: RmsWorkload) -> np.ndarray:
