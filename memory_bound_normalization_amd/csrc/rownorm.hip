@@ -48,31 +48,44 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nblocks, int gro
   return (i / group) * span + xcd * group + (i % group);
 }
 
-// Sum of v over the WPR waves of one row. The wave total is parked in float
-// `which` of the wave's first chunk (see the header comment).
-template <int WPR>
-__device__ __forceinline__ float row_sum(float v, u32x4* buf, int t, int wave, int which) {
-  float s = wave_sum(v);
-  if constexpr (WPR > 1) {
-    float* parked = reinterpret_cast<float*>(buf);
-    if ((t & 63) == 0) parked[wave * 256 + which] = s;  // 256 floats = 64 chunks
-    __syncthreads();
-    s = 0.f;
+// Sums of v[rr] over the WPR waves of each of the RPL rows a lane set serves,
+// with one barrier for all of them. The wave total of row rr is parked in
+// float `which` of the wave's first chunk of that row (see the header comment).
+template <int WPR, int RPL>
+__device__ __forceinline__ void rows_sum(float (&v)[RPL], u32x4* buf0, int nchunk, int t, int wave,
+                                         int which) {
 #pragma unroll
-    for (int i = 0; i < WPR; ++i) s += parked[i * 256 + which];
+  for (int rr = 0; rr < RPL; ++rr) v[rr] = wave_sum(v[rr]);
+  if constexpr (WPR > 1) {
+    if ((t & 63) == 0) {
+#pragma unroll
+      for (int rr = 0; rr < RPL; ++rr)
+        reinterpret_cast<float*>(buf0 + (size_t)rr * nchunk)[wave * 256 + which] = v[rr];  // 256 floats = 64 chunks
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      const float* parked = reinterpret_cast<const float*>(buf0 + (size_t)rr * nchunk);
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < WPR; ++i) s += parked[i * 256 + which];
+      v[rr] = s;
+    }
   }
-  return s;
 }
 
-// FULL: the row is exactly MAXC chunks per lane (the power-of-two widths), so
-// no chunk needs a bounds predicate.
-template <Norm MODE, int WPR, int ROWS, int MAXC, bool FULL>
+// One workgroup = ROWS lane sets of 64 * WPR lanes; each lane set serves RPL
+// consecutive rows with the same lanes, so one set of weight (and bias)
+// registers serves RPL rows and the weight is fetched from L2 once per RPL
+// rows. FULL: the row is exactly MAXC chunks per lane (the power-of-two
+// widths), so no chunk needs a bounds predicate.
+template <Norm MODE, int WPR, int ROWS, int RPL, int MAXC, bool FULL>
 __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a) {
-  constexpr int TPR = 64 * WPR;  // lanes per row
+  constexpr int TPR = 64 * WPR;  // lanes per lane set
   constexpr bool kHasW = MODE != Norm::kL2;
   constexpr bool kHasB = MODE == Norm::kLayer;
   constexpr bool kHasR = MODE == Norm::kAddRms;
-  extern __shared__ u32x4 lds_rows[];  // ROWS * nchunk chunks of 16 bytes (or more, see launcher)
+  extern __shared__ u32x4 lds_rows[];  // ROWS * RPL * nchunk chunks (or more, see launcher)
 
   const int nchunk = a.nchunk;
   const int tid = threadIdx.x;
@@ -80,31 +93,37 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
   const int t = tid - slot * TPR;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t block = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group);
-  const int64_t row = block * ROWS + slot;
-  const bool live = row < a.M;
+  const int64_t row0 = (block * ROWS + slot) * RPL;
 
-  u32x4* buf = lds_rows + (size_t)slot * nchunk;
-  const int64_t row_off = row * nchunk;  // in chunks
+  u32x4* buf0 = lds_rows + (size_t)slot * RPL * nchunk;  // row rr at buf0 + rr * nchunk
 
-  // HBM -> LDS: the whole row, all chunks in flight before any wait.
-  if (live) {
-    const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + row_off;
+  // HBM -> LDS: every row of the lane set, all chunks in flight before any wait.
 #pragma unroll
-    for (int j = 0; j < MAXC; ++j) {
-      const int k = j * TPR + t;
-      if (FULL || k < nchunk) load_lds_16(xrow + k, (lds_void*)(buf + j * TPR + wave * 64));
+  for (int rr = 0; rr < RPL; ++rr) {
+    if (row0 + rr < a.M) {
+      const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + (row0 + rr) * nchunk;
+      u32x4* buf = buf0 + (size_t)rr * nchunk;
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int k = j * TPR + t;
+        if (FULL || k < nchunk) load_lds_16(xrow + k, (lds_void*)(buf + j * TPR + wave * 64));
+      }
     }
   }
   // Residual chunks go to VGPRs (consumed once); weights and bias to VGPRs
   // (L2 hits after the first rows), all overlapping the row copy.
-  u32x4 rreg[kHasR ? MAXC : 1], wreg[kHasW ? MAXC : 1], breg[kHasB ? MAXC : 1];
+  u32x4 rreg[kHasR ? RPL : 1][kHasR ? MAXC : 1], wreg[kHasW ? MAXC : 1], breg[kHasB ? MAXC : 1];
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
     const int k = j * TPR + t;
     const bool in = FULL || k < nchunk;
-    if constexpr (kHasR)
-      rreg[j] = (live && in) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r) + row_off + k)
-                             : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kHasR) {
+#pragma unroll
+      for (int rr = 0; rr < RPL; ++rr)
+        rreg[rr][j] = (row0 + rr < a.M && in)
+                          ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r) + (row0 + rr) * nchunk + k)
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
     if constexpr (kHasW) wreg[j] = in ? reinterpret_cast<const u32x4*>(a.w)[k] : u32x4{0u, 0u, 0u, 0u};
     if constexpr (kHasB) breg[j] = in ? reinterpret_cast<const u32x4*>(a.b)[k] : u32x4{0u, 0u, 0u, 0u};
   }
@@ -113,91 +132,118 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
   // Pass 1 (from LDS): sum of squares, or sum for LayerNorm. For the residual
   // add, h = bf16(x + r) is formed here, written back over x in LDS and
   // stored; the norm is taken of the rounded h.
-  float acc0 = 0.f, acc1 = 0.f;
-  u32x4 first = {0u, 0u, 0u, 0u};  // chunk j = 0, kept for the later passes
+  float s1[RPL];
+  u32x4 first[RPL];  // chunk j = 0 of each row, kept for the later passes
 #pragma unroll
-  for (int j = 0; j < MAXC; ++j) {
-    const int k = j * TPR + t;
-    if (FULL || k < nchunk) {
-      u32x4 v = buf[k];
-      if constexpr (kHasR) {
-        u32x4 hv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          hv[e] = pack_bf16x2(bf16_lo(v[e]) + bf16_lo(rreg[j][e]), bf16_hi(v[e]) + bf16_hi(rreg[j][e]));
-        v = hv;
-        buf[k] = hv;
-        if (live) store_nt_16(reinterpret_cast<u32x4*>(a.h) + row_off + k, hv);
-      }
-      if (j == 0) first = v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = bf16_lo(v[e]);
-        const float q = bf16_hi(v[e]);
-        if constexpr (MODE == Norm::kLayer) {
-          acc0 += p;
-          acc1 += q;
-        } else {
-          acc0 = __builtin_fmaf(p, p, acc0);
-          acc1 = __builtin_fmaf(q, q, acc1);
-        }
-      }
-    }
-  }
-  // Chunk wave * 64 (lane 0's first chunk) is in VGPRs now and is not read
-  // from LDS again; the launch tables guarantee nchunk >= 64 * WPR, so every
-  // wave owns such a chunk to park its partial sums in.
-  const float s1 = row_sum<WPR>(acc0 + acc1, buf, t, wave, 0);
-
-  float mu = 0.f, scale;
-  if constexpr (MODE == Norm::kLayer) {
-    // Pass 1b (from LDS): centred second moment.
-    mu = s1 * a.inv_n;
-    acc0 = acc1 = 0.f;
+  for (int rr = 0; rr < RPL; ++rr) {
+    u32x4* buf = buf0 + (size_t)rr * nchunk;
+    const bool live = row0 + rr < a.M;
+    float acc0 = 0.f, acc1 = 0.f;
+    first[rr] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
       const int k = j * TPR + t;
       if (FULL || k < nchunk) {
-        const u32x4 v = (j == 0) ? first : buf[k];
+        u32x4 v = buf[k];
+        if constexpr (kHasR) {
+          u32x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            hv[e] = pack_bf16x2(bf16_lo(v[e]) + bf16_lo(rreg[rr][j][e]),
+                                bf16_hi(v[e]) + bf16_hi(rreg[rr][j][e]));
+          v = hv;
+          buf[k] = hv;
+          if (live) store_nt_16(reinterpret_cast<u32x4*>(a.h) + (row0 + rr) * nchunk + k, hv);
+        }
+        if (j == 0) first[rr] = v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = bf16_lo(v[e]) - mu;
-          const float q = bf16_hi(v[e]) - mu;
-          acc0 = __builtin_fmaf(p, p, acc0);
-          acc1 = __builtin_fmaf(q, q, acc1);
+          const float p = bf16_lo(v[e]);
+          const float q = bf16_hi(v[e]);
+          if constexpr (MODE == Norm::kLayer) {
+            acc0 += p;
+            acc1 += q;
+          } else {
+            acc0 = __builtin_fmaf(p, p, acc0);
+            acc1 = __builtin_fmaf(q, q, acc1);
+          }
         }
       }
     }
-    const float var = row_sum<WPR>(acc0 + acc1, buf, t, wave, 1) * a.inv_n;
-    scale = __builtin_amdgcn_rsqf(var + a.eps);
+    s1[rr] = acc0 + acc1;
+  }
+  // Chunk wave * 64 of each row (lane 0's first chunk) is in VGPRs now and is
+  // not read from LDS again; the launch tables guarantee nchunk >= 64 * WPR, so
+  // every wave owns such a chunk to park its partial sums in.
+  rows_sum<WPR, RPL>(s1, buf0, nchunk, t, wave, 0);
+
+  float mu[RPL], scale[RPL];
+  if constexpr (MODE == Norm::kLayer) {
+    // Pass 1b (from LDS): centred second moment.
+    float s2[RPL];
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      const u32x4* buf = buf0 + (size_t)rr * nchunk;
+      mu[rr] = s1[rr] * a.inv_n;
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int k = j * TPR + t;
+        if (FULL || k < nchunk) {
+          const u32x4 v = (j == 0) ? first[rr] : buf[k];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = bf16_lo(v[e]) - mu[rr];
+            const float q = bf16_hi(v[e]) - mu[rr];
+            acc0 = __builtin_fmaf(p, p, acc0);
+            acc1 = __builtin_fmaf(q, q, acc1);
+          }
+        }
+      }
+      s2[rr] = acc0 + acc1;
+    }
+    rows_sum<WPR, RPL>(s2, buf0, nchunk, t, wave, 1);
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) scale[rr] = __builtin_amdgcn_rsqf(s2[rr] * a.inv_n + a.eps);
   } else if constexpr (MODE == Norm::kL2) {
-    const float nrm = __builtin_sqrtf(s1);
-    scale = 1.0f / ((nrm < a.eps) ? a.eps : nrm);  // NaN norms stay NaN
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      const float nrm = __builtin_sqrtf(s1[rr]);
+      scale[rr] = 1.0f / ((nrm < a.eps) ? a.eps : nrm);  // NaN norms stay NaN
+      mu[rr] = 0.f;
+    }
   } else {
-    scale = __builtin_amdgcn_rsqf(__builtin_fmaf(s1, a.inv_n, a.eps));
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      scale[rr] = __builtin_amdgcn_rsqf(__builtin_fmaf(s1[rr], a.inv_n, a.eps));
+      mu[rr] = 0.f;
+    }
   }
 
   // Pass 2 (from LDS): normalize, weight, round to bf16, streaming stores.
-  if (live) {
-    u32x4* yrow = reinterpret_cast<u32x4*>(a.y) + row_off;
+#pragma unroll
+  for (int rr = 0; rr < RPL; ++rr) {
+    if (row0 + rr >= a.M) continue;
+    const u32x4* buf = buf0 + (size_t)rr * nchunk;
+    u32x4* yrow = reinterpret_cast<u32x4*>(a.y) + (row0 + rr) * nchunk;
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
       const int k = j * TPR + t;
       if (FULL || k < nchunk) {
-        const u32x4 v = (j == 0) ? first : buf[k];
+        const u32x4 v = (j == 0) ? first[rr] : buf[k];
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float p = bf16_lo(v[e]), q = bf16_hi(v[e]);
           if constexpr (MODE == Norm::kLayer) {
-            p = __builtin_fmaf((p - mu) * scale, bf16_lo(wreg[j][e]), bf16_lo(breg[j][e]));
-            q = __builtin_fmaf((q - mu) * scale, bf16_hi(wreg[j][e]), bf16_hi(breg[j][e]));
+            p = __builtin_fmaf((p - mu[rr]) * scale[rr], bf16_lo(wreg[j][e]), bf16_lo(breg[j][e]));
+            q = __builtin_fmaf((q - mu[rr]) * scale[rr], bf16_hi(wreg[j][e]), bf16_hi(breg[j][e]));
           } else if constexpr (MODE == Norm::kL2) {
-            p *= scale;
-            q *= scale;
+            p *= scale[rr];
+            q *= scale[rr];
           } else {
-            p = (p * scale) * bf16_lo(wreg[j][e]);
-            q = (q * scale) * bf16_hi(wreg[j][e]);
+            p = (p * scale[rr]) * bf16_lo(wreg[j][e]);
+            q = (q * scale[rr]) * bf16_hi(wreg[j][e]);
           }
           o[e] = pack_bf16x2(p, q);
         }
@@ -214,65 +260,78 @@ constexpr size_t kLdsPerCU = 160 * 1024;
 
 struct RowNormCfg {
   int max_nchunk;    // widest row (in 16-byte chunks) this entry serves
-  int wpr, rows, maxc;
+  bool exact;        // serves only rows of exactly max_nchunk chunks
+  int wpr, rows, rpl, maxc;
   int wgs_per_cu;    // occupancy cap (0 = as many as LDS, waves and VGPRs allow)
   int xcd_group;     // row blocks per XCD run (0 = dispatch order)
   RowNormKernel ragged;  // any width up to max_nchunk
   RowNormKernel full;    // width exactly max_nchunk
 };
 
-#define MBN_CFG(MODE, WPR, ROWS, MAXC, CAP, GROUP)                                   \
-  RowNormCfg {                                                                       \
-    64 * (WPR) * (MAXC), WPR, ROWS, MAXC, CAP, GROUP,                                \
-        &rownorm_kernel<MODE, WPR, ROWS, MAXC, false>,                               \
-        &rownorm_kernel<MODE, WPR, ROWS, MAXC, true>                                 \
+#define MBN_CFG_(MODE, EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP)                     \
+  RowNormCfg {                                                                      \
+    64 * (WPR) * (MAXC), EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP,                   \
+        &rownorm_kernel<MODE, WPR, ROWS, RPL, MAXC, false>,                         \
+        &rownorm_kernel<MODE, WPR, ROWS, RPL, MAXC, true>                           \
   }
+// serves every width up to 64 * WPR * MAXC chunks (down to the previous entry)
+#define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, false, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+// serves only the width 64 * WPR * MAXC chunks; a later entry covers the band
+#define MBN_CFG_EXACT(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, true, WPR, ROWS, RPL, MAXC, CAP, GROUP)
 
-// Per-width launch tables, narrowest first: the first entry whose max_nchunk
-// covers the row is used. Every entry with WPR > 1 starts where the previous
-// entry ends, at or above 64 * WPR chunks, which the parked partial sums need.
+// Per-width launch tables, narrowest first: the first entry that serves the
+// row width is used. Every entry with WPR > 1 serves only widths of at least
+// 64 * WPR chunks, which the parked partial sums need (exact entries, or the
+// previous band ending at or above 64 * WPR).
 //
-// RMSNorm entries for N = 4096 ... 32768 were chosen by timing every shape /
-// cap / group combination on MI355X at M*N = 2^26 ... 2^28 (median of 7
-// repeats); the other bands and the other modes start from the same shapes,
-// with the 16-chunk entry replaced where its extra weight / residual registers
-// would not fit as well.
+// Entries for N = 4096 ... 32768 were chosen by timing every shape / cap /
+// group combination on MI355X at M*N = 2^26 ... 2^28 (median of 5-7 repeats);
+// the narrower and wider bands are untuned.
 #define MBN_NARROW_BANDS(MODE)                                                     \
-  MBN_CFG(MODE, 1, 4, 1, 0, 0), /* N <= 512 */                                     \
-      MBN_CFG(MODE, 1, 4, 2, 0, 0), /* N <= 1024 */                                \
-      MBN_CFG(MODE, 1, 4, 4, 0, 0), /* N <= 2048 */                                \
-      MBN_CFG(MODE, 4, 2, 2, 0, 8), /* N <= 4096:  512 threads, 2 rows */          \
-      MBN_CFG(MODE, 8, 1, 2, 0, 0)  /* N <= 8192:  512 threads */
+  MBN_CFG(MODE, 1, 4, 1, 1, 0, 0),     /* N <= 512 */                              \
+      MBN_CFG(MODE, 1, 4, 1, 2, 0, 0), /* N <= 1024 */                             \
+      MBN_CFG(MODE, 1, 4, 1, 4, 0, 0)  /* N <= 2048 */
 
 #define MBN_WIDE_BANDS(MODE)                                                       \
-  MBN_CFG(MODE, 16, 1, 4, 0, 0),  /* N <= 32768: 1024 threads */                   \
-      MBN_CFG(MODE, 16, 1, 8, 0, 0) /* N <= 65536: 1024 threads */
+  MBN_CFG(MODE, 16, 1, 1, 4, 0, 0),    /* N <= 32768: 1024 threads */              \
+      MBN_CFG(MODE, 16, 1, 1, 8, 0, 0) /* N <= 65536: 1024 threads */
 
 const RowNormCfg kRmsTable[] = {
     MBN_NARROW_BANDS(Norm::kRms),
-    MBN_CFG(Norm::kRms, 2, 2, 16, 2, 4),  // N <= 16384: 256 threads, 2 rows, 2 WGs/CU
+    MBN_CFG(Norm::kRms, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows, 4 WGs/CU
+    MBN_CFG(Norm::kRms, 4, 1, 2, 4, 0, 0),   // N <= 8192:  256 threads x 2 rows
+    MBN_CFG(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
     MBN_WIDE_BANDS(Norm::kRms),
 };
 const RowNormCfg kAddRmsTable[] = {
     MBN_NARROW_BANDS(Norm::kAddRms),
-    MBN_CFG(Norm::kAddRms, 4, 1, 8, 3, 4),  // N <= 16384: 256 threads, 3 WGs/CU
+    MBN_CFG(Norm::kAddRms, 4, 2, 1, 2, 0, 8),          // N <= 4096:  2 x 256 threads
+    MBN_CFG_EXACT(Norm::kAddRms, 16, 1, 1, 1, 4, 64),  // N == 8192: 1024 threads, 4 WGs/CU
+    MBN_CFG(Norm::kAddRms, 8, 1, 1, 2, 0, 0),          // N <= 8192:  512 threads
+    MBN_CFG(Norm::kAddRms, 2, 1, 1, 16, 2, 4),         // N <= 16384: 128 threads, 2 WGs/CU
     MBN_WIDE_BANDS(Norm::kAddRms),
 };
 const RowNormCfg kLayerTable[] = {
     MBN_NARROW_BANDS(Norm::kLayer),
-    MBN_CFG(Norm::kLayer, 4, 1, 8, 3, 4),  // N <= 16384: 256 threads, 3 WGs/CU
-    MBN_WIDE_BANDS(Norm::kLayer),
+    MBN_CFG(Norm::kLayer, 4, 2, 1, 2, 0, 8),   // N <= 4096:  2 x 256 threads
+    MBN_CFG(Norm::kLayer, 4, 1, 2, 4, 0, 0),   // N <= 8192:  256 threads x 2 rows
+    MBN_CFG(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
+    MBN_CFG(Norm::kLayer, 4, 1, 1, 16, 0, 2),  // N <= 32768: 256 threads
+    MBN_CFG(Norm::kLayer, 16, 1, 1, 8, 0, 0),  // N <= 65536
 };
 const RowNormCfg kL2Table[] = {
     MBN_NARROW_BANDS(Norm::kL2),
-    MBN_CFG(Norm::kL2, 2, 2, 16, 2, 4),  // N <= 16384
+    MBN_CFG(Norm::kL2, 4, 2, 1, 2, 0, 8),          // N <= 4096:  2 x 256 threads
+    MBN_CFG_EXACT(Norm::kL2, 16, 1, 1, 1, 0, 0),   // N == 8192: 1024 threads
+    MBN_CFG(Norm::kL2, 8, 1, 1, 2, 0, 0),          // N <= 8192:  512 threads
+    MBN_CFG(Norm::kL2, 4, 1, 1, 8, 3, 4),          // N <= 16384: 256 threads, 3 WGs/CU
     MBN_WIDE_BANDS(Norm::kL2),
 };
 
 template <size_t K>
 const RowNormCfg* pick(const RowNormCfg (&table)[K], int nchunk) {
   for (const RowNormCfg& c : table)
-    if (nchunk <= c.max_nchunk) return &c;
+    if (c.exact ? nchunk == c.max_nchunk : nchunk <= c.max_nchunk) return &c;
   return nullptr;
 }
 
@@ -300,9 +359,10 @@ hipError_t launch_rownorm(Norm mode, RowNormArgs args, hipStream_t stream) {
   }
   if (!cfg) return hipErrorInvalidValue;
   if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant
-  const int64_t blocks = (args.M + cfg->rows - 1) / cfg->rows;
+  const int rows_per_wg = cfg->rows * cfg->rpl;
+  const int64_t blocks = (args.M + rows_per_wg - 1) / rows_per_wg;
   const int64_t N = (int64_t)nchunk * 8;
-  const size_t lds = rownorm_lds_bytes(cfg->rows, N, cfg->wgs_per_cu);
+  const size_t lds = rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
   args.inv_n = 1.0f / (float)N;
   const RowNormKernel kernel = (nchunk == cfg->max_nchunk) ? cfg->full : cfg->ragged;
   args.xcd_group = cfg->xcd_group;

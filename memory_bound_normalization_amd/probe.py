@@ -71,7 +71,7 @@ def _per_kernel(d: str, counter: str):
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
     res = {"rmsnorm": [], "copy": []}
     for (_, name), v in sorted(acc.items(), key=lambda kv: int(kv[0][0])):
-        if "rmsnorm_kernel" in name:
+        if "rownorm_kernel" in name:
             res["rmsnorm"].append(v)
         elif "copy" in name.lower() or "elementwise" in name.lower():
             res["copy"].append(v)

@@ -1,0 +1,56 @@
+"""Host-side checks of the row-norm launch tables in rownorm.hip (no GPU):
+bands cover every width up to MBN_RMSNORM_MAX_N in increasing order, every
+entry with several waves per row serves only widths of at least 64 * WPR chunks
+(each wave parks its partial sum in its own first chunk), workgroups stay within
+1024 threads and the staged rows within the 160 KiB of LDS of a CU."""
+
+import os
+import re
+
+import pytest
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "memory_bound_normalization_amd", "csrc", "rownorm.hip")
+CFG = r"MBN_CFG(_EXACT)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
+
+
+def _tables():
+    s = open(SRC).read()
+    macros = {}
+    for name in ("MBN_NARROW_BANDS", "MBN_WIDE_BANDS"):
+        body = s[s.index("#define " + name):].split("\n\n")[0]
+        macros[name] = re.findall(CFG, body)
+    out = {}
+    for tname, body in re.findall(r"const RowNormCfg (k\w+)\[\] = \{(.*?)\n\};", s, re.S):
+        entries = []
+        for line in body.split("\n"):
+            line = line.strip()
+            found = macros.get(line.split("(")[0], None) if line.startswith("MBN_") and "BANDS" in line else None
+            for e in (found if found is not None else re.findall(CFG, line)):
+                exact, *nums = e
+                entries.append((exact == "_EXACT", *map(int, nums)))
+        out[tname] = entries
+    return out
+
+
+TABLES = _tables()
+
+
+def test_all_four_tables_found():
+    assert set(TABLES) == {"kRmsTable", "kAddRmsTable", "kLayerTable", "kL2Table"}
+
+
+@pytest.mark.parametrize("name", sorted(TABLES))
+def test_table_invariants(name):
+    prev = 0
+    for exact, wpr, rows, rpl, maxc, cap, grp in TABLES[name]:
+        top = 64 * wpr * maxc
+        lowest = top if exact else prev + 1
+        assert wpr == 1 or lowest >= 64 * wpr, (name, wpr, maxc)
+        assert 64 * wpr * rows <= 1024
+        assert rows * rpl * top * 16 <= 160 * 1024
+        assert cap >= 0 and grp >= 0
+        if not exact:
+            assert top > prev
+            prev = top
+    assert prev * 8 == 65536  # the widest band reaches MBN_RMSNORM_MAX_N
