@@ -7,12 +7,15 @@
 // are applied with no trip through memory, and each half is stored once. There
 // is no store followed by a reload, hence no barrier between them.
 //
-// Mapping: one wave per (token, group of 4 heads). A head of 128 bf16 is 16
-// lanes x 16 bytes, i.e. one DPP row, so the head's sum of squares is a
-// 16-lane DPP reduction and the rotary partner of lane j (the chunk 64
+// Mapping: one workgroup per token. A head of 128 bf16 is 16 lanes x 16
+// bytes, i.e. one DPP row, so a wave holds 4 heads, the head's sum of squares
+// is a 16-lane DPP reduction and the rotary partner of lane j (the chunk 64
 // elements away) is lane j ^ 8 of the same row, fetched with row_ror:8.
-// The wave first evaluates the token's 64 angles in fp64 (one per lane) and
-// shares cos / sin through 1 KiB of LDS.
+// Wave 0 evaluates the token's 64 angles in fp64 (one per lane) once and
+// shares cos / sin through 1 KiB of LDS; the waves then step over the token's
+// heads 4 at a time. Few tokens: one wave per 4 heads (a single step, lowest
+// latency). Many tokens: 4 waves per token, looping, so the per-token angle
+// work is not repeated in every wave.
 //
 // Precision: x * w is exact in fp32 (two 8-bit significands). The rotation
 // x*w*cos -/+ x'*w'*sin is formed in fp64 because outputs of near-cancelling
@@ -29,31 +32,29 @@ constexpr int kHeadDim = 128;
 constexpr int kHalf = kHeadDim / 2;
 constexpr int kHeadsPerWave = 4;
 
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(1024)
 qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w,
                     const uint16_t* __restrict__ k_w, const int64_t* __restrict__ positions,
-                    int n_q, int n_heads, int groups, int64_t row_stride, float eps,
-                    double theta) {
+                    int n_q, int n_heads, int64_t row_stride, float eps, double theta) {
   __shared__ double2 cs[kHalf];  // (cos, sin) of the token's 64 angles
 
-  const int lane = threadIdx.x;
-  const int64_t token = blockIdx.x / groups;
-  const int group = (int)(blockIdx.x - token * groups);
-  const int head = group * kHeadsPerWave + (lane >> 4);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int waves = blockDim.x >> 6;
+  const int64_t token = blockIdx.x;
   const int j = lane & 15;  // 16-byte chunk of the head: elements [8j, 8j + 8)
-  const bool live = head < n_heads;
+  uint16_t* const trow = qkv + token * row_stride;
 
-  // Issue the head load first so it overlaps the angle computation.
-  uint16_t* hp = qkv + token * row_stride + (int64_t)head * kHeadDim + 8 * j;
-  const uint16_t* wp = (head < n_q ? q_w : k_w) + 8 * j;
+  // Issue the first head load before the angle computation so the two overlap.
+  int head = wave * kHeadsPerWave + (lane >> 4);
   u32x4 xv = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-  if (live) {
-    xv = *reinterpret_cast<const u32x4*>(hp);
-    wv = *reinterpret_cast<const u32x4*>(wp);
+  if (head < n_heads) {
+    xv = *reinterpret_cast<const u32x4*>(trow + (int64_t)head * kHeadDim + 8 * j);
+    wv = *reinterpret_cast<const u32x4*>((head < n_q ? q_w : k_w) + 8 * j);
   }
 
   // Angle i = lane: phi = pos * theta^(-2i/D), fp64.
-  {
+  if (wave == 0) {
     const double pos = (double)positions[token];
     const double inv_freq = pow(theta, -(double)(2 * lane) / (double)kHeadDim);
     double s, c;
@@ -62,39 +63,52 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
   }
   __syncthreads();
 
-  float x[8], xw[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = bf16_lo(xv[e]);
-    x[2 * e + 1] = bf16_hi(xv[e]);
-    xw[2 * e] = x[2 * e] * bf16_lo(wv[e]);
-    xw[2 * e + 1] = x[2 * e + 1] * bf16_hi(wv[e]);
-  }
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
-  const float ss = row16_sum(acc);
-  const float rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, 1.0f / kHeadDim, eps));
-
-  float xwp[8];  // partner chunk (64 elements away), same head
-#pragma unroll
-  for (int e = 0; e < 8; ++e) xwp[e] = dpp<kDppRowRor8>(xw[e]);
-
-  // first half: o_i = u_i cos - u_{i+64} sin; second half: o = u cos + u_{i-64} sin
   const double sgn = (j < 8) ? -1.0 : 1.0;
   const int i0 = 8 * (j & 7);
-  float o[8];
+  // Every lane of a wave runs the same number of steps (the DPP exchanges need
+  // the whole row of 16 lanes): the loop bound is the wave's first head.
+  for (int base = wave * kHeadsPerWave; base < n_heads; base += waves * kHeadsPerWave) {
+    head = base + (lane >> 4);
+    const bool live = head < n_heads;
+    if (base != wave * kHeadsPerWave && live) {
+      xv = *reinterpret_cast<const u32x4*>(trow + (int64_t)head * kHeadDim + 8 * j);
+      wv = *reinterpret_cast<const u32x4*>((head < n_q ? q_w : k_w) + 8 * j);
+    } else if (!live) {
+      xv = u32x4{0u, 0u, 0u, 0u};
+      wv = u32x4{0u, 0u, 0u, 0u};
+    }
+    float x[8], xw[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const double2 a = cs[i0 + e];
-    const double r = __builtin_fma((double)xwp[e], sgn * a.y, (double)xw[e] * a.x);
-    o[e] = (float)r * rstd;
-  }
-  if (live) {
-    u32x4 out;
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(xv[e]);
+      x[2 * e + 1] = bf16_hi(xv[e]);
+      xw[2 * e] = x[2 * e] * bf16_lo(wv[e]);
+      xw[2 * e + 1] = x[2 * e + 1] * bf16_hi(wv[e]);
+    }
+    float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
-    *reinterpret_cast<u32x4*>(hp) = out;
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
+    const float ss = row16_sum(acc);
+    const float rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, 1.0f / kHeadDim, eps));
+
+    float xwp[8];  // partner chunk (64 elements away), same head
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xwp[e] = dpp<kDppRowRor8>(xw[e]);
+
+    // first half: o_i = u_i cos - u_{i+64} sin; second half: o = u cos + u_{i-64} sin
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double2 a = cs[i0 + e];
+      const double r = __builtin_fma((double)xwp[e], sgn * a.y, (double)xw[e] * a.x);
+      o[e] = (float)r * rstd;
+    }
+    if (live) {
+      u32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+      *reinterpret_cast<u32x4*>(trow + (int64_t)head * kHeadDim + 8 * j) = out;
+    }
   }
 }
 
@@ -105,13 +119,15 @@ hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
                                int n_kv_heads, float eps, float theta, hipStream_t stream) {
   const int n_heads = n_q_heads + n_kv_heads;
   const int groups = (n_heads + kHeadsPerWave - 1) / kHeadsPerWave;
-  const int64_t blocks = T * groups;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  // Up to 1024 tokens: one wave per 4-head group (at most 16 waves); beyond,
+  // 4 waves per token. Chosen on MI355X for 32 q + 8 k heads (T = 256: 3.4 us
+  // vs 4.1 us with 4 waves; T = 65536: 249 us vs 363 us with 10 waves).
+  const int waves = (T <= 1024) ? (groups < 16 ? groups : 16) : (groups < 4 ? groups : 4);
   const int64_t row_stride = (int64_t)(n_q_heads + 2 * n_kv_heads) * kHeadDim;
-  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)blocks), dim3(64), 0, stream,
+  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)T), dim3(64 * waves), 0, stream,
                      static_cast<uint16_t*>(qkv), static_cast<const uint16_t*>(q_w),
-                     static_cast<const uint16_t*>(k_w), positions, n_q_heads, n_heads, groups,
-                     row_stride, eps, (double)theta);
+                     static_cast<const uint16_t*>(k_w), positions, n_q_heads, n_heads, row_stride,
+                     eps, (double)theta);
   return hipGetLastError();
 }
 

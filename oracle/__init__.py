@@ -11,7 +11,7 @@ once to bf16 (round to nearest, ties to even) at the end:
 
 * ``rmsnorm_fwd``       -- row-wise RMSNorm, y = x / sqrt(mean(x^2) + eps) * w
   ("[Inductor] Codegen Gluon", section 3.1, the RMSNorm reference workload:
-  an x*x accumulation, then x * rstd * weight).
+  a sum of x squared, then x scaled by rstd and the weight).
 * ``add_rmsnorm_fwd``, ``layernorm_fwd``, ``l2norm_fwd`` -- the rest of the
   reused-input norm family (see ``oracle/norms.py`` for sources and readings).
 * ``qk_norm_rope_fwd``  -- per-head RMSNorm with q/k weights followed by

@@ -20,8 +20,8 @@ values:
     store bf16(o) in place of x (one rounding)
 
 Readings where the page is silent (each listed in the design notes):
-* The rotary formula is not written on the page; "the two rotary halves" and a
-  NeoX-style rotary embedding are read as the rotate-half pairing (i, i + D/2)
+* The rotary formula is not written on the page; loading each head as its two
+  rotary halves, with a NeoX-style rotary embedding, is read as the rotate-half pairing (i, i + D/2)
   with inverse frequencies theta^(-2i/D).
 * One weight vector of length D per kind (q or k), shared by every head of that
   kind.

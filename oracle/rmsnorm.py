@@ -1,8 +1,9 @@
 """RMSNorm forward, plain definition in float64 (test infrastructure only).
 
 Source: "[Inductor] Codegen Gluon", section 3.1 ("MVP: RMSNorm with
-TMA-Cached Reused Input"). The reference workload reads x twice: once to
-accumulate x*x, once to form x * rstd * weight. Written out per row i:
+TMA-Cached Reused Input"). The reference workload needs x twice: for the sum
+of its squares, and again when it is scaled by rstd and the weight. Written
+out per row i:
 
     ms_i   = (1/N) * sum_j x_ij^2          mean over the N columns
     rstd_i = 1 / sqrt(ms_i + eps)          eps inside the square root

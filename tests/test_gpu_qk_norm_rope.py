@@ -54,14 +54,19 @@ def test_workload():
     assert np.array_equal(got, again), "not deterministic"
 
 
-@pytest.mark.parametrize("hq,hk", [(1, 0), (0, 1), (3, 1), (5, 2), (4, 4), (32, 8), (64, 8), (2, 1)])
+@pytest.mark.parametrize("hq,hk", [(1, 0), (0, 1), (3, 1), (5, 2), (4, 4), (32, 8), (64, 8), (2, 1), (60, 9)])
 def test_head_counts(hq, hk):
     _check(19, hq, hk, seed=hq * 100 + hk)
 
 
-@pytest.mark.parametrize("T", [1, 2, 255, 257, 1000])
+@pytest.mark.parametrize("T", [1, 2, 255, 257, 1000, 1024, 1025, 3000])
 def test_token_counts(T):
     _check(T, 8, 2, seed=T)
+
+
+def test_many_tokens_few_and_many_heads():
+    _check(2048, 2, 1, seed=16, pos=np.arange(2048) * 3)
+    _check(1500, 64, 8, seed=17)
 
 
 def test_positions():

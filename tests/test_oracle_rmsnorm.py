@@ -2,7 +2,7 @@
 
 The pages print no worked numeric example, so the oracle is pinned by what the
 mathematics fixes ("[Inductor] Codegen Gluon", section 3.1, defines the
-computation: an x*x accumulation, then x * rstd * weight).
+computation: the sum of squares of x, then x scaled by rstd and the weight).
 """
 
 import math
