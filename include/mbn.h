@@ -164,6 +164,29 @@ MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,
                              int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
                              void* stream);
 
+/*
+ * qk_norm_rope_partial_fwd -- qk_norm_rope_fwd with a rotary part shorter than
+ * the head.
+ *
+ * "[pretuned] Optimize fused_qk_norm_rope on B200", Summary: with a partial
+ * rotary dimension the full-head normalization is kept, since the values past
+ * the rotary part must still be normalized. With R = rotary_dim:
+ *     rstd and u[d] = x[d] * rstd * w[d] over the whole head (d < D)
+ *     phi_i = positions[t] * theta^(-2i/R)        for i in [0, R/2)
+ *     out[i]     = u[i]     * cos(phi_i) - u[i+R/2] * sin(phi_i)
+ *     out[i+R/2] = u[i+R/2] * cos(phi_i) + u[i]     * sin(phi_i)
+ *     out[d]     = u[d]                            for d in [R, D)
+ * rotary_dim == head_dim is exactly qk_norm_rope_fwd.
+ *
+ *   rotary_dim  even, 0 < rotary_dim <= head_dim (else MBN_EINVAL); the
+ *               kernels handle multiples of 16 (else MBN_EUNSUPPORTED)
+ *   every other argument as for qk_norm_rope_fwd.
+ */
+MBN_API int qk_norm_rope_partial_fwd(void* qkv, const void* q_w, const void* k_w,
+                                     const int64_t* positions, int64_t T, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
+                                     float eps, float theta, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 MBN_API const char* mbn_strerror(int status);
 

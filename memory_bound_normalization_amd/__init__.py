@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         h.l2norm_fwd.restype = ctypes.c_int
         h.qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, f32, vp]
         h.qk_norm_rope_fwd.restype = ctypes.c_int
+        h.qk_norm_rope_partial_fwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, f32, f32, vp]
+        h.qk_norm_rope_partial_fwd.restype = ctypes.c_int
         h.mbn_strerror.argtypes = [ctypes.c_int]
         h.mbn_strerror.restype = ctypes.c_char_p
         _LIB = h
@@ -213,9 +215,13 @@ def l2norm_fwd(x, y=None, eps: float = 1e-12, stream=None):
 
 def qk_norm_rope_fwd(
     qkv, q_w, k_w, positions, n_q_heads: int, n_kv_heads: int, head_dim: int = MBN_QK_HEAD_DIM,
-    eps: float = 1e-6, theta: float = 1e6, stream=None,
+    eps: float = 1e-6, theta: float = 1e6, stream=None, rotary_dim: int | None = None,
 ):
-    """In-place per-head RMSNorm (q_w / k_w) + rotate-half RoPE on qkv [T, (Hq+2Hkv)*D]."""
+    """In-place per-head RMSNorm (q_w / k_w) + rotate-half RoPE on qkv [T, (Hq+2Hkv)*D].
+
+    ``rotary_dim`` (default: head_dim) rotates only the first rotary_dim values
+    of each head (qk_norm_rope_partial_fwd); the rest are normalized only.
+    """
     import torch
 
     _check_bf16_cuda("qkv", qkv)
@@ -228,11 +234,20 @@ def qk_norm_rope_fwd(
         raise ValueError("qkv must have shape [T, (n_q_heads + 2 * n_kv_heads) * head_dim]")
     if positions.numel() != t:
         raise ValueError("positions must have T entries")
-    rc = lib().qk_norm_rope_fwd(
-        qkv.data_ptr(), q_w.data_ptr(), k_w.data_ptr(), positions.data_ptr(), t,
-        int(n_q_heads), int(n_kv_heads), int(head_dim), float(eps), float(theta),
-        _stream_handle(stream, qkv.device),
-    )
+    if rotary_dim is None:
+        rc = lib().qk_norm_rope_fwd(
+            qkv.data_ptr(), q_w.data_ptr(), k_w.data_ptr(), positions.data_ptr(), t,
+            int(n_q_heads), int(n_kv_heads), int(head_dim), float(eps), float(theta),
+            _stream_handle(stream, qkv.device),
+        )
+        where = "qk_norm_rope_fwd"
+    else:
+        rc = lib().qk_norm_rope_partial_fwd(
+            qkv.data_ptr(), q_w.data_ptr(), k_w.data_ptr(), positions.data_ptr(), t,
+            int(n_q_heads), int(n_kv_heads), int(head_dim), int(rotary_dim), float(eps),
+            float(theta), _stream_handle(stream, qkv.device),
+        )
+        where = "qk_norm_rope_partial_fwd"
     if rc != MBN_OK:
-        raise MbnError(rc, "qk_norm_rope_fwd")
+        raise MbnError(rc, where)
     return qkv

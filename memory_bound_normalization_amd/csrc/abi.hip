@@ -108,14 +108,15 @@ MBN_API int l2norm_fwd(const void* x, void* y, int64_t M, int64_t N, float eps, 
                 stream);
 }
 
-MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,
-                             const int64_t* positions, int64_t T, int32_t n_q_heads,
-                             int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
-                             void* stream) {
+MBN_API int qk_norm_rope_partial_fwd(void* qkv, const void* q_w, const void* k_w,
+                                     const int64_t* positions, int64_t T, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
+                                     float eps, float theta, void* stream) {
   if (T < 0 || n_q_heads < 0 || n_kv_heads < 0 || head_dim <= 0 || (head_dim & 1))
     return MBN_EINVAL;
+  if (rotary_dim <= 0 || (rotary_dim & 1) || rotary_dim > head_dim) return MBN_EINVAL;
   if (!valid_eps(eps) || !isfinite(theta) || !(theta > 0.0f)) return MBN_EINVAL;
-  if (head_dim != MBN_QK_HEAD_DIM) return MBN_EUNSUPPORTED;
+  if (head_dim != MBN_QK_HEAD_DIM || rotary_dim % 16 != 0) return MBN_EUNSUPPORTED;
   const int64_t heads = (int64_t)n_q_heads + n_kv_heads;
   if (T == 0 || heads == 0) return MBN_OK;
   if (!qkv || !positions || (n_q_heads > 0 && !q_w) || (n_kv_heads > 0 && !k_w))
@@ -133,9 +134,18 @@ MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,
       (n_kv_heads > 0 && overlap(k_w, wbytes, qkv, span)) || overlap(positions, T * 8, qkv, span))
     return MBN_EINVAL;
   const hipError_t err = mbn::launch_qk_norm_rope(qkv, q_w, k_w, positions, T, n_q_heads,
-                                                  n_kv_heads, eps, theta,
+                                                  n_kv_heads, rotary_dim, eps, theta,
                                                   static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MBN_OK : MBN_EHIP;
+}
+
+MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,
+                             const int64_t* positions, int64_t T, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
+                             void* stream) {
+  if (head_dim <= 0 || (head_dim & 1)) return MBN_EINVAL;
+  return qk_norm_rope_partial_fwd(qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads, head_dim,
+                                  head_dim, eps, theta, stream);
 }
 
 MBN_API const char* mbn_strerror(int status) {

@@ -31,8 +31,10 @@ hipError_t launch_rownorm(Norm mode, RowNormArgs args, hipStream_t stream);
 // Dynamic LDS bytes a row-norm launch requests (exposed for tuning tools).
 size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu);
 
+// rotary_dim: a multiple of 16 in [16, 128]; 128 is the full-rotary case.
 hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
                                const int64_t* positions, int64_t T, int n_q_heads,
-                               int n_kv_heads, float eps, float theta, hipStream_t stream);
+                               int n_kv_heads, int rotary_dim, float eps, float theta,
+                               hipStream_t stream);
 
 }  // namespace mbn

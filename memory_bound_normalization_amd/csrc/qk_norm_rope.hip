@@ -17,6 +17,12 @@
 // latency). Many tokens: 4 waves per token, looping, so the per-token angle
 // work is not repeated in every wave.
 //
+// Partial rotary (rotary_dim R < 128, a multiple of 16; the page keeps the
+// full-head norm for it since the tail must still be normalized): the RMS and
+// the weight cover the whole head, chunks [0, R/8) rotate with the partner
+// chunk R/16 away (fetched with ds_bpermute instead of row_ror:8) and angles
+// pos * theta^(-2i/R), and chunks [R/8, 16) are stored normalized only.
+//
 // Precision: x * w is exact in fp32 (two 8-bit significands). The rotation
 // x*w*cos -/+ x'*w'*sin is formed in fp64 because outputs of near-cancelling
 // pairs are judged on an absolute floor of about 1e-6, which fp32 products of
@@ -35,8 +41,9 @@ constexpr int kHeadsPerWave = 4;
 __global__ void __launch_bounds__(1024)
 qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w,
                     const uint16_t* __restrict__ k_w, const int64_t* __restrict__ positions,
-                    int n_q, int n_heads, int64_t row_stride, float eps, double theta) {
-  __shared__ double2 cs[kHalf];  // (cos, sin) of the token's 64 angles
+                    int n_q, int n_heads, int64_t row_stride, int rot_chunks, float eps,
+                    double theta) {
+  __shared__ double2 cs[kHalf];  // (cos, sin) of the token's rot_chunks * 8 angles
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -53,18 +60,26 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
     wv = *reinterpret_cast<const u32x4*>((head < n_q ? q_w : k_w) + 8 * j);
   }
 
-  // Angle i = lane: phi = pos * theta^(-2i/D), fp64.
-  if (wave == 0) {
+  // Angle i = lane: phi = pos * theta^(-2i/R), fp64, R = rotary dimension.
+  const int half = 8 * rot_chunks;  // R / 2
+  if (wave == 0 && lane < half) {
     const double pos = (double)positions[token];
-    const double inv_freq = pow(theta, -(double)(2 * lane) / (double)kHeadDim);
+    const double inv_freq = pow(theta, -(double)(2 * lane) / (double)(2 * half));
     double s, c;
     sincos(pos * inv_freq, &s, &c);
     cs[lane] = make_double2(c, s);
   }
   __syncthreads();
 
-  const double sgn = (j < 8) ? -1.0 : 1.0;
-  const int i0 = 8 * (j & 7);
+  // Chunk j < rot_chunks pairs with j + rot_chunks (sign -), chunk j in
+  // [rot_chunks, 2 rot_chunks) with j - rot_chunks (sign +); later chunks are
+  // not rotated.
+  const bool full = rot_chunks == 8;
+  const bool rotated = j < 2 * rot_chunks;
+  const bool first_half = j < rot_chunks;
+  const double sgn = first_half ? -1.0 : 1.0;
+  const int i0 = 8 * (first_half ? j : j - rot_chunks);
+  const int partner = (lane & ~15) | (rotated ? (first_half ? j + rot_chunks : j - rot_chunks) : j);
   // Every lane of a wave runs the same number of steps (the DPP exchanges need
   // the whole row of 16 lanes): the loop bound is the wave's first head.
   for (int base = wave * kHeadsPerWave; base < n_heads; base += waves * kHeadsPerWave) {
@@ -91,17 +106,28 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
     const float ss = row16_sum(acc);
     const float rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, 1.0f / kHeadDim, eps));
 
-    float xwp[8];  // partner chunk (64 elements away), same head
+    float xwp[8];  // partner chunk (R/2 elements away), same head
+    if (full) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xwp[e] = dpp<kDppRowRor8>(xw[e]);
+      for (int e = 0; e < 8; ++e) xwp[e] = dpp<kDppRowRor8>(xw[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        xwp[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(partner << 2, __float_as_int(xw[e])));
+    }
 
-    // first half: o_i = u_i cos - u_{i+64} sin; second half: o = u cos + u_{i-64} sin
+    // first half: o_i = u_i cos - u_{i+R/2} sin; second half: o = u cos + u_{i-R/2} sin
     float o[8];
+    if (rotated) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double2 a = cs[i0 + e];
-      const double r = __builtin_fma((double)xwp[e], sgn * a.y, (double)xw[e] * a.x);
-      o[e] = (float)r * rstd;
+      for (int e = 0; e < 8; ++e) {
+        const double2 a = cs[i0 + e];
+        const double r = __builtin_fma((double)xwp[e], sgn * a.y, (double)xw[e] * a.x);
+        o[e] = (float)r * rstd;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = xw[e] * rstd;
     }
     if (live) {
       u32x4 out;
@@ -116,7 +142,8 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
 
 hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
                                const int64_t* positions, int64_t T, int n_q_heads,
-                               int n_kv_heads, float eps, float theta, hipStream_t stream) {
+                               int n_kv_heads, int rotary_dim, float eps, float theta,
+                               hipStream_t stream) {
   const int n_heads = n_q_heads + n_kv_heads;
   const int groups = (n_heads + kHeadsPerWave - 1) / kHeadsPerWave;
   // Up to 1024 tokens: one wave per 4-head group (at most 16 waves); beyond,
@@ -127,7 +154,7 @@ hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
   hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)T), dim3(64 * waves), 0, stream,
                      static_cast<uint16_t*>(qkv), static_cast<const uint16_t*>(q_w),
                      static_cast<const uint16_t*>(k_w), positions, n_q_heads, n_heads, row_stride,
-                     eps, (double)theta);
+                     rotary_dim / 16, eps, (double)theta);
   return hipGetLastError();
 }
 

@@ -30,6 +30,10 @@ Readings where the page is silent (each listed in the design notes):
 * Layout per token: [q_0 .. q_{n_q-1} | k_0 .. k_{n_kv-1} | v_0 .. v_{n_kv-1}],
   each head D contiguous values; the v heads are neither read nor written.
 * eps and theta are taken as the float32 values the C interface receives.
+* Partial rotary (rotary_dim R < D; the page keeps the full-head norm for it
+  because the tail past the rotary part must still be normalized): the RMS and
+  the weight cover all D values; the rotation acts on u[0:R] alone, pairing
+  (i, i + R/2) with angles p_t * theta^(-2i/R); u[R:D] is stored unrotated.
 """
 
 from __future__ import annotations
@@ -66,9 +70,12 @@ def rope_rotate_neox(u: np.ndarray, pos, theta: float) -> np.ndarray:
 
 def qk_norm_rope_fwd_f64(
     qkv_bits, q_w_bits, k_w_bits, positions, n_q_heads: int, n_kv_heads: int,
-    head_dim: int, eps: float, theta: float,
+    head_dim: int, eps: float, theta: float, rotary_dim: int | None = None,
 ) -> np.ndarray:
     """Unrounded float64 outputs of the q and k heads, shape [T, n_q + n_kv, D]."""
+    rot = head_dim if rotary_dim is None else rotary_dim
+    if rot % 2 or not 0 < rot <= head_dim:
+        raise ValueError("rotary_dim must be even and in (0, head_dim]")
     qkv_bits = np.asarray(qkv_bits, dtype=np.uint16)
     t = qkv_bits.shape[0]
     h = n_q_heads + n_kv_heads
@@ -86,19 +93,25 @@ def qk_norm_rope_fwd_f64(
         ms = np.mean(x * x, axis=-1)
         rstd = 1.0 / np.sqrt(ms + eps64)
         u = x * rstd[..., None] * w[None, :, :]
-        return rope_rotate_neox(u, pos[:, None], theta64)
+        rotated = rope_rotate_neox(u[..., :rot], pos[:, None], theta64)
+        return np.concatenate([rotated, u[..., rot:]], axis=-1)
 
 
 def qk_norm_rope_fwd(
     qkv_bits, q_w_bits, k_w_bits, positions, n_q_heads: int, n_kv_heads: int,
-    head_dim: int, eps: float, theta: float,
+    head_dim: int, eps: float, theta: float, rotary_dim: int | None = None,
 ) -> np.ndarray:
-    """Return a copy of qkv (bf16 bits) with q and k heads normalized and rotated."""
+    """Return a copy of qkv (bf16 bits) with q and k heads normalized and rotated.
+
+    ``rotary_dim`` (default: head_dim) rotates only the first rotary_dim values
+    of each head; the rest are normalized and weighted only.
+    """
     qkv_bits = np.asarray(qkv_bits, dtype=np.uint16)
     t = qkv_bits.shape[0]
     h = n_q_heads + n_kv_heads
     o = qk_norm_rope_fwd_f64(
-        qkv_bits, q_w_bits, k_w_bits, positions, n_q_heads, n_kv_heads, head_dim, eps, theta
+        qkv_bits, q_w_bits, k_w_bits, positions, n_q_heads, n_kv_heads, head_dim, eps, theta,
+        rotary_dim,
     )
     out = qkv_bits.copy()
     out[:, : h * head_dim] = f64_to_bf16_bits(o).reshape(t, h * head_dim)

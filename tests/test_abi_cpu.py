@@ -37,7 +37,8 @@ def _header_constants():
 
 def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {
-        "rmsnorm_fwd", "add_rmsnorm_fwd", "layernorm_fwd", "l2norm_fwd", "qk_norm_rope_fwd", "mbn_strerror"}
+        "rmsnorm_fwd", "add_rmsnorm_fwd", "layernorm_fwd", "l2norm_fwd", "qk_norm_rope_fwd",
+        "qk_norm_rope_partial_fwd", "mbn_strerror"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -216,3 +217,19 @@ def test_new_entry_points_empty_is_a_noop(lib):
     assert lib.add_rmsnorm_fwd(None, None, None, None, None, 0, 64, 1e-6, None) == mbn.MBN_OK
     assert lib.layernorm_fwd(None, None, None, None, 0, 64, 1e-5, None) == mbn.MBN_OK
     assert lib.l2norm_fwd(None, None, 0, 64, 1e-12, None) == mbn.MBN_OK
+
+
+@pytest.mark.parametrize(
+    "rot, status",
+    [(0, mbn.MBN_EINVAL), (-16, mbn.MBN_EINVAL), (33, mbn.MBN_EINVAL), (144, mbn.MBN_EINVAL),
+     (24, mbn.MBN_EUNSUPPORTED), (8, mbn.MBN_EUNSUPPORTED), (100, mbn.MBN_EUNSUPPORTED)],
+)
+def test_qk_partial_rejects(lib, rot, status):
+    args = (FAKE, FAKE + 0x10000000, FAKE + 0x10001000, FAKE + 0x10002000, 4, 4, 2, 128, rot, 1e-6, 1e6, None)
+    assert lib.qk_norm_rope_partial_fwd(*args) == status
+
+
+def test_qk_partial_other_checks_still_apply(lib):
+    # a valid rotary_dim with an invalid head_dim / null pointer is still rejected before any HIP call
+    assert lib.qk_norm_rope_partial_fwd(FAKE, FAKE, FAKE, FAKE, 4, 4, 2, 64, 32, 1e-6, 1e6, None) == mbn.MBN_EUNSUPPORTED
+    assert lib.qk_norm_rope_partial_fwd(None, FAKE, FAKE, FAKE, 4, 4, 2, 128, 64, 1e-6, 1e6, None) == mbn.MBN_EINVAL

@@ -17,12 +17,12 @@ torch = pytest.importorskip("torch")
 D = 128
 
 
-def _run(qkv_bits, q_w_bits, k_w_bits, pos, hq, hk, eps, theta):
+def _run(qkv_bits, q_w_bits, k_w_bits, pos, hq, hk, eps, theta, rotary_dim=None):
     qkv = to_gpu_bf16(qkv_bits)
     q_w = to_gpu_bf16(q_w_bits)
     k_w = to_gpu_bf16(k_w_bits)
     p = torch.from_numpy(np.asarray(pos, dtype=np.int64)).cuda()
-    mbn.qk_norm_rope_fwd(qkv, q_w, k_w, p, hq, hk, D, eps=eps, theta=theta)
+    mbn.qk_norm_rope_fwd(qkv, q_w, k_w, p, hq, hk, D, eps=eps, theta=theta, rotary_dim=rotary_dim)
     torch.cuda.synchronize()
     return from_gpu_bf16(qkv)
 
@@ -118,3 +118,23 @@ def test_empty_and_errors():
     with pytest.raises(mbn.MbnError) as e:
         mbn.qk_norm_rope_fwd(qkv, w64, w64, p, 4, 1, 64)
     assert e.value.status == mbn.MBN_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("rot", [16, 32, 48, 64, 96, 112, 128])
+@pytest.mark.parametrize("T", [7, 1500])
+def test_partial_rotary(rot, T):
+    print(f"[qk] partial rotary_dim={rot} T={T}", flush=True)
+    rng = np.random.default_rng(rot * 10 + T)
+    hq, hk = 5, 2
+    qkv = random_bf16_bits(rng, (T, (hq + 2 * hk) * D))
+    q_w = random_bf16_bits(rng, (D,), lo=0.5, hi=1.5)
+    k_w = random_bf16_bits(rng, (D,), lo=0.5, hi=1.5)
+    pos = rng.integers(0, 100000, size=T)
+    got = _run(qkv, q_w, k_w, pos, hq, hk, 1e-6, 1e6, rotary_dim=rot)
+    ref = oracle_qk(qkv, q_w, k_w, pos, hq, hk, D, 1e-6, 1e6, rotary_dim=rot)
+    nk = (hq + hk) * D
+    assert np.array_equal(got[:, nk:], qkv[:, nk:]), "v heads changed"
+    assert_parity(got, ref, f"partial rot={rot} T={T}")
+    if rot == 128:
+        full = _run(qkv, q_w, k_w, pos, hq, hk, 1e-6, 1e6)
+        assert np.array_equal(full, got), "rotary_dim = head_dim differs from the full-rotary entry point"

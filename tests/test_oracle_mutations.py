@@ -32,6 +32,8 @@ MUTATIONS = [
      "np.tile(k_w, (n_q_heads, 1)), np.tile(q_w, (n_kv_heads, 1))"),
     ("qk_norm_rope.py", "ms = np.mean(x * x, axis=-1)", "ms = np.mean(x * x)"),
     ("qk_norm_rope.py", "rstd = 1.0 / np.sqrt(ms + eps64)", "rstd = 1.0 / np.sqrt(ms)"),
+    ("qk_norm_rope.py", "rotated = rope_rotate_neox(u[..., :rot], pos[:, None], theta64)",
+     "rotated = rope_rotate_neox(u, pos[:, None], theta64)[..., :rot]"),
     ("norms.py", "return h_bits, rmsnorm_fwd(h_bits, w_bits, eps)", "return h_bits, rmsnorm_fwd(x_bits, w_bits, eps)"),
     ("norms.py", "h_bits = f64_to_bf16_bits(x + r)", "h_bits = f64_to_bf16_bits(x + r * 0.5)"),
     ("norms.py", "var = np.sum(d * d, axis=1) / n", "var = np.sum(d * d, axis=1) / max(n - 1, 1)"),

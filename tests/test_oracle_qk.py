@@ -222,3 +222,52 @@ def test_workload_shape_and_runs():
     out = qk_norm_rope_fwd(qkv, q_w, k_w, pos, 32, 8, 128, eps, theta)
     assert np.array_equal(out[:, 5120:], qkv[:, 5120:])
     assert np.all(np.isfinite(bf16_bits_to_f64(out)))
+
+
+# ---------------- partial rotary ----------------
+
+@pytest.mark.parametrize("rot", [16, 32, 64, 96])
+def test_partial_rotary_tail_is_per_head_rmsnorm(rot):
+    """The tail past rotary_dim is the plain weighted per-head RMSNorm."""
+    rng = np.random.default_rng(60 + rot)
+    t, hq, hk = 5, 3, 2
+    qkv, q_w, k_w = _small_case(rng, t, hq, hk)
+    pos = np.arange(t, dtype=np.int64) * 37 + 3
+    out = qk_norm_rope_fwd(qkv, q_w, k_w, pos, hq, hk, D, 1e-6, 1e6, rotary_dim=rot)
+    heads = qkv[:, : (hq + hk) * D].reshape(t, hq + hk, D)
+    oh = out[:, : (hq + hk) * D].reshape(t, hq + hk, D)
+    ref_q = rmsnorm_fwd(heads[:, :hq].reshape(-1, D), q_w, 1e-6).reshape(t, hq, D)
+    ref_k = rmsnorm_fwd(heads[:, hq:].reshape(-1, D), k_w, 1e-6).reshape(t, hk, D)
+    assert np.array_equal(oh[:, :hq, rot:], ref_q[:, :, rot:])
+    assert np.array_equal(oh[:, hq:, rot:], ref_k[:, :, rot:])
+    # the rotary part differs from the plain norm (positions are not 0) ...
+    assert not np.array_equal(oh[:, :hq, :rot], ref_q[:, :, :rot])
+    # ... and preserves the norm of each rotated pair
+    f = qk_norm_rope_fwd_f64(qkv, q_w, k_w, pos, hq, hk, D, 1e-6, 1e6, rotary_dim=rot)
+    u = qk_norm_rope_fwd_f64(qkv, q_w, k_w, np.zeros(t, np.int64), hq, hk, D, 1e-6, 1e6, rotary_dim=rot)
+    h2 = rot // 2
+    assert np.allclose(f[..., :h2] ** 2 + f[..., h2:rot] ** 2, u[..., :h2] ** 2 + u[..., h2:rot] ** 2,
+                       rtol=1e-13, atol=1e-15)
+
+
+def test_partial_rotary_uses_its_own_frequencies():
+    """Pairing (i, i + R/2) with angle p * theta^(-2i/R), via the matrix form at D = R."""
+    rng = np.random.default_rng(70)
+    rot = 32
+    qkv, q_w, k_w = _small_case(rng, 3, 1, 0)
+    pos = np.array([0, 5, 211], dtype=np.int64)
+    f = qk_norm_rope_fwd_f64(qkv, q_w, k_w, pos, 1, 0, D, 1e-6, 1e6, rotary_dim=rot)
+    u = qk_norm_rope_fwd_f64(qkv, q_w, k_w, np.zeros(3, np.int64), 1, 0, D, 1e-6, 1e6, rotary_dim=rot)
+    for ti in range(3):
+        r = _rope_matrix(float(pos[ti]), rot, 1e6)
+        assert np.allclose(f[ti, 0, :rot], r @ u[ti, 0, :rot], rtol=0, atol=1e-13)
+        assert np.array_equal(f[ti, 0, rot:], u[ti, 0, rot:])
+
+
+def test_full_rotary_dim_is_the_default():
+    rng = np.random.default_rng(71)
+    qkv, q_w, k_w = _small_case(rng, 4, 2, 1)
+    pos = np.arange(4, dtype=np.int64) * 9
+    a = qk_norm_rope_fwd(qkv, q_w, k_w, pos, 2, 1, D, 1e-6, 1e6)
+    b = qk_norm_rope_fwd(qkv, q_w, k_w, pos, 2, 1, D, 1e-6, 1e6, rotary_dim=D)
+    assert np.array_equal(a, b)
