@@ -19,11 +19,12 @@ once to bf16 (round to nearest, ties to even) at the end:
   tensor, in place, v heads untouched ("[pretuned] Optimize fused_qk_norm_rope
   on B200", Summary).
 
-The oracle shares no code with the HIP path. It takes raw bf16 bit patterns
-(numpy ``uint16``) and returns raw bf16 bit patterns.
+The oracle shares no code with the HIP path. It takes raw 16-bit patterns
+(numpy ``uint16``; bf16 by default, fp16 with ``dtype="f16"``) and returns raw
+16-bit patterns of the same type.
 """
 
-from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+from .bf16 import bf16_bits_to_f64, f16_bits_to_f64, f64_to_bf16_bits, f64_to_f16_bits, narrow, widen
 from .rmsnorm import rmsnorm_fwd, rmsnorm_fwd_f64
 from .norms import add_rmsnorm_fwd, l2norm_fwd, l2norm_fwd_f64, layernorm_fwd, layernorm_fwd_f64
 from .qk_norm_rope import (
@@ -36,6 +37,10 @@ from .qk_norm_rope import (
 __all__ = [
     "bf16_bits_to_f64",
     "f64_to_bf16_bits",
+    "f16_bits_to_f64",
+    "f64_to_f16_bits",
+    "narrow",
+    "widen",
     "rmsnorm_fwd",
     "rmsnorm_fwd_f64",
     "add_rmsnorm_fwd",

@@ -20,33 +20,35 @@ TEST INFRASTRUCTURE ONLY.
   a scale by the inverse norm. Reading: the eps guard of the usual
   normalize-by-L2 operator, y_ij = RNE_bf16(x_ij / max(sqrt(sum_j x_ij^2), eps)).
 
-All arithmetic in float64 from the exact bf16 inputs; eps is the float32 value
-the C interface receives; one rounding to bf16 per output.
+All arithmetic in float64 from the exact 16-bit inputs (bf16, or fp16 for the
+fp16 variants); eps is the float32 value the C interface receives; one rounding
+to the storage type per output.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+from .bf16 import narrow, widen
 from .rmsnorm import rmsnorm_fwd
 
 
-def add_rmsnorm_fwd(x_bits, r_bits, w_bits, eps: float):
-    """Return (h_bits, y_bits): h = bf16(x + r), y = RMSNorm(h) * w in bf16."""
-    x = bf16_bits_to_f64(x_bits)
-    r = bf16_bits_to_f64(r_bits)
+def add_rmsnorm_fwd(x_bits, r_bits, w_bits, eps: float, dtype: str = "bf16"):
+    """Return (h_bits, y_bits): h = round(x + r), y = RMSNorm(h) * w, both rounded
+    to the storage type ``dtype``."""
+    x = widen(x_bits, dtype)
+    r = widen(r_bits, dtype)
     if x.shape != r.shape:
         raise ValueError("x and r must have the same shape")
     with np.errstate(all="ignore"):
-        h_bits = f64_to_bf16_bits(x + r)
-    return h_bits, rmsnorm_fwd(h_bits, w_bits, eps)
+        h_bits = narrow(x + r, dtype)
+    return h_bits, rmsnorm_fwd(h_bits, w_bits, eps, dtype)
 
 
-def layernorm_fwd_f64(x_bits, w_bits, b_bits, eps: float) -> np.ndarray:
-    x = bf16_bits_to_f64(x_bits)
-    w = bf16_bits_to_f64(w_bits)
-    b = bf16_bits_to_f64(b_bits)
+def layernorm_fwd_f64(x_bits, w_bits, b_bits, eps: float, dtype: str = "bf16") -> np.ndarray:
+    x = widen(x_bits, dtype)
+    w = widen(w_bits, dtype)
+    b = widen(b_bits, dtype)
     if x.ndim != 2 or w.shape != (x.shape[1],) or b.shape != (x.shape[1],):
         raise ValueError("expected x [M, N], w [N], b [N]")
     n = x.shape[1]
@@ -61,13 +63,13 @@ def layernorm_fwd_f64(x_bits, w_bits, b_bits, eps: float) -> np.ndarray:
         return d * rstd[:, None] * w[None, :] + b[None, :]
 
 
-def layernorm_fwd(x_bits, w_bits, b_bits, eps: float) -> np.ndarray:
-    """LayerNorm of bf16 x [M, N] with bf16 weight and bias [N]; bf16 bits out."""
-    return f64_to_bf16_bits(layernorm_fwd_f64(x_bits, w_bits, b_bits, eps))
+def layernorm_fwd(x_bits, w_bits, b_bits, eps: float, dtype: str = "bf16") -> np.ndarray:
+    """LayerNorm of x [M, N] with weight and bias [N]; 16-bit patterns of ``dtype`` out."""
+    return narrow(layernorm_fwd_f64(x_bits, w_bits, b_bits, eps, dtype), dtype)
 
 
-def l2norm_fwd_f64(x_bits, eps: float) -> np.ndarray:
-    x = bf16_bits_to_f64(x_bits)
+def l2norm_fwd_f64(x_bits, eps: float, dtype: str = "bf16") -> np.ndarray:
+    x = widen(x_bits, dtype)
     if x.ndim != 2:
         raise ValueError("expected x [M, N]")
     if x.size == 0:
@@ -78,6 +80,6 @@ def l2norm_fwd_f64(x_bits, eps: float) -> np.ndarray:
         return x / np.maximum(nrm, eps64)[:, None]
 
 
-def l2norm_fwd(x_bits, eps: float) -> np.ndarray:
-    """Row-wise x / max(||x||_2, eps) of bf16 x [M, N]; bf16 bits out."""
-    return f64_to_bf16_bits(l2norm_fwd_f64(x_bits, eps))
+def l2norm_fwd(x_bits, eps: float, dtype: str = "bf16") -> np.ndarray:
+    """Row-wise x / max(||x||_2, eps) of x [M, N]; 16-bit patterns of ``dtype`` out."""
+    return narrow(l2norm_fwd_f64(x_bits, eps, dtype), dtype)

@@ -40,7 +40,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+from .bf16 import narrow, widen
 
 
 def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
@@ -70,7 +70,7 @@ def rope_rotate_neox(u: np.ndarray, pos, theta: float) -> np.ndarray:
 
 def qk_norm_rope_fwd_f64(
     qkv_bits, q_w_bits, k_w_bits, positions, n_q_heads: int, n_kv_heads: int,
-    head_dim: int, eps: float, theta: float, rotary_dim: int | None = None,
+    head_dim: int, eps: float, theta: float, rotary_dim: int | None = None, dtype: str = "bf16",
 ) -> np.ndarray:
     """Unrounded float64 outputs of the q and k heads, shape [T, n_q + n_kv, D]."""
     rot = head_dim if rotary_dim is None else rotary_dim
@@ -82,9 +82,9 @@ def qk_norm_rope_fwd_f64(
     d = head_dim
     if qkv_bits.shape[1] != (n_q_heads + 2 * n_kv_heads) * d:
         raise ValueError("qkv row width does not match the head counts")
-    x = bf16_bits_to_f64(qkv_bits[:, : h * d]).reshape(t, h, d)
-    q_w = bf16_bits_to_f64(q_w_bits)
-    k_w = bf16_bits_to_f64(k_w_bits)
+    x = widen(qkv_bits[:, : h * d], dtype).reshape(t, h, d)
+    q_w = widen(q_w_bits, dtype)
+    k_w = widen(k_w_bits, dtype)
     w = np.concatenate([np.tile(q_w, (n_q_heads, 1)), np.tile(k_w, (n_kv_heads, 1))], axis=0)
     eps64 = float(np.float32(eps))
     theta64 = float(np.float32(theta))
@@ -99,9 +99,9 @@ def qk_norm_rope_fwd_f64(
 
 def qk_norm_rope_fwd(
     qkv_bits, q_w_bits, k_w_bits, positions, n_q_heads: int, n_kv_heads: int,
-    head_dim: int, eps: float, theta: float, rotary_dim: int | None = None,
+    head_dim: int, eps: float, theta: float, rotary_dim: int | None = None, dtype: str = "bf16",
 ) -> np.ndarray:
-    """Return a copy of qkv (bf16 bits) with q and k heads normalized and rotated.
+    """Return a copy of qkv (16-bit patterns) with q and k heads normalized and rotated.
 
     ``rotary_dim`` (default: head_dim) rotates only the first rotary_dim values
     of each head; the rest are normalized and weighted only.
@@ -111,8 +111,8 @@ def qk_norm_rope_fwd(
     h = n_q_heads + n_kv_heads
     o = qk_norm_rope_fwd_f64(
         qkv_bits, q_w_bits, k_w_bits, positions, n_q_heads, n_kv_heads, head_dim, eps, theta,
-        rotary_dim,
+        rotary_dim, dtype,
     )
     out = qkv_bits.copy()
-    out[:, : h * head_dim] = f64_to_bf16_bits(o).reshape(t, h * head_dim)
+    out[:, : h * head_dim] = narrow(o, dtype).reshape(t, h * head_dim)
     return out

@@ -24,13 +24,13 @@ from __future__ import annotations
 
 import numpy as np
 
-from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+from .bf16 import narrow, widen
 
 
-def rmsnorm_fwd_f64(x_bits, w_bits, eps: float) -> np.ndarray:
-    """Unrounded float64 RMSNorm output for bf16 inputs x [M, N] and w [N]."""
-    x = bf16_bits_to_f64(x_bits)
-    w = bf16_bits_to_f64(w_bits)
+def rmsnorm_fwd_f64(x_bits, w_bits, eps: float, dtype: str = "bf16") -> np.ndarray:
+    """Unrounded float64 RMSNorm output for 16-bit inputs x [M, N] and w [N]."""
+    x = widen(x_bits, dtype)
+    w = widen(w_bits, dtype)
     if x.ndim != 2 or w.ndim != 1 or x.shape[1] != w.shape[0]:
         raise ValueError(f"expected x [M, N] and w [N], got {x.shape} and {w.shape}")
     n = x.shape[1]
@@ -43,9 +43,10 @@ def rmsnorm_fwd_f64(x_bits, w_bits, eps: float) -> np.ndarray:
         return (x * rstd[:, None]) * w[None, :]
 
 
-def rmsnorm_fwd(x_bits, w_bits, eps: float) -> np.ndarray:
-    """RMSNorm of bf16 x [M, N] with bf16 weight w [N]; returns y [M, N] as bf16 bits.
+def rmsnorm_fwd(x_bits, w_bits, eps: float, dtype: str = "bf16") -> np.ndarray:
+    """RMSNorm of x [M, N] with weight w [N]; returns y [M, N] as 16-bit patterns.
 
-    Float64 throughout, one rounding to bf16 at the end.
+    ``dtype`` is the storage type of inputs and output ("bf16" or "f16").
+    Float64 throughout, one rounding to the storage type at the end.
     """
-    return f64_to_bf16_bits(rmsnorm_fwd_f64(x_bits, w_bits, eps))
+    return narrow(rmsnorm_fwd_f64(x_bits, w_bits, eps, dtype), dtype)

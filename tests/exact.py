@@ -149,3 +149,40 @@ def exact_l2norm_row(xs, eps) -> list:
         ctx.prec = PREC
         d = max(root, e)
         return [Fraction(_dec(x) / d) for x in xs]
+
+
+def f16_fields_value(bits: int):
+    """Exact value of an IEEE binary16 pattern from its fields (Fraction or float special)."""
+    bits &= 0xFFFF
+    sign = -1 if bits >> 15 else 1
+    e = (bits >> 10) & 0x1F
+    f = bits & 0x3FF
+    if e == 0x1F:
+        return float("nan") if f else float("inf") * sign
+    if e == 0:
+        return sign * Fraction(f, 1024) * Fraction(1, 2**14)
+    return sign * (1 + Fraction(f, 1024)) * Fraction(2) ** (e - 15)
+
+
+def round_exact_to_f16(v) -> int:
+    """Round an exact rational to binary16 (nearest, ties to even); return the bits."""
+    v = Fraction(v)
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    eff = max(e, -14)
+    n = _round_half_even(a / Fraction(2) ** (eff - 10))
+    if eff == -14 and n < 1024:  # subnormal (or zero)
+        return sign | n
+    if n == 2048:
+        eff += 1
+        n = 1024
+    if eff > 15:
+        return sign | 0x7C00
+    return sign | ((eff + 15) << 10) | (n - 1024)
