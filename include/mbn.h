@@ -187,6 +187,31 @@ MBN_API int qk_norm_rope_partial_fwd(void* qkv, const void* q_w, const void* k_w
                                      int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
                                      float eps, float theta, void* stream);
 
+/*
+ * fp16 variants -- the same operators on IEEE binary16 data.
+ *
+ * "[Inductor] Codegen Gluon", section 3.2, lists fp16 inputs among the
+ * broadened cases of the reused-input norms. Every tensor argument that is
+ * bf16 above is binary16 here (x, r, w, b, h, y, qkv, q_w, k_w); the formulas,
+ * layouts, alias rules, validation and status codes are those of the bf16
+ * entry point of the same name; arithmetic is fp32 (fp64 for the angles and
+ * rotation products) and each output is rounded once to nearest even in
+ * binary16 (overflow gives +-inf). The full-rotary QK case is
+ * qk_norm_rope_partial_fwd_f16 with rotary_dim == head_dim.
+ */
+MBN_API int rmsnorm_fwd_f16(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                            float eps, void* stream);
+MBN_API int add_rmsnorm_fwd_f16(const void* x, const void* r, const void* w, void* h, void* y,
+                                int64_t M, int64_t N, float eps, void* stream);
+MBN_API int layernorm_fwd_f16(const void* x, const void* w, const void* b, void* y, int64_t M,
+                              int64_t N, float eps, void* stream);
+MBN_API int l2norm_fwd_f16(const void* x, void* y, int64_t M, int64_t N, float eps,
+                           void* stream);
+MBN_API int qk_norm_rope_partial_fwd_f16(void* qkv, const void* q_w, const void* k_w,
+                                         const int64_t* positions, int64_t T, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
+                                         float eps, float theta, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 MBN_API const char* mbn_strerror(int status);
 

@@ -1,11 +1,12 @@
-"""Python binding of libmbn.so: bf16 RMSNorm and fused QK-norm + rotary on MI355X.
+"""Python binding of libmbn.so: RMSNorm family and fused QK-norm + rotary on MI355X.
 
 Argument marshalling only: every step of the computation runs in the library's
 HIP kernels. PyTorch supplies device memory and streams. There is no CPU
 fallback; importing works without a GPU, but any call raises if the library is
 not built or the tensors are not on the GPU.
 
-Functions with the C names take torch tensors:
+Functions with the C names take torch tensors, all bfloat16 or all float16
+(float16 tensors are routed to the ``*_f16`` entry points):
 
 * ``rmsnorm_fwd(x, w, y=None, eps=1e-6, stream=None)`` -- x [..., N] bf16,
   w [N] bf16; returns y (allocated like x when not given; ``y is x`` runs in
@@ -89,6 +90,11 @@ def lib() -> ctypes.CDLL:
         h.qk_norm_rope_fwd.restype = ctypes.c_int
         h.qk_norm_rope_partial_fwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, f32, f32, vp]
         h.qk_norm_rope_partial_fwd.restype = ctypes.c_int
+        for name in ("rmsnorm_fwd", "add_rmsnorm_fwd", "layernorm_fwd", "l2norm_fwd",
+                     "qk_norm_rope_partial_fwd"):
+            f16 = getattr(h, name + "_f16")
+            f16.argtypes = getattr(h, name).argtypes
+            f16.restype = ctypes.c_int
         h.mbn_strerror.argtypes = [ctypes.c_int]
         h.mbn_strerror.restype = ctypes.c_char_p
         _LIB = h
@@ -112,17 +118,26 @@ def _stream_handle(stream, device):
     return int(stream)
 
 
-def _check_bf16_cuda(name, t):
+def _check_bf16_cuda(name, t, dtype=None):
+    """Check a 16-bit GPU tensor; ``dtype`` (if given) is the call's storage type."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    want = (torch.bfloat16, torch.float16) if dtype is None else (dtype,)
+    if t.dtype not in want:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in want)}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU (no CPU path exists)")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _fn(name, dtype):
+    """The C entry point for the storage type of the call."""
+    import torch
+
+    return getattr(lib(), name + "_f16" if dtype == torch.float16 else name)
 
 
 def rmsnorm_fwd(x, w, y=None, eps: float = 1e-6, stream=None):
@@ -130,18 +145,18 @@ def rmsnorm_fwd(x, w, y=None, eps: float = 1e-6, stream=None):
     import torch
 
     _check_bf16_cuda("x", x)
-    _check_bf16_cuda("w", w)
+    _check_bf16_cuda("w", w, x.dtype)
     n = x.shape[-1] if x.dim() > 0 else 0
     if w.dim() != 1 or w.shape[0] != n:
         raise ValueError(f"w must have shape [{n}], got {tuple(w.shape)}")
     if y is None:
         y = torch.empty_like(x)
     else:
-        _check_bf16_cuda("y", y)
+        _check_bf16_cuda("y", y, x.dtype)
         if y.shape != x.shape:
             raise ValueError("y must have the shape of x")
     m = x.numel() // n if n else 0
-    rc = lib().rmsnorm_fwd(
+    rc = _fn("rmsnorm_fwd", x.dtype)(
         x.data_ptr(), w.data_ptr(), y.data_ptr(), m, n, float(eps), _stream_handle(stream, x.device)
     )
     if rc != MBN_OK:
@@ -159,14 +174,14 @@ def _out_like(x, y, name):
 
     if y is None:
         return torch.empty_like(x)
-    _check_bf16_cuda(name, y)
+    _check_bf16_cuda(name, y, x.dtype)
     if y.shape != x.shape:
         raise ValueError(f"{name} must have the shape of x")
     return y
 
 
-def _check_vec(name, v, n):
-    _check_bf16_cuda(name, v)
+def _check_vec(name, v, n, dtype):
+    _check_bf16_cuda(name, v, dtype)
     if v.dim() != 1 or v.shape[0] != n:
         raise ValueError(f"{name} must have shape [{n}], got {tuple(v.shape)}")
 
@@ -174,14 +189,14 @@ def _check_vec(name, v, n):
 def add_rmsnorm_fwd(x, r, w, h=None, y=None, eps: float = 1e-6, stream=None):
     """h = bf16(x + r); y = h * rsqrt(mean(h^2, -1) + eps) * w. Returns (h, y)."""
     _check_bf16_cuda("x", x)
-    _check_bf16_cuda("r", r)
+    _check_bf16_cuda("r", r, x.dtype)
     if r.shape != x.shape:
         raise ValueError("r must have the shape of x")
     m, n = _rows_of(x)
-    _check_vec("w", w, n)
+    _check_vec("w", w, n, x.dtype)
     h = _out_like(x, h, "h")
     y = _out_like(x, y, "y")
-    rc = lib().add_rmsnorm_fwd(x.data_ptr(), r.data_ptr(), w.data_ptr(), h.data_ptr(), y.data_ptr(),
+    rc = _fn("add_rmsnorm_fwd", x.dtype)(x.data_ptr(), r.data_ptr(), w.data_ptr(), h.data_ptr(), y.data_ptr(),
                                m, n, float(eps), _stream_handle(stream, x.device))
     if rc != MBN_OK:
         raise MbnError(rc, "add_rmsnorm_fwd")
@@ -192,10 +207,10 @@ def layernorm_fwd(x, w, b, y=None, eps: float = 1e-5, stream=None):
     """y = (x - mean) * rsqrt(var + eps) * w + b over the last dim of bf16 x."""
     _check_bf16_cuda("x", x)
     m, n = _rows_of(x)
-    _check_vec("w", w, n)
-    _check_vec("b", b, n)
+    _check_vec("w", w, n, x.dtype)
+    _check_vec("b", b, n, x.dtype)
     y = _out_like(x, y, "y")
-    rc = lib().layernorm_fwd(x.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(), m, n,
+    rc = _fn("layernorm_fwd", x.dtype)(x.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(), m, n,
                              float(eps), _stream_handle(stream, x.device))
     if rc != MBN_OK:
         raise MbnError(rc, "layernorm_fwd")
@@ -207,7 +222,7 @@ def l2norm_fwd(x, y=None, eps: float = 1e-12, stream=None):
     _check_bf16_cuda("x", x)
     m, n = _rows_of(x)
     y = _out_like(x, y, "y")
-    rc = lib().l2norm_fwd(x.data_ptr(), y.data_ptr(), m, n, float(eps), _stream_handle(stream, x.device))
+    rc = _fn("l2norm_fwd", x.dtype)(x.data_ptr(), y.data_ptr(), m, n, float(eps), _stream_handle(stream, x.device))
     if rc != MBN_OK:
         raise MbnError(rc, "l2norm_fwd")
     return y
@@ -225,8 +240,8 @@ def qk_norm_rope_fwd(
     import torch
 
     _check_bf16_cuda("qkv", qkv)
-    _check_bf16_cuda("q_w", q_w)
-    _check_bf16_cuda("k_w", k_w)
+    _check_bf16_cuda("q_w", q_w, qkv.dtype)
+    _check_bf16_cuda("k_w", k_w, qkv.dtype)
     if positions.dtype != torch.int64 or not positions.is_cuda or not positions.is_contiguous():
         raise TypeError("positions must be a contiguous int64 GPU tensor")
     t = qkv.shape[0] if qkv.dim() else 0
@@ -234,7 +249,7 @@ def qk_norm_rope_fwd(
         raise ValueError("qkv must have shape [T, (n_q_heads + 2 * n_kv_heads) * head_dim]")
     if positions.numel() != t:
         raise ValueError("positions must have T entries")
-    if rotary_dim is None:
+    if rotary_dim is None and qkv.dtype == torch.bfloat16:
         rc = lib().qk_norm_rope_fwd(
             qkv.data_ptr(), q_w.data_ptr(), k_w.data_ptr(), positions.data_ptr(), t,
             int(n_q_heads), int(n_kv_heads), int(head_dim), float(eps), float(theta),
@@ -242,12 +257,13 @@ def qk_norm_rope_fwd(
         )
         where = "qk_norm_rope_fwd"
     else:
-        rc = lib().qk_norm_rope_partial_fwd(
+        rot = head_dim if rotary_dim is None else rotary_dim
+        rc = _fn("qk_norm_rope_partial_fwd", qkv.dtype)(
             qkv.data_ptr(), q_w.data_ptr(), k_w.data_ptr(), positions.data_ptr(), t,
-            int(n_q_heads), int(n_kv_heads), int(head_dim), int(rotary_dim), float(eps),
+            int(n_q_heads), int(n_kv_heads), int(head_dim), int(rot), float(eps),
             float(theta), _stream_handle(stream, qkv.device),
         )
-        where = "qk_norm_rope_partial_fwd"
+        where = "qk_norm_rope_partial_fwd" + ("_f16" if qkv.dtype == torch.float16 else "")
     if rc != MBN_OK:
         raise MbnError(rc, where)
     return qkv

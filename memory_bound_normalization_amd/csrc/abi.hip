@@ -35,8 +35,8 @@ bool bad_alias(const void* out, const void* in, int64_t bytes) {
   return out != in && overlap(out, bytes, in, bytes);
 }
 
-int launch(mbn::Norm mode, mbn::RowNormArgs a, void* stream) {
-  const hipError_t err = mbn::launch_rownorm(mode, a, static_cast<hipStream_t>(stream));
+int launch(mbn::Norm mode, mbn::Storage dt, mbn::RowNormArgs a, void* stream) {
+  const hipError_t err = mbn::launch_rownorm(mode, dt, a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MBN_OK : MBN_EHIP;
 }
 
@@ -55,23 +55,22 @@ mbn::RowNormArgs row_args(const void* x, const void* r, const void* w, const voi
   return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps,
-                        void* stream) {
+// Entry-point bodies, shared by the bf16 and fp16 variants (the storage type
+// changes nothing in the checks: both are 2 bytes per element).
+int rmsnorm_impl(mbn::Storage dt, const void* x, const void* w, void* y, int64_t M, int64_t N,
+                 float eps, void* stream) {
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !w || !y) return MBN_EINVAL;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return MBN_EUNSUPPORTED;
   const int64_t bytes = M * N * 2;
   if (bad_alias(y, x, bytes) || overlap(w, N * 2, y, bytes)) return MBN_EINVAL;
-  return launch(mbn::Norm::kRms, row_args(x, nullptr, w, nullptr, nullptr, y, M, N, eps), stream);
+  return launch(mbn::Norm::kRms, dt, row_args(x, nullptr, w, nullptr, nullptr, y, M, N, eps),
+                stream);
 }
 
-MBN_API int add_rmsnorm_fwd(const void* x, const void* r, const void* w, void* h, void* y,
-                            int64_t M, int64_t N, float eps, void* stream) {
+int add_rmsnorm_impl(mbn::Storage dt, const void* x, const void* r, const void* w, void* h,
+                     void* y, int64_t M, int64_t N, float eps, void* stream) {
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !r || !w || !h || !y) return MBN_EINVAL;
@@ -82,11 +81,11 @@ MBN_API int add_rmsnorm_fwd(const void* x, const void* r, const void* w, void* h
       bad_alias(y, x, bytes) || bad_alias(y, r, bytes) || overlap(w, N * 2, h, bytes) ||
       overlap(w, N * 2, y, bytes))
     return MBN_EINVAL;
-  return launch(mbn::Norm::kAddRms, row_args(x, r, w, nullptr, h, y, M, N, eps), stream);
+  return launch(mbn::Norm::kAddRms, dt, row_args(x, r, w, nullptr, h, y, M, N, eps), stream);
 }
 
-MBN_API int layernorm_fwd(const void* x, const void* w, const void* b, void* y, int64_t M,
-                          int64_t N, float eps, void* stream) {
+int layernorm_impl(mbn::Storage dt, const void* x, const void* w, const void* b, void* y,
+                   int64_t M, int64_t N, float eps, void* stream) {
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !w || !b || !y) return MBN_EINVAL;
@@ -95,23 +94,23 @@ MBN_API int layernorm_fwd(const void* x, const void* w, const void* b, void* y, 
   const int64_t bytes = M * N * 2;
   if (bad_alias(y, x, bytes) || overlap(w, N * 2, y, bytes) || overlap(b, N * 2, y, bytes))
     return MBN_EINVAL;
-  return launch(mbn::Norm::kLayer, row_args(x, nullptr, w, b, nullptr, y, M, N, eps), stream);
+  return launch(mbn::Norm::kLayer, dt, row_args(x, nullptr, w, b, nullptr, y, M, N, eps), stream);
 }
 
-MBN_API int l2norm_fwd(const void* x, void* y, int64_t M, int64_t N, float eps, void* stream) {
+int l2norm_impl(mbn::Storage dt, const void* x, void* y, int64_t M, int64_t N, float eps,
+                void* stream) {
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !y) return MBN_EINVAL;
   if (!aligned(x, 16) || !aligned(y, 16)) return MBN_EUNSUPPORTED;
   if (bad_alias(y, x, M * N * 2)) return MBN_EINVAL;
-  return launch(mbn::Norm::kL2, row_args(x, nullptr, nullptr, nullptr, nullptr, y, M, N, eps),
-                stream);
+  return launch(mbn::Norm::kL2, dt,
+                row_args(x, nullptr, nullptr, nullptr, nullptr, y, M, N, eps), stream);
 }
 
-MBN_API int qk_norm_rope_partial_fwd(void* qkv, const void* q_w, const void* k_w,
-                                     const int64_t* positions, int64_t T, int32_t n_q_heads,
-                                     int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
-                                     float eps, float theta, void* stream) {
+int qk_impl(mbn::Storage dt, void* qkv, const void* q_w, const void* k_w,
+            const int64_t* positions, int64_t T, int32_t n_q_heads, int32_t n_kv_heads,
+            int32_t head_dim, int32_t rotary_dim, float eps, float theta, void* stream) {
   if (T < 0 || n_q_heads < 0 || n_kv_heads < 0 || head_dim <= 0 || (head_dim & 1))
     return MBN_EINVAL;
   if (rotary_dim <= 0 || (rotary_dim & 1) || rotary_dim > head_dim) return MBN_EINVAL;
@@ -133,19 +132,80 @@ MBN_API int qk_norm_rope_partial_fwd(void* qkv, const void* q_w, const void* k_w
   if ((n_q_heads > 0 && overlap(q_w, wbytes, qkv, span)) ||
       (n_kv_heads > 0 && overlap(k_w, wbytes, qkv, span)) || overlap(positions, T * 8, qkv, span))
     return MBN_EINVAL;
-  const hipError_t err = mbn::launch_qk_norm_rope(qkv, q_w, k_w, positions, T, n_q_heads,
-                                                  n_kv_heads, rotary_dim, eps, theta,
-                                                  static_cast<hipStream_t>(stream));
+  const hipError_t err =
+      mbn::launch_qk_norm_rope(dt, qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads,
+                               rotary_dim, eps, theta, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MBN_OK : MBN_EHIP;
+}
+
+constexpr mbn::Storage kBf16 = mbn::Storage::kBf16;
+constexpr mbn::Storage kF16 = mbn::Storage::kF16;
+
+}  // namespace
+
+extern "C" {
+
+MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps,
+                        void* stream) {
+  return rmsnorm_impl(kBf16, x, w, y, M, N, eps, stream);
+}
+
+MBN_API int add_rmsnorm_fwd(const void* x, const void* r, const void* w, void* h, void* y,
+                            int64_t M, int64_t N, float eps, void* stream) {
+  return add_rmsnorm_impl(kBf16, x, r, w, h, y, M, N, eps, stream);
+}
+
+MBN_API int layernorm_fwd(const void* x, const void* w, const void* b, void* y, int64_t M,
+                          int64_t N, float eps, void* stream) {
+  return layernorm_impl(kBf16, x, w, b, y, M, N, eps, stream);
+}
+
+MBN_API int l2norm_fwd(const void* x, void* y, int64_t M, int64_t N, float eps, void* stream) {
+  return l2norm_impl(kBf16, x, y, M, N, eps, stream);
+}
+
+MBN_API int qk_norm_rope_partial_fwd(void* qkv, const void* q_w, const void* k_w,
+                                     const int64_t* positions, int64_t T, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
+                                     float eps, float theta, void* stream) {
+  return qk_impl(kBf16, qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads, head_dim, rotary_dim,
+                 eps, theta, stream);
 }
 
 MBN_API int qk_norm_rope_fwd(void* qkv, const void* q_w, const void* k_w,
                              const int64_t* positions, int64_t T, int32_t n_q_heads,
                              int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
                              void* stream) {
-  if (head_dim <= 0 || (head_dim & 1)) return MBN_EINVAL;
-  return qk_norm_rope_partial_fwd(qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads, head_dim,
-                                  head_dim, eps, theta, stream);
+  return qk_impl(kBf16, qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads, head_dim, head_dim,
+                 eps, theta, stream);
+}
+
+MBN_API int rmsnorm_fwd_f16(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                            float eps, void* stream) {
+  return rmsnorm_impl(kF16, x, w, y, M, N, eps, stream);
+}
+
+MBN_API int add_rmsnorm_fwd_f16(const void* x, const void* r, const void* w, void* h, void* y,
+                                int64_t M, int64_t N, float eps, void* stream) {
+  return add_rmsnorm_impl(kF16, x, r, w, h, y, M, N, eps, stream);
+}
+
+MBN_API int layernorm_fwd_f16(const void* x, const void* w, const void* b, void* y, int64_t M,
+                              int64_t N, float eps, void* stream) {
+  return layernorm_impl(kF16, x, w, b, y, M, N, eps, stream);
+}
+
+MBN_API int l2norm_fwd_f16(const void* x, void* y, int64_t M, int64_t N, float eps,
+                           void* stream) {
+  return l2norm_impl(kF16, x, y, M, N, eps, stream);
+}
+
+MBN_API int qk_norm_rope_partial_fwd_f16(void* qkv, const void* q_w, const void* k_w,
+                                         const int64_t* positions, int64_t T, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
+                                         float eps, float theta, void* stream) {
+  return qk_impl(kF16, qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads, head_dim, rotary_dim,
+                 eps, theta, stream);
 }
 
 MBN_API const char* mbn_strerror(int status) {

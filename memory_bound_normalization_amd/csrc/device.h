@@ -25,6 +25,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Storage types of 16-bit data: widen either half of a dword to fp32 (exact)
+// and narrow two fp32 values to one dword, rounding to nearest even.
+struct Bf16 {
+  static __device__ __forceinline__ float lo(uint32_t v) { return bf16_lo(v); }
+  static __device__ __forceinline__ float hi(uint32_t v) { return bf16_hi(v); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+};
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct F16 {
+  static __device__ __forceinline__ float lo(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f32x2 f = {a, b};
+    f16x2 h = __builtin_convertvector(f, f16x2);
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
 // DPP lane permutations inside a row of 16 lanes.
 enum : int {
   kDppQuadXor1 = 0xB1,    // quad_perm [1,0,3,2]

@@ -8,17 +8,20 @@
 
 namespace mbn {
 
+// Storage type of every 16-bit tensor of a call.
+enum class Storage : int { kBf16 = 0, kF16 = 1 };
+
 // Row-wise norms served by one kernel template (rownorm.hip).
 enum class Norm : int { kRms = 0, kAddRms = 1, kLayer = 2, kL2 = 3 };
 
 // Kernel arguments of every row norm; unused pointers are null.
 struct RowNormArgs {
-  const uint16_t* x;  // [M, N] bf16 input
-  const uint16_t* r;  // [M, N] bf16 residual (kAddRms)
-  const uint16_t* w;  // [N] bf16 weight (all but kL2)
-  const uint16_t* b;  // [N] bf16 bias (kLayer)
-  uint16_t* h;        // [M, N] bf16 x + r (kAddRms)
-  uint16_t* y;        // [M, N] bf16 output
+  const uint16_t* x;  // [M, N] input (16-bit storage type of the call)
+  const uint16_t* r;  // [M, N] residual (kAddRms)
+  const uint16_t* w;  // [N] weight (all but kL2)
+  const uint16_t* b;  // [N] bias (kLayer)
+  uint16_t* h;        // [M, N] x + r (kAddRms)
+  uint16_t* y;        // [M, N] output
   int64_t M;
   int nchunk;         // N / 8
   float inv_n;        // 1 / N, set by the launcher
@@ -26,13 +29,13 @@ struct RowNormArgs {
   int xcd_group;      // set by the launcher
 };
 
-hipError_t launch_rownorm(Norm mode, RowNormArgs args, hipStream_t stream);
+hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream);
 
 // Dynamic LDS bytes a row-norm launch requests (exposed for tuning tools).
 size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu);
 
 // rotary_dim: a multiple of 16 in [16, 128]; 128 is the full-rotary case.
-hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
+hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const void* k_w,
                                const int64_t* positions, int64_t T, int n_q_heads,
                                int n_kv_heads, int rotary_dim, float eps, float theta,
                                hipStream_t stream);

@@ -23,7 +23,8 @@
 // chunk R/16 away (fetched with ds_bpermute instead of row_ror:8) and angles
 // pos * theta^(-2i/R), and chunks [R/8, 16) are stored normalized only.
 //
-// Precision: x * w is exact in fp32 (two 8-bit significands). The rotation
+// Precision: x * w is exact in fp32 (two 8-bit significands for bf16, two
+// 11-bit ones for fp16). The rotation
 // x*w*cos -/+ x'*w'*sin is formed in fp64 because outputs of near-cancelling
 // pairs are judged on an absolute floor of about 1e-6, which fp32 products of
 // magnitude ~7 would consume on their own; rstd only scales the result
@@ -38,6 +39,7 @@ constexpr int kHeadDim = 128;
 constexpr int kHalf = kHeadDim / 2;
 constexpr int kHeadsPerWave = 4;
 
+template <typename DT>
 __global__ void __launch_bounds__(1024)
 qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w,
                     const uint16_t* __restrict__ k_w, const int64_t* __restrict__ positions,
@@ -95,10 +97,10 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
     float x[8], xw[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_lo(xv[e]);
-      x[2 * e + 1] = bf16_hi(xv[e]);
-      xw[2 * e] = x[2 * e] * bf16_lo(wv[e]);
-      xw[2 * e + 1] = x[2 * e + 1] * bf16_hi(wv[e]);
+      x[2 * e] = DT::lo(xv[e]);
+      x[2 * e + 1] = DT::hi(xv[e]);
+      xw[2 * e] = x[2 * e] * DT::lo(wv[e]);
+      xw[2 * e + 1] = x[2 * e + 1] * DT::hi(wv[e]);
     }
     float acc = 0.f;
 #pragma unroll
@@ -132,7 +134,7 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
     if (live) {
       u32x4 out;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+      for (int e = 0; e < 4; ++e) out[e] = DT::pack(o[2 * e], o[2 * e + 1]);
       *reinterpret_cast<u32x4*>(trow + (int64_t)head * kHeadDim + 8 * j) = out;
     }
   }
@@ -140,7 +142,7 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
 
 }  // namespace
 
-hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
+hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const void* k_w,
                                const int64_t* positions, int64_t T, int n_q_heads,
                                int n_kv_heads, int rotary_dim, float eps, float theta,
                                hipStream_t stream) {
@@ -151,7 +153,8 @@ hipError_t launch_qk_norm_rope(void* qkv, const void* q_w, const void* k_w,
   // vs 4.1 us with 4 waves; T = 65536: 249 us vs 363 us with 10 waves).
   const int waves = (T <= 1024) ? (groups < 16 ? groups : 16) : (groups < 4 ? groups : 4);
   const int64_t row_stride = (int64_t)(n_q_heads + 2 * n_kv_heads) * kHeadDim;
-  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)T), dim3(64 * waves), 0, stream,
+  hipLaunchKernelGGL(dtype == Storage::kF16 ? qk_norm_rope_kernel<F16> : qk_norm_rope_kernel<Bf16>,
+                     dim3((unsigned)T), dim3(64 * waves), 0, stream,
                      static_cast<uint16_t*>(qkv), static_cast<const uint16_t*>(q_w),
                      static_cast<const uint16_t*>(k_w), positions, n_q_heads, n_heads, row_stride,
                      rotary_dim / 16, eps, (double)theta);

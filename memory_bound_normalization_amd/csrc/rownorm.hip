@@ -1,5 +1,6 @@
 // Row-wise norms for gfx950 with each row staged in LDS: RMSNorm, residual add
-// + RMSNorm, LayerNorm and L2Norm.
+// + RMSNorm, LayerNorm and L2Norm, on bf16 or fp16 data (fp16 is among the
+// broadened inputs of "[Inductor] Codegen Gluon", section 3.2).
 //
 // The method ("[Inductor] Codegen Gluon", section 3.1, RMSNorm as the reference
 // workload; section 3.2 for the rest of the family): the input row is needed
@@ -79,7 +80,7 @@ __device__ __forceinline__ void rows_sum(float (&v)[RPL], u32x4* buf0, int nchun
 // registers serves RPL rows and the weight is fetched from L2 once per RPL
 // rows. FULL: the row is exactly MAXC chunks per lane (the power-of-two
 // widths), so no chunk needs a bounds predicate.
-template <Norm MODE, int WPR, int ROWS, int RPL, int MAXC, bool FULL>
+template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL>
 __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a) {
   constexpr int TPR = 64 * WPR;  // lanes per lane set
   constexpr bool kHasW = MODE != Norm::kL2;
@@ -149,8 +150,8 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
           u32x4 hv;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            hv[e] = pack_bf16x2(bf16_lo(v[e]) + bf16_lo(rreg[rr][j][e]),
-                                bf16_hi(v[e]) + bf16_hi(rreg[rr][j][e]));
+            hv[e] = DT::pack(DT::lo(v[e]) + DT::lo(rreg[rr][j][e]),
+                                DT::hi(v[e]) + DT::hi(rreg[rr][j][e]));
           v = hv;
           buf[k] = hv;
           if (live) store_nt_16(reinterpret_cast<u32x4*>(a.h) + (row0 + rr) * nchunk + k, hv);
@@ -158,8 +159,8 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
         if (j == 0) first[rr] = v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = bf16_lo(v[e]);
-          const float q = bf16_hi(v[e]);
+          const float p = DT::lo(v[e]);
+          const float q = DT::hi(v[e]);
           if constexpr (MODE == Norm::kLayer) {
             acc0 += p;
             acc1 += q;
@@ -193,8 +194,8 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
           const u32x4 v = (j == 0) ? first[rr] : buf[k];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = bf16_lo(v[e]) - mu[rr];
-            const float q = bf16_hi(v[e]) - mu[rr];
+            const float p = DT::lo(v[e]) - mu[rr];
+            const float q = DT::hi(v[e]) - mu[rr];
             acc0 = __builtin_fmaf(p, p, acc0);
             acc1 = __builtin_fmaf(q, q, acc1);
           }
@@ -234,18 +235,18 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float p = bf16_lo(v[e]), q = bf16_hi(v[e]);
+          float p = DT::lo(v[e]), q = DT::hi(v[e]);
           if constexpr (MODE == Norm::kLayer) {
-            p = __builtin_fmaf((p - mu[rr]) * scale[rr], bf16_lo(wreg[j][e]), bf16_lo(breg[j][e]));
-            q = __builtin_fmaf((q - mu[rr]) * scale[rr], bf16_hi(wreg[j][e]), bf16_hi(breg[j][e]));
+            p = __builtin_fmaf((p - mu[rr]) * scale[rr], DT::lo(wreg[j][e]), DT::lo(breg[j][e]));
+            q = __builtin_fmaf((q - mu[rr]) * scale[rr], DT::hi(wreg[j][e]), DT::hi(breg[j][e]));
           } else if constexpr (MODE == Norm::kL2) {
             p *= scale[rr];
             q *= scale[rr];
           } else {
-            p = (p * scale[rr]) * bf16_lo(wreg[j][e]);
-            q = (q * scale[rr]) * bf16_hi(wreg[j][e]);
+            p = (p * scale[rr]) * DT::lo(wreg[j][e]);
+            q = (q * scale[rr]) * DT::hi(wreg[j][e]);
           }
-          o[e] = pack_bf16x2(p, q);
+          o[e] = DT::pack(p, q);
         }
         store_nt_16(yrow + k, o);
       }
@@ -264,15 +265,17 @@ struct RowNormCfg {
   int wpr, rows, rpl, maxc;
   int wgs_per_cu;    // occupancy cap (0 = as many as LDS, waves and VGPRs allow)
   int xcd_group;     // row blocks per XCD run (0 = dispatch order)
-  RowNormKernel ragged;  // any width up to max_nchunk
-  RowNormKernel full;    // width exactly max_nchunk
+  RowNormKernel ragged[2];  // any width up to max_nchunk; [bf16, fp16]
+  RowNormKernel full[2];    // width exactly max_nchunk; [bf16, fp16]
 };
 
-#define MBN_CFG_(MODE, EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP)                     \
-  RowNormCfg {                                                                      \
-    64 * (WPR) * (MAXC), EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP,                   \
-        &rownorm_kernel<MODE, WPR, ROWS, RPL, MAXC, false>,                         \
-        &rownorm_kernel<MODE, WPR, ROWS, RPL, MAXC, true>                           \
+#define MBN_CFG_(MODE, EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP)                       \
+  RowNormCfg {                                                                        \
+    64 * (WPR) * (MAXC), EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP,                     \
+        {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, false>,                    \
+         &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, false>},                    \
+        {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, true>,                     \
+         &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, true>}                      \
   }
 // serves every width up to 64 * WPR * MAXC chunks (down to the previous entry)
 #define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, false, WPR, ROWS, RPL, MAXC, CAP, GROUP)
@@ -348,7 +351,7 @@ size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu) {
   return lds;
 }
 
-hipError_t launch_rownorm(Norm mode, RowNormArgs args, hipStream_t stream) {
+hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream) {
   const int nchunk = args.nchunk;
   const RowNormCfg* cfg = nullptr;
   switch (mode) {
@@ -364,7 +367,8 @@ hipError_t launch_rownorm(Norm mode, RowNormArgs args, hipStream_t stream) {
   const int64_t N = (int64_t)nchunk * 8;
   const size_t lds = rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
   args.inv_n = 1.0f / (float)N;
-  const RowNormKernel kernel = (nchunk == cfg->max_nchunk) ? cfg->full : cfg->ragged;
+  const int d = dtype == Storage::kF16 ? 1 : 0;
+  const RowNormKernel kernel = (nchunk == cfg->max_nchunk) ? cfg->full[d] : cfg->ragged[d];
   args.xcd_group = cfg->xcd_group;
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * cfg->wpr * cfg->rows), lds, stream,
                      args);

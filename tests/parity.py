@@ -5,24 +5,27 @@ bf16 value widened to float64,
 
     |y_gpu - y_ref| <= 2^-7 * |y_ref| + 1e-6
 
-i.e. one bf16 ulp relative plus an absolute floor for outputs near zero. NaN
-positions must match exactly; infinities must match exactly.
+i.e. one bf16 ulp relative plus an absolute floor for outputs near zero; for
+fp16 data the relative term is one fp16 ulp, 2^-10 * |y_ref|. NaN positions
+must match exactly; infinities must match exactly.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from oracle import bf16_bits_to_f64
+from oracle import bf16_bits_to_f64, widen
 
 REL_TOL = 2.0**-7
+REL_TOL_F16 = 2.0**-10
 ABS_TOL = 1e-6
 
 
-def to_gpu_bf16(bits: np.ndarray, device="cuda"):
+def to_gpu_bf16(bits: np.ndarray, device="cuda", dtype="bf16"):
     import torch
 
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(device)
 
 
 def from_gpu_bf16(t) -> np.ndarray:
@@ -31,27 +34,28 @@ def from_gpu_bf16(t) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def tolerance_violations(got_bits, ref_bits):
+def tolerance_violations(got_bits, ref_bits, dtype="bf16"):
     """Return a boolean mask of outputs outside the tolerance (NaN/inf aware)."""
-    g = bf16_bits_to_f64(got_bits)
-    r = bf16_bits_to_f64(ref_bits)
+    g = widen(got_bits, dtype)
+    r = widen(ref_bits, dtype)
+    rel = REL_TOL_F16 if dtype == "f16" else REL_TOL
     nan_r, nan_g = np.isnan(r), np.isnan(g)
     with np.errstate(invalid="ignore"):
-        ok = (np.abs(g - r) <= REL_TOL * np.abs(r) + ABS_TOL) | (g == r)
+        ok = (np.abs(g - r) <= rel * np.abs(r) + ABS_TOL) | (g == r)
     ok = np.where(nan_r | nan_g, nan_r & nan_g, ok)
     return ~ok
 
 
-def assert_parity(got_bits, ref_bits, what: str = ""):
+def assert_parity(got_bits, ref_bits, what: str = "", dtype="bf16"):
     got_bits = np.asarray(got_bits)
     ref_bits = np.asarray(ref_bits)
     assert got_bits.shape == ref_bits.shape, (got_bits.shape, ref_bits.shape)
-    bad = tolerance_violations(got_bits, ref_bits)
+    bad = tolerance_violations(got_bits, ref_bits, dtype)
     n = int(np.count_nonzero(bad))
     if n:
         idx = np.argwhere(bad)[:8]
-        g = bf16_bits_to_f64(got_bits)
-        r = bf16_bits_to_f64(ref_bits)
+        g = widen(got_bits, dtype)
+        r = widen(ref_bits, dtype)
         rows = [f"  at {tuple(int(v) for v in i)}: gpu {g[tuple(i)]!r} oracle {r[tuple(i)]!r}" for i in idx]
         raise AssertionError(f"{what}: {n} of {bad.size} outputs outside tolerance\n" + "\n".join(rows))
 

@@ -38,7 +38,8 @@ def _header_constants():
 def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {
         "rmsnorm_fwd", "add_rmsnorm_fwd", "layernorm_fwd", "l2norm_fwd", "qk_norm_rope_fwd",
-        "qk_norm_rope_partial_fwd", "mbn_strerror"}
+        "qk_norm_rope_partial_fwd", "rmsnorm_fwd_f16", "add_rmsnorm_fwd_f16", "layernorm_fwd_f16",
+        "l2norm_fwd_f16", "qk_norm_rope_partial_fwd_f16", "mbn_strerror"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -233,3 +234,21 @@ def test_qk_partial_other_checks_still_apply(lib):
     # a valid rotary_dim with an invalid head_dim / null pointer is still rejected before any HIP call
     assert lib.qk_norm_rope_partial_fwd(FAKE, FAKE, FAKE, FAKE, 4, 4, 2, 64, 32, 1e-6, 1e6, None) == mbn.MBN_EUNSUPPORTED
     assert lib.qk_norm_rope_partial_fwd(None, FAKE, FAKE, FAKE, 4, 4, 2, 128, 64, 1e-6, 1e6, None) == mbn.MBN_EINVAL
+
+
+def test_f16_entry_points_validate_like_bf16(lib):
+    """Every invalid-by-construction call gets the same status from both storage types."""
+    cases = [
+        ("rmsnorm_fwd", (FAKE, FAKE + B, FAKE + 16, 4, 64, 1e-6, None)),
+        ("rmsnorm_fwd", (FAKE, FAKE + B, FAKE + 2 * B, 4, 12, 1e-6, None)),
+        ("rmsnorm_fwd", (None, FAKE + B, FAKE + 2 * B, 4, 64, 1e-6, None)),
+        ("add_rmsnorm_fwd", (FAKE, FAKE + B, FAKE + 2 * B, FAKE + 3 * B, FAKE + 3 * B, 4, 64, 1e-6, None)),
+        ("layernorm_fwd", (FAKE, FAKE + B, FAKE + 2 * B, FAKE + 3 * B + 2, 4, 64, 1e-5, None)),
+        ("l2norm_fwd", (FAKE, FAKE + B, -1, 64, 1e-12, None)),
+        ("qk_norm_rope_partial_fwd", (FAKE, FAKE + B, FAKE + B + 4096, FAKE + B + 8192, 4, 4, 2, 128, 24, 1e-6, 1e6, None)),
+        ("qk_norm_rope_partial_fwd", (FAKE, FAKE + B, FAKE + B + 4096, FAKE + B + 8192, 4, 4, 2, 128, 256, 1e-6, 1e6, None)),
+    ]
+    for name, args in cases:
+        a = getattr(lib, name)(*args)
+        b = getattr(lib, name + "_f16")(*args)
+        assert a == b and a != mbn.MBN_OK, (name, args, a, b)
