@@ -138,3 +138,22 @@ def test_partial_rotary(rot, T):
     if rot == 128:
         full = _run(qkv, q_w, k_w, pos, hq, hk, 1e-6, 1e6)
         assert np.array_equal(full, got), "rotary_dim = head_dim differs from the full-rotary entry point"
+
+
+def test_many_tokens_sampled():
+    """65536 tokens (the 4-wave looping schedule): sampled tokens against the oracle."""
+    T, hq, hk = 65536, 32, 8
+    print(f"[qk] large T={T}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    qkv = torch.randn(T, (hq + 2 * hk) * D, device="cuda", generator=g).to(torch.bfloat16)
+    q_w = (torch.rand(D, device="cuda", generator=g) + 0.5).to(torch.bfloat16)
+    k_w = (torch.rand(D, device="cuda", generator=g) + 0.5).to(torch.bfloat16)
+    pos = torch.arange(T, device="cuda", dtype=torch.int64)
+    before = from_gpu_bf16(qkv)
+    mbn.qk_norm_rope_fwd(qkv, q_w, k_w, pos, hq, hk, D, eps=1e-6, theta=1e6)
+    torch.cuda.synchronize()
+    after = from_gpu_bf16(qkv)
+    toks = np.array([0, 1, 1023, 1024, 30000, T - 1])
+    ref = oracle_qk(before[toks], from_gpu_bf16(q_w), from_gpu_bf16(k_w), toks, hq, hk, D, 1e-6, 1e6)
+    assert_parity(after[toks], ref, "large T")
+    assert np.array_equal(after[:, (hq + hk) * D:], before[:, (hq + hk) * D:])

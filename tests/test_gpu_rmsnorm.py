@@ -145,3 +145,18 @@ def test_workloads(name):
     mbn.rmsnorm_fwd(x, w, x, eps=eps)
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int16), y.view(torch.int16)), "in place differs"
+
+
+def test_many_rows_sampled():
+    """262144 rows (grids far beyond 65535 workgroups): sampled rows against the oracle."""
+    M, N = 262144, 2048
+    print(f"[rmsnorm] large M={M} N={N}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = (torch.randn(M, N, device="cuda", generator=g) * 2).to(torch.bfloat16)
+    w = (torch.rand(N, device="cuda", generator=g) + 0.5).to(torch.bfloat16)
+    y = mbn.rmsnorm_fwd(x, w, eps=1e-6)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 4095, 65535, 65536, 131071, 200000, M - 2, M - 1], device="cuda")
+    xb, wb = from_gpu_bf16(x[rows]), from_gpu_bf16(w)
+    assert_parity(from_gpu_bf16(y[rows]), oracle_rmsnorm(xb, wb, 1e-6), "large M")
+    assert torch.isfinite(y.float()).all()
