@@ -29,7 +29,14 @@ struct RowNormArgs {
   int xcd_group;      // set by the launcher
 };
 
-hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream);
+// Which row-norm kernel serves a launch: kAuto picks by width and row count;
+// the others force a path (tuning tools; kPersistent fails with
+// hipErrorInvalidValue for widths or modes it does not serve). grid > 0
+// overrides the persistent grid size.
+enum class RowNormPath : int { kAuto = 0, kOneShot = 1, kPersistent = 2 };
+
+hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream,
+                          RowNormPath path = RowNormPath::kAuto, int grid = 0);
 
 // Dynamic LDS bytes a row-norm launch requests (exposed for tuning tools).
 size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu);

@@ -50,36 +50,211 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nblocks, int gro
 }
 
 // Sums of v[rr] over the WPR waves of each of the RPL rows a lane set serves,
-// with one barrier for all of them. The wave total of row rr is parked in
-// float `which` of the wave's first chunk of that row (see the header comment).
+// with one barrier for all of them. The wave totals go to `part` when given
+// (a small LDS array, [2][RPL][WPR] floats: `which` selects the half), else
+// they are parked in float `which` of each wave's first chunk of that row
+// (see the header comment).
 template <int WPR, int RPL>
-__device__ __forceinline__ void rows_sum(float (&v)[RPL], u32x4* buf0, int nchunk, int t, int wave,
-                                         int which) {
+__device__ __forceinline__ void rows_sum(float (&v)[RPL], u32x4* buf0, float* part, int nchunk,
+                                         int t, int wave, int which) {
 #pragma unroll
   for (int rr = 0; rr < RPL; ++rr) v[rr] = wave_sum(v[rr]);
   if constexpr (WPR > 1) {
     if ((t & 63) == 0) {
 #pragma unroll
-      for (int rr = 0; rr < RPL; ++rr)
-        reinterpret_cast<float*>(buf0 + (size_t)rr * nchunk)[wave * 256 + which] = v[rr];  // 256 floats = 64 chunks
+      for (int rr = 0; rr < RPL; ++rr) {
+        if (part) part[(which * RPL + rr) * WPR + wave] = v[rr];
+        else reinterpret_cast<float*>(buf0 + (size_t)rr * nchunk)[wave * 256 + which] = v[rr];  // 256 floats = 64 chunks
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int rr = 0; rr < RPL; ++rr) {
-      const float* parked = reinterpret_cast<const float*>(buf0 + (size_t)rr * nchunk);
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < WPR; ++i) s += parked[i * 256 + which];
+      for (int i = 0; i < WPR; ++i)
+        s += part ? part[(which * RPL + rr) * WPR + i]
+                  : reinterpret_cast<const float*>(buf0 + (size_t)rr * nchunk)[i * 256 + which];
       v[rr] = s;
     }
   }
 }
 
-// One workgroup = ROWS lane sets of 64 * WPR lanes; each lane set serves RPL
-// consecutive rows with the same lanes, so one set of weight (and bias)
-// registers serves RPL rows and the weight is fetched from L2 once per RPL
-// rows. FULL: the row is exactly MAXC chunks per lane (the power-of-two
-// widths), so no chunk needs a bounds predicate.
+// HBM -> LDS for the RPL rows starting at row0: every chunk in flight before
+// any wait. Lane t of the lane set loads chunks j * 64 * WPR + t.
+template <int WPR, int RPL, int MAXC, bool FULL>
+__device__ __forceinline__ void stage_rows(const RowNormArgs& a, u32x4* buf0, int64_t row0, int t,
+                                           int wave) {
+  constexpr int TPR = 64 * WPR;
+  const int nchunk = a.nchunk;
+#pragma unroll
+  for (int rr = 0; rr < RPL; ++rr) {
+    if (row0 + rr < a.M) {
+      const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + (row0 + rr) * nchunk;
+      u32x4* buf = buf0 + (size_t)rr * nchunk;
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int k = j * TPR + t;
+        if (FULL || k < nchunk) load_lds_16(xrow + k, (lds_void*)(buf + j * TPR + wave * 64));
+      }
+    }
+  }
+}
+
+template <Norm MODE>
+struct Regs {
+  static constexpr bool kHasW = MODE != Norm::kL2;
+  static constexpr bool kHasB = MODE == Norm::kLayer;
+  static constexpr bool kHasR = MODE == Norm::kAddRms;
+};
+
+// Weight (and bias) chunks of this lane into VGPRs: L2 hits after the first rows.
+template <Norm MODE, int WPR, int MAXC, bool FULL>
+__device__ __forceinline__ void load_affine(const RowNormArgs& a, int t,
+                                            u32x4 (&wreg)[Regs<MODE>::kHasW ? MAXC : 1],
+                                            u32x4 (&breg)[Regs<MODE>::kHasB ? MAXC : 1]) {
+  constexpr int TPR = 64 * WPR;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * TPR + t;
+    const bool in = FULL || k < a.nchunk;
+    if constexpr (Regs<MODE>::kHasW)
+      wreg[j] = in ? reinterpret_cast<const u32x4*>(a.w)[k] : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (Regs<MODE>::kHasB)
+      breg[j] = in ? reinterpret_cast<const u32x4*>(a.b)[k] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// The passes of the persistent kernel, once a row set has landed in LDS:
+// pass 1 (sum of squares, or sum for LayerNorm), the reductions (LayerNorm: a
+// second, centred pass), and pass 2 (normalize, weight, round, streaming
+// stores). The same arithmetic, in the same order, as the one-shot kernel.
+template <Norm MODE, typename DT, int WPR, int RPL, int MAXC, bool FULL>
+__device__ __forceinline__ void finish_rows(const RowNormArgs& a, u32x4* buf0, float* part,
+                                            int64_t row0, int t, int wave,
+                                            const u32x4 (&wreg)[Regs<MODE>::kHasW ? MAXC : 1],
+                                            const u32x4 (&breg)[Regs<MODE>::kHasB ? MAXC : 1]) {
+  static_assert(!Regs<MODE>::kHasR, "the residual add runs one-shot only");
+  constexpr int TPR = 64 * WPR;
+  const int nchunk = a.nchunk;
+  float s1[RPL];
+  u32x4 first[RPL];  // chunk j = 0 of each row, kept for the later passes
+#pragma unroll
+  for (int rr = 0; rr < RPL; ++rr) {
+    const u32x4* buf = buf0 + (size_t)rr * nchunk;
+    float acc0 = 0.f, acc1 = 0.f;
+    first[rr] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * TPR + t;
+      if (FULL || k < nchunk) {
+        const u32x4 v = buf[k];
+        if (j == 0) first[rr] = v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = DT::lo(v[e]);
+          const float q = DT::hi(v[e]);
+          if constexpr (MODE == Norm::kLayer) {
+            acc0 += p;
+            acc1 += q;
+          } else {
+            acc0 = __builtin_fmaf(p, p, acc0);
+            acc1 = __builtin_fmaf(q, q, acc1);
+          }
+        }
+      }
+    }
+    s1[rr] = acc0 + acc1;
+  }
+  rows_sum<WPR, RPL>(s1, buf0, part, nchunk, t, wave, 0);
+
+  float mu[RPL], scale[RPL];
+  if constexpr (MODE == Norm::kLayer) {
+    // Pass 1b (from LDS): centred second moment.
+    float s2[RPL];
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      const u32x4* buf = buf0 + (size_t)rr * nchunk;
+      mu[rr] = s1[rr] * a.inv_n;
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int k = j * TPR + t;
+        if (FULL || k < nchunk) {
+          const u32x4 v = (j == 0) ? first[rr] : buf[k];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = DT::lo(v[e]) - mu[rr];
+            const float q = DT::hi(v[e]) - mu[rr];
+            acc0 = __builtin_fmaf(p, p, acc0);
+            acc1 = __builtin_fmaf(q, q, acc1);
+          }
+        }
+      }
+      s2[rr] = acc0 + acc1;
+    }
+    rows_sum<WPR, RPL>(s2, buf0, part, nchunk, t, wave, 1);
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) scale[rr] = __builtin_amdgcn_rsqf(s2[rr] * a.inv_n + a.eps);
+  } else if constexpr (MODE == Norm::kL2) {
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      const float nrm = __builtin_sqrtf(s1[rr]);
+      scale[rr] = 1.0f / ((nrm < a.eps) ? a.eps : nrm);  // NaN norms stay NaN
+      mu[rr] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      scale[rr] = __builtin_amdgcn_rsqf(__builtin_fmaf(s1[rr], a.inv_n, a.eps));
+      mu[rr] = 0.f;
+    }
+  }
+
+  // Pass 2 (from LDS): normalize, weight, round, streaming stores.
+#pragma unroll
+  for (int rr = 0; rr < RPL; ++rr) {
+    if (row0 + rr >= a.M) continue;
+    const u32x4* buf = buf0 + (size_t)rr * nchunk;
+    u32x4* yrow = reinterpret_cast<u32x4*>(a.y) + (row0 + rr) * nchunk;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * TPR + t;
+      if (FULL || k < nchunk) {
+        const u32x4 v = (j == 0) ? first[rr] : buf[k];
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float p = DT::lo(v[e]), q = DT::hi(v[e]);
+          if constexpr (MODE == Norm::kLayer) {
+            p = __builtin_fmaf((p - mu[rr]) * scale[rr], DT::lo(wreg[j][e]), DT::lo(breg[j][e]));
+            q = __builtin_fmaf((q - mu[rr]) * scale[rr], DT::hi(wreg[j][e]), DT::hi(breg[j][e]));
+          } else if constexpr (MODE == Norm::kL2) {
+            p *= scale[rr];
+            q *= scale[rr];
+          } else {
+            p = (p * scale[rr]) * DT::lo(wreg[j][e]);
+            q = (q * scale[rr]) * DT::hi(wreg[j][e]);
+          }
+          o[e] = DT::pack(p, q);
+        }
+        store_nt_16(yrow + k, o);
+      }
+    }
+  }
+}
+
+// One-shot kernel: one workgroup = ROWS lane sets of 64 * WPR lanes; each
+// lane set serves RPL consecutive rows with the same lanes, so one set of
+// weight (and bias) registers serves RPL rows and the weight is fetched from
+// L2 once per RPL rows. FULL: the row is exactly MAXC chunks per lane (the
+// power-of-two widths), so no chunk needs a bounds predicate.
+//
+// Its staging and passes stay in this one body rather than calling the
+// helpers above: with the row copy issued from a separate inlined helper the
+// compiler scheduled the LDS reads of the LayerNorm passes less far ahead,
+// 4-6% slower at N >= 16384 on MI355X (RMSNorm, L2Norm and the residual add
+// unchanged).
 template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL>
 __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a) {
   constexpr int TPR = 64 * WPR;  // lanes per lane set
@@ -176,7 +351,7 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
   // Chunk wave * 64 of each row (lane 0's first chunk) is in VGPRs now and is
   // not read from LDS again; the launch tables guarantee nchunk >= 64 * WPR, so
   // every wave owns such a chunk to park its partial sums in.
-  rows_sum<WPR, RPL>(s1, buf0, nchunk, t, wave, 0);
+  rows_sum<WPR, RPL>(s1, buf0, nullptr, nchunk, t, wave, 0);
 
   float mu[RPL], scale[RPL];
   if constexpr (MODE == Norm::kLayer) {
@@ -203,7 +378,7 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
       }
       s2[rr] = acc0 + acc1;
     }
-    rows_sum<WPR, RPL>(s2, buf0, nchunk, t, wave, 1);
+    rows_sum<WPR, RPL>(s2, buf0, nullptr, nchunk, t, wave, 1);
 #pragma unroll
     for (int rr = 0; rr < RPL; ++rr) scale[rr] = __builtin_amdgcn_rsqf(s2[rr] * a.inv_n + a.eps);
   } else if constexpr (MODE == Norm::kL2) {
@@ -251,6 +426,45 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
         store_nt_16(yrow + k, o);
       }
     }
+  }
+}
+
+// Persistent kernel ("[Inductor] Codegen Gluon", section 3.3: copies of the
+// next tile in flight while the current one is computed): a grid of at most
+// a few workgroups per CU, each looping over row sets g, g + G, g + 2G, ...
+// with two LDS buffers. As soon as a row set has landed, the next one's DMA
+// is issued into the other buffer, so it overlaps this row set's passes and
+// stores; the weight (and bias) registers are loaded once per workgroup.
+// Cross-wave partials use a separate [2 parities][2][RPL][WPR] LDS array
+// instead of parking: a wave's next DMA refills its own first chunk while
+// slower waves may still be reading partials of the previous row set. The
+// barrier inside each reduction orders reuse of a parity two row sets later.
+// Not for the residual add (its residual registers would need double
+// buffering too).
+template <Norm MODE, typename DT, int WPR, int RPL, int MAXC, bool FULL>
+__global__ void __launch_bounds__(64 * WPR) rownorm_persistent_kernel(RowNormArgs a) {
+  static_assert(MODE != Norm::kAddRms, "no persistent residual add");
+  constexpr int kPart = 2 * RPL * WPR;  // floats per parity
+  extern __shared__ u32x4 lds_rows[];  // 2 * RPL * nchunk chunks, then 2 * kPart floats
+
+  const int nchunk = a.nchunk;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t sets = (a.M + RPL - 1) / RPL;
+  float* part_base = reinterpret_cast<float*>(lds_rows + (size_t)2 * RPL * nchunk);
+
+  u32x4 wreg[Regs<MODE>::kHasW ? MAXC : 1], breg[Regs<MODE>::kHasB ? MAXC : 1];
+  load_affine<MODE, WPR, MAXC, FULL>(a, t, wreg, breg);
+
+  int64_t set = blockIdx.x;
+  if (set < sets) stage_rows<WPR, RPL, MAXC, FULL>(a, lds_rows, set * RPL, t, wave);
+  for (int it = 0; set < sets; set += gridDim.x, ++it) {
+    u32x4* cur = lds_rows + (size_t)(it & 1) * RPL * nchunk;
+    u32x4* nxt = lds_rows + (size_t)((it + 1) & 1) * RPL * nchunk;
+    wait_vmem();  // this row set has landed (and the previous one's stores have completed)
+    if (set + gridDim.x < sets) stage_rows<WPR, RPL, MAXC, FULL>(a, nxt, (set + gridDim.x) * RPL, t, wave);
+    finish_rows<MODE, DT, WPR, RPL, MAXC, FULL>(a, cur, part_base + (it & 1) * kPart, set * RPL, t, wave,
+                                                wreg, breg);
   }
 }
 
@@ -338,6 +552,72 @@ const RowNormCfg* pick(const RowNormCfg (&table)[K], int nchunk) {
   return nullptr;
 }
 
+
+// Persistent launches (rownorm_persistent_kernel) for the middle widths, for
+// RMSNorm, LayerNorm and L2Norm: an entry serves widths [min_nchunk,
+// max_nchunk] (chunks) at row counts [min_rows, max_rows]; the first entry
+// that matches is used, else the one-shot table. Entries and windows come from
+// an interleaved timing sweep on MI355X (N = 2560 ... 8192, M = 256 ... 8192,
+// grids of 512 ... 2048 workgroups, cold and warm caches): the persistent
+// kernel is kept wherever it was at least as fast as the one-shot kernel,
+// typically by 5-20% where the one-shot grid is only a few workgroups per CU
+// deep. The best grid keeps about 40-64 KiB of row copies in flight per CU.
+struct PersistentCfg {
+  int min_nchunk, max_nchunk;  // widths served, in 16-byte chunks
+  int wpr, rpl, maxc;
+  int grid;                    // workgroups launched (fewer if there are fewer row sets)
+  int64_t min_rows, max_rows;  // row counts served
+  RowNormKernel ragged[2];     // [bf16, fp16]
+  RowNormKernel full[2];       // width exactly 64 * wpr * maxc chunks
+};
+
+#define MBN_PCFG(MODE, LO, HI, WPR, RPL, MAXC, GRID, MINROWS, MAXROWS)                \
+  PersistentCfg {                                                                     \
+    LO, HI, WPR, RPL, MAXC, GRID, MINROWS, MAXROWS,                                   \
+        {&rownorm_persistent_kernel<MODE, Bf16, WPR, RPL, MAXC, false>,               \
+         &rownorm_persistent_kernel<MODE, F16, WPR, RPL, MAXC, false>},               \
+        {&rownorm_persistent_kernel<MODE, Bf16, WPR, RPL, MAXC, true>,                \
+         &rownorm_persistent_kernel<MODE, F16, WPR, RPL, MAXC, true>}                 \
+  }
+
+const PersistentCfg kRmsPersistent[] = {
+    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 1, 8192),   // 2048 < N <= 3072
+    MBN_PCFG(Norm::kRms, 385, 512, 4, 1, 2, 1536, 1, 256),    // 3072 < N <= 4096
+    MBN_PCFG(Norm::kRms, 385, 512, 4, 1, 2, 1536, 1536, 8192),
+    MBN_PCFG(Norm::kRms, 513, 768, 4, 1, 4, 1024, 1, 8192),   // 4096 < N <= 6144
+    MBN_PCFG(Norm::kRms, 769, 1024, 4, 1, 4, 1024, 1, 256),   // 6144 < N <= 8192
+    MBN_PCFG(Norm::kRms, 769, 1024, 4, 1, 4, 1024, 1536, 4096),
+};
+const PersistentCfg kLayerPersistent[] = {
+    MBN_PCFG(Norm::kLayer, 257, 384, 4, 1, 2, 2048, 1, 8192),
+    MBN_PCFG(Norm::kLayer, 385, 512, 4, 1, 2, 1536, 1, 8192),
+    MBN_PCFG(Norm::kLayer, 513, 768, 4, 1, 4, 1024, 1, 1536),
+    MBN_PCFG(Norm::kLayer, 513, 768, 4, 1, 4, 1024, 2560, 8192),
+    MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 1, 768),
+    MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 1536, 8192),
+};
+const PersistentCfg kL2Persistent[] = {
+    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 1, 8192),
+    MBN_PCFG(Norm::kL2, 385, 512, 4, 1, 2, 1536, 1536, 8192),
+    MBN_PCFG(Norm::kL2, 513, 768, 4, 1, 4, 1536, 768, 4096),
+    MBN_PCFG(Norm::kL2, 769, 1024, 4, 1, 4, 1024, 512, 6144),
+};
+
+template <size_t K>
+const PersistentCfg* pick_persistent(const PersistentCfg (&table)[K], int nchunk, int64_t M,
+                                     bool any_rows) {
+  for (const PersistentCfg& c : table)
+    if (nchunk >= c.min_nchunk && nchunk <= c.max_nchunk &&
+        (any_rows || (M >= c.min_rows && M <= c.max_rows)))
+      return &c;
+  return nullptr;
+}
+
+// LDS of a persistent launch: two buffers of RPL rows, then the partials
+// ([2 parities][2 reductions][RPL][WPR] floats).
+size_t persistent_lds_bytes(const PersistentCfg& c, int nchunk) {
+  return (size_t)2 * c.rpl * nchunk * 16 + (size_t)4 * c.rpl * c.wpr * sizeof(float);
+}
 }  // namespace
 
 // Dynamic LDS of a launch: the staged rows, raised to kLdsPerCU / cap when an
@@ -351,8 +631,35 @@ size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu) {
   return lds;
 }
 
-hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream) {
+hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream,
+                          RowNormPath path, int grid) {
   const int nchunk = args.nchunk;
+  const int64_t N = (int64_t)nchunk * 8;
+  const int d = dtype == Storage::kF16 ? 1 : 0;
+  args.inv_n = 1.0f / (float)N;
+  args.xcd_group = 0;
+
+  if (path != RowNormPath::kOneShot) {
+    const bool forced = path == RowNormPath::kPersistent;
+    const PersistentCfg* pc = nullptr;
+    switch (mode) {
+      case Norm::kRms: pc = pick_persistent(kRmsPersistent, nchunk, args.M, forced); break;
+      case Norm::kLayer: pc = pick_persistent(kLayerPersistent, nchunk, args.M, forced); break;
+      case Norm::kL2: pc = pick_persistent(kL2Persistent, nchunk, args.M, forced); break;
+      case Norm::kAddRms: break;
+    }
+    if (forced && !pc) return hipErrorInvalidValue;
+    if (pc) {
+      const int64_t sets = (args.M + pc->rpl - 1) / pc->rpl;
+      int64_t g = grid > 0 ? grid : pc->grid;
+      if (g > sets) g = sets;
+      const RowNormKernel kernel = (nchunk == 64 * pc->wpr * pc->maxc) ? pc->full[d] : pc->ragged[d];
+      hipLaunchKernelGGL(kernel, dim3((unsigned)g), dim3(64 * pc->wpr), persistent_lds_bytes(*pc, nchunk),
+                         stream, args);
+      return hipGetLastError();
+    }
+  }
+
   const RowNormCfg* cfg = nullptr;
   switch (mode) {
     case Norm::kRms: cfg = pick(kRmsTable, nchunk); break;
@@ -364,10 +671,7 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
   if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant
   const int rows_per_wg = cfg->rows * cfg->rpl;
   const int64_t blocks = (args.M + rows_per_wg - 1) / rows_per_wg;
-  const int64_t N = (int64_t)nchunk * 8;
   const size_t lds = rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
-  args.inv_n = 1.0f / (float)N;
-  const int d = dtype == Storage::kF16 ? 1 : 0;
   const RowNormKernel kernel = (nchunk == cfg->max_nchunk) ? cfg->full[d] : cfg->ragged[d];
   args.xcd_group = cfg->xcd_group;
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * cfg->wpr * cfg->rows), lds, stream,

@@ -2,7 +2,9 @@
 bands cover every width up to MBN_RMSNORM_MAX_N in increasing order, every
 entry with several waves per row serves only widths of at least 64 * WPR chunks
 (each wave parks its partial sum in its own first chunk), workgroups stay within
-1024 threads and the staged rows within the 160 KiB of LDS of a CU."""
+1024 threads and the staged rows within the 160 KiB of LDS of a CU; the
+persistent tables serve only widths their kernel covers, with sane row windows
+and double buffers that fit in LDS."""
 
 import os
 import re
@@ -54,3 +56,50 @@ def test_table_invariants(name):
             assert top > prev
             prev = top
     assert prev * 8 == 65536  # the widest band reaches MBN_RMSNORM_MAX_N
+
+
+PCFG = r"MBN_PCFG\(Norm::(\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
+
+
+def _persistent():
+    s = open(SRC).read()
+    out = {}
+    for tname, body in re.findall(r"const PersistentCfg (k\w+)\[\] = \{(.*?)\n\};", s, re.S):
+        out[tname] = [tuple(map(int, e[1:])) for e in re.findall(PCFG, body)]
+    return out
+
+
+PERSISTENT = _persistent()
+
+
+def test_persistent_tables_found():
+    assert set(PERSISTENT) == {"kRmsPersistent", "kLayerPersistent", "kL2Persistent"}
+    assert all(PERSISTENT.values())
+
+
+@pytest.mark.parametrize("name", sorted(PERSISTENT))
+def test_persistent_invariants(name):
+    for lo, hi, wpr, rpl, maxc, grid, min_rows, max_rows in PERSISTENT[name]:
+        assert 1 <= lo <= hi <= 64 * wpr * maxc, (name, lo, hi)
+        assert 64 * wpr * (maxc // 2) < hi or maxc == 1  # no narrower kernel would do
+        assert 64 * wpr <= 1024 and rpl >= 1
+        # two buffers of rpl rows plus the partial sums
+        assert 2 * rpl * hi * 16 + 4 * rpl * wpr * 4 <= 160 * 1024
+        assert 256 <= grid <= 8 * 256
+        assert 1 <= min_rows <= max_rows
+
+
+@pytest.mark.parametrize("name", sorted(PERSISTENT))
+def test_persistent_windows_do_not_overlap(name):
+    """Within one width band the row windows are disjoint, so the first match
+    is the only match."""
+    bands = {}
+    for lo, hi, *_, min_rows, max_rows in PERSISTENT[name]:
+        bands.setdefault((lo, hi), []).append((min_rows, max_rows))
+    spans = sorted(bands)
+    for (a_lo, a_hi), (b_lo, b_hi) in zip(spans, spans[1:]):
+        assert a_hi < b_lo  # bands are disjoint too
+    for windows in bands.values():
+        windows.sort()
+        for (_, a_max), (b_min, _) in zip(windows, windows[1:]):
+            assert a_max < b_min
