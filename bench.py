@@ -99,7 +99,8 @@ def cpu_baseline(x_bits, w_bits, eps, n: int, budget_s: float):
 
 def suite(steps: int, warmup: int) -> int:
     """Per-workload timing table (one JSON line per workload): all five inputs,
-    the pages' 3 x 3 RMSNorm shape grid, and the rest of the norm family.
+    the pages' 3 x 3 RMSNorm shape grid, widths that are not whole 16-byte
+    chunks, and the rest of the norm family.
 
     Workloads whose footprint is under 1 GiB rotate over enough copies of their
     buffers that successive launches cannot be served from the 256 MiB Infinity
@@ -178,6 +179,24 @@ def suite(steps: int, warmup: int) -> int:
                               "batch_mean_us": round(timed.batch_us, 2),
                               "pct_of_8TBps_batch": round(b / timed.batch_us / 1e3 / 80.0, 2)}), flush=True)
             del xs, ys, x0
+    # Widths that are not whole 16-byte chunks (the any-width kernels: 4-, 2-
+    # and 1-element accesses), from the same input.
+    for N in (16380, 16382, 16383):
+        M = 16384
+        x0 = x_full[:, :N].contiguous()
+        w = w_full[:N].contiguous()
+        nrot = max(1, -(-(1 << 30) // (2 * M * N * 2)))
+        xs = [x0] + [x0.clone() for _ in range(nrot - 1)]
+        ys = [torch.empty_like(x0) for _ in range(nrot)]
+        med, best = timed(lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps), nrot)
+        b = 2 * M * N * 2 + 2 * N
+        print(json.dumps({"workload": f"any_{M}x{N}", "kernel": "rmsnorm_fwd", "M": M, "N": N,
+                          "rotating_sets": nrot, "median_us": round(med, 2), "best_us": round(best, 2),
+                          "GBps_median": round(b / med / 1e3, 1),
+                          "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2),
+                          "batch_mean_us": round(timed.batch_us, 2),
+                          "pct_of_8TBps_batch": round(b / timed.batch_us / 1e3 / 80.0, 2)}), flush=True)
+        del xs, ys, x0
     del x_full, w_full
     torch.cuda.empty_cache()
 

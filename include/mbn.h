@@ -32,12 +32,13 @@ extern "C" {
                               eps negative / NaN / infinite, odd head_dim,
                               overlapping input and output ranges */
 #define MBN_EUNSUPPORTED 2 /* valid but outside what the kernels handle: row
-                              width not a multiple of 8, wider than
-                              MBN_RMSNORM_MAX_N, pointer not 16-byte aligned,
-                              head_dim other than MBN_QK_HEAD_DIM */
+                              wider than MBN_RMSNORM_MAX_N, a row-norm pointer
+                              at an odd address, a QK pointer not 16-byte
+                              aligned, head_dim other than MBN_QK_HEAD_DIM */
 #define MBN_EHIP 3         /* the kernel launch failed */
 
-/* Widest RMSNorm row: one row is staged whole in LDS (2 bytes per element). */
+/* Widest row of the row norms: one row is staged whole in LDS (2 bytes per
+ * element). */
 #define MBN_RMSNORM_MAX_N 65536
 /* Head size handled by qk_norm_rope_fwd. */
 #define MBN_QK_HEAD_DIM 128
@@ -61,10 +62,15 @@ extern "C" {
  *          allowed; any other overlap of y with x or w is MBN_EINVAL.
  *   M      rows, >= 0 (M == 0 returns MBN_OK, pointers may then be NULL);
  *          at most 2^31 - 1
- *   N      row width, 1 <= N <= MBN_RMSNORM_MAX_N, N % 8 == 0
+ *   N      row width, 1 <= N <= MBN_RMSNORM_MAX_N
  *   eps    finite, >= 0 (added inside the square root)
  *   stream hipStream_t or NULL
- * x, w and y must be 16-byte aligned.
+ * x, w and y must be 2-byte aligned (an odd address is MBN_EUNSUPPORTED).
+ * Launch path (same results to the documented tolerance, not bit-identical):
+ * when N % 8 == 0 and every pointer is 16-byte aligned, the staged-row
+ * kernels (16-byte row chunks); otherwise the any-width kernels, which access
+ * one element at a time, read and write nothing outside the rows, and are
+ * slower. The same holds for add_rmsnorm_fwd, layernorm_fwd and l2norm_fwd.
  * IEEE behaviour: a NaN in a row makes the row NaN; an infinite element makes
  * the finite elements of its row 0 and itself NaN; a zero row gives 0 when
  * eps > 0 and NaN when eps == 0. Rows whose sum of squares overflows fp32
@@ -90,7 +96,8 @@ MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_
  *   M, N, eps, stream: as for rmsnorm_fwd.
  * h and y may each coincide exactly with x or with r (in place); h and y must
  * not overlap each other, and no other overlap is allowed (MBN_EINVAL). All
- * five pointers must be 16-byte aligned.
+ * five pointers must be 2-byte aligned (16-byte aligned with N % 8 == 0 for
+ * the staged-row kernels).
  */
 MBN_API int add_rmsnorm_fwd(const void* x, const void* r, const void* w, void* h, void* y,
                             int64_t M, int64_t N, float eps, void* stream);
@@ -109,7 +116,7 @@ MBN_API int add_rmsnorm_fwd(const void* x, const void* r, const void* w, void* h
  *
  *   x      device, bf16 [M, N];  w, b  device, bf16 [N];  y  device, bf16 [M, N]
  *   M, N, eps, stream: as for rmsnorm_fwd. y == x allowed; w and b must not
- *   overlap y. All pointers 16-byte aligned.
+ *   overlap y. Pointer alignment and launch path as for rmsnorm_fwd.
  */
 MBN_API int layernorm_fwd(const void* x, const void* w, const void* b, void* y, int64_t M,
                           int64_t N, float eps, void* stream);
@@ -122,8 +129,8 @@ MBN_API int layernorm_fwd(const void* x, const void* w, const void* b, void* y, 
  *     y[i,j] = bf16( x[i,j] / max( sqrt( sum_j x[i,j]^2 ), eps ) )
  * A NaN anywhere in a row makes the row NaN; eps = 0 and a zero row give NaN.
  *
- *   x, y   device, bf16 [M, N] (y == x allowed), 16-byte aligned
- *   M, N, eps, stream: as for rmsnorm_fwd.
+ *   x, y   device, bf16 [M, N] (y == x allowed)
+ *   M, N, eps, stream, pointer alignment, launch path: as for rmsnorm_fwd.
  */
 MBN_API int l2norm_fwd(const void* x, void* y, int64_t M, int64_t N, float eps, void* stream);
 

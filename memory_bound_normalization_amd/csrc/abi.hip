@@ -25,7 +25,7 @@ bool valid_eps(float eps) { return isfinite(eps) && eps >= 0.0f; }
 int check_rows(int64_t M, int64_t N, float eps) {
   if (M < 0 || N <= 0 || !valid_eps(eps)) return MBN_EINVAL;
   if (M == 0) return -1;
-  if (N % 8 != 0 || N > MBN_RMSNORM_MAX_N || M > 0x7fffffffLL) return MBN_EUNSUPPORTED;
+  if (N > MBN_RMSNORM_MAX_N || M > 0x7fffffffLL) return MBN_EUNSUPPORTED;
   return MBN_OK;
 }
 
@@ -35,24 +35,46 @@ bool bad_alias(const void* out, const void* in, int64_t bytes) {
   return out != in && overlap(out, bytes, in, bytes);
 }
 
-int launch(mbn::Norm mode, mbn::Storage dt, mbn::RowNormArgs a, void* stream) {
-  const hipError_t err = mbn::launch_rownorm(mode, dt, a, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? MBN_OK : MBN_EHIP;
-}
+// Row-norm pointers must be element (2-byte) aligned; null ones (unused
+// operands) pass.
+bool elem_aligned(const void* p) { return aligned(p, 2); }
+bool chunk_aligned(const void* p) { return aligned(p, 16); }
 
-mbn::RowNormArgs row_args(const void* x, const void* r, const void* w, const void* b,
-                                 void* h, void* y, int64_t M, int64_t N, float eps) {
-  mbn::RowNormArgs a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.r = static_cast<const uint16_t*>(r);
-  a.w = static_cast<const uint16_t*>(w);
-  a.b = static_cast<const uint16_t*>(b);
-  a.h = static_cast<uint16_t*>(h);
-  a.y = static_cast<uint16_t*>(y);
-  a.M = M;
-  a.nchunk = (int)(N / 8);
-  a.eps = eps;
-  return a;
+// Launch a row norm: the staged-row kernels when every row is whole 16-byte
+// chunks (N % 8 == 0, all pointers 16-byte aligned), else the any-width
+// kernels. Unused operands are null.
+int launch(mbn::Norm mode, mbn::Storage dt, const void* x, const void* r, const void* w,
+           const void* b, void* h, void* y, int64_t M, int64_t N, float eps, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool chunked = N % 8 == 0 && chunk_aligned(x) && chunk_aligned(r) && chunk_aligned(w) &&
+                       chunk_aligned(b) && chunk_aligned(h) && chunk_aligned(y);
+  hipError_t err;
+  if (chunked) {
+    mbn::RowNormArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.r = static_cast<const uint16_t*>(r);
+    a.w = static_cast<const uint16_t*>(w);
+    a.b = static_cast<const uint16_t*>(b);
+    a.h = static_cast<uint16_t*>(h);
+    a.y = static_cast<uint16_t*>(y);
+    a.M = M;
+    a.nchunk = (int)(N / 8);
+    a.eps = eps;
+    err = mbn::launch_rownorm(mode, dt, a, s);
+  } else {
+    mbn::RowNormAnyArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.r = static_cast<const uint16_t*>(r);
+    a.w = static_cast<const uint16_t*>(w);
+    a.b = static_cast<const uint16_t*>(b);
+    a.h = static_cast<uint16_t*>(h);
+    a.y = static_cast<uint16_t*>(y);
+    a.M = M;
+    a.n = (int)N;
+    a.eps = eps;
+    err = mbn::launch_rownorm_any(mode, dt, a, s);
+  }
+  return err == hipSuccess ? MBN_OK : MBN_EHIP;
 }
 
 // Entry-point bodies, shared by the bf16 and fp16 variants (the storage type
@@ -62,11 +84,10 @@ int rmsnorm_impl(mbn::Storage dt, const void* x, const void* w, void* y, int64_t
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !w || !y) return MBN_EINVAL;
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return MBN_EUNSUPPORTED;
+  if (!elem_aligned(x) || !elem_aligned(w) || !elem_aligned(y)) return MBN_EUNSUPPORTED;
   const int64_t bytes = M * N * 2;
   if (bad_alias(y, x, bytes) || overlap(w, N * 2, y, bytes)) return MBN_EINVAL;
-  return launch(mbn::Norm::kRms, dt, row_args(x, nullptr, w, nullptr, nullptr, y, M, N, eps),
-                stream);
+  return launch(mbn::Norm::kRms, dt, x, nullptr, w, nullptr, nullptr, y, M, N, eps, stream);
 }
 
 int add_rmsnorm_impl(mbn::Storage dt, const void* x, const void* r, const void* w, void* h,
@@ -74,14 +95,15 @@ int add_rmsnorm_impl(mbn::Storage dt, const void* x, const void* r, const void* 
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !r || !w || !h || !y) return MBN_EINVAL;
-  if (!aligned(x, 16) || !aligned(r, 16) || !aligned(w, 16) || !aligned(h, 16) || !aligned(y, 16))
+  if (!elem_aligned(x) || !elem_aligned(r) || !elem_aligned(w) || !elem_aligned(h) ||
+      !elem_aligned(y))
     return MBN_EUNSUPPORTED;
   const int64_t bytes = M * N * 2;
   if (overlap(h, bytes, y, bytes) || bad_alias(h, x, bytes) || bad_alias(h, r, bytes) ||
       bad_alias(y, x, bytes) || bad_alias(y, r, bytes) || overlap(w, N * 2, h, bytes) ||
       overlap(w, N * 2, y, bytes))
     return MBN_EINVAL;
-  return launch(mbn::Norm::kAddRms, dt, row_args(x, r, w, nullptr, h, y, M, N, eps), stream);
+  return launch(mbn::Norm::kAddRms, dt, x, r, w, nullptr, h, y, M, N, eps, stream);
 }
 
 int layernorm_impl(mbn::Storage dt, const void* x, const void* w, const void* b, void* y,
@@ -89,12 +111,12 @@ int layernorm_impl(mbn::Storage dt, const void* x, const void* w, const void* b,
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !w || !b || !y) return MBN_EINVAL;
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(b, 16) || !aligned(y, 16))
+  if (!elem_aligned(x) || !elem_aligned(w) || !elem_aligned(b) || !elem_aligned(y))
     return MBN_EUNSUPPORTED;
   const int64_t bytes = M * N * 2;
   if (bad_alias(y, x, bytes) || overlap(w, N * 2, y, bytes) || overlap(b, N * 2, y, bytes))
     return MBN_EINVAL;
-  return launch(mbn::Norm::kLayer, dt, row_args(x, nullptr, w, b, nullptr, y, M, N, eps), stream);
+  return launch(mbn::Norm::kLayer, dt, x, nullptr, w, b, nullptr, y, M, N, eps, stream);
 }
 
 int l2norm_impl(mbn::Storage dt, const void* x, void* y, int64_t M, int64_t N, float eps,
@@ -102,10 +124,9 @@ int l2norm_impl(mbn::Storage dt, const void* x, void* y, int64_t M, int64_t N, f
   const int st = check_rows(M, N, eps);
   if (st != MBN_OK) return st < 0 ? MBN_OK : st;
   if (!x || !y) return MBN_EINVAL;
-  if (!aligned(x, 16) || !aligned(y, 16)) return MBN_EUNSUPPORTED;
+  if (!elem_aligned(x) || !elem_aligned(y)) return MBN_EUNSUPPORTED;
   if (bad_alias(y, x, M * N * 2)) return MBN_EINVAL;
-  return launch(mbn::Norm::kL2, dt,
-                row_args(x, nullptr, nullptr, nullptr, nullptr, y, M, N, eps), stream);
+  return launch(mbn::Norm::kL2, dt, x, nullptr, nullptr, nullptr, nullptr, y, M, N, eps, stream);
 }
 
 int qk_impl(mbn::Storage dt, void* qkv, const void* q_w, const void* k_w,

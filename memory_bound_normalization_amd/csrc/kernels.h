@@ -38,6 +38,27 @@ enum class RowNormPath : int { kAuto = 0, kOneShot = 1, kPersistent = 2 };
 hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream,
                           RowNormPath path = RowNormPath::kAuto, int grid = 0);
 
+// Arguments of the any-width row norms (rownorm_any.hip): pointers need only
+// 2-byte alignment and N may be any width up to MBN_RMSNORM_MAX_N.
+struct RowNormAnyArgs {
+  const uint16_t* x;
+  const uint16_t* r;
+  const uint16_t* w;
+  const uint16_t* b;
+  uint16_t* h;
+  uint16_t* y;
+  int64_t M;
+  int n;        // N
+  float inv_n;  // set by the launcher
+  float eps;
+};
+
+hipError_t launch_rownorm_any(Norm mode, Storage dtype, RowNormAnyArgs args, hipStream_t stream);
+
+// Elements per access (4, 2 or 1) the any-width kernels use for these
+// arguments: the widest group that divides N and every pointer's alignment.
+int rownorm_any_group(const RowNormAnyArgs& args);
+
 // Dynamic LDS bytes a row-norm launch requests (exposed for tuning tools).
 size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu);
 

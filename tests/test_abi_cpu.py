@@ -83,13 +83,13 @@ def rms(lib, x=FAKE, w=FAKE + 0x10000000, y=FAKE + 0x20000000, M=4, N=64, eps=1e
         (dict(x=None), mbn.MBN_EINVAL),
         (dict(w=None), mbn.MBN_EINVAL),
         (dict(y=None), mbn.MBN_EINVAL),
-        (dict(N=12), mbn.MBN_EUNSUPPORTED),
-        (dict(N=1), mbn.MBN_EUNSUPPORTED),
         (dict(N=65544), mbn.MBN_EUNSUPPORTED),
+        (dict(N=65537), mbn.MBN_EUNSUPPORTED),
         (dict(M=1 << 31), mbn.MBN_EUNSUPPORTED),
-        (dict(x=FAKE + 2), mbn.MBN_EUNSUPPORTED),
-        (dict(w=FAKE + 0x10000008), mbn.MBN_EUNSUPPORTED),
-        (dict(y=FAKE + 0x20000004), mbn.MBN_EUNSUPPORTED),
+        (dict(x=FAKE + 1), mbn.MBN_EUNSUPPORTED),  # odd address: not an element boundary
+        (dict(w=FAKE + 0x10000001), mbn.MBN_EUNSUPPORTED),
+        (dict(y=FAKE + 0x20000003), mbn.MBN_EUNSUPPORTED),
+        (dict(N=12, x=FAKE + 3), mbn.MBN_EUNSUPPORTED),  # any-width path, odd x
         (dict(y=FAKE + 16), mbn.MBN_EINVAL),  # partial overlap of y with x
         (dict(w=FAKE + 0x20000000 + 64), mbn.MBN_EINVAL),  # w inside y
     ],
@@ -163,8 +163,9 @@ B = 0x10000000  # spacing of the fake buffers below
         (dict(eps=float("nan")), mbn.MBN_EINVAL),
         (dict(r=None), mbn.MBN_EINVAL),
         (dict(h=None), mbn.MBN_EINVAL),
-        (dict(N=20), mbn.MBN_EUNSUPPORTED),
-        (dict(r=FAKE + 1 * B + 8), mbn.MBN_EUNSUPPORTED),
+        (dict(N=65544), mbn.MBN_EUNSUPPORTED),
+        (dict(r=FAKE + 1 * B + 1), mbn.MBN_EUNSUPPORTED),
+        (dict(h=FAKE + 3 * B + 5), mbn.MBN_EUNSUPPORTED),
         (dict(h=FAKE + 4 * B), mbn.MBN_EINVAL),  # h == y
         (dict(h=FAKE + 4 * B + 64), mbn.MBN_EINVAL),  # h overlaps y
         (dict(y=FAKE + 16), mbn.MBN_EINVAL),  # y overlaps x partially
@@ -186,7 +187,7 @@ def test_add_rmsnorm_rejects(lib, kw, status):
         (dict(b=None), mbn.MBN_EINVAL),
         (dict(w=None), mbn.MBN_EINVAL),
         (dict(N=65544), mbn.MBN_EUNSUPPORTED),
-        (dict(b=FAKE + 2 * B + 4), mbn.MBN_EUNSUPPORTED),
+        (dict(b=FAKE + 2 * B + 1), mbn.MBN_EUNSUPPORTED),
         (dict(b=FAKE + 3 * B + 32), mbn.MBN_EINVAL),  # b inside y
         (dict(y=FAKE + 496), mbn.MBN_EINVAL),  # y overlaps the tail of x
     ],
@@ -203,8 +204,8 @@ def test_layernorm_rejects(lib, kw, status):
         (dict(M=-3), mbn.MBN_EINVAL),
         (dict(x=None), mbn.MBN_EINVAL),
         (dict(eps=float("inf")), mbn.MBN_EINVAL),
-        (dict(N=4), mbn.MBN_EUNSUPPORTED),
-        (dict(y=FAKE + 1 * B + 2), mbn.MBN_EUNSUPPORTED),
+        (dict(N=70000), mbn.MBN_EUNSUPPORTED),
+        (dict(y=FAKE + 1 * B + 7), mbn.MBN_EUNSUPPORTED),
         (dict(y=FAKE + 256), mbn.MBN_EINVAL),
     ],
 )

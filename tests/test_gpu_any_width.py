@@ -1,0 +1,150 @@
+"""GPU parity of the any-width row norms (rows that are not whole 16-byte
+chunks, N % 8 != 0, or pointers that are only element-aligned) against the
+fp64 oracle, every output compared.
+
+The kernels access groups of 4, 2 or 1 elements (N % 4 == 0, N % 2 == 0,
+odd N, or pointers aligned to less); the widths cover every band of each
+group size's launch table (up to 1024/4096/8192/32768/65536 elements, the
+LDS-staged band of odd widths above 32768) on both sides of the band edges.
+Row counts include a single row and counts that are not a multiple of
+anything. Outputs are written into views of larger buffers whose
+guard elements must stay untouched: the element-wise path reads and writes
+nothing outside its rows, including the neighbouring rows' elements that
+share a 16-byte chunk.
+"""
+
+import numpy as np
+import pytest
+
+import memory_bound_normalization_amd as mbn
+from oracle import add_rmsnorm_fwd as o_add, l2norm_fwd as o_l2, layernorm_fwd as o_ln, rmsnorm_fwd as o_rms
+from parity import assert_parity, from_gpu_bf16, to_gpu_bf16
+from workloads import f32_to_bf16_bits, random_bf16_bits
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+WIDTHS = [
+    1, 3, 7, 9, 511, 513, 2047, 2049, 8191, 8193, 12345, 32767, 32769, 40001, 65535,  # odd: 1 element
+    2, 6, 1002, 1026, 4094, 4098, 8190, 8194, 32766, 32770, 65534,  # N % 4 == 2: 2 elements
+    12, 100, 1004, 1028, 4092, 4100, 8188, 8196, 32764, 32772, 40000, 65532,  # N % 8 == 4: 4 elements
+]
+GUARD = 5  # guard elements on each side of an output view
+FILL = 0x4B00  # bf16 / fp16 bit pattern the guards hold
+
+
+def _rows(N):
+    return 1 if N > 32768 else (3 if N > 8192 else 37)
+
+
+def _inputs(M, N, seed, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    if dtype == "f16":
+        f = lambda a: a.astype(np.float16).view(np.uint16)  # noqa: E731
+        return (f(rng.standard_normal((M, N))), f(rng.standard_normal((M, N))),
+                f(rng.uniform(0.5, 1.5, N)), f(rng.uniform(-0.5, 0.5, N)))
+    return (random_bf16_bits(rng, (M, N)), random_bf16_bits(rng, (M, N)),
+            random_bf16_bits(rng, (N,), lo=0.5, hi=1.5), random_bf16_bits(rng, (N,), lo=-0.5, hi=0.5))
+
+
+def _guarded(M, N, dtype):
+    """An output buffer with GUARD fill elements before and after an [M, N] view."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    buf = torch.full((M * N + 2 * GUARD,), 0, dtype=torch.int16, device="cuda")
+    buf.fill_(FILL)
+    buf = buf.view(tdt)
+    return buf, buf[GUARD : GUARD + M * N].view(M, N)
+
+
+def _guards_intact(buf, M, N):
+    g = torch.cat([buf[:GUARD], buf[GUARD + M * N :]]).view(torch.int16).cpu().numpy().view(np.uint16)
+    return bool(np.all(g == FILL))
+
+
+def _check(op, M, N, seed, dtype="bf16", eps=1e-6):
+    print(f"[any-width {op} {dtype}] M={M} N={N}", flush=True)
+    x, r, w, b = _inputs(M, N, seed, dtype)
+    xg, rg = to_gpu_bf16(x, dtype=dtype), to_gpu_bf16(r, dtype=dtype)
+    wg, bg = to_gpu_bf16(w, dtype=dtype), to_gpu_bf16(b, dtype=dtype)
+    ybuf, y = _guarded(M, N, dtype)
+    if op == "rms":
+        mbn.rmsnorm_fwd(xg, wg, y, eps=eps)
+        ref = o_rms(x, w, eps, dtype=dtype)
+    elif op == "layer":
+        mbn.layernorm_fwd(xg, wg, bg, y, eps=eps)
+        ref = o_ln(x, w, b, eps, dtype=dtype)
+    elif op == "l2":
+        mbn.l2norm_fwd(xg, y, eps=eps)
+        ref = o_l2(x, eps, dtype=dtype)
+    else:
+        hbuf, h = _guarded(M, N, dtype)
+        mbn.add_rmsnorm_fwd(xg, rg, wg, h=h, y=y, eps=eps)
+        rh, ref = o_add(x, r, w, eps, dtype=dtype)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_gpu_bf16(h), rh), f"h = round(x + r) not bit-exact, {op} M={M} N={N}"
+        assert _guards_intact(hbuf, M, N), "wrote outside h"
+    torch.cuda.synchronize()
+    assert_parity(from_gpu_bf16(y), ref, f"{op} M={M} N={N} {dtype}", dtype=dtype)
+    assert _guards_intact(ybuf, M, N), "wrote outside y"
+
+
+@pytest.mark.parametrize("N", WIDTHS)
+@pytest.mark.parametrize("op", ["rms", "add", "layer", "l2"])
+def test_any_width(op, N):
+    _check(op, _rows(N), N, seed=N)
+
+
+@pytest.mark.parametrize("N", [3, 1001, 8191, 40001, 4098, 4100, 40000])
+@pytest.mark.parametrize("op", ["rms", "add", "layer", "l2"])
+def test_any_width_f16(op, N):
+    _check(op, _rows(N), N, seed=N + 1, dtype="f16", eps=1e-5)
+
+
+@pytest.mark.parametrize("M", [1, 2, 65, 20000])
+def test_any_width_row_counts(M):
+    _check("rms", M, 1001, seed=M)
+    _check("layer", M, 1001, seed=M + 1)
+    _check("add", M, 1004, seed=M + 2)
+    _check("l2", M, 1002, seed=M + 3)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 4])
+def test_aligned_width_with_misaligned_pointers(offset):
+    """N % 8 == 0 but x at an offset of 1, 2 or 4 elements (2, 4 or 8 bytes):
+    the any-width kernels serve it with 1-, 2- or 4-element groups."""
+    M, N = 9, 4096
+    x, r, w, b = _inputs(M, N, 11 + offset)
+    for op in ("rms", "layer", "l2"):
+        print(f"[any-width misaligned {op}] M={M} N={N} offset={offset}", flush=True)
+        xb = torch.zeros(M * N + offset, dtype=torch.bfloat16, device="cuda")
+        xb[offset:] = to_gpu_bf16(x).view(-1)
+        xv = xb[offset:].view(M, N)
+        if op == "rms":
+            y, ref = mbn.rmsnorm_fwd(xv, to_gpu_bf16(w)), o_rms(x, w, 1e-6)
+        elif op == "layer":
+            y, ref = mbn.layernorm_fwd(xv, to_gpu_bf16(w), to_gpu_bf16(b), eps=1e-6), o_ln(x, w, b, 1e-6)
+        else:
+            y, ref = mbn.l2norm_fwd(xv, eps=1e-6), o_l2(x, 1e-6)
+        torch.cuda.synchronize()
+        assert_parity(from_gpu_bf16(y), ref, f"misaligned {op} offset {offset}")
+
+
+def test_in_place_and_special_rows():
+    M, N = 6, 4099
+    rng = np.random.default_rng(12)
+    x = random_bf16_bits(rng, (M, N))
+    w = random_bf16_bits(rng, (N,), lo=0.5, hi=1.5)
+    x[1, 17] = 0x7FC0  # NaN
+    x[2, :] = 0  # zero row
+    x[3, 4098] = 0x7F80  # +inf in the last element
+    x[4, :] = f32_to_bf16_bits(np.full(N, 1e15, dtype=np.float32))
+    ref = o_rms(x, w, 1e-6)
+    xg = to_gpu_bf16(x)
+    mbn.rmsnorm_fwd(xg, to_gpu_bf16(w), xg, eps=1e-6)  # in place
+    torch.cuda.synchronize()
+    assert_parity(from_gpu_bf16(xg), ref, "in place, special rows")
+    # eps = 0: the zero row becomes NaN
+    xg = to_gpu_bf16(x)
+    y = mbn.rmsnorm_fwd(xg, to_gpu_bf16(w), eps=0.0)
+    torch.cuda.synchronize()
+    assert_parity(from_gpu_bf16(y), o_rms(x, w, 0.0), "eps = 0")

@@ -106,13 +106,23 @@ def test_non_default_stream():
     assert_parity(from_gpu_bf16(y), oracle_rmsnorm(x, w, 1e-6), "side stream")
 
 
-def test_misaligned_pointer_is_rejected():
-    x = torch.zeros(4 * 64 + 8, dtype=torch.bfloat16, device="cuda")
-    w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
-    xv = x[1 : 1 + 4 * 64].view(4, 64)  # 2-byte offset
-    with pytest.raises(mbn.MbnError) as e:
-        mbn.rmsnorm_fwd(xv, w)
-    assert e.value.status == mbn.MBN_EUNSUPPORTED
+def test_misaligned_pointer_takes_the_any_width_path():
+    """x and y at a 2-byte offset (not 16-byte aligned): served element-wise,
+    correct, and nothing outside the rows is written."""
+    rng = np.random.default_rng(8)
+    M, N = 4, 64
+    x = random_bf16_bits(rng, (M, N))
+    w = random_bf16_bits(rng, (N,), lo=0.5, hi=1.5)
+    xb = torch.zeros(M * N + 8, dtype=torch.bfloat16, device="cuda")
+    yb = torch.full((M * N + 8,), 7.0, dtype=torch.bfloat16, device="cuda")
+    xb[1 : 1 + M * N] = to_gpu_bf16(x).view(-1)
+    xv = xb[1 : 1 + M * N].view(M, N)
+    yv = yb[3 : 3 + M * N].view(M, N)
+    mbn.rmsnorm_fwd(xv, to_gpu_bf16(w), yv)
+    torch.cuda.synchronize()
+    assert_parity(from_gpu_bf16(yv), oracle_rmsnorm(x, w, 1e-6), "misaligned x, y")
+    guard = torch.cat([yb[:3], yb[3 + M * N :]])
+    assert bool((guard == 7.0).all()), "wrote outside y"
 
 
 def _sample_rows(M, rng, extra=()):
