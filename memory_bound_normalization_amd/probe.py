@@ -10,6 +10,17 @@ kernel) as the calibration: the counters of the copy, whose true HBM traffic is
 known (512 MiB read, 512 MiB written), give the factor that converts each
 counter reading into bytes. `summarize` prints the per-launch HBM traffic of the
 RMSNorm kernel from the two runs' counter CSV files.
+
+    rocprofv3 --kernel-trace --stats -d <dir> -o run -- python -m memory_bound_normalization_amd.probe ceiling
+    python -m memory_bound_normalization_amd.probe ceiling-summary <dir>
+
+`ceiling` times plain streaming kernels of torch on the same 512 MiB buffers
+(read only: a sum; write only: a fill; read + write: a copy and a scale)
+beside rmsnorm_fwd, each over two alternating buffer sets (1 GiB apart, so
+nothing is served from the 256 MiB Infinity Cache); `ceiling-summary` turns
+the kernel trace into GB/s per kernel. It measures what the memory system
+gives a 50/50 read/write stream on this part, the reference for the RMSNorm
+kernel's fraction of peak.
 """
 
 from __future__ import annotations
@@ -48,6 +59,78 @@ def run() -> None:
         z.copy_(x)
         torch.cuda.synchronize()
         print(f"copy launch {i} done", flush=True)
+
+
+CEIL_REPS = 20
+
+
+def ceiling() -> None:
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+    from workloads import RMS_WORKLOADS, make_rms_inputs
+
+    wl = RMS_WORKLOADS["rms_16384x16384"]
+    x_bits, w_bits, eps = make_rms_inputs(wl)
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xs = [x0, x0.clone()]
+    ys = [torch.empty_like(x0), torch.empty_like(x0)]
+    cases = [
+        ("read only (sum)", COPY_BYTES, lambda i: xs[i].sum(dtype=torch.float32)),
+        ("write only (fill)", COPY_BYTES, lambda i: ys[i].fill_(1.0)),
+        ("read + write (copy)", 2 * COPY_BYTES, lambda i: ys[i].copy_(xs[i])),
+        ("read + write (scale)", 2 * COPY_BYTES, lambda i: torch.mul(xs[i], 2.0, out=ys[i])),
+        ("rmsnorm_fwd", 2 * COPY_BYTES + 2 * 16384, lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps)),
+    ]
+    for name, nbytes, fn in cases:
+        for i in range(3):
+            fn(i % 2)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(CEIL_REPS)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            fn(i % 2)
+            b.record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        med = us[len(us) // 2]
+        print(json.dumps({"case": name, "bytes": nbytes, "median_us": round(med, 2),
+                          "GBps": round(nbytes / med / 1e3, 1), "pct_of_8TBps": round(nbytes / med / 1e3 / 80, 2)}),
+              flush=True)
+
+
+def ceiling_summary(d: str) -> None:
+    """GB/s per kernel from a rocprofv3 kernel trace of `ceiling`."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # dispatches of >= 20 us are the 512 MiB kernels; the last ones come in
+    # blocks of 3 warm-up + CEIL_REPS per case, in the order of `ceiling`
+    # (before them: the clone that makes the second buffer set)
+    big = [r for r in rows if int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) > 20000]
+    names = ["read only (sum)", "write only (fill)", "read + write (copy)", "read + write (scale)", "rmsnorm_fwd"]
+    nbytes = [COPY_BYTES, COPY_BYTES, 2 * COPY_BYTES, 2 * COPY_BYTES, 2 * COPY_BYTES + 2 * 16384]
+    per = 3 + CEIL_REPS
+    if len(big) < per * len(names):
+        raise SystemExit(f"expected {per * len(names)} large dispatches, found {len(big)}")
+    big = big[len(big) - per * len(names):]
+    for k, (name, nb) in enumerate(zip(names, nbytes)):
+        grp = big[k * per + 3 : (k + 1) * per]
+        d_us = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+        med = d_us[len(d_us) // 2]
+        kname = grp[0]["Kernel_Name"].split("(")[0][:60]
+        print(f"{name:<22} {med:9.2f} us {nb / med / 1e3:8.0f} GB/s {nb / med / 1e3 / 80:6.1f}%   {kname}")
 
 
 def _rows(d: str):
@@ -98,7 +181,11 @@ def summarize(fetch_dir: str, write_dir: str) -> None:
 
 
 if __name__ == "__main__":
-    if len(sys.argv) >= 2 and sys.argv[1] == "run":
+    if len(sys.argv) >= 2 and sys.argv[1] == "ceiling":
+        ceiling()
+    elif len(sys.argv) >= 3 and sys.argv[1] == "ceiling-summary":
+        ceiling_summary(sys.argv[2])
+    elif len(sys.argv) >= 2 and sys.argv[1] == "run":
         run()
     elif len(sys.argv) == 4 and sys.argv[1] == "summarize":
         summarize(sys.argv[2], sys.argv[3])
