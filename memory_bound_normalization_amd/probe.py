@@ -2,13 +2,14 @@
 
     rocprofv3 --pmc FETCH_SIZE -d <dir> -o run -- python -m memory_bound_normalization_amd.probe run
     rocprofv3 --pmc WRITE_SIZE -d <dir> -o run -- python -m memory_bound_normalization_amd.probe run
-    python -m memory_bound_normalization_amd.probe summarize <fetch_dir> <write_dir>
+    python -m memory_bound_normalization_amd.probe summarize <fetch_dir> <write_dir> [workload]
 
-`run` launches rmsnorm_fwd on x[16384, 16384] (the benchmark workload) a few
-times, then a plain device-to-device copy of the same 512 MiB (torch's copy
+`run [workload]` launches rmsnorm_fwd on x[16384, 16384] (the benchmark
+workload; or another RMSNorm workload of `workloads`, e.g. rms_4096x32768) a
+few times, then a plain device-to-device copy of the same x (torch's copy
 kernel) as the calibration: the counters of the copy, whose true HBM traffic is
-known (512 MiB read, 512 MiB written), give the factor that converts each
-counter reading into bytes. `summarize` prints the per-launch HBM traffic of the
+known (x's bytes read and written), give the factor that converts each counter
+reading into bytes. `summarize` prints the per-launch HBM traffic of the
 RMSNorm kernel from the two runs' counter CSV files.
 
     rocprofv3 --kernel-trace --stats -d <dir> -o run -- python -m memory_bound_normalization_amd.probe ceiling
@@ -35,7 +36,10 @@ LAUNCHES = 5
 COPY_BYTES = 16384 * 16384 * 2
 
 
-def run() -> None:
+DEFAULT_WORKLOAD = "rms_16384x16384"
+
+
+def run(workload: str = DEFAULT_WORKLOAD) -> None:
     sys.path.insert(0, ROOT)
     import numpy as np
     import torch
@@ -43,7 +47,7 @@ def run() -> None:
     import memory_bound_normalization_amd as mbn
     from workloads import RMS_WORKLOADS, make_rms_inputs
 
-    wl = RMS_WORKLOADS["rms_16384x16384"]
+    wl = RMS_WORKLOADS[workload]
     x_bits, w_bits, eps = make_rms_inputs(wl)
     dev = torch.device("cuda:0")
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -161,19 +165,25 @@ def _per_kernel(d: str, counter: str):
     return res
 
 
-def summarize(fetch_dir: str, write_dir: str) -> None:
+def summarize(fetch_dir: str, write_dir: str, workload: str = DEFAULT_WORKLOAD) -> None:
+    sys.path.insert(0, ROOT)
+    from workloads import RMS_WORKLOADS
+
+    wl = RMS_WORKLOADS[workload]
+    copy_bytes = wl.M * wl.N * 2  # the calibration copy moves x once each way
     f = _per_kernel(fetch_dir, "FETCH_SIZE")
     w = _per_kernel(write_dir, "WRITE_SIZE")
     mean = lambda v: sum(v) / len(v)  # noqa: E731
     f_r, f_c = mean(f["rmsnorm"]), mean(f["copy"])
     w_r, w_c = mean(w["rmsnorm"]), mean(w["copy"])
-    f_scale = COPY_BYTES / f_c
-    w_scale = COPY_BYTES / w_c
+    f_scale = copy_bytes / f_c
+    w_scale = copy_bytes / w_c
     fetch_b = f_r * f_scale
     write_b = w_r * w_scale
     print(f"rmsnorm FETCH_SIZE per launch (raw, KiB units): {f_r:.1f}  over {len(f['rmsnorm'])} launches")
     print(f"rmsnorm WRITE_SIZE per launch (raw, KiB units): {w_r:.1f}  over {len(w['rmsnorm'])} launches")
-    print(f"copy    FETCH_SIZE per launch (raw): {f_c:.1f}   WRITE_SIZE: {w_c:.1f}   true bytes each way: {COPY_BYTES}")
+    print(f"workload: {workload}  algorithmic_bytes_per_launch: {wl.algorithmic_bytes}")
+    print(f"copy    FETCH_SIZE per launch (raw): {f_c:.1f}   WRITE_SIZE: {w_c:.1f}   true bytes each way: {copy_bytes}")
     print(f"calibration factors (bytes per counter unit): fetch {f_scale:.3f}  write {w_scale:.3f}")
     print(f"fetch_bytes_per_launch: {fetch_b:.0f}")
     print(f"write_bytes_per_launch: {write_b:.0f}")
@@ -185,9 +195,9 @@ if __name__ == "__main__":
         ceiling()
     elif len(sys.argv) >= 3 and sys.argv[1] == "ceiling-summary":
         ceiling_summary(sys.argv[2])
-    elif len(sys.argv) >= 2 and sys.argv[1] == "run":
-        run()
-    elif len(sys.argv) == 4 and sys.argv[1] == "summarize":
-        summarize(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) in (2, 3) and sys.argv[1] == "run":
+        run(*sys.argv[2:])
+    elif len(sys.argv) in (4, 5) and sys.argv[1] == "summarize":
+        summarize(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
