@@ -501,48 +501,53 @@ struct RowNormCfg {
 // 64 * WPR chunks, which the parked partial sums need (exact entries, or the
 // previous band ending at or above 64 * WPR).
 //
-// Entries for N = 4096 ... 32768 were chosen by timing every shape / cap /
-// group combination on MI355X at M*N = 2^26 ... 2^28 (median of 5-7 repeats);
-// the narrower and wider bands are untuned.
-#define MBN_NARROW_BANDS(MODE)                                                     \
-  MBN_CFG(MODE, 1, 4, 1, 1, 0, 0),     /* N <= 512 */                              \
-      MBN_CFG(MODE, 1, 4, 1, 2, 0, 0), /* N <= 1024 */                             \
-      MBN_CFG(MODE, 1, 4, 1, 4, 0, 0)  /* N <= 2048 */
-
-#define MBN_WIDE_BANDS(MODE)                                                       \
-  MBN_CFG(MODE, 16, 1, 1, 4, 0, 0),    /* N <= 32768: 1024 threads */              \
-      MBN_CFG(MODE, 16, 1, 1, 8, 0, 0) /* N <= 65536: 1024 threads */
+// Entries for N = 1024 ... 65536 were chosen by timing every shape / cap /
+// group combination of the kernel template on MI355X at M * N = 2^26, 2^27
+// and 2^28 (buffers rotated over >= 1 GiB, so nothing is served from the
+// 256 MiB Infinity Cache), taking the best geometric mean over the three;
+// RMSNorm at N = 16384 keeps the entry that is fastest at M = 16384. The
+// N <= 512 band is untuned.
+#define MBN_FIRST_BAND(MODE) MBN_CFG(MODE, 1, 4, 1, 1, 0, 0) /* N <= 512 */
 
 const RowNormCfg kRmsTable[] = {
-    MBN_NARROW_BANDS(Norm::kRms),
+    MBN_FIRST_BAND(Norm::kRms),
+    MBN_CFG(Norm::kRms, 1, 4, 1, 2, 0, 16),  // N <= 1024:  4 x 64 threads
+    MBN_CFG(Norm::kRms, 2, 2, 2, 2, 4, 8),   // N <= 2048:  2 x 128 threads x 2 rows, 4 WGs/CU
     MBN_CFG(Norm::kRms, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows, 4 WGs/CU
-    MBN_CFG(Norm::kRms, 4, 1, 2, 4, 0, 0),   // N <= 8192:  256 threads x 2 rows
+    MBN_CFG(Norm::kRms, 4, 1, 1, 4, 4, 8),   // N <= 8192:  256 threads, 4 WGs/CU
     MBN_CFG(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
-    MBN_WIDE_BANDS(Norm::kRms),
+    MBN_CFG(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N <= 32768: 1024 threads
+    MBN_CFG(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N <= 65536: 1024 threads
 };
 const RowNormCfg kAddRmsTable[] = {
-    MBN_NARROW_BANDS(Norm::kAddRms),
-    MBN_CFG(Norm::kAddRms, 4, 2, 1, 2, 0, 8),          // N <= 4096:  2 x 256 threads
-    MBN_CFG_EXACT(Norm::kAddRms, 16, 1, 1, 1, 4, 64),  // N == 8192: 1024 threads, 4 WGs/CU
-    MBN_CFG(Norm::kAddRms, 8, 1, 1, 2, 0, 0),          // N <= 8192:  512 threads
-    MBN_CFG(Norm::kAddRms, 2, 1, 1, 16, 2, 4),         // N <= 16384: 128 threads, 2 WGs/CU
-    MBN_WIDE_BANDS(Norm::kAddRms),
+    MBN_FIRST_BAND(Norm::kAddRms),
+    MBN_CFG(Norm::kAddRms, 1, 4, 1, 2, 4, 16),  // N <= 1024
+    MBN_CFG(Norm::kAddRms, 1, 4, 1, 4, 2, 8),   // N <= 2048
+    MBN_CFG(Norm::kAddRms, 4, 1, 1, 2, 4, 16),  // N <= 4096:  256 threads, 4 WGs/CU
+    MBN_CFG(Norm::kAddRms, 8, 1, 1, 2, 2, 8),   // N <= 8192:  512 threads, 2 WGs/CU
+    MBN_CFG(Norm::kAddRms, 4, 1, 1, 8, 3, 4),   // N <= 16384: 256 threads, 3 WGs/CU
+    MBN_CFG(Norm::kAddRms, 16, 1, 1, 4, 2, 2),  // N <= 32768: 1024 threads
+    MBN_CFG(Norm::kAddRms, 16, 1, 1, 8, 0, 0),  // N <= 65536
 };
 const RowNormCfg kLayerTable[] = {
-    MBN_NARROW_BANDS(Norm::kLayer),
-    MBN_CFG(Norm::kLayer, 4, 2, 1, 2, 0, 8),   // N <= 4096:  2 x 256 threads
-    MBN_CFG(Norm::kLayer, 4, 1, 2, 4, 0, 0),   // N <= 8192:  256 threads x 2 rows
+    MBN_FIRST_BAND(Norm::kLayer),
+    MBN_CFG(Norm::kLayer, 1, 4, 2, 2, 4, 0),   // N <= 1024
+    MBN_CFG(Norm::kLayer, 2, 2, 2, 2, 4, 8),   // N <= 2048
+    MBN_CFG(Norm::kLayer, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows
+    MBN_CFG(Norm::kLayer, 8, 1, 2, 2, 4, 16),  // N <= 8192:  512 threads x 2 rows
     MBN_CFG(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
-    MBN_CFG(Norm::kLayer, 4, 1, 1, 16, 0, 2),  // N <= 32768: 256 threads
-    MBN_CFG(Norm::kLayer, 16, 1, 1, 8, 0, 0),  // N <= 65536
+    MBN_CFG(Norm::kLayer, 4, 1, 1, 16, 0, 4),  // N <= 32768: 256 threads
+    MBN_CFG(Norm::kLayer, 8, 1, 1, 16, 1, 0),  // N <= 65536: 512 threads
 };
 const RowNormCfg kL2Table[] = {
-    MBN_NARROW_BANDS(Norm::kL2),
-    MBN_CFG(Norm::kL2, 4, 2, 1, 2, 0, 8),          // N <= 4096:  2 x 256 threads
-    MBN_CFG_EXACT(Norm::kL2, 16, 1, 1, 1, 0, 0),   // N == 8192: 1024 threads
-    MBN_CFG(Norm::kL2, 8, 1, 1, 2, 0, 0),          // N <= 8192:  512 threads
-    MBN_CFG(Norm::kL2, 4, 1, 1, 8, 3, 4),          // N <= 16384: 256 threads, 3 WGs/CU
-    MBN_WIDE_BANDS(Norm::kL2),
+    MBN_FIRST_BAND(Norm::kL2),
+    MBN_CFG(Norm::kL2, 1, 4, 2, 2, 4, 0),   // N <= 1024
+    MBN_CFG(Norm::kL2, 2, 2, 2, 2, 4, 0),   // N <= 2048
+    MBN_CFG(Norm::kL2, 2, 2, 1, 4, 4, 0),   // N <= 4096:  2 x 128 threads
+    MBN_CFG(Norm::kL2, 8, 1, 1, 2, 0, 0),   // N <= 8192:  512 threads
+    MBN_CFG(Norm::kL2, 4, 1, 1, 8, 3, 4),   // N <= 16384: 256 threads, 3 WGs/CU
+    MBN_CFG(Norm::kL2, 16, 1, 1, 4, 0, 8),  // N <= 32768: 1024 threads
+    MBN_CFG(Norm::kL2, 16, 1, 1, 8, 0, 0),  // N <= 65536
 };
 
 template <size_t K>
@@ -557,11 +562,12 @@ const RowNormCfg* pick(const RowNormCfg (&table)[K], int nchunk) {
 // RMSNorm, LayerNorm and L2Norm: an entry serves widths [min_nchunk,
 // max_nchunk] (chunks) at row counts [min_rows, max_rows]; the first entry
 // that matches is used, else the one-shot table. Entries and windows come from
-// an interleaved timing sweep on MI355X (N = 2560 ... 8192, M = 256 ... 8192,
-// grids of 512 ... 2048 workgroups, cold and warm caches): the persistent
-// kernel is kept wherever it was at least as fast as the one-shot kernel,
-// typically by 5-20% where the one-shot grid is only a few workgroups per CU
-// deep. The best grid keeps about 40-64 KiB of row copies in flight per CU.
+// an interleaved timing sweep on MI355X against the one-shot tables (N = 2560
+// ... 8192, M = 256 ... 8192, grids of 512 ... 2048 workgroups, cold and warm
+// caches): the persistent kernel is used where, at every measured width of
+// the band and with both caches, it took at most 98% of the one-shot time
+// (typically 80-95%, where a one-shot grid is only a few workgroups per CU
+// deep). The best grid keeps about 40-64 KiB of row copies in flight per CU.
 struct PersistentCfg {
   int min_nchunk, max_nchunk;  // widths served, in 16-byte chunks
   int wpr, rpl, maxc;
@@ -581,26 +587,24 @@ struct PersistentCfg {
   }
 
 const PersistentCfg kRmsPersistent[] = {
-    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 1, 8192),   // 2048 < N <= 3072
-    MBN_PCFG(Norm::kRms, 385, 512, 4, 1, 2, 1536, 1, 256),    // 3072 < N <= 4096
-    MBN_PCFG(Norm::kRms, 385, 512, 4, 1, 2, 1536, 1536, 8192),
-    MBN_PCFG(Norm::kRms, 513, 768, 4, 1, 4, 1024, 1, 8192),   // 4096 < N <= 6144
-    MBN_PCFG(Norm::kRms, 769, 1024, 4, 1, 4, 1024, 1, 256),   // 6144 < N <= 8192
-    MBN_PCFG(Norm::kRms, 769, 1024, 4, 1, 4, 1024, 1536, 4096),
+    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 1, 1536),  // 2048 < N <= 3072
+    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 2560, 8192),
+    MBN_PCFG(Norm::kRms, 385, 512, 4, 1, 2, 1536, 1536, 8192),  // 3072 < N <= 4096
+    MBN_PCFG(Norm::kRms, 513, 768, 4, 1, 4, 1024, 1, 6144),     // 4096 < N <= 6144
+    MBN_PCFG(Norm::kRms, 769, 1024, 4, 1, 4, 1024, 1536, 3072),  // 6144 < N <= 8192
 };
 const PersistentCfg kLayerPersistent[] = {
-    MBN_PCFG(Norm::kLayer, 257, 384, 4, 1, 2, 2048, 1, 8192),
+    MBN_PCFG(Norm::kLayer, 257, 384, 4, 1, 2, 1536, 1, 8192),
     MBN_PCFG(Norm::kLayer, 385, 512, 4, 1, 2, 1536, 1, 8192),
-    MBN_PCFG(Norm::kLayer, 513, 768, 4, 1, 4, 1024, 1, 1536),
-    MBN_PCFG(Norm::kLayer, 513, 768, 4, 1, 4, 1024, 2560, 8192),
+    MBN_PCFG(Norm::kLayer, 513, 768, 4, 1, 4, 1024, 1, 8192),
     MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 1, 768),
-    MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 1536, 8192),
+    MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 1536, 6144),
 };
 const PersistentCfg kL2Persistent[] = {
-    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 1, 8192),
-    MBN_PCFG(Norm::kL2, 385, 512, 4, 1, 2, 1536, 1536, 8192),
-    MBN_PCFG(Norm::kL2, 513, 768, 4, 1, 4, 1536, 768, 4096),
-    MBN_PCFG(Norm::kL2, 769, 1024, 4, 1, 4, 1024, 512, 6144),
+    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 1, 1536),
+    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 2560, 6144),
+    MBN_PCFG(Norm::kL2, 513, 768, 4, 1, 4, 1024, 1536, 2560),
+    MBN_PCFG(Norm::kL2, 769, 1024, 4, 1, 4, 1024, 1536, 2560),
 };
 
 template <size_t K>

@@ -1,8 +1,8 @@
 """GPU parity of the persistent row-norm kernel against the fp64 oracle.
 
 For RMSNorm, LayerNorm and L2Norm with 2048 < N <= 8192 the launcher runs, at
-the row counts its tables name (up to 8192 rows), a persistent grid of 1024 to
-2048 workgroups, each looping over rows with two LDS buffers (the next row's
+the row counts its tables name (within 1 ... 8192 rows), a persistent grid of
+1024 to 2048 workgroups, each looping over rows with two LDS buffers (the next row's
 copy in flight while the current one is normalized). These shapes make
 workgroups loop up to four times, put the last iteration on a partial set of
 workgroups, cover both edges of each width band, ragged widths, both storage
@@ -88,10 +88,10 @@ def test_persistent_f16(op, N):
                   dtype="f16")
 
 
-@pytest.mark.parametrize("M", [256, 257, 1535, 1536, 4096, 4097, 8192, 8193])
+@pytest.mark.parametrize("M", [1535, 1536, 1537, 2559, 2560, 3072, 3073, 8192, 8193])
 def test_row_window_edges(M):
-    """Either side of the RMSNorm row windows at N = 8192 ([1, 256] and
-    [1536, 4096]) and of the 8192-row limit at N = 3072."""
+    """Either side of the RMSNorm row windows: [1536, 3072] at N = 8192 and
+    [1, 1536], [2560, 8192] at N = 3072 (persistent inside, one-shot outside)."""
     for N in (8192, 3072):
         print(f"[persistent rms edge] M={M} N={N}", flush=True)
         x, w, b = _inputs(M, N, seed=M, dtype="bf16")

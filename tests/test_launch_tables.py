@@ -19,15 +19,15 @@ CFG = r"MBN_CFG(_EXACT)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+),
 def _tables():
     s = open(SRC).read()
     macros = {}
-    for name in ("MBN_NARROW_BANDS", "MBN_WIDE_BANDS"):
-        body = s[s.index("#define " + name):].split("\n\n")[0]
+    for name in ("MBN_FIRST_BAND",):
+        body = s[s.index("#define " + name):].split("\n")[0]
         macros[name] = re.findall(CFG, body)
     out = {}
     for tname, body in re.findall(r"const RowNormCfg (k\w+)\[\] = \{(.*?)\n\};", s, re.S):
         entries = []
         for line in body.split("\n"):
             line = line.strip()
-            found = macros.get(line.split("(")[0], None) if line.startswith("MBN_") and "BANDS" in line else None
+            found = macros.get(line.split("(")[0], None) if line.startswith("MBN_FIRST_BAND") else None
             for e in (found if found is not None else re.findall(CFG, line)):
                 exact, *nums = e
                 entries.append((exact == "_EXACT", *map(int, nums)))
