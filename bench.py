@@ -73,6 +73,57 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+class HipTimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence.
+
+    A default event record performs a system-scope release (an L2 writeback and
+    invalidate) when it completes; the HIP header documents this flag for
+    events used only to measure time, to avoid that cost and its effect on
+    the following work. Measured on MI355X around each 170 us RMSNorm launch:
+    default events (torch's) read 170.8 us, these 169.1 us, the rocprofv3
+    kernel trace 166.4 us. Recorded on the stream the kernels run on.
+    """
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, stream):
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")  # already loaded by torch
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(stream.cuda_stream)
+        self.events = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        self.events.append(e)
+        return e
+
+    def record(self, e):
+        rc = self.hip.hipEventRecord(e, self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def host_threads() -> int:
     """Host threads for the CPU baseline: the CPUs this process may run on,
     at most 16 (the host share of one GPU)."""
@@ -129,8 +180,8 @@ def cpu_baseline(x_bits, w_bits, eps, n: int, budget_s: float):
 
 def suite(steps: int, warmup: int) -> int:
     """Per-workload timing table (one JSON line per workload): all five inputs,
-    the pages' 3 x 3 RMSNorm shape grid, widths that are not whole 16-byte
-    chunks, and the rest of the norm family.
+    the pages' 3 x 3 RMSNorm shape grid, fp16 storage, widths that are not
+    whole 16-byte chunks, and the rest of the norm family.
 
     Workloads whose footprint is under 1 GiB rotate over enough copies of their
     buffers that successive launches cannot be served from the 256 MiB Infinity
@@ -150,23 +201,25 @@ def suite(steps: int, warmup: int) -> int:
 
     def timed(fn, nrot):
         """(median, best) of per-launch event pairs, and the mean of a back-to-back batch."""
+        timer = HipTimingEvents(stream)
         for i in range(warmup):
             fn(i % nrot)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        ev = [(timer.new(), timer.new()) for _ in range(steps)]
         for i in range(steps):
-            ev[i][0].record(stream)
+            timer.record(ev[i][0])
             fn(i % nrot)
-            ev[i][1].record(stream)
+            timer.record(ev[i][1])
         torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record(stream)
+        us = sorted(timer.elapsed_ms(a, b) * 1e3 for a, b in ev)
+        b0, b1 = timer.new(), timer.new()
+        timer.record(b0)
         for i in range(steps):
             fn(i % nrot)
-        b1.record(stream)
+        timer.record(b1)
         torch.cuda.synchronize()
-        timed.batch_us = b0.elapsed_time(b1) * 1e3 / steps
+        timed.batch_us = timer.elapsed_ms(b0, b1) * 1e3 / steps
+        timer.close()
         return us[len(us) // 2], us[0]
 
     for name, wl in RMS_WORKLOADS.items():
@@ -209,6 +262,25 @@ def suite(steps: int, warmup: int) -> int:
                               "batch_mean_us": round(timed.batch_us, 2),
                               "pct_of_8TBps_batch": round(b / timed.batch_us / 1e3 / 80.0, 2)}), flush=True)
             del xs, ys, x0
+    # fp16 storage: the same kernels with the F16 traits, same input in fp16.
+    for name in ("rms_16384x16384", "rms_8192x8192"):
+        wl16 = RMS_WORKLOADS[name]
+        M, N = wl16.M, wl16.N
+        x0 = x_full[:M, :N].to(torch.float16).contiguous()
+        w = w_full[:N].to(torch.float16).contiguous()
+        nrot = max(1, -(-(1 << 30) // (2 * M * N * 2)))
+        xs = [x0] + [x0.clone() for _ in range(nrot - 1)]
+        ys = [torch.empty_like(x0) for _ in range(nrot)]
+        med, best = timed(lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps), nrot)
+        b = 2 * M * N * 2 + 2 * N
+        print(json.dumps({"workload": f"{name}_f16", "kernel": "rmsnorm_fwd_f16", "M": M, "N": N,
+                          "rotating_sets": nrot, "median_us": round(med, 2), "best_us": round(best, 2),
+                          "GBps_median": round(b / med / 1e3, 1),
+                          "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2),
+                          "batch_mean_us": round(timed.batch_us, 2),
+                          "pct_of_8TBps_batch": round(b / timed.batch_us / 1e3 / 80.0, 2)}), flush=True)
+        del xs, ys, x0
+
     # Widths that are not whole 16-byte chunks (the any-width kernels: 4-, 2-
     # and 1-element accesses), from the same input.
     for N in (16380, 16382, 16383):
@@ -280,7 +352,11 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # The part runs ~1.7% slower for the first few hundred milliseconds of
+    # sustained load (measured: 171.4 us per launch fresh, 168.5 us after 2000
+    # launches, 171 us again after 3 s idle); 2000 warm-up steps (~0.4 s) start
+    # the timed steps in the steady state.
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true",
@@ -328,22 +404,24 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
 
+    timer = HipTimingEvents(stream)
+
     def step(ev=None):
         if ev is not None:
-            ev[0].record(stream)
+            timer.record(ev[0])
         mbn.rmsnorm_fwd(x, w, y, eps=eps)
         if ev is not None:
-            ev[1].record(stream)
+            timer.record(ev[1])
         mbn.qk_norm_rope_fwd(qkv, q_w, k_w, positions, qwl.n_q_heads, qwl.n_kv_heads,
                              qwl.head_dim, eps=qeps, theta=theta)
         if ev is not None:
-            ev[2].record(stream)
+            timer.record(ev[2])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[timer.new() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -351,8 +429,9 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    rms_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    qk_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    rms_ms = [timer.elapsed_ms(e[0], e[1]) for e in evs]
+    qk_ms = [timer.elapsed_ms(e[1], e[2]) for e in evs]
+    timer.close()
     rms_mean_s = sum(rms_ms) / len(rms_ms) / 1e3
     qk_mean_s = sum(qk_ms) / len(qk_ms) / 1e3
     rms_bytes = wl.algorithmic_bytes

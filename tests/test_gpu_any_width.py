@@ -2,10 +2,13 @@
 chunks, N % 8 != 0, or pointers that are only element-aligned) against the
 fp64 oracle, every output compared.
 
-The kernels access groups of 4, 2 or 1 elements (N % 4 == 0, N % 2 == 0,
-odd N, or pointers aligned to less); the widths cover every band of each
-group size's launch table (up to 1024/4096/8192/32768/65536 elements, the
-LDS-staged band of odd widths above 32768) on both sides of the band edges.
+The kernels access groups of 4, 2 or 1 elements: 4 whenever every pointer is
+8-byte aligned (for N % 4 != 0 with a 0-3 element head and tail per row and
+shifted weight groups), 2 or 1 for pointers aligned to less (here: views at
+an element offset). The widths cover every band of each group size's launch
+table (up to 1024/4096/8192/32768/65536 elements, the LDS-staged band of
+single elements above 32768) on both sides of the band edges, and every
+head length 0-3 (consecutive rows start at different offsets mod 4).
 Row counts include a single row and counts that are not a multiple of
 anything. Outputs are written into views of larger buffers whose
 guard elements must stay untouched: the element-wise path reads and writes
@@ -29,7 +32,7 @@ WIDTHS = [
     2, 6, 1002, 1026, 4094, 4098, 8190, 8194, 32766, 32770, 65534,  # N % 4 == 2: 2 elements
     12, 100, 1004, 1028, 4092, 4100, 8188, 8196, 32764, 32772, 40000, 65532,  # N % 8 == 4: 4 elements
 ]
-GUARD = 5  # guard elements on each side of an output view
+GUARD = 8  # guard elements around an output view (16 bytes: keeps the view's alignment)
 FILL = 0x4B00  # bf16 / fp16 bit pattern the guards hold
 
 
@@ -47,26 +50,32 @@ def _inputs(M, N, seed, dtype="bf16"):
             random_bf16_bits(rng, (N,), lo=0.5, hi=1.5), random_bf16_bits(rng, (N,), lo=-0.5, hi=0.5))
 
 
-def _guarded(M, N, dtype):
-    """An output buffer with GUARD fill elements before and after an [M, N] view."""
+def _guarded(M, N, dtype, guard=GUARD):
+    """An output buffer with `guard` fill elements before and GUARD after an [M, N] view."""
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
-    buf = torch.full((M * N + 2 * GUARD,), 0, dtype=torch.int16, device="cuda")
+    buf = torch.full((M * N + guard + GUARD,), 0, dtype=torch.int16, device="cuda")
     buf.fill_(FILL)
     buf = buf.view(tdt)
-    return buf, buf[GUARD : GUARD + M * N].view(M, N)
+    return buf, buf[guard : guard + M * N].view(M, N)
 
 
-def _guards_intact(buf, M, N):
-    g = torch.cat([buf[:GUARD], buf[GUARD + M * N :]]).view(torch.int16).cpu().numpy().view(np.uint16)
+def _guards_intact_at(buf, M, N, guard):
+    g = torch.cat([buf[:guard], buf[guard + M * N :]]).view(torch.int16).cpu().numpy().view(np.uint16)
     return bool(np.all(g == FILL))
 
 
-def _check(op, M, N, seed, dtype="bf16", eps=1e-6):
-    print(f"[any-width {op} {dtype}] M={M} N={N}", flush=True)
+def _check(op, M, N, seed, dtype="bf16", eps=1e-6, offset=0):
+    """`offset` (elements) places x and the outputs at that offset from an
+    aligned address, which selects the 2- or 1-element kernels."""
+    print(f"[any-width {op} {dtype}] M={M} N={N} offset={offset}", flush=True)
     x, r, w, b = _inputs(M, N, seed, dtype)
     xg, rg = to_gpu_bf16(x, dtype=dtype), to_gpu_bf16(r, dtype=dtype)
     wg, bg = to_gpu_bf16(w, dtype=dtype), to_gpu_bf16(b, dtype=dtype)
-    ybuf, y = _guarded(M, N, dtype)
+    if offset:
+        xb = torch.zeros(M * N + offset, dtype=xg.dtype, device="cuda")
+        xb[offset:] = xg.view(-1)
+        xg = xb[offset:].view(M, N)
+    ybuf, y = _guarded(M, N, dtype, GUARD + offset)
     if op == "rms":
         mbn.rmsnorm_fwd(xg, wg, y, eps=eps)
         ref = o_rms(x, w, eps, dtype=dtype)
@@ -77,21 +86,33 @@ def _check(op, M, N, seed, dtype="bf16", eps=1e-6):
         mbn.l2norm_fwd(xg, y, eps=eps)
         ref = o_l2(x, eps, dtype=dtype)
     else:
-        hbuf, h = _guarded(M, N, dtype)
+        hbuf, h = _guarded(M, N, dtype, GUARD + offset)
         mbn.add_rmsnorm_fwd(xg, rg, wg, h=h, y=y, eps=eps)
         rh, ref = o_add(x, r, w, eps, dtype=dtype)
         torch.cuda.synchronize()
         assert np.array_equal(from_gpu_bf16(h), rh), f"h = round(x + r) not bit-exact, {op} M={M} N={N}"
-        assert _guards_intact(hbuf, M, N), "wrote outside h"
+        assert _guards_intact_at(hbuf, M, N, GUARD + offset), "wrote outside h"
     torch.cuda.synchronize()
     assert_parity(from_gpu_bf16(y), ref, f"{op} M={M} N={N} {dtype}", dtype=dtype)
-    assert _guards_intact(ybuf, M, N), "wrote outside y"
+    assert _guards_intact_at(ybuf, M, N, GUARD + offset), "wrote outside y"
 
 
 @pytest.mark.parametrize("N", WIDTHS)
 @pytest.mark.parametrize("op", ["rms", "add", "layer", "l2"])
 def test_any_width(op, N):
     _check(op, _rows(N), N, seed=N)
+
+
+# views at an element offset: 1 element -> 2-byte accesses, 2 -> 4-byte (even N)
+SMALL_GROUP_WIDTHS = [1, 7, 513, 2049, 8193, 32769, 65535, 2, 1026, 4098, 8194, 32770, 65534]
+
+
+@pytest.mark.parametrize("N", SMALL_GROUP_WIDTHS)
+@pytest.mark.parametrize("op", ["rms", "add", "layer", "l2"])
+def test_any_width_small_groups(op, N):
+    _check(op, _rows(N), N, seed=N + 7, offset=1 if N % 2 else 2)
+    if N % 2 == 0:
+        _check(op, _rows(N), N, seed=N + 8, offset=1)
 
 
 @pytest.mark.parametrize("N", [3, 1001, 8191, 40001, 4098, 4100, 40000])
