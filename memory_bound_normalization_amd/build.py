@@ -4,6 +4,9 @@
 
 Compiles every ``csrc/*.hip`` file with hipcc into one shared library next to
 this file. No fast-math: the kernels rely on IEEE fp32/fp64 behaviour.
+``build_stream()`` compiles ``probe_csrc/*.hip`` into libmbn_stream.so, the
+plain streaming kernels the measurement tools time beside the norms (not part
+of the normalization path).
 """
 
 from __future__ import annotations
@@ -20,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmbn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+PROBE_CSRC = os.path.join(PKG, "probe_csrc")
+STREAM_LIB_PATH = os.path.join(PKG, "libmbn_stream.so")
 ARCH = "gfx950"
 
 
@@ -30,11 +35,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmbn.so)")
 
 
-def sources() -> list[str]:
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def sources(src_dir: str = CSRC) -> list[str]:
+    return sorted(glob.glob(os.path.join(src_dir, "*.hip")))
 
 
-def compile_command(out: str, extra: list[str] | None = None) -> list[str]:
+def compile_command(out: str, extra: list[str] | None = None, src_dir: str = CSRC) -> list[str]:
     return [
         hipcc(),
         f"--offload-arch={ARCH}",
@@ -49,14 +54,15 @@ def compile_command(out: str, extra: list[str] | None = None) -> list[str]:
         "-I", INCLUDE,
         *(extra or []),
         "-o", out,
-        *sources(),
+        *sources(src_dir),
     ]
 
 
-def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = None) -> str:
+def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = None,
+          src_dir: str = CSRC) -> str:
     """Compile the library; always rebuilds. Returns the path of the .so."""
     tmp = out + ".tmp"
-    cmd = compile_command(tmp, extra)
+    cmd = compile_command(tmp, extra, src_dir)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,5 +73,11 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = 
     return out
 
 
+def build_stream(verbose: bool = False) -> str:
+    """Compile libmbn_stream.so (the streaming reference kernels); always rebuilds."""
+    return build(verbose=verbose, out=STREAM_LIB_PATH, src_dir=PROBE_CSRC)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_stream(verbose=True))

@@ -15,13 +15,15 @@ RMSNorm kernel from the two runs' counter CSV files.
     rocprofv3 --kernel-trace --stats -d <dir> -o run -- python -m memory_bound_normalization_amd.probe ceiling
     python -m memory_bound_normalization_amd.probe ceiling-summary <dir>
 
-`ceiling` times plain streaming kernels of torch on the same 512 MiB buffers
-(read only: a sum; write only: a fill; read + write: a copy and a scale)
-beside rmsnorm_fwd, each over two alternating buffer sets (1 GiB apart, so
-nothing is served from the 256 MiB Infinity Cache); `ceiling-summary` turns
-the kernel trace into GB/s per kernel. It measures what the memory system
-gives a 50/50 read/write stream on this part, the reference for the RMSNorm
-kernel's fraction of peak.
+`ceiling` times plain streaming kernels on the same 512 MiB buffers beside
+rmsnorm_fwd: torch's (read only: a sum; write only: a fill; read + write: a
+copy and a scale) and the hand-written ones of libmbn_stream.so (read only,
+write only and copy with the row-norm kernels' 16-byte non-temporal accesses,
+at per-workgroup footprints of 4 to 64 KiB), each over two alternating buffer
+sets (1 GiB apart, so nothing is served from the 256 MiB Infinity Cache);
+`ceiling-summary` turns the kernel trace into GB/s per kernel. It measures what
+the memory system gives a pure-read, a pure-write and a 50/50 read/write stream
+on this part, the reference for the RMSNorm kernel's fraction of peak.
 """
 
 from __future__ import annotations
@@ -67,6 +69,46 @@ def run(workload: str = DEFAULT_WORKLOAD) -> None:
 
 CEIL_REPS = 20
 
+# (case, bytes moved per launch, kind, lanes, chunks): kind "torch-*" is one of
+# torch's kernels, "read" / "write" / "copy" a libmbn_stream.so kernel with
+# workgroups of `lanes` lanes moving `chunks` 16-byte chunks each.
+CEILING_CASES = [
+    ("read only (torch sum)", COPY_BYTES, "torch-sum", 0, 0),
+    ("write only (torch fill)", COPY_BYTES, "torch-fill", 0, 0),
+    ("copy (torch copy_)", 2 * COPY_BYTES, "torch-copy", 0, 0),
+    ("read + write (torch scale)", 2 * COPY_BYTES, "torch-scale", 0, 0),
+    ("read only, 4 KiB/WG", COPY_BYTES, "read", 256, 1),
+    ("read only, 32 KiB/WG", COPY_BYTES, "read", 256, 8),
+    ("write only, 4 KiB/WG", COPY_BYTES, "write", 256, 1),
+    ("write only, 32 KiB/WG", COPY_BYTES, "write", 256, 8),
+    ("copy, 4 KiB/WG", 2 * COPY_BYTES, "copy", 256, 1),
+    ("copy, 8 KiB/WG", 2 * COPY_BYTES, "copy", 512, 1),
+    ("copy, 16 KiB/WG", 2 * COPY_BYTES, "copy", 1024, 1),
+    ("copy, 16 KiB/WG (4 per lane)", 2 * COPY_BYTES, "copy", 256, 4),
+    ("copy, 32 KiB/WG", 2 * COPY_BYTES, "copy", 256, 8),
+    ("copy, 32 KiB/WG (1024 lanes)", 2 * COPY_BYTES, "copy", 1024, 2),
+    ("copy, 64 KiB/WG", 2 * COPY_BYTES, "copy", 256, 16),
+    ("rmsnorm_fwd", 2 * COPY_BYTES + 2 * 16384, "rmsnorm", 0, 0),
+]
+
+
+def stream_lib():
+    """ctypes handle of libmbn_stream.so (the streaming reference kernels)."""
+    import ctypes
+
+    from memory_bound_normalization_amd.build import STREAM_LIB_PATH
+
+    if not os.path.exists(STREAM_LIB_PATH):
+        raise RuntimeError(f"{STREAM_LIB_PATH} is missing: run `python -m memory_bound_normalization_amd.build`")
+    h = ctypes.CDLL(STREAM_LIB_PATH)
+    vp, sz, i32, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32
+    h.mbn_stream_copy.argtypes = [vp, vp, sz, i32, i32, vp]
+    h.mbn_stream_read.argtypes = [vp, vp, sz, i32, i32, vp]
+    h.mbn_stream_write.argtypes = [vp, sz, i32, i32, u32, vp]
+    for f in (h.mbn_stream_copy, h.mbn_stream_read, h.mbn_stream_write):
+        f.restype = i32
+    return h
+
 
 def ceiling() -> None:
     sys.path.insert(0, ROOT)
@@ -76,6 +118,7 @@ def ceiling() -> None:
     import torch
 
     import memory_bound_normalization_amd as mbn
+    from memory_bound_normalization_amd.timing import HipTimingEvents
     from workloads import RMS_WORKLOADS, make_rms_inputs
 
     wl = RMS_WORKLOADS["rms_16384x16384"]
@@ -85,24 +128,52 @@ def ceiling() -> None:
     w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     xs = [x0, x0.clone()]
     ys = [torch.empty_like(x0), torch.empty_like(x0)]
-    cases = [
-        ("read only (sum)", COPY_BYTES, lambda i: xs[i].sum(dtype=torch.float32)),
-        ("write only (fill)", COPY_BYTES, lambda i: ys[i].fill_(1.0)),
-        ("read + write (copy)", 2 * COPY_BYTES, lambda i: ys[i].copy_(xs[i])),
-        ("read + write (scale)", 2 * COPY_BYTES, lambda i: torch.mul(xs[i], 2.0, out=ys[i])),
-        ("rmsnorm_fwd", 2 * COPY_BYTES + 2 * 16384, lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps)),
-    ]
-    for name, nbytes, fn in cases:
+    sink = torch.empty(1024 * 16, dtype=torch.uint8, device=dev)
+    sl = stream_lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"libmbn_stream status {rc}")
+
+    def fn_for(kind, lanes, chunks):
+        if kind == "torch-sum":
+            return lambda i: xs[i].sum(dtype=torch.float32)
+        if kind == "torch-fill":
+            return lambda i: ys[i].fill_(1.0)
+        if kind == "torch-copy":
+            return lambda i: ys[i].copy_(xs[i])
+        if kind == "torch-scale":
+            return lambda i: torch.mul(xs[i], 2.0, out=ys[i])
+        if kind == "read":
+            return lambda i: ok(sl.mbn_stream_read(xs[i].data_ptr(), sink.data_ptr(), COPY_BYTES, lanes, chunks, sp))
+        if kind == "write":
+            return lambda i: ok(sl.mbn_stream_write(ys[i].data_ptr(), COPY_BYTES, lanes, chunks, 0x3F803F80, sp))
+        if kind == "copy":
+            return lambda i: ok(sl.mbn_stream_copy(xs[i].data_ptr(), ys[i].data_ptr(), COPY_BYTES, lanes, chunks, sp))
+        return lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps)
+
+    # the copy kernel copies (checked before the timed cases)
+    ok(sl.mbn_stream_copy(xs[0].data_ptr(), ys[0].data_ptr(), COPY_BYTES, 256, 8, sp))
+    torch.cuda.synchronize()
+    if not torch.equal(ys[0].view(torch.int16), xs[0].view(torch.int16)):
+        raise RuntimeError("stream copy produced a different buffer")
+
+    timer = HipTimingEvents(stream)
+    for name, nbytes, kind, lanes, chunks in CEILING_CASES:
+        fn = fn_for(kind, lanes, chunks)
         for i in range(3):
             fn(i % 2)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(CEIL_REPS)]
+        ev = [(timer.new(), timer.new()) for _ in range(CEIL_REPS)]
         for i, (a, b) in enumerate(ev):
-            a.record()
+            timer.record(a)
             fn(i % 2)
-            b.record()
+            timer.record(b)
         torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        us = sorted(timer.elapsed_ms(a, b) * 1e3 for a, b in ev)
+        timer.close()
         med = us[len(us) // 2]
         print(json.dumps({"case": name, "bytes": nbytes, "median_us": round(med, 2),
                           "GBps": round(nbytes / med / 1e3, 1), "pct_of_8TBps": round(nbytes / med / 1e3 / 80, 2)}),
@@ -119,22 +190,23 @@ def ceiling_summary(d: str) -> None:
         with open(f) as fh:
             rows.extend(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    # dispatches of >= 20 us are the 512 MiB kernels; the last ones come in
-    # blocks of 3 warm-up + CEIL_REPS per case, in the order of `ceiling`
-    # (before them: the clone that makes the second buffer set)
+    # dispatches of >= 20 us are the 512 MiB kernels: the last ones come in
+    # blocks of 3 warm-up + CEIL_REPS per case, in the order of CEILING_CASES
+    # (before them: the clone that makes the second buffer set and the check
+    # of the copy kernel)
     big = [r for r in rows if int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) > 20000]
-    names = ["read only (sum)", "write only (fill)", "read + write (copy)", "read + write (scale)", "rmsnorm_fwd"]
-    nbytes = [COPY_BYTES, COPY_BYTES, 2 * COPY_BYTES, 2 * COPY_BYTES, 2 * COPY_BYTES + 2 * 16384]
     per = 3 + CEIL_REPS
-    if len(big) < per * len(names):
-        raise SystemExit(f"expected {per * len(names)} large dispatches, found {len(big)}")
-    big = big[len(big) - per * len(names):]
-    for k, (name, nb) in enumerate(zip(names, nbytes)):
+    n = len(CEILING_CASES)
+    if len(big) < per * n:
+        raise SystemExit(f"expected {per * n} large dispatches, found {len(big)}")
+    big = big[len(big) - per * n :]
+    for k, (name, nb, *_rest) in enumerate(CEILING_CASES):
         grp = big[k * per + 3 : (k + 1) * per]
         d_us = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
         med = d_us[len(d_us) // 2]
-        kname = grp[0]["Kernel_Name"].split("(")[0][:60]
-        print(f"{name:<22} {med:9.2f} us {nb / med / 1e3:8.0f} GB/s {nb / med / 1e3 / 80:6.1f}%   {kname}")
+        kname = grp[0]["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        kname = kname.removeprefix("void ")[:60]
+        print(f"{name:<30} {med:9.2f} us {nb / med / 1e3:8.0f} GB/s {nb / med / 1e3 / 80:6.1f}%   {kname}")
 
 
 def _rows(d: str):

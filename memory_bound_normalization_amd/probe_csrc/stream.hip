@@ -1,0 +1,121 @@
+// Plain HBM streaming kernels for gfx950: read only, write only and copy, at a
+// chosen per-workgroup footprint. Not part of the normalization path: they
+// measure what the memory system gives a pure-read, pure-write and 50/50
+// read/write stream on this part, the reference the row-norm kernels' fraction
+// of peak is read against. Built into libmbn_stream.so (a library of its own).
+//
+// A workgroup of LANES lanes moves LANES * CHUNKS 16-byte chunks (lane t owns
+// chunks j * LANES + t), with the same non-temporal 16-byte loads and stores
+// as the row-norm kernels: every chunk of a workgroup is in flight before the
+// first one is consumed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int LANES, int CHUNKS>
+__global__ void __launch_bounds__(LANES) stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst) {
+  const size_t base = (size_t)blockIdx.x * LANES * CHUNKS;
+  u32x4 v[CHUNKS];
+#pragma unroll
+  for (int j = 0; j < CHUNKS; ++j) v[j] = __builtin_nontemporal_load(src + base + (size_t)j * LANES + threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < CHUNKS; ++j) __builtin_nontemporal_store(v[j], dst + base + (size_t)j * LANES + threadIdx.x);
+}
+
+// The xor of everything read is stored only when it equals `key` (never, for
+// the caller's data in practice), so the loads cannot be dropped; `sink`
+// receives at most LANES chunks per workgroup.
+template <int LANES, int CHUNKS>
+__global__ void __launch_bounds__(LANES) stream_read(const u32x4* __restrict__ src, u32x4* __restrict__ sink,
+                                                     uint32_t key) {
+  const size_t base = (size_t)blockIdx.x * LANES * CHUNKS;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < CHUNKS; ++j) acc ^= __builtin_nontemporal_load(src + base + (size_t)j * LANES + threadIdx.x);
+  if (acc.x == key && acc.y == key) sink[threadIdx.x] = acc;
+}
+
+template <int LANES, int CHUNKS>
+__global__ void __launch_bounds__(LANES) stream_write(u32x4* __restrict__ dst, uint32_t value) {
+  const size_t base = (size_t)blockIdx.x * LANES * CHUNKS;
+  const u32x4 v = {value, value, value, value};
+#pragma unroll
+  for (int j = 0; j < CHUNKS; ++j) __builtin_nontemporal_store(v, dst + base + (size_t)j * LANES + threadIdx.x);
+}
+
+struct Shape {
+  int lanes, chunks;
+  void (*copy)(const u32x4*, u32x4*);
+  void (*read)(const u32x4*, u32x4*, uint32_t);
+  void (*write)(u32x4*, uint32_t);
+};
+
+#define MBN_STREAM_SHAPE(L, C) \
+  Shape { L, C, &stream_copy<L, C>, &stream_read<L, C>, &stream_write<L, C> }
+
+// Footprints per workgroup: 4, 8, 16, 32 and 64 KiB.
+const Shape kShapes[] = {
+    MBN_STREAM_SHAPE(256, 1), MBN_STREAM_SHAPE(512, 1), MBN_STREAM_SHAPE(1024, 1), MBN_STREAM_SHAPE(256, 4),
+    MBN_STREAM_SHAPE(256, 8), MBN_STREAM_SHAPE(1024, 2), MBN_STREAM_SHAPE(256, 16),
+};
+
+const Shape* find(int lanes, int chunks) {
+  for (const Shape& s : kShapes)
+    if (s.lanes == lanes && s.chunks == chunks) return &s;
+  return nullptr;
+}
+
+// 0 = ok, 1 = invalid (bytes not whole workgroups, misaligned pointer, no
+// such shape), 3 = launch failed.
+int check(const void* p, size_t bytes, int lanes, int chunks, const Shape** s) {
+  *s = find(lanes, chunks);
+  if (!*s || !p || ((uintptr_t)p & 15) != 0) return 1;
+  const size_t per_wg = (size_t)lanes * chunks * 16;
+  if (bytes == 0 || bytes % per_wg != 0 || bytes / per_wg > 0x7fffffffull) return 1;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) int mbn_stream_copy(const void* src, void* dst, size_t bytes, int lanes,
+                                                           int chunks, void* stream) {
+  const Shape* s;
+  int rc = check(src, bytes, lanes, chunks, &s);
+  if (rc == 0) rc = check(dst, bytes, lanes, chunks, &s);
+  if (rc) return rc;
+  const size_t grid = bytes / ((size_t)lanes * chunks * 16);
+  hipLaunchKernelGGL(s->copy, dim3((unsigned)grid), dim3(lanes), 0, (hipStream_t)stream,
+                     (const u32x4*)src, (u32x4*)dst);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// sink: device buffer of at least lanes * 16 bytes (written only in the
+// improbable case described above).
+__attribute__((visibility("default"))) int mbn_stream_read(const void* src, void* sink, size_t bytes, int lanes,
+                                                           int chunks, void* stream) {
+  const Shape* s;
+  int rc = check(src, bytes, lanes, chunks, &s);
+  if (rc) return rc;
+  if (!sink || ((uintptr_t)sink & 15) != 0) return 1;
+  const size_t grid = bytes / ((size_t)lanes * chunks * 16);
+  hipLaunchKernelGGL(s->read, dim3((unsigned)grid), dim3(lanes), 0, (hipStream_t)stream, (const u32x4*)src,
+                     (u32x4*)sink, 0x9e3779b9u);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+__attribute__((visibility("default"))) int mbn_stream_write(void* dst, size_t bytes, int lanes, int chunks,
+                                                            uint32_t value, void* stream) {
+  const Shape* s;
+  const int rc = check(dst, bytes, lanes, chunks, &s);
+  if (rc) return rc;
+  const size_t grid = bytes / ((size_t)lanes * chunks * 16);
+  hipLaunchKernelGGL(s->write, dim3((unsigned)grid), dim3(lanes), 0, (hipStream_t)stream, (u32x4*)dst, value);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+}  // extern "C"

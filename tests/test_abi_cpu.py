@@ -253,3 +253,22 @@ def test_f16_entry_points_validate_like_bf16(lib):
         a = getattr(lib, name)(*args)
         b = getattr(lib, name + "_f16")(*args)
         assert a == b and a != mbn.MBN_OK, (name, args, a, b)
+
+
+def test_stream_reference_library_loads_and_validates():
+    """libmbn_stream.so (the streaming kernels the ceiling measurement times)
+    exports its three entry points and rejects, before any launch, sizes that
+    are not whole workgroups, unknown workgroup shapes and misaligned or null
+    pointers."""
+    from memory_bound_normalization_amd import build as b
+    from memory_bound_normalization_amd.probe import stream_lib
+
+    if not os.path.exists(b.STREAM_LIB_PATH):
+        b.build_stream()
+    h = stream_lib()
+    assert h.mbn_stream_copy(FAKE, FAKE + (1 << 30), 4096 + 16, 256, 1, None) == 1  # ragged
+    assert h.mbn_stream_copy(FAKE, FAKE + (1 << 30), 4096, 256, 3, None) == 1  # no such shape
+    assert h.mbn_stream_copy(FAKE + 8, FAKE + (1 << 30), 4096, 256, 1, None) == 1  # misaligned
+    assert h.mbn_stream_copy(FAKE, 0, 4096, 256, 1, None) == 1  # null
+    assert h.mbn_stream_read(FAKE, 0, 4096, 256, 1, None) == 1  # null sink
+    assert h.mbn_stream_write(FAKE, 0, 256, 1, 0, None) == 1  # empty
