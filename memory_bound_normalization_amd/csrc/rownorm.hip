@@ -476,6 +476,7 @@ constexpr size_t kLdsPerCU = 160 * 1024;
 struct RowNormCfg {
   int max_nchunk;    // widest row (in 16-byte chunks) this entry serves
   bool exact;        // serves only rows of exactly max_nchunk chunks
+  int64_t max_rows;  // serves only launches of at most max_rows rows (0: any)
   int wpr, rows, rpl, maxc;
   int wgs_per_cu;    // occupancy cap (0 = as many as LDS, waves and VGPRs allow)
   int xcd_group;     // row blocks per XCD run (0 = dispatch order)
@@ -483,18 +484,23 @@ struct RowNormCfg {
   RowNormKernel full[2];    // width exactly max_nchunk; [bf16, fp16]
 };
 
-#define MBN_CFG_(MODE, EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP)                       \
+#define MBN_CFG_(MODE, EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)              \
   RowNormCfg {                                                                        \
-    64 * (WPR) * (MAXC), EXACT, WPR, ROWS, RPL, MAXC, CAP, GROUP,                     \
+    64 * (WPR) * (MAXC), EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP,            \
         {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, false>,                    \
          &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, false>},                    \
         {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, true>,                     \
          &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, true>}                      \
   }
 // serves every width up to 64 * WPR * MAXC chunks (down to the previous entry)
-#define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, false, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+#define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
 // serves only the width 64 * WPR * MAXC chunks; a later entry covers the band
-#define MBN_CFG_EXACT(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, true, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+#define MBN_CFG_EXACT(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, true, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+// serves the widths of the band that ends at 64 * WPR * MAXC chunks, for
+// launches of at most MAXROWS rows (row windows precede the band's entry for
+// any row count, in increasing MAXROWS)
+#define MBN_CFG_ROWS(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, false, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)
 
 // Per-width launch tables, narrowest first: the first entry that serves the
 // row width is used. Every entry with WPR > 1 serves only widths of at least
@@ -506,54 +512,113 @@ struct RowNormCfg {
 // and 2^28 (buffers rotated over >= 1 GiB, so nothing is served from the
 // 256 MiB Infinity Cache), taking the best geometric mean over the three;
 // RMSNorm at N = 16384 keeps the entry that is fastest at M = 16384. The
-// N <= 512 band is untuned.
+// N <= 512 band is untuned. Row windows (MBN_CFG_ROWS) come from the same
+// timing at N = 1024 ... 32768 and M = 256 ... 32768 with M * N < 2^26: the
+// sampled row counts of a band were split into windows, each given the
+// configuration with the least total log-time over its rows that is nowhere
+// more than 1% slower than the band's general entry, at a cost of 5% per
+// window (so a window must pay for itself); launches of more rows than the
+// last window use the general entry. An A/B of the library against the
+// tables without windows (GPU kernel durations, both orders, at widths and
+// row counts between the sampled ones too) then shortened the residual-add
+// and L2Norm windows that were slower there.
 #define MBN_FIRST_BAND(MODE) MBN_CFG(MODE, 1, 4, 1, 1, 0, 0) /* N <= 512 */
 
 const RowNormCfg kRmsTable[] = {
     MBN_FIRST_BAND(Norm::kRms),
+    MBN_CFG_ROWS(Norm::kRms, 2048, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 2048
+    MBN_CFG_ROWS(Norm::kRms, 8192, 1, 4, 2, 2, 4, 0),  // N <= 1024, M <= 8192
     MBN_CFG(Norm::kRms, 1, 4, 1, 2, 0, 16),  // N <= 1024:  4 x 64 threads
+    MBN_CFG_ROWS(Norm::kRms, 256, 2, 2, 1, 2, 1, 0),  // N <= 2048, M <= 256
+    MBN_CFG_ROWS(Norm::kRms, 2048, 1, 4, 1, 4, 4, 0),  // N <= 2048, M <= 2048
+    MBN_CFG_ROWS(Norm::kRms, 4096, 1, 4, 2, 4, 2, 0),  // N <= 2048, M <= 4096
     MBN_CFG(Norm::kRms, 2, 2, 2, 2, 4, 8),   // N <= 2048:  2 x 128 threads x 2 rows, 4 WGs/CU
+    MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 2, 0, 0),  // N <= 4096, M <= 512
+    MBN_CFG_ROWS(Norm::kRms, 1024, 2, 2, 1, 4, 3, 0),  // N <= 4096, M <= 1024
+    MBN_CFG_ROWS(Norm::kRms, 4096, 2, 1, 2, 4, 0, 0),  // N <= 4096, M <= 4096
     MBN_CFG(Norm::kRms, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows, 4 WGs/CU
+    MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 4, 0, 0),  // N <= 8192, M <= 512
+    MBN_CFG_ROWS(Norm::kRms, 1024, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 1024
+    MBN_CFG_ROWS(Norm::kRms, 2048, 2, 1, 2, 8, 0, 0),  // N <= 8192, M <= 2048
     MBN_CFG(Norm::kRms, 4, 1, 1, 4, 4, 8),   // N <= 8192:  256 threads, 4 WGs/CU
+    MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
+    MBN_CFG_ROWS(Norm::kRms, 1024, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1024
     MBN_CFG(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
     MBN_CFG(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N <= 32768: 1024 threads
     MBN_CFG(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N <= 65536: 1024 threads
 };
 const RowNormCfg kAddRmsTable[] = {
     MBN_FIRST_BAND(Norm::kAddRms),
+    MBN_CFG_ROWS(Norm::kAddRms, 4096, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 4096
+    MBN_CFG_ROWS(Norm::kAddRms, 32768, 1, 4, 2, 2, 0, 0),  // N <= 1024, M <= 32768
     MBN_CFG(Norm::kAddRms, 1, 4, 1, 2, 4, 16),  // N <= 1024
+    MBN_CFG_ROWS(Norm::kAddRms, 1024, 2, 2, 1, 2, 0, 0),  // N <= 2048, M <= 1024
+    MBN_CFG_ROWS(Norm::kAddRms, 8192, 2, 2, 2, 2, 4, 0),  // N <= 2048, M <= 8192
     MBN_CFG(Norm::kAddRms, 1, 4, 1, 4, 2, 8),   // N <= 2048
+    MBN_CFG_ROWS(Norm::kAddRms, 256, 4, 1, 1, 2, 4, 0),  // N <= 4096, M <= 256
+    MBN_CFG_ROWS(Norm::kAddRms, 512, 4, 2, 1, 2, 0, 16),  // N <= 4096, M <= 512
+    MBN_CFG_ROWS(Norm::kAddRms, 1024, 4, 1, 1, 2, 4, 16),  // N <= 4096, M <= 1024 (the band's general entry)
+    MBN_CFG_ROWS(Norm::kAddRms, 4096, 1, 4, 1, 8, 0, 0),  // N <= 4096, M <= 4096
     MBN_CFG(Norm::kAddRms, 4, 1, 1, 2, 4, 16),  // N <= 4096:  256 threads, 4 WGs/CU
+    MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 2, 1, 64),  // N <= 8192, M <= 256
+    MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 2, 0, 0),  // N <= 8192, M <= 512
+    MBN_CFG_ROWS(Norm::kAddRms, 2048, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 2048
     MBN_CFG(Norm::kAddRms, 8, 1, 1, 2, 2, 8),   // N <= 8192:  512 threads, 2 WGs/CU
+    MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 4, 4, 0),  // N <= 16384, M <= 256
+    MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 4, 0, 0),  // N <= 16384, M <= 512
+    MBN_CFG_ROWS(Norm::kAddRms, 1024, 16, 1, 4, 2, 0, 0),  // N <= 16384, M <= 1024
     MBN_CFG(Norm::kAddRms, 4, 1, 1, 8, 3, 4),   // N <= 16384: 256 threads, 3 WGs/CU
+    MBN_CFG_ROWS(Norm::kAddRms, 512, 4, 1, 1, 16, 2, 0),  // N <= 32768, M <= 512
     MBN_CFG(Norm::kAddRms, 16, 1, 1, 4, 2, 2),  // N <= 32768: 1024 threads
     MBN_CFG(Norm::kAddRms, 16, 1, 1, 8, 0, 0),  // N <= 65536
 };
 const RowNormCfg kLayerTable[] = {
     MBN_FIRST_BAND(Norm::kLayer),
+    MBN_CFG_ROWS(Norm::kLayer, 2048, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 2048
     MBN_CFG(Norm::kLayer, 1, 4, 2, 2, 4, 0),   // N <= 1024
+    MBN_CFG_ROWS(Norm::kLayer, 2048, 2, 2, 1, 2, 0, 0),  // N <= 2048, M <= 2048
+    MBN_CFG_ROWS(Norm::kLayer, 4096, 1, 4, 2, 4, 0, 0),  // N <= 2048, M <= 4096
     MBN_CFG(Norm::kLayer, 2, 2, 2, 2, 4, 8),   // N <= 2048
+    MBN_CFG_ROWS(Norm::kLayer, 512, 4, 1, 1, 2, 4, 2),  // N <= 4096, M <= 512
+    MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 2, 1, 2, 2, 0),  // N <= 4096, M <= 1024
+    MBN_CFG_ROWS(Norm::kLayer, 2048, 1, 4, 1, 8, 2, 0),  // N <= 4096, M <= 2048
     MBN_CFG(Norm::kLayer, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows
+    MBN_CFG_ROWS(Norm::kLayer, 512, 8, 1, 1, 2, 3, 0),  // N <= 8192, M <= 512
+    MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 4, 2, 0),  // N <= 8192, M <= 1024
+    MBN_CFG_ROWS(Norm::kLayer, 2048, 8, 1, 4, 2, 2, 0),  // N <= 8192, M <= 2048
     MBN_CFG(Norm::kLayer, 8, 1, 2, 2, 4, 16),  // N <= 8192:  512 threads x 2 rows
+    MBN_CFG_ROWS(Norm::kLayer, 512, 16, 1, 1, 2, 2, 0),  // N <= 16384, M <= 512
+    MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 8, 2, 0),  // N <= 16384, M <= 1024
     MBN_CFG(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
+    MBN_CFG_ROWS(Norm::kLayer, 256, 8, 1, 1, 8, 1, 0),  // N <= 32768, M <= 256
     MBN_CFG(Norm::kLayer, 4, 1, 1, 16, 0, 4),  // N <= 32768: 256 threads
     MBN_CFG(Norm::kLayer, 8, 1, 1, 16, 1, 0),  // N <= 65536: 512 threads
 };
 const RowNormCfg kL2Table[] = {
     MBN_FIRST_BAND(Norm::kL2),
+    MBN_CFG_ROWS(Norm::kL2, 2048, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 2048
     MBN_CFG(Norm::kL2, 1, 4, 2, 2, 4, 0),   // N <= 1024
+    MBN_CFG_ROWS(Norm::kL2, 1024, 1, 4, 1, 4, 4, 0),  // N <= 2048, M <= 1024
     MBN_CFG(Norm::kL2, 2, 2, 2, 2, 4, 0),   // N <= 2048
+    MBN_CFG_ROWS(Norm::kL2, 768, 4, 1, 1, 2, 0, 0),  // N <= 4096, M <= 768
     MBN_CFG(Norm::kL2, 2, 2, 1, 4, 4, 0),   // N <= 4096:  2 x 128 threads
+    MBN_CFG_ROWS(Norm::kL2, 1024, 8, 1, 1, 2, 0, 0),  // N <= 8192, M <= 1024
+    MBN_CFG_ROWS(Norm::kL2, 2048, 8, 1, 4, 2, 0, 0),  // N <= 8192, M <= 2048
     MBN_CFG(Norm::kL2, 8, 1, 1, 2, 0, 0),   // N <= 8192:  512 threads
+    MBN_CFG_ROWS(Norm::kL2, 512, 8, 1, 1, 4, 2, 0),  // N <= 16384, M <= 512
+    MBN_CFG_ROWS(Norm::kL2, 2048, 2, 2, 1, 16, 2, 0),  // N <= 16384, M <= 2048
     MBN_CFG(Norm::kL2, 4, 1, 1, 8, 3, 4),   // N <= 16384: 256 threads, 3 WGs/CU
+    MBN_CFG_ROWS(Norm::kL2, 256, 8, 1, 1, 8, 2, 0),  // N <= 32768, M <= 256
+    MBN_CFG_ROWS(Norm::kL2, 1024, 4, 1, 1, 16, 2, 16),  // N <= 32768, M <= 1024
     MBN_CFG(Norm::kL2, 16, 1, 1, 4, 0, 8),  // N <= 32768: 1024 threads
     MBN_CFG(Norm::kL2, 16, 1, 1, 8, 0, 0),  // N <= 65536
 };
 
 template <size_t K>
-const RowNormCfg* pick(const RowNormCfg (&table)[K], int nchunk) {
+const RowNormCfg* pick(const RowNormCfg (&table)[K], int nchunk, int64_t M) {
   for (const RowNormCfg& c : table)
-    if (c.exact ? nchunk == c.max_nchunk : nchunk <= c.max_nchunk) return &c;
+    if ((c.exact ? nchunk == c.max_nchunk : nchunk <= c.max_nchunk) && (c.max_rows == 0 || M <= c.max_rows))
+      return &c;
   return nullptr;
 }
 
@@ -562,12 +627,13 @@ const RowNormCfg* pick(const RowNormCfg (&table)[K], int nchunk) {
 // RMSNorm, LayerNorm and L2Norm: an entry serves widths [min_nchunk,
 // max_nchunk] (chunks) at row counts [min_rows, max_rows]; the first entry
 // that matches is used, else the one-shot table. Entries and windows come from
-// an interleaved timing sweep on MI355X against the one-shot tables (N = 2560
-// ... 8192, M = 256 ... 8192, grids of 512 ... 2048 workgroups, cold and warm
-// caches): the persistent kernel is used where, at every measured width of
-// the band and with both caches, it took at most 98% of the one-shot time
-// (typically 80-95%, where a one-shot grid is only a few workgroups per CU
-// deep). The best grid keeps about 40-64 KiB of row copies in flight per CU.
+// an interleaved timing sweep on MI355X against the one-shot tables (row
+// windows included): N = 2560 ... 8192, M = 256 ... 8192, grids of 512 ...
+// 2048 workgroups, cold and warm caches. The persistent kernel is used at a
+// sampled row count where, at every measured width of the band and with both
+// caches, it took at most 98% of the one-shot time (typically 80-95%); a
+// window ends half way (geometrically) between such a row count and one where
+// it lost. The best grid keeps about 40-64 KiB of row copies in flight per CU.
 struct PersistentCfg {
   int min_nchunk, max_nchunk;  // widths served, in 16-byte chunks
   int wpr, rpl, maxc;
@@ -587,24 +653,23 @@ struct PersistentCfg {
   }
 
 const PersistentCfg kRmsPersistent[] = {
-    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 1, 1536),  // 2048 < N <= 3072
-    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 2560, 8192),
-    MBN_PCFG(Norm::kRms, 385, 512, 4, 1, 2, 1536, 1536, 8192),  // 3072 < N <= 4096
-    MBN_PCFG(Norm::kRms, 513, 768, 4, 1, 4, 1024, 1, 6144),     // 4096 < N <= 6144
-    MBN_PCFG(Norm::kRms, 769, 1024, 4, 1, 4, 1024, 1536, 3072),  // 6144 < N <= 8192
+    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 725, 1448),   // 2048 < N <= 3072
+    MBN_PCFG(Norm::kRms, 257, 384, 4, 1, 2, 2048, 5017, 8192),
+    MBN_PCFG(Norm::kRms, 385, 512, 4, 1, 2, 1536, 2509, 8192),  // 3072 < N <= 4096
+    MBN_PCFG(Norm::kRms, 513, 768, 4, 1, 4, 1024, 1449, 7094),  // 4096 < N <= 6144
+    MBN_PCFG(Norm::kRms, 769, 1024, 4, 1, 4, 1024, 2509, 3547),  // 6144 < N <= 8192
 };
 const PersistentCfg kLayerPersistent[] = {
     MBN_PCFG(Norm::kLayer, 257, 384, 4, 1, 2, 1536, 1, 8192),
-    MBN_PCFG(Norm::kLayer, 385, 512, 4, 1, 2, 1536, 1, 8192),
-    MBN_PCFG(Norm::kLayer, 513, 768, 4, 1, 4, 1024, 1, 8192),
-    MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 1, 768),
-    MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 1536, 6144),
+    MBN_PCFG(Norm::kLayer, 385, 512, 4, 1, 2, 1536, 725, 1448),
+    MBN_PCFG(Norm::kLayer, 385, 512, 4, 1, 2, 1536, 2509, 5017),
+    MBN_PCFG(Norm::kLayer, 513, 768, 4, 1, 4, 1024, 725, 8192),
+    MBN_PCFG(Norm::kLayer, 769, 1024, 4, 1, 4, 1024, 2509, 5017),
 };
 const PersistentCfg kL2Persistent[] = {
-    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 1, 1536),
-    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 2560, 6144),
-    MBN_PCFG(Norm::kL2, 513, 768, 4, 1, 4, 1024, 1536, 2560),
-    MBN_PCFG(Norm::kL2, 769, 1024, 4, 1, 4, 1024, 1536, 2560),
+    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 363, 1448),
+    MBN_PCFG(Norm::kL2, 257, 384, 4, 1, 2, 2048, 2509, 7094),
+    MBN_PCFG(Norm::kL2, 513, 768, 4, 1, 4, 1024, 725, 1448),
 };
 
 template <size_t K>
@@ -666,10 +731,10 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
 
   const RowNormCfg* cfg = nullptr;
   switch (mode) {
-    case Norm::kRms: cfg = pick(kRmsTable, nchunk); break;
-    case Norm::kAddRms: cfg = pick(kAddRmsTable, nchunk); break;
-    case Norm::kLayer: cfg = pick(kLayerTable, nchunk); break;
-    case Norm::kL2: cfg = pick(kL2Table, nchunk); break;
+    case Norm::kRms: cfg = pick(kRmsTable, nchunk, args.M); break;
+    case Norm::kAddRms: cfg = pick(kAddRmsTable, nchunk, args.M); break;
+    case Norm::kLayer: cfg = pick(kLayerTable, nchunk, args.M); break;
+    case Norm::kL2: cfg = pick(kL2Table, nchunk, args.M); break;
   }
   if (!cfg) return hipErrorInvalidValue;
   if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant

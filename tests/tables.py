@@ -1,0 +1,59 @@
+"""Parser of the row-norm launch tables in rownorm.hip, shared by the host-side
+table checks and the GPU tests that must reach every table entry (no GPU
+needed here)."""
+
+import os
+import re
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "memory_bound_normalization_amd", "csrc", "rownorm.hip")
+CFG = r"MBN_CFG(_EXACT|_ROWS)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
+
+
+def _tables():
+    s = open(SRC).read()
+    macros = {}
+    for name in ("MBN_FIRST_BAND",):
+        body = s[s.index("#define " + name):].split("\n")[0]
+        macros[name] = re.findall(CFG, body)
+    out = {}
+    for tname, body in re.findall(r"const RowNormCfg (k\w+)\[\] = \{(.*?)\n\};", s, re.S):
+        entries = []
+        for line in body.split("\n"):
+            line = line.strip()
+            found = macros.get(line.split("(")[0], None) if line.startswith("MBN_FIRST_BAND") else None
+            for e in (found if found is not None else re.findall(CFG, line)):
+                kind, *nums = e
+                nums = [int(v) for v in nums if v != ""]
+                max_rows = 0
+                if kind == "_ROWS":
+                    max_rows, nums = nums[0], nums[1:]
+                # (exact, max_rows, wpr, rows, rpl, maxc, cap, grp)
+                entries.append((kind == "_EXACT", max_rows, *nums))
+        out[tname] = entries
+    return out
+
+
+PCFG = r"MBN_PCFG\(Norm::(\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
+
+
+def _persistent():
+    s = open(SRC).read()
+    out = {}
+    for tname, body in re.findall(r"const PersistentCfg (k\w+)\[\] = \{(.*?)\n\};", s, re.S):
+        out[tname] = [tuple(map(int, e[1:])) for e in re.findall(PCFG, body)]
+    return out
+
+
+
+TABLES = _tables()
+PERSISTENT = _persistent()
+
+PERSISTENT_TABLE = {"rms": "kRmsPersistent", "layer": "kLayerPersistent", "l2": "kL2Persistent"}
+
+
+def persistent_windows(op, nchunk):
+    """(grid, min_rows, max_rows) of the persistent entries of `op` that serve
+    rows of `nchunk` 16-byte chunks."""
+    return [(grid, lo_r, hi_r) for lo, hi, wpr, rpl, maxc, grid, lo_r, hi_r in PERSISTENT[PERSISTENT_TABLE[op]]
+            if lo <= nchunk <= hi]

@@ -1,13 +1,13 @@
 """GPU parity of the persistent row-norm kernel against the fp64 oracle.
 
 For RMSNorm, LayerNorm and L2Norm with 2048 < N <= 8192 the launcher runs, at
-the row counts its tables name (within 1 ... 8192 rows), a persistent grid of
-1024 to 2048 workgroups, each looping over rows with two LDS buffers (the next row's
-copy in flight while the current one is normalized). These shapes make
-workgroups loop up to four times, put the last iteration on a partial set of
-workgroups, cover both edges of each width band, ragged widths, both storage
-types, and row counts on either side of each row window (one-shot kernel
-there). Every output is compared.
+the row counts its tables name, a persistent grid of 1024 to 2048 workgroups,
+each looping over rows with two LDS buffers (the next row's copy in flight
+while the current one is normalized). The row counts below are read from the
+tables: the top of every row window (workgroups loop up to eight times, the
+last iteration on a partial set of workgroups), both edges of every window
+(one-shot kernel just outside), a small launch, at both edges of each width
+band, ragged widths and both storage types. Every output is compared.
 """
 
 import numpy as np
@@ -16,6 +16,7 @@ import pytest
 import memory_bound_normalization_amd as mbn
 from oracle import l2norm_fwd as o_l2, layernorm_fwd as o_ln, rmsnorm_fwd as o_rms
 from parity import assert_parity, from_gpu_bf16, to_gpu_bf16
+from tables import persistent_windows
 from workloads import f32_to_bf16_bits, random_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -26,10 +27,17 @@ torch = pytest.importorskip("torch")
 WIDTHS = [2056, 3000, 3072, 3080, 4096, 4104, 6144, 6152, 8184, 8192]
 
 
-def _rows(N):
-    # 200: inside the small-row windows; 3001 and 5000/8192: several loops per
-    # workgroup (grids of 1024 to 2048), ragged last loop
-    return [200, 3001, 8192] if N <= 4096 else [200, 3001, 5000]
+def _rows(op, N):
+    # a small launch, and the top of each row window of this width (several
+    # loops per workgroup where it exceeds the grid, ragged last loop)
+    return [200] + [hi for _, _, hi in persistent_windows(op, N // 8)]
+
+
+def _edges(op, N):
+    rows = set()
+    for _, lo, hi in persistent_windows(op, N // 8):
+        rows |= {m for m in (lo - 1, lo, hi, hi + 1) if m >= 1}
+    return sorted(rows)
 
 
 def _inputs(M, N, seed, dtype):
@@ -72,30 +80,39 @@ def _oracle(op, x, w, b, eps, dtype):
 @pytest.mark.parametrize("op", ["rms", "layer", "l2"])
 @pytest.mark.parametrize("N", WIDTHS)
 def test_persistent_widths(op, N):
-    for M in _rows(N):
+    for M in _rows(op, N):
         print(f"[persistent {op}] M={M} N={N}", flush=True)
         x, w, b = _inputs(M, N, seed=M + N, dtype="bf16")
         assert_parity(_run(op, x, w, b, 1e-6, "bf16"), _oracle(op, x, w, b, 1e-6, "bf16"), f"{op} M={M} N={N}")
 
 
 @pytest.mark.parametrize("op", ["rms", "layer", "l2"])
-@pytest.mark.parametrize("N", [3000, 8192])
+@pytest.mark.parametrize("N", [3000, 6144])
 def test_persistent_f16(op, N):
-    M = 3001
+    M = max([200] + [hi for _, _, hi in persistent_windows(op, N // 8)])
     print(f"[persistent {op} f16] M={M} N={N}", flush=True)
     x, w, b = _inputs(M, N, seed=N, dtype="f16")
     assert_parity(_run(op, x, w, b, 1e-5, "f16"), _oracle(op, x, w, b, 1e-5, "f16"), f"{op} f16 M={M} N={N}",
                   dtype="f16")
 
 
-@pytest.mark.parametrize("M", [1535, 1536, 1537, 2559, 2560, 3072, 3073, 8192, 8193])
-def test_row_window_edges(M):
-    """Either side of the RMSNorm row windows: [1536, 3072] at N = 8192 and
-    [1, 1536], [2560, 8192] at N = 3072 (persistent inside, one-shot outside)."""
-    for N in (8192, 3072):
-        print(f"[persistent rms edge] M={M} N={N}", flush=True)
+@pytest.mark.parametrize("op", ["rms", "layer", "l2"])
+@pytest.mark.parametrize("N", [3072, 4096, 6144, 8192])
+def test_row_window_edges(op, N):
+    """Either side of each row window of the persistent tables (persistent
+    inside, one-shot outside), at the top width of each band."""
+    for M in _edges(op, N):
+        print(f"[persistent {op} edge] M={M} N={N}", flush=True)
         x, w, b = _inputs(M, N, seed=M, dtype="bf16")
-        assert_parity(_run("rms", x, w, b, 1e-6, "bf16"), o_rms(x, w, 1e-6), f"rms M={M} N={N}")
+        assert_parity(_run(op, x, w, b, 1e-6, "bf16"), _oracle(op, x, w, b, 1e-6, "bf16"), f"{op} M={M} N={N}")
+
+
+def test_every_band_has_a_window():
+    """The tables above still reach the persistent kernel in every band the
+    tests name (so the parity cases exercise it)."""
+    for op, widths in (("rms", (3072, 4096, 6144, 8192)), ("layer", (3072, 4096, 6144, 8192)), ("l2", (3072, 6144))):
+        for N in widths:
+            assert persistent_windows(op, N // 8), (op, N)
 
 
 def test_special_rows_between_normal_ones():

@@ -2,40 +2,16 @@
 bands cover every width up to MBN_RMSNORM_MAX_N in increasing order, every
 entry with several waves per row serves only widths of at least 64 * WPR chunks
 (each wave parks its partial sum in its own first chunk), workgroups stay within
-1024 threads and the staged rows within the 160 KiB of LDS of a CU; the
-persistent tables serve only widths their kernel covers, with sane row windows
-and double buffers that fit in LDS."""
-
-import os
-import re
+1024 threads and the staged rows within the 160 KiB of LDS of a CU, and the
+row windows of a band precede its entry for any row count, in increasing order
+and with its width; the persistent tables serve only widths their kernel
+covers, with sane row windows and double buffers that fit in LDS."""
 
 import pytest
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "memory_bound_normalization_amd", "csrc", "rownorm.hip")
-CFG = r"MBN_CFG(_EXACT)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
+from tables import PERSISTENT, TABLES
 
 
-def _tables():
-    s = open(SRC).read()
-    macros = {}
-    for name in ("MBN_FIRST_BAND",):
-        body = s[s.index("#define " + name):].split("\n")[0]
-        macros[name] = re.findall(CFG, body)
-    out = {}
-    for tname, body in re.findall(r"const RowNormCfg (k\w+)\[\] = \{(.*?)\n\};", s, re.S):
-        entries = []
-        for line in body.split("\n"):
-            line = line.strip()
-            found = macros.get(line.split("(")[0], None) if line.startswith("MBN_FIRST_BAND") else None
-            for e in (found if found is not None else re.findall(CFG, line)):
-                exact, *nums = e
-                entries.append((exact == "_EXACT", *map(int, nums)))
-        out[tname] = entries
-    return out
-
-
-TABLES = _tables()
 
 
 def test_all_four_tables_found():
@@ -45,31 +21,37 @@ def test_all_four_tables_found():
 @pytest.mark.parametrize("name", sorted(TABLES))
 def test_table_invariants(name):
     prev = 0
-    for exact, wpr, rows, rpl, maxc, cap, grp in TABLES[name]:
+    window = None  # (band top, max_rows) of the last row window
+    for exact, max_rows, wpr, rows, rpl, maxc, cap, grp in TABLES[name]:
         top = 64 * wpr * maxc
         lowest = top if exact else prev + 1
         assert wpr == 1 or lowest >= 64 * wpr, (name, wpr, maxc)
         assert 64 * wpr * rows <= 1024
         assert rows * rpl * top * 16 <= 160 * 1024
         assert cap >= 0 and grp >= 0
-        if not exact:
+        if max_rows:
+            assert not exact and top > prev, (name, max_rows)
+            if window is not None and window[0] == top:
+                assert max_rows > window[1], (name, top, max_rows)  # increasing windows
+            else:
+                assert window is None or window[0] == prev, (name, top)  # the previous band closed
+            window = (top, max_rows)
+        elif not exact:
             assert top > prev
+            assert window is None or window[0] == top, (name, top)  # windows end in their band's entry
+            window = None
             prev = top
+    assert window is None
     assert prev * 8 == 65536  # the widest band reaches MBN_RMSNORM_MAX_N
 
 
-PCFG = r"MBN_PCFG\(Norm::(\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
+def test_row_windows_present():
+    """Every table has row windows for the small launches of its middle bands."""
+    for name, entries in TABLES.items():
+        assert sum(1 for e in entries if e[1]) >= 5, name
 
 
-def _persistent():
-    s = open(SRC).read()
-    out = {}
-    for tname, body in re.findall(r"const PersistentCfg (k\w+)\[\] = \{(.*?)\n\};", s, re.S):
-        out[tname] = [tuple(map(int, e[1:])) for e in re.findall(PCFG, body)]
-    return out
 
-
-PERSISTENT = _persistent()
 
 
 def test_persistent_tables_found():
