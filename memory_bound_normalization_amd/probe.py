@@ -15,6 +15,14 @@ RMSNorm kernel from the two runs' counter CSV files.
     rocprofv3 --kernel-trace --stats -d <dir> -o run -- python -m memory_bound_normalization_amd.probe ceiling
     python -m memory_bound_normalization_amd.probe ceiling-summary <dir>
 
+    rocprofv3 --kernel-trace -d <dir> -o run -- python -m memory_bound_normalization_amd.probe small
+    python -m memory_bound_normalization_amd.probe small-summary <dir>
+
+`small` launches the two small workloads (RMSNorm on x[1024, 4096], QK-norm +
+RoPE on 256 tokens) beside plain copies of the same bytes and a one-workgroup
+write; `small-summary` gives their GPU durations, the floor such launches sit
+on.
+
 `ceiling` times plain streaming kernels on the same 512 MiB buffers beside
 rmsnorm_fwd: torch's (read only: a sum; write only: a fill; read + write: a
 copy and a scale) and the hand-written ones of libmbn_stream.so (read only,
@@ -209,6 +217,102 @@ def ceiling_summary(d: str) -> None:
         print(f"{name:<30} {med:9.2f} us {nb / med / 1e3:8.0f} GB/s {nb / med / 1e3 / 80:6.1f}%   {kname}")
 
 
+# The small workloads beside a plain copy of the same bytes: (case, bytes per
+# launch, kind, lanes, chunks) as in CEILING_CASES; "rms-small" is rmsnorm_fwd
+# on x[1024, 4096], "qk" qk_norm_rope_fwd on 256 tokens of 32 + 8 + 8 heads.
+SMALL_RMS_BYTES = 1024 * 4096 * 2
+SMALL_QK_BYTES = 256 * 40 * 128 * 2
+SMALL_CASES = [
+    ("copy 8 MiB, 4 KiB/WG", 2 * SMALL_RMS_BYTES, "copy", 256, 1),
+    ("copy 8 MiB, 8 KiB/WG", 2 * SMALL_RMS_BYTES, "copy", 512, 1),
+    ("copy 8 MiB, 16 KiB/WG", 2 * SMALL_RMS_BYTES, "copy", 1024, 1),
+    ("rmsnorm_fwd 1024x4096", 2 * SMALL_RMS_BYTES + 2 * 4096, "rms-small", 0, 0),
+    ("copy 2.5 MiB, 4 KiB/WG", 2 * SMALL_QK_BYTES, "copy", 256, 1),
+    ("copy 2.5 MiB, 8 KiB/WG", 2 * SMALL_QK_BYTES, "copy", 512, 1),
+    ("qk_norm_rope_fwd 256 tokens", 2 * SMALL_QK_BYTES + 512 + 8 * 256, "qk", 0, 0),
+    ("write 4 KiB (one workgroup)", 4096, "write-tiny", 256, 1),
+]
+SMALL_REPS = 200
+
+
+def small() -> None:
+    """Times the small workloads and plain copies of their bytes, buffers
+    rotated over >= 1 GiB (cold) except the in-place QK tensor set (64 copies,
+    160 MiB); read the durations from a kernel trace (`small-summary`)."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+    from workloads import QK_WORKLOADS, RMS_WORKLOADS, make_qk_inputs, make_rms_inputs
+
+    dev = torch.device("cuda:0")
+    sl = stream_lib()
+    sp = torch.cuda.current_stream(dev).cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"libmbn_stream status {rc}")
+
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    x_bits, w_bits, eps = make_rms_inputs(RMS_WORKLOADS["rms_1024x4096"])
+    nrot = (1 << 30) // (2 * SMALL_RMS_BYTES)
+    xs = [up(x_bits) for _ in range(nrot)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+    w = up(w_bits)
+    qwl = QK_WORKLOADS["qk_256"]
+    qkv_bits, qw_bits, kw_bits, pos, qeps, theta = make_qk_inputs(qwl)
+    qs = [up(qkv_bits) for _ in range(64)]
+    qw, kw = up(qw_bits), up(kw_bits)
+    posg = torch.from_numpy(pos).to(dev)
+    qrot = 64
+    # the copies of the QK case move the q and k heads' bytes, one tensor per launch
+    qk_src = [torch.empty(SMALL_QK_BYTES // 2, dtype=torch.bfloat16, device=dev) for _ in range(qrot)]
+    qk_dst = [torch.empty_like(qk_src[0]) for _ in range(qrot)]
+    torch.cuda.synchronize()
+    for name, nbytes, kind, lanes, chunks in SMALL_CASES:
+        for i in range(SMALL_REPS + 20):
+            if kind == "copy" and nbytes == 2 * SMALL_RMS_BYTES:
+                ok(sl.mbn_stream_copy(xs[i % nrot].data_ptr(), ys[i % nrot].data_ptr(), SMALL_RMS_BYTES, lanes, chunks, sp))
+            elif kind == "copy":
+                ok(sl.mbn_stream_copy(qk_src[i % qrot].data_ptr(), qk_dst[i % qrot].data_ptr(), SMALL_QK_BYTES, lanes,
+                                      chunks, sp))
+            elif kind == "rms-small":
+                mbn.rmsnorm_fwd(xs[i % nrot], w, ys[i % nrot], eps=eps)
+            elif kind == "qk":
+                mbn.qk_norm_rope_fwd(qs[i % qrot], qw, kw, posg, qwl.n_q_heads, qwl.n_kv_heads, qwl.head_dim,
+                                     eps=qeps, theta=theta)
+            else:
+                ok(sl.mbn_stream_write(ys[0].data_ptr(), 4096, lanes, chunks, 0, sp))
+        torch.cuda.synchronize()
+        print(f"{name}: {SMALL_REPS + 20} launches", flush=True)
+
+
+def small_summary(d: str) -> None:
+    """Median GPU duration of each `small` case (its last SMALL_REPS launches)."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ours = [r for r in rows if any(k in r["Kernel_Name"] for k in ("stream_", "rownorm", "qk_norm_rope"))]
+    per = SMALL_REPS + 20
+    if len(ours) < per * len(SMALL_CASES):
+        raise SystemExit(f"expected {per * len(SMALL_CASES)} dispatches, found {len(ours)}")
+    ours = ours[len(ours) - per * len(SMALL_CASES):]
+    for k, (name, nb, *_rest) in enumerate(SMALL_CASES):
+        grp = ours[k * per + 20 : (k + 1) * per]
+        d_us = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+        med = d_us[len(d_us) // 2]
+        kname = grp[0]["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        kname = kname.removeprefix("void ").replace("mbn::", "")[:48]
+        print(f"{name:<30} {med:8.2f} us  p10 {d_us[len(d_us) // 10]:7.2f}  {nb / med / 1e3:7.0f} GB/s "
+              f"{nb / med / 1e3 / 80:6.1f}%   {kname}")
+
+
 def _rows(d: str):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -267,6 +371,10 @@ if __name__ == "__main__":
         ceiling()
     elif len(sys.argv) >= 3 and sys.argv[1] == "ceiling-summary":
         ceiling_summary(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "small":
+        small()
+    elif len(sys.argv) == 3 and sys.argv[1] == "small-summary":
+        small_summary(sys.argv[2])
     elif len(sys.argv) in (2, 3) and sys.argv[1] == "run":
         run(*sys.argv[2:])
     elif len(sys.argv) in (4, 5) and sys.argv[1] == "summarize":
