@@ -247,6 +247,198 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_any_kernel(RowNormAnyArgs 
   }
 }
 
+// The 16 bytes at byte offset sh (even, 0 ... 14) of the 32 bytes lo:hi.
+template <int Q>
+__device__ __forceinline__ u32x4 window_q(u32x4 lo, u32x4 hi, uint32_t r) {
+  const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbyte(d[Q + i + 1], d[Q + i], r);
+  return o;
+}
+__device__ __forceinline__ u32x4 window16(u32x4 lo, u32x4 hi, int sh) {
+  const uint32_t r = (uint32_t)(sh & 3);
+  switch (sh >> 2) {
+    case 0: return window_q<0>(lo, hi, r);
+    case 1: return window_q<1>(lo, hi, r);
+    case 2: return window_q<2>(lo, hi, r);
+    default: return window_q<3>(lo, hi, r);
+  }
+}
+
+// Element e (0 ... 7) of a 16-byte chunk, as raw 16-bit bits.
+__device__ __forceinline__ uint32_t chunk_elem(u32x4 v, int e) { return (v[e >> 1] >> (16 * (e & 1))) & 0xffffu; }
+
+// Elements [p0, p0 + 8) of the N-element vector p as one chunk: the 16 bytes
+// straddle two aligned chunks of p (uniform shift per row). `whole`: all eight
+// are elements of p (the interior chunks), else only those in [0, N) are read
+// and the rest are zero.
+__device__ __forceinline__ u32x4 vec_chunk(const uint16_t* p, int64_t p0, int N, bool whole) {
+  if (whole) {
+    const uintptr_t wa = reinterpret_cast<uintptr_t>(p) + 2 * p0;
+    const u32x4* A = reinterpret_cast<const u32x4*>(wa & ~(uintptr_t)15);
+    const int sh = (int)(wa & 15);
+    const u32x4 lo = A[0];
+    return sh ? window16(lo, A[1], sh) : lo;
+  }
+  u32x4 o = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < 8; ++e) {
+    const int64_t q = p0 + e;
+    if (q >= 0 && q < N) o[e >> 1] |= (uint32_t)p[q] << (16 * (e & 1));
+  }
+  return o;
+}
+
+// Row norms whose rows start anywhere inside a 16-byte block (N % 8 != 0, or
+// element-aligned base pointers), with x, y (and r, h) at the same address
+// modulo 16. One workgroup per row. The aligned 16-byte chunks that cover the
+// row are copied HBM -> LDS as in the staged-row kernels; the first and last
+// of them may hold up to 7 elements of the neighbouring rows (same 16-byte
+// block, so never another page), which are loaded but masked out of every
+// sum and never stored. Compute runs in that chunk grid, which y shares, so
+// every interior chunk is one 16-byte store; the two edge chunks store their
+// row elements one by one. The weight (bias) chunk of an output chunk starts
+// h elements before the chunk (h = the row's offset in its first block): two
+// aligned 16-byte loads from L2, shifted by a byte count that is uniform over
+// the row.
+template <Norm MODE, typename DT, int WAVES, int MAXC>
+__global__ void __launch_bounds__(64 * WAVES) rownorm_s16_kernel(RowNormAnyArgs a) {
+  constexpr int T = 64 * WAVES;
+  constexpr bool kHasR = MODE == Norm::kAddRms;
+  __shared__ float part[2][WAVES];
+  extern __shared__ u32x4 lds_s16[];  // the row's chunks
+  const int N = a.n;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t e0 = (int64_t)blockIdx.x * N;  // first element of this row
+  const uintptr_t xs = reinterpret_cast<uintptr_t>(a.x + e0);
+  const int h = (int)((xs & 15) >> 1);  // elements of the first block before the row
+  const int nck = (h + N + 7) >> 3;     // chunks covering the row
+  auto chunk_ptr = [&](const uint16_t* base) {
+    return reinterpret_cast<const u32x4*>(reinterpret_cast<uintptr_t>(base + e0) - 2 * (uintptr_t)h);
+  };
+  const u32x4* xc = chunk_ptr(a.x);
+
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * T + t;
+    if (k < nck) load_lds_16(xc + k, (lds_void*)(lds_s16 + j * T + wave * 64));
+  }
+  u32x4 rreg[kHasR ? MAXC : 1];
+  if constexpr (kHasR) {
+    const u32x4* rc = chunk_ptr(a.r);
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * T + t;
+      rreg[j] = k < nck ? __builtin_nontemporal_load(rc + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  wait_vmem();
+
+  // Element e of chunk k is row element 8k + e - h; a row element iff in [0, N).
+  auto in_row = [&](int k, int e) { const int p = 8 * k + e - h; return p >= 0 && p < N; };
+  auto is_edge = [&](int k) { return k == 0 || k == nck - 1; };
+
+  // Pass 1 (from LDS): sum of squares (sum for LayerNorm) over the row's
+  // elements; the residual add forms h = round(x + r), stores it and
+  // continues with the rounded h.
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * T + t;
+    if (k < nck) {
+      u32x4 v = lds_s16[k];
+      const bool edge = is_edge(k);
+      if constexpr (kHasR) {
+        u32x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hv[e] = DT::pack(DT::lo(v[e]) + DT::lo(rreg[j][e]), DT::hi(v[e]) + DT::hi(rreg[j][e]));
+        v = hv;
+        lds_s16[k] = hv;
+        if (edge) {
+          for (int e = 0; e < 8; ++e)
+            if (in_row(k, e)) __builtin_nontemporal_store((uint16_t)chunk_elem(hv, e), a.h + e0 + 8 * k + e - h);
+        } else {
+          store_nt_16(const_cast<u32x4*>(chunk_ptr(a.h)) + k, hv);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float val = (e & 1) ? DT::hi(v[e >> 1]) : DT::lo(v[e >> 1]);
+        if (edge && !in_row(k, e)) val = 0.f;
+        acc = MODE == Norm::kLayer ? acc + val : __builtin_fmaf(val, val, acc);
+      }
+    }
+  }
+  const float s1 = group_sum<WAVES>(acc, part[0], wave);
+
+  float mu = 0.f, scale;
+  if constexpr (MODE == Norm::kLayer) {
+    mu = s1 * a.inv_n;
+    float acc2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * T + t;
+      if (k < nck) {
+        const u32x4 v = lds_s16[k];
+        const bool edge = is_edge(k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float d = ((e & 1) ? DT::hi(v[e >> 1]) : DT::lo(v[e >> 1])) - mu;
+          if (edge && !in_row(k, e)) d = 0.f;
+          acc2 = __builtin_fmaf(d, d, acc2);
+        }
+      }
+    }
+    const float s2 = group_sum<WAVES>(acc2, part[1], wave);
+    scale = __builtin_amdgcn_rsqf(s2 * a.inv_n + a.eps);
+  } else if constexpr (MODE == Norm::kL2) {
+    const float nrm = __builtin_sqrtf(s1);
+    scale = 1.0f / ((nrm < a.eps) ? a.eps : nrm);  // NaN norms stay NaN
+  } else {
+    scale = __builtin_amdgcn_rsqf(__builtin_fmaf(s1, a.inv_n, a.eps));
+  }
+
+  u32x4* yc = const_cast<u32x4*>(chunk_ptr(a.y));
+
+  // Pass 2 (from LDS): normalize, weight (and bias), round, store.
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * T + t;
+    if (k < nck) {
+      const u32x4 v = lds_s16[k];
+      const bool edge = is_edge(k);
+      const int64_t p0 = 8 * (int64_t)k - h;
+      u32x4 wv{}, bv{};
+      if constexpr (MODE != Norm::kL2) wv = vec_chunk(a.w, p0, N, !edge);
+      if constexpr (MODE == Norm::kLayer) bv = vec_chunk(a.b, p0, N, !edge);
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p = DT::lo(v[e]), q = DT::hi(v[e]);
+        if constexpr (MODE == Norm::kLayer) {
+          p = __builtin_fmaf((p - mu) * scale, DT::lo(wv[e]), DT::lo(bv[e]));
+          q = __builtin_fmaf((q - mu) * scale, DT::hi(wv[e]), DT::hi(bv[e]));
+        } else if constexpr (MODE == Norm::kL2) {
+          p *= scale;
+          q *= scale;
+        } else {
+          p = (p * scale) * DT::lo(wv[e]);
+          q = (q * scale) * DT::hi(wv[e]);
+        }
+        o[e] = DT::pack(p, q);
+      }
+      if (edge) {
+        for (int e = 0; e < 8; ++e)
+          if (in_row(k, e)) __builtin_nontemporal_store((uint16_t)chunk_elem(o, e), a.y + e0 + p0 + e);
+      } else {
+        store_nt_16(yc + k, o);
+      }
+    }
+  }
+}
+
 typedef void (*RowNormAnyKernel)(RowNormAnyArgs);
 
 // One band of widths: groups per lane and lanes per row for each group size.
@@ -296,6 +488,39 @@ const AnyCfg kAny4[] = {
     MBN_ANY_CFG4(16, 16),  // N <= 65536
 };
 
+// The 16-byte staged kernels (rownorm_s16_kernel), by the widest chunk count
+// a row of the launch can cover ((N + 14) / 8: up to 7 elements of the
+// first block precede the row).
+struct S16Cfg {
+  int max_nck;
+  int waves;
+  RowNormAnyKernel k[4][2];  // [mode][bf16, fp16]
+};
+#define MBN_S16_MODE(MODE, W, C) \
+  { &rownorm_s16_kernel<MODE, Bf16, W, C>, &rownorm_s16_kernel<MODE, F16, W, C> }
+#define MBN_S16(W, C)                                                                        \
+  S16Cfg {                                                                                   \
+    64 * (W) * (C), W, {                                                                     \
+      MBN_S16_MODE(Norm::kRms, W, C), MBN_S16_MODE(Norm::kAddRms, W, C),                     \
+          MBN_S16_MODE(Norm::kLayer, W, C), MBN_S16_MODE(Norm::kL2, W, C)                    \
+    }                                                                                        \
+  }
+// Eight chunks per lane throughout; the lanes per row follow the width (a
+// sweep of 1-16 waves x 1-32 chunks x occupancy caps on MI355X at N = 2047,
+// 4095, 8191, 16380, 16383, 16384 (element offset 1) and 32767: these were
+// the fastest or within 2% of it, without caps).
+const S16Cfg kS16[] = {
+    MBN_S16(1, 8),   // N <= 4082:  64 lanes
+    MBN_S16(2, 8),   // N <= 8178:  128 lanes
+    MBN_S16(4, 8),   // N <= 16370: 256 lanes
+    MBN_S16(8, 8),   // N <= 32754: 512 lanes
+    MBN_S16(16, 8),  // N <= 65522: 1024 lanes
+};
+// Narrower rows keep the element-group kernels, and so do rows of whole
+// 4-element groups on 8-byte aligned pointers (N % 4 == 0), where those
+// kernels measured faster (16384 x 16380: 195 against 207 us).
+constexpr int kS16MinN = 1024;
+
 template <size_t K>
 const AnyCfg* pick_any(const AnyCfg (&table)[K], int groups) {
   for (const AnyCfg& c : table)
@@ -319,13 +544,29 @@ int rownorm_any_group(const RowNormAnyArgs& a) {
 
 hipError_t launch_rownorm_any(Norm mode, Storage dtype, RowNormAnyArgs args, hipStream_t stream) {
   if (args.n <= 0 || args.M <= 0 || args.M > 0x7fffffffLL) return hipErrorInvalidValue;
+  args.inv_n = 1.0f / (float)args.n;
+  const int d = dtype == Storage::kF16 ? 1 : 0;
+  // Row tensors at the same address modulo 16 share one chunk grid: the
+  // 16-byte staged kernels.
+  const uintptr_t m16 = reinterpret_cast<uintptr_t>(args.x) & 15;
+  auto same16 = [&](const void* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 15) == m16; };
+  const bool groups4 = args.n % 4 == 0 && rownorm_any_group(args) == 4;
+  if (args.n >= kS16MinN && !groups4 && same16(args.y) && same16(args.r) && same16(args.h)) {
+    const int max_nck = (args.n + 14) >> 3;
+    for (const S16Cfg& c : kS16) {
+      if (max_nck <= c.max_nck) {
+        hipLaunchKernelGGL(c.k[(int)mode][d], dim3((unsigned)args.M), dim3(64 * c.waves), (size_t)max_nck * 16,
+                           stream, args);
+        return hipGetLastError();
+      }
+    }
+  }
   const int g = rownorm_any_group(args);
   const bool shift = g == 4 && args.n % 4 != 0;
   const int groups = (args.n + g - 1) / g;  // shifted rows hold at most N / 4 whole groups
   const AnyCfg* cfg = g == 4 ? pick_any(kAny4, groups) : g == 2 ? pick_any(kAny2, groups) : pick_any(kAny1, groups);
   if (!cfg) return hipErrorInvalidValue;
-  args.inv_n = 1.0f / (float)args.n;
-  const RowNormAnyKernel kernel = cfg->k[shift ? 1 : 0][(int)mode][dtype == Storage::kF16 ? 1 : 0];
+  const RowNormAnyKernel kernel = cfg->k[shift ? 1 : 0][(int)mode][d];
   const size_t lds = cfg->stage ? (size_t)args.n * 2 : 0;
   hipLaunchKernelGGL(kernel, dim3((unsigned)args.M), dim3(64 * cfg->waves), lds, stream, args);
   return hipGetLastError();

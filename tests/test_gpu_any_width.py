@@ -2,18 +2,24 @@
 chunks, N % 8 != 0, or pointers that are only element-aligned) against the
 fp64 oracle, every output compared.
 
-The kernels access groups of 4, 2 or 1 elements: 4 whenever every pointer is
-8-byte aligned (for N % 4 != 0 with a 0-3 element head and tail per row and
-shifted weight groups), 2 or 1 for pointers aligned to less (here: views at
-an element offset). The widths cover every band of each group size's launch
-table (up to 1024/4096/8192/32768/65536 elements, the LDS-staged band of
-single elements above 32768) on both sides of the band edges, and every
-head length 0-3 (consecutive rows start at different offsets mod 4).
-Row counts include a single row and counts that are not a multiple of
-anything. Outputs are written into views of larger buffers whose
-guard elements must stay untouched: the element-wise path reads and writes
-nothing outside its rows, including the neighbouring rows' elements that
-share a 16-byte chunk.
+Two kernel families serve these launches. From N = 1024, when x, y (and r, h)
+sit at the same address modulo 16 (except for N % 4 == 0 with 8-byte aligned
+pointers, which stay on 4-element groups), the 16-byte staged kernels copy the
+aligned chunks that cover each row into LDS (the edge chunks hold elements of
+the neighbouring rows, masked out), compute in that chunk grid and store
+interior chunks whole and edge chunks element by element; the weight chunks
+are shifted windows. Otherwise the element-group kernels access groups of 4,
+2 or 1 elements: 4 whenever every pointer is 8-byte aligned (for N % 4 != 0
+with a 0-3 element head and tail per row and shifted weight groups), 2 or 1
+for pointers aligned to less. The widths cover every band of both families'
+launch tables on both sides of the band edges, and every head length (rows
+start at different offsets); views at an element offset reach the small
+groups (narrow rows, or y at another offset than x modulo 16) and the staged
+kernels' non-zero block offsets. Row counts include a single row and counts
+that are not a multiple of anything. Outputs are written into views of larger
+buffers whose guard elements must stay untouched: no kernel writes outside
+its rows, including the neighbouring rows' elements that share a 16-byte
+chunk.
 """
 
 import numpy as np
@@ -31,13 +37,14 @@ WIDTHS = [
     1, 3, 7, 9, 511, 513, 2047, 2049, 8191, 8193, 12345, 32767, 32769, 40001, 65535,  # odd: 1 element
     2, 6, 1002, 1026, 4094, 4098, 8190, 8194, 32766, 32770, 65534,  # N % 4 == 2: 2 elements
     12, 100, 1004, 1028, 4092, 4100, 8188, 8196, 32764, 32772, 40000, 65532,  # N % 8 == 4: 4 elements
+    4082, 4083, 8178, 8179, 16370, 16371, 32754, 32755, 65522, 65523,  # staged-kernel band edges
 ]
 GUARD = 8  # guard elements around an output view (16 bytes: keeps the view's alignment)
 FILL = 0x4B00  # bf16 / fp16 bit pattern the guards hold
 
 
 def _rows(N):
-    return 1 if N > 32768 else (3 if N > 8192 else 37)
+    return 3 if N > 32768 else (5 if N > 8192 else 37)
 
 
 def _inputs(M, N, seed, dtype="bf16"):
@@ -64,10 +71,12 @@ def _guards_intact_at(buf, M, N, guard):
     return bool(np.all(g == FILL))
 
 
-def _check(op, M, N, seed, dtype="bf16", eps=1e-6, offset=0):
-    """`offset` (elements) places x and the outputs at that offset from an
-    aligned address, which selects the 2- or 1-element kernels."""
-    print(f"[any-width {op} {dtype}] M={M} N={N} offset={offset}", flush=True)
+def _check(op, M, N, seed, dtype="bf16", eps=1e-6, offset=0, out_offset=None):
+    """`offset` (elements) places x and r at that offset from an aligned
+    address, `out_offset` (default: the same) the outputs: element-aligned
+    pointers (2- or 1-element groups, or staged chunks at a block offset)."""
+    out_offset = offset if out_offset is None else out_offset
+    print(f"[any-width {op} {dtype}] M={M} N={N} offset={offset} out_offset={out_offset}", flush=True)
     x, r, w, b = _inputs(M, N, seed, dtype)
     xg, rg = to_gpu_bf16(x, dtype=dtype), to_gpu_bf16(r, dtype=dtype)
     wg, bg = to_gpu_bf16(w, dtype=dtype), to_gpu_bf16(b, dtype=dtype)
@@ -75,7 +84,10 @@ def _check(op, M, N, seed, dtype="bf16", eps=1e-6, offset=0):
         xb = torch.zeros(M * N + offset, dtype=xg.dtype, device="cuda")
         xb[offset:] = xg.view(-1)
         xg = xb[offset:].view(M, N)
-    ybuf, y = _guarded(M, N, dtype, GUARD + offset)
+        rb = torch.zeros(M * N + offset, dtype=rg.dtype, device="cuda")
+        rb[offset:] = rg.view(-1)
+        rg = rb[offset:].view(M, N)
+    ybuf, y = _guarded(M, N, dtype, GUARD + out_offset)
     if op == "rms":
         mbn.rmsnorm_fwd(xg, wg, y, eps=eps)
         ref = o_rms(x, w, eps, dtype=dtype)
@@ -86,15 +98,15 @@ def _check(op, M, N, seed, dtype="bf16", eps=1e-6, offset=0):
         mbn.l2norm_fwd(xg, y, eps=eps)
         ref = o_l2(x, eps, dtype=dtype)
     else:
-        hbuf, h = _guarded(M, N, dtype, GUARD + offset)
+        hbuf, h = _guarded(M, N, dtype, GUARD + out_offset)
         mbn.add_rmsnorm_fwd(xg, rg, wg, h=h, y=y, eps=eps)
         rh, ref = o_add(x, r, w, eps, dtype=dtype)
         torch.cuda.synchronize()
         assert np.array_equal(from_gpu_bf16(h), rh), f"h = round(x + r) not bit-exact, {op} M={M} N={N}"
-        assert _guards_intact_at(hbuf, M, N, GUARD + offset), "wrote outside h"
+        assert _guards_intact_at(hbuf, M, N, GUARD + out_offset), "wrote outside h"
     torch.cuda.synchronize()
     assert_parity(from_gpu_bf16(y), ref, f"{op} M={M} N={N} {dtype}", dtype=dtype)
-    assert _guards_intact_at(ybuf, M, N, GUARD + offset), "wrote outside y"
+    assert _guards_intact_at(ybuf, M, N, GUARD + out_offset), "wrote outside y"
 
 
 @pytest.mark.parametrize("N", WIDTHS)
@@ -113,6 +125,18 @@ def test_any_width_small_groups(op, N):
     _check(op, _rows(N), N, seed=N + 7, offset=1 if N % 2 else 2)
     if N % 2 == 0:
         _check(op, _rows(N), N, seed=N + 8, offset=1)
+
+
+# x (and r) at one offset, the outputs at another modulo 16 bytes: the
+# element-group kernels at every width (1-, 2- and 4-element groups)
+MIXED_WIDTHS = [2049, 8193, 32769, 65535, 1026, 8194, 32770, 4100, 40000, 4096]
+
+
+@pytest.mark.parametrize("N", MIXED_WIDTHS)
+@pytest.mark.parametrize("op", ["rms", "add", "layer", "l2"])
+def test_any_width_mixed_offsets(op, N):
+    _check(op, _rows(N), N, seed=N + 9, offset=1, out_offset=0)
+    _check(op, _rows(N), N, seed=N + 10, offset=0, out_offset=4 if N % 4 == 0 else 2)
 
 
 @pytest.mark.parametrize("N", [3, 1001, 8191, 40001, 4098, 4100, 40000])
