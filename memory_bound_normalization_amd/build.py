@@ -6,7 +6,8 @@ Compiles every ``csrc/*.hip`` file with hipcc into one shared library next to
 this file. No fast-math: the kernels rely on IEEE fp32/fp64 behaviour.
 ``build_stream()`` compiles ``probe_csrc/*.hip`` into libmbn_stream.so, the
 plain streaming kernels the measurement tools time beside the norms (not part
-of the normalization path).
+of the normalization path). ``build_c_client()`` compiles the plain C client
+of the C ABI the tests use (``tests/c_abi``) with gcc.
 """
 
 from __future__ import annotations
@@ -73,6 +74,29 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = 
     return out
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi", "mbn_c_client.c")
+C_CLIENT_LIB = os.path.join(ROOT, "tests", "c_abi", "libmbn_c_client.so")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile tests/c_abi/libmbn_c_client.so (C, against libmbn.so and the
+    HIP runtime only); always rebuilds. Needs libmbn.so built first."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-shared", "-fPIC", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_CLIENT_SRC,
+           "-L", PKG, "-lmbn", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../memory_bound_normalization_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", C_CLIENT_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"gcc failed with status {res.returncode}")
+    os.replace(C_CLIENT_LIB + ".tmp", C_CLIENT_LIB)
+    return C_CLIENT_LIB
+
+
 def build_stream(verbose: bool = False) -> str:
     """Compile libmbn_stream.so (the streaming reference kernels); always rebuilds."""
     return build(verbose=verbose, out=STREAM_LIB_PATH, src_dir=PROBE_CSRC)
@@ -81,3 +105,4 @@ def build_stream(verbose: bool = False) -> str:
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_stream(verbose=True))
+    print(build_c_client(verbose=True))

@@ -272,3 +272,12 @@ def test_stream_reference_library_loads_and_validates():
     assert h.mbn_stream_copy(FAKE, 0, 4096, 256, 1, None) == 1  # null
     assert h.mbn_stream_read(FAKE, 0, 4096, 256, 1, None) == 1  # null sink
     assert h.mbn_stream_write(FAKE, 0, 256, 1, 0, None) == 1  # empty
+
+
+def test_c_client_builds_and_sees_host_validation():
+    """The plain C client links against libmbn.so and the HIP runtime only;
+    a call the library rejects on the host returns MBN_EINVAL without a GPU."""
+    if not os.path.exists(mbn_build.C_CLIENT_LIB):
+        mbn_build.build_c_client()
+    lib = ctypes.CDLL(mbn_build.C_CLIENT_LIB)
+    assert lib.mbn_c_client_reject() == mbn.MBN_EINVAL
