@@ -14,10 +14,11 @@
 // The inverse frequencies theta^(-2i/R) do not depend on the token: the host
 // evaluates them once per launch in fp64 and passes them as kernel arguments.
 // Wave 0 forms the token's 64 angles pos * inv_freq and their sin / cos in
-// fp64 (one per lane) once and shares cos / sin through 1 KiB of LDS; the waves then step over the token's
-// heads 4 at a time. Few tokens: one wave per 4 heads (a single step, lowest
-// latency). Many tokens: 4 waves per token, looping, so the per-token angle
-// work is not repeated in every wave.
+// fp64 (one per lane) once and shares cos / sin through 1 KiB of LDS; the
+// waves then step over the token's heads 4 at a time. Few tokens: one wave
+// per 4 heads (a single step, lowest latency); up to 1024 tokens half as many
+// waves, two steps each. Many tokens: 4 waves per token, looping, so the
+// per-token angle work is not repeated in every wave.
 //
 // Partial rotary (rotary_dim R < 128, a multiple of 16; the page keeps the
 // full-head norm for it since the tail must still be normalized): the RMS and
@@ -156,10 +157,13 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
                                hipStream_t stream) {
   const int n_heads = n_q_heads + n_kv_heads;
   const int groups = (n_heads + kHeadsPerWave - 1) / kHeadsPerWave;
-  // Up to 1024 tokens: one wave per 4-head group (at most 16 waves); beyond,
-  // 4 waves per token. Chosen on MI355X for 32 q + 8 k heads (T = 256: 3.4 us
-  // vs 4.1 us with 4 waves; T = 65536: 249 us vs 363 us with 10 waves).
-  const int waves = (T <= 1024) ? (groups < 16 ? groups : 16) : (groups < 4 ? groups : 4);
+  // Up to 512 tokens: one wave per 4-head group (at most 16 waves, a single
+  // step); up to 1024, half as many waves (two steps); beyond, 4 waves per
+  // token. Chosen on MI355X for 32 q + 8 k heads, back to back: T = 256 3.4 us
+  // with 10 waves against 4.1 us with 4; T = 1024 8.6 us with 5 waves against
+  // 9.6 us with 10; T = 65536 249 us with 4 waves against 363 us with 10.
+  const int all = groups < 16 ? groups : 16;
+  const int waves = T <= 512 ? all : T <= 1024 ? (all + 1) / 2 : (groups < 4 ? groups : 4);
   const int64_t row_stride = (int64_t)(n_q_heads + 2 * n_kv_heads) * kHeadDim;
   // The inverse frequency of pair i is theta^(-2i/R): fp64 pow on the host
   // (the C library's pow, within an ulp), once per launch rather than once per
