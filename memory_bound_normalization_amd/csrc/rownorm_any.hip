@@ -3,17 +3,24 @@
 // "[Inductor] Codegen Gluon", section 3.2, includes) or whose base pointers
 // are not 16-byte aligned. Same operations and arithmetic as rownorm.hip
 // (RMSNorm, residual add + RMSNorm, LayerNorm, L2Norm; bf16 or fp16 storage).
-// Every access is one group of G consecutive elements (G = 4, 2 or 1: 8, 4 or
-// 2 bytes), the widest that the pointers' alignment allows, and nothing
-// outside a row is read or written. With 8-byte aligned pointers and N % 4 !=
-// 0 (SHIFT), a row starts mid-group: its first 0-3 elements (head) and last
-// 0-3 (tail) are single-element accesses by a few lanes, the groups between
-// are 8-byte aligned in x and y, and each weight (bias) group is assembled
-// from the two aligned weight groups around it, shifted by the head length.
+// Two kernel families, one workgroup per row in both:
 //
-// One workgroup per row, 64 * WAVES lanes. Lane t owns the groups
-// g = j * (64 * WAVES) + t, j < MAXG: they are loaded once into VGPRs (all
-// loads of a batch issued before the first use) and the passes run from
+// rownorm_s16_kernel (from N = 1024, with x, y, r and h at one address modulo
+// 16, unless N % 4 == 0 on 8-byte aligned pointers): the aligned 16-byte
+// blocks that cover the row go HBM -> LDS as in the staged-row kernels; the
+// neighbouring rows' elements in the two edge blocks are masked out and never
+// stored. See the kernel's comment.
+//
+// rownorm_any_kernel (the other launches): every access is one group of G
+// consecutive elements (G = 4, 2 or 1: 8, 4 or 2 bytes), the widest that the
+// pointers' alignment allows, and nothing outside a row is read or written.
+// With 8-byte aligned pointers and N % 4 != 0 (SHIFT), a row starts mid-group:
+// its first 0-3 elements (head) and last 0-3 (tail) are single-element
+// accesses by a few lanes, the groups between are 8-byte aligned in x and y,
+// and each weight (bias) group is assembled from the two aligned weight groups
+// around it, shifted by the head length. 64 * WAVES lanes; lane t owns the
+// groups g = j * (64 * WAVES) + t, j < MAXG: they are loaded once into VGPRs
+// (all loads of a batch issued before the first use) and the passes run from
 // there, so the row is read from HBM once, as in the method; LDS carries the
 // cross-wave partial sums. Rows wider than 32 groups per lane (STAGE) are
 // loaded in batches of 32 and kept in LDS for the later passes. Weights and
