@@ -132,7 +132,8 @@ def cpu_baseline(x_bits, w_bits, eps, n: int, budget_s: float):
 def suite(steps: int, warmup: int) -> int:
     """Per-workload timing table (one JSON line per workload): all five inputs,
     the pages' 3 x 3 RMSNorm shape grid, fp16 storage, widths that are not
-    whole 16-byte chunks, and the rest of the norm family.
+    whole 16-byte chunks, a view at an element offset, small launches, and the
+    rest of the norm family.
 
     Workloads whose footprint is under 1 GiB rotate over enough copies of their
     buffers that successive launches cannot be served from the 256 MiB Infinity
@@ -244,6 +245,41 @@ def suite(steps: int, warmup: int) -> int:
         med, best = timed(lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps), nrot)
         b = 2 * M * N * 2 + 2 * N
         print(json.dumps({"workload": f"any_{M}x{N}", "kernel": "rmsnorm_fwd", "M": M, "N": N,
+                          "rotating_sets": nrot, "median_us": round(med, 2), "best_us": round(best, 2),
+                          "GBps_median": round(b / med / 1e3, 1),
+                          "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2),
+                          "batch_mean_us": round(timed.batch_us, 2),
+                          "pct_of_8TBps_batch": round(b / timed.batch_us / 1e3 / 80.0, 2)}), flush=True)
+        del xs, ys, x0
+    # A view at an element offset of 1 (rows start 2 bytes into a 16-byte
+    # block): the 16-byte staged any-width kernel.
+    M = N = 16384
+    nrot = 2
+    bufs = [torch.empty(M * N + 8, dtype=torch.bfloat16, device=dev) for _ in range(2 * nrot)]
+    for i in range(nrot):
+        bufs[i][1:1 + M * N].copy_(x_full.view(-1))
+    xs = [bufs[i][1:1 + M * N].view(M, N) for i in range(nrot)]
+    ys = [bufs[nrot + i][1:1 + M * N].view(M, N) for i in range(nrot)]
+    med, best = timed(lambda i: mbn.rmsnorm_fwd(xs[i], w_full, ys[i], eps=eps), nrot)
+    b = 2 * M * N * 2 + 2 * N
+    print(json.dumps({"workload": f"view_{M}x{N}_o1", "kernel": "rmsnorm_fwd", "M": M, "N": N,
+                      "rotating_sets": nrot, "median_us": round(med, 2), "best_us": round(best, 2),
+                      "GBps_median": round(b / med / 1e3, 1),
+                      "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2),
+                      "batch_mean_us": round(timed.batch_us, 2),
+                      "pct_of_8TBps_batch": round(b / timed.batch_us / 1e3 / 80.0, 2)}), flush=True)
+    del xs, ys, bufs
+    # Small launches (row windows of the launch tables), leading blocks of the
+    # same input.
+    for M, N in ((256, 16384), (1024, 8192), (1024, 16384), (2048, 2048)):
+        x0 = x_full[:M, :N].contiguous()
+        w = w_full[:N].contiguous()
+        nrot = max(1, -(-(1 << 30) // (2 * M * N * 2)))
+        xs = [x0] + [x0.clone() for _ in range(nrot - 1)]
+        ys = [torch.empty_like(x0) for _ in range(nrot)]
+        med, best = timed(lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps), nrot)
+        b = 2 * M * N * 2 + 2 * N
+        print(json.dumps({"workload": f"small_{M}x{N}", "kernel": "rmsnorm_fwd", "M": M, "N": N,
                           "rotating_sets": nrot, "median_us": round(med, 2), "best_us": round(best, 2),
                           "GBps_median": round(b / med / 1e3, 1),
                           "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2),
