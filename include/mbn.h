@@ -69,12 +69,12 @@ extern "C" {
  * Launch path (same results to the documented tolerance, not bit-identical):
  * when N % 8 == 0 and every pointer is 16-byte aligned, the staged-row
  * kernels (16-byte row chunks); otherwise the any-width kernels. Those never
- * write outside the rows. From N = 1024, when x and y sit at the same address
- * modulo 16 (and unless N % 4 == 0 with every pointer 8-byte aligned), they
- * copy the 16-byte blocks that hold row elements (so they may read up to 14
- * bytes before and after a row, inside those blocks, never another page);
- * otherwise they access groups of 4, 2 or 1 elements and read nothing outside
- * the rows. The same holds for add_rmsnorm_fwd (x, r, h and y at one address
+ * write outside the rows. When x and y sit at the same address modulo 16 and
+ * either N >= 1024 (unless N % 4 == 0 with every pointer 8-byte aligned) or
+ * N >= 256 with a pointer that is not 8-byte aligned, they copy the 16-byte
+ * blocks that hold row elements (so they may read up to 14 bytes before and
+ * after a row, inside those blocks, never another page); otherwise they access
+ * groups of 4, 2 or 1 elements and read nothing outside the rows. The same holds for add_rmsnorm_fwd (x, r, h and y at one address
  * modulo 16), layernorm_fwd and l2norm_fwd.
  * IEEE behaviour: a NaN in a row makes the row NaN; an infinite element makes
  * the finite elements of its row 0 and itself NaN; a zero row gives 0 when

@@ -5,8 +5,9 @@
 // (RMSNorm, residual add + RMSNorm, LayerNorm, L2Norm; bf16 or fp16 storage).
 // Two kernel families, one workgroup per row in both:
 //
-// rownorm_s16_kernel (from N = 1024, with x, y, r and h at one address modulo
-// 16, unless N % 4 == 0 on 8-byte aligned pointers): the aligned 16-byte
+// rownorm_s16_kernel (with x, y, r and h at one address modulo 16: from
+// N = 1024 unless N % 4 == 0 on 8-byte aligned pointers, and from N = 256 on
+// pointers that are not 8-byte aligned): the aligned 16-byte
 // blocks that cover the row go HBM -> LDS as in the staged-row kernels; the
 // neighbouring rows' elements in the two edge blocks are masked out and never
 // stored. See the kernel's comment.
@@ -517,16 +518,24 @@ struct S16Cfg {
 // 4095, 8191, 16380, 16383, 16384 (element offset 1) and 32767: these were
 // the fastest or within 2% of it, without caps).
 const S16Cfg kS16[] = {
-    MBN_S16(1, 8),   // N <= 4082:  64 lanes
+    MBN_S16(1, 1),   // N <= 498:   64 lanes
+    MBN_S16(1, 2),   // N <= 1010
+    MBN_S16(1, 4),   // N <= 2034
+    MBN_S16(1, 8),   // N <= 4082
     MBN_S16(2, 8),   // N <= 8178:  128 lanes
     MBN_S16(4, 8),   // N <= 16370: 256 lanes
     MBN_S16(8, 8),   // N <= 32754: 512 lanes
     MBN_S16(16, 8),  // N <= 65522: 1024 lanes
 };
-// Narrower rows keep the element-group kernels, and so do rows of whole
-// 4-element groups on 8-byte aligned pointers (N % 4 == 0), where those
-// kernels measured faster (16384 x 16380: 195 against 207 us).
+// From kS16MinN on, the staged kernels serve every width except rows of whole
+// 4-element groups on 8-byte aligned pointers (N % 4 == 0), where the group
+// kernels measured faster (16384 x 16380: 195 against 207 us); from
+// kS16MinNarrow they serve only pointers that are not 8-byte aligned (2- and
+// 1-element groups otherwise: 65536 x 1001 at an element offset 73 against
+// 153 us, 131072 x 511 102 against 154 us, while on 8-byte aligned pointers
+// the 4-element groups are faster: 65536 x 1001 64 against 69 us).
 constexpr int kS16MinN = 1024;
+constexpr int kS16MinNarrow = 256;
 
 template <size_t K>
 const AnyCfg* pick_any(const AnyCfg (&table)[K], int groups) {
@@ -557,8 +566,9 @@ hipError_t launch_rownorm_any(Norm mode, Storage dtype, RowNormAnyArgs args, hip
   // 16-byte staged kernels.
   const uintptr_t m16 = reinterpret_cast<uintptr_t>(args.x) & 15;
   auto same16 = [&](const void* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 15) == m16; };
-  const bool groups4 = args.n % 4 == 0 && rownorm_any_group(args) == 4;
-  if (args.n >= kS16MinN && !groups4 && same16(args.y) && same16(args.r) && same16(args.h)) {
+  const int g4 = rownorm_any_group(args);
+  const bool s16 = args.n >= kS16MinN ? !(args.n % 4 == 0 && g4 == 4) : (args.n >= kS16MinNarrow && g4 < 4);
+  if (s16 && same16(args.y) && same16(args.r) && same16(args.h)) {
     const int max_nck = (args.n + 14) >> 3;
     for (const S16Cfg& c : kS16) {
       if (max_nck <= c.max_nck) {

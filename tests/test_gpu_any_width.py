@@ -2,9 +2,10 @@
 chunks, N % 8 != 0, or pointers that are only element-aligned) against the
 fp64 oracle, every output compared.
 
-Two kernel families serve these launches. From N = 1024, when x, y (and r, h)
-sit at the same address modulo 16 (except for N % 4 == 0 with 8-byte aligned
-pointers, which stay on 4-element groups), the 16-byte staged kernels copy the
+Two kernel families serve these launches. When x, y (and r, h) sit at the
+same address modulo 16, from N = 1024 (except for N % 4 == 0 with 8-byte
+aligned pointers, which stay on 4-element groups) and from N = 256 on pointers
+that are not 8-byte aligned, the 16-byte staged kernels copy the
 aligned chunks that cover each row into LDS (the edge chunks hold elements of
 the neighbouring rows, masked out), compute in that chunk grid and store
 interior chunks whole and edge chunks element by element; the weight chunks
@@ -116,7 +117,8 @@ def test_any_width(op, N):
 
 
 # views at an element offset: 1 element -> 2-byte accesses, 2 -> 4-byte (even N)
-SMALL_GROUP_WIDTHS = [1, 7, 513, 2049, 8193, 32769, 65535, 2, 1026, 4098, 8194, 32770, 65534]
+SMALL_GROUP_WIDTHS = [1, 7, 255, 256, 300, 498, 499, 513, 1010, 1011, 2034, 2035, 2049, 8193, 32769, 65535,
+                      2, 1026, 4098, 8194, 32770, 65534]
 
 
 @pytest.mark.parametrize("N", SMALL_GROUP_WIDTHS)
