@@ -75,6 +75,47 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def streaming_copy_reference(x, y, stream, steps: int, warmup: int):
+    """The best 50/50 read/write stream measured on this part -- the
+    hand-written copy of libmbn_stream.so with 4 KiB per workgroup (16-byte
+    non-temporal loads and stores, the row-norm kernels' accesses) -- timed
+    the same way as the RMSNorm (timing events around each launch) on the same
+    512 MiB buffers: the reference roofline.frac is read against. None when
+    libmbn_stream.so is not built."""
+    try:
+        from memory_bound_normalization_amd.probe import stream_lib
+
+        sl = stream_lib()
+    except (RuntimeError, OSError):
+        return None
+    nbytes = x.numel() * x.element_size()
+    sp = stream.cuda_stream
+
+    def launch():
+        rc = sl.mbn_stream_copy(x.data_ptr(), y.data_ptr(), nbytes, 256, 1, sp)
+        if rc != 0:
+            raise RuntimeError(f"mbn_stream_copy status {rc}")
+
+    for _ in range(warmup):
+        launch()
+    timer = HipTimingEvents(stream)
+    ev = [(timer.new(), timer.new()) for _ in range(steps)]
+    for a, b in ev:
+        timer.record(a)
+        launch()
+        timer.record(b)
+    import torch
+
+    torch.cuda.synchronize()
+    us = [timer.elapsed_ms(a, b) * 1e3 for a, b in ev]
+    timer.close()
+    mean = sum(us) / len(us)
+    return {"kernel": "stream_copy<256, 1> (4 KiB per workgroup, libmbn_stream.so)",
+            "bytes_per_launch": 2 * nbytes, "mean_us": round(mean, 2),
+            "GBps": round(2 * nbytes / mean / 1e3, 1),
+            "frac": round(2 * nbytes / mean / 1e3 / HBM_PEAK_GBPS, 4)}
+
+
 def host_threads() -> int:
     """Host threads for the CPU baseline: the CPUs this process may run on,
     at most 16 (the host share of one GPU)."""
@@ -466,6 +507,11 @@ def main() -> int:
             "note": "2.5 MiB in place; stays in L2/MALL across steps; launch-latency bound",
         },
     }
+    # Context for roofline.frac, measured after the timed steps (it overwrites y).
+    copy_ref = streaming_copy_reference(x, y, stream, args.steps, min(args.warmup, 500))
+    if copy_ref is not None:
+        copy_ref["rmsnorm_over_copy"] = round(achieved / copy_ref["GBps"], 4)
+        out["roofline"]["streaming_copy_reference"] = copy_ref
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_bits, w_bits, eps, wl.N, args.cpu_budget)
     print(json.dumps(out), flush=True)
