@@ -475,32 +475,41 @@ constexpr size_t kLdsPerCU = 160 * 1024;
 
 struct RowNormCfg {
   int max_nchunk;    // widest row (in 16-byte chunks) this entry serves
+  int full_nchunk;   // the kernel's capacity, 64 * wpr * maxc chunks (>= max_nchunk)
   bool exact;        // serves only rows of exactly max_nchunk chunks
   int64_t max_rows;  // serves only launches of at most max_rows rows (0: any)
   int wpr, rows, rpl, maxc;
   int wgs_per_cu;    // occupancy cap (0 = as many as LDS, waves and VGPRs allow)
   int xcd_group;     // row blocks per XCD run (0 = dispatch order)
   RowNormKernel ragged[2];  // any width up to max_nchunk; [bf16, fp16]
-  RowNormKernel full[2];    // width exactly max_nchunk; [bf16, fp16]
+  RowNormKernel full[2];    // width exactly full_nchunk; [bf16, fp16]
 };
 
-#define MBN_CFG_(MODE, EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)              \
+#define MBN_CFG_(MODE, MAXCH, EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)       \
   RowNormCfg {                                                                        \
-    64 * (WPR) * (MAXC), EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP,            \
+    MAXCH, 64 * (WPR) * (MAXC), EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP,     \
         {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, false>,                    \
          &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, false>},                    \
         {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, true>,                     \
          &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, true>}                      \
   }
 // serves every width up to 64 * WPR * MAXC chunks (down to the previous entry)
-#define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+#define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
 // serves only the width 64 * WPR * MAXC chunks; a later entry covers the band
-#define MBN_CFG_EXACT(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) MBN_CFG_(MODE, true, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+#define MBN_CFG_EXACT(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
 // serves the widths of the band that ends at 64 * WPR * MAXC chunks, for
 // launches of at most MAXROWS rows (row windows precede the band's entry for
 // any row count, in increasing MAXROWS)
 #define MBN_CFG_ROWS(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
-  MBN_CFG_(MODE, false, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+// sub-band: serves the widths from the band's lower edge (or the previous
+// sub-band) up to MAXN elements, MAXN / 8 <= 64 * WPR * MAXC, at the row
+// counts the band's row windows leave; sub-bands follow the band's windows
+// and precede its entry, in increasing MAXN
+#define MBN_CFG_UPTO(MODE, MAXN, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, (MAXN) / 8, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
 
 // Per-width launch tables, narrowest first: the first entry that serves the
 // row width is used. Every entry with WPR > 1 serves only widths of at least
@@ -521,7 +530,13 @@ struct RowNormCfg {
 // last window use the general entry. An A/B of the library against the
 // tables without windows (GPU kernel durations, both orders, at widths and
 // row counts between the sampled ones too) then shortened the residual-add
-// and L2Norm windows that were slower there.
+// and L2Norm windows that were slower there. RMSNorm sub-bands
+// (MBN_CFG_UPTO): the band entries are tuned at the band's top width, and
+// between powers of two a configuration with fewer chunks per lane did
+// better; each sub-band entry was nowhere more than 1% slower than the band
+// entry at the widths timed inside it (4352 ... 6144, 8448 ... 15360,
+// 16896 ... 19456, at M * N = 2^26, 2^27 and 2^28, rotated buffers), and 1-9%
+// faster at all but the top width of the first.
 #define MBN_FIRST_BAND(MODE) MBN_CFG(MODE, 1, 4, 1, 1, 0, 0) /* N <= 512 */
 
 const RowNormCfg kRmsTable[] = {
@@ -540,10 +555,14 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 4, 0, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 1024
     MBN_CFG_ROWS(Norm::kRms, 2048, 2, 1, 2, 8, 0, 0),  // N <= 8192, M <= 2048
+    MBN_CFG_UPTO(Norm::kRms, 6144, 6, 1, 2, 2, 4, 0),  // 4096 < N <= 6144: 384 threads x 2 rows
     MBN_CFG(Norm::kRms, 4, 1, 1, 4, 4, 8),   // N <= 8192:  256 threads, 4 WGs/CU
     MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 1024, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1024
+    MBN_CFG_UPTO(Norm::kRms, 12288, 12, 1, 2, 2, 0, 0),  // 8192 < N <= 12288: 768 threads x 2 rows
+    MBN_CFG_UPTO(Norm::kRms, 15360, 16, 1, 2, 2, 0, 0),  // 12288 < N <= 15360: 1024 threads x 2 rows
     MBN_CFG(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
+    MBN_CFG_UPTO(Norm::kRms, 19456, 8, 1, 1, 5, 3, 0),  // 16384 < N <= 19456: 512 threads
     MBN_CFG(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N <= 32768: 1024 threads
     MBN_CFG(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N <= 65536: 1024 threads
 };
@@ -741,7 +760,8 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
   const int rows_per_wg = cfg->rows * cfg->rpl;
   const int64_t blocks = (args.M + rows_per_wg - 1) / rows_per_wg;
   const size_t lds = rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
-  const RowNormKernel kernel = (nchunk == cfg->max_nchunk) ? cfg->full[d] : cfg->ragged[d];
+  if (nchunk > cfg->full_nchunk) return hipErrorInvalidValue;  // table invariant
+  const RowNormKernel kernel = (nchunk == cfg->full_nchunk) ? cfg->full[d] : cfg->ragged[d];
   args.xcd_group = cfg->xcd_group;
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * cfg->wpr * cfg->rows), lds, stream,
                      args);

@@ -4,10 +4,29 @@ needed here)."""
 
 import os
 import re
+from collections import namedtuple
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "memory_bound_normalization_amd", "csrc", "rownorm.hip")
-CFG = r"MBN_CFG(_EXACT|_ROWS)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
+CFG = r"MBN_CFG(_EXACT|_ROWS|_UPTO)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
+
+
+class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto")):
+    """One launch-table entry. `upto` is the widest row (chunks) a sub-band
+    entry (MBN_CFG_UPTO) serves, 0 for the other kinds; `top` is the widest row
+    any entry serves and `capacity` its kernel's 64 * wpr * maxc chunks."""
+
+    @property
+    def capacity(self):
+        return 64 * self.wpr * self.maxc
+
+    @property
+    def top(self):
+        return self.upto or self.capacity
+
+    @property
+    def sub(self):
+        return self.upto > 0
 
 
 def _tables():
@@ -26,10 +45,13 @@ def _tables():
                 kind, *nums = e
                 nums = [int(v) for v in nums if v != ""]
                 max_rows = 0
+                upto = 0
                 if kind == "_ROWS":
                     max_rows, nums = nums[0], nums[1:]
-                # (exact, max_rows, wpr, rows, rpl, maxc, cap, grp)
-                entries.append((kind == "_EXACT", max_rows, *nums))
+                elif kind == "_UPTO":
+                    assert nums[0] % 8 == 0, line
+                    upto, nums = nums[0] // 8, nums[1:]
+                entries.append(Entry(kind == "_EXACT", max_rows, *nums, upto))
         out[tname] = entries
     return out
 

@@ -26,12 +26,12 @@ def _cases():
     for tname, op in OPS.items():
         prev = 0
         pending = []
-        for exact, max_rows, wpr, rows, rpl, maxc, cap, grp in TABLES[tname]:
-            top = 64 * wpr * maxc
-            if max_rows:
-                pending.append((max_rows, top))
+        for e in TABLES[tname]:
+            top = e.top
+            if e.max_rows:
+                pending.append((e.max_rows, top))
                 continue
-            if not exact:
+            if not e.exact and not e.sub:
                 below = 0  # the previous window's top row count
                 for max_rows_w, top_w in pending:
                     assert top_w == top

@@ -4,14 +4,13 @@ entry with several waves per row serves only widths of at least 64 * WPR chunks
 (each wave parks its partial sum in its own first chunk), workgroups stay within
 1024 threads and the staged rows within the 160 KiB of LDS of a CU, and the
 row windows of a band precede its entry for any row count, in increasing order
-and with its width; the persistent tables serve only widths their kernel
+and with its width, and sub-band entries come between a band's windows and
+its entry, in increasing width; the persistent tables serve only widths their kernel
 covers, with sane row windows and double buffers that fit in LDS."""
 
 import pytest
 
 from tables import PERSISTENT, TABLES
-
-
 
 
 def test_all_four_tables_found():
@@ -20,38 +19,52 @@ def test_all_four_tables_found():
 
 @pytest.mark.parametrize("name", sorted(TABLES))
 def test_table_invariants(name):
-    prev = 0
+    prev = 0  # widest row of the previous band
     window = None  # (band top, max_rows) of the last row window
-    for exact, max_rows, wpr, rows, rpl, maxc, cap, grp in TABLES[name]:
-        top = 64 * wpr * maxc
-        lowest = top if exact else prev + 1
-        assert wpr == 1 or lowest >= 64 * wpr, (name, wpr, maxc)
-        assert 64 * wpr * rows <= 1024
-        assert rows * rpl * top * 16 <= 160 * 1024
-        assert cap >= 0 and grp >= 0
-        if max_rows:
-            assert not exact and top > prev, (name, max_rows)
+    sub_top = 0  # widest row of the last sub-band of the current band
+    for e in TABLES[name]:
+        top = e.top
+        lowest = top if e.exact else max(prev, sub_top) + 1
+        assert e.wpr == 1 or lowest >= 64 * e.wpr, (name, e)
+        assert 64 * e.wpr * e.rows <= 1024
+        assert e.rows * e.rpl * e.capacity * 16 <= 160 * 1024
+        assert e.cap >= 0 and e.grp >= 0
+        assert top <= e.capacity, (name, e)
+        if e.max_rows:
+            assert not e.exact and not e.sub and top > prev, (name, e)
+            assert not sub_top, (name, e)  # windows precede the band's sub-bands
             if window is not None and window[0] == top:
-                assert max_rows > window[1], (name, top, max_rows)  # increasing windows
+                assert e.max_rows > window[1], (name, e)  # increasing windows
             else:
                 assert window is None or window[0] == prev, (name, top)  # the previous band closed
-            window = (top, max_rows)
-        elif not exact:
-            assert top > prev
+            window = (top, e.max_rows)
+        elif e.sub:
+            assert top > max(prev, sub_top), (name, e)  # increasing sub-bands
+            sub_top = top
+        elif not e.exact:
+            assert top > max(prev, sub_top)
             assert window is None or window[0] == top, (name, top)  # windows end in their band's entry
             window = None
+            sub_top = 0
             prev = top
-    assert window is None
+    assert window is None and not sub_top
     assert prev * 8 == 65536  # the widest band reaches MBN_RMSNORM_MAX_N
+
+
+def test_sub_bands_inside_their_band():
+    """A sub-band entry serves part of the band whose entry follows it, never
+    the band's top width (which the band entry keeps)."""
+    for name, entries in TABLES.items():
+        for i, e in enumerate(entries):
+            if e.sub:
+                band = next(f for f in entries[i + 1:] if not f.sub and not f.max_rows and not f.exact)
+                assert e.top < band.top, (name, e)
 
 
 def test_row_windows_present():
     """Every table has row windows for the small launches of its middle bands."""
     for name, entries in TABLES.items():
-        assert sum(1 for e in entries if e[1]) >= 5, name
-
-
-
+        assert sum(1 for e in entries if e.max_rows) >= 5, name
 
 
 def test_persistent_tables_found():
