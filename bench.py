@@ -333,6 +333,26 @@ def suite(steps: int, warmup: int) -> int:
         med, best = timed(lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps), nrot)
         report(f"width_{M}x{N}", "rmsnorm_fwd", nrot, med, best, 2 * M * N * 2 + 2 * N, M=M, N=N)
         del xs, ys, x0
+    # The other norms at widths with entries of their own between powers of
+    # two (r: the rows of x in reverse order; bias: the weights reversed).
+    for kname, N in (("add_rmsnorm_fwd", 5120), ("layernorm_fwd", 12288), ("l2norm_fwd", 12288)):
+        M = (1 << 27) // N
+        x0 = torch.cat([x_full[:, :N]] * -(-M // 16384))[:M].contiguous()
+        w = w_full[:N].contiguous()
+        bias = w_full[:N].flip(0).contiguous()
+        streams = 4 if kname == "add_rmsnorm_fwd" else 2
+        nrot = max(1, -(-(1 << 30) // (streams * M * N * 2)))
+        xs = [x0] + [x0.clone() for _ in range(nrot - 1)]
+        rs = [x.flip(0).contiguous() for x in xs] if kname == "add_rmsnorm_fwd" else None
+        hs = [torch.empty_like(x0) for _ in range(nrot)] if kname == "add_rmsnorm_fwd" else None
+        ys = [torch.empty_like(x0) for _ in range(nrot)]
+        fn = {"add_rmsnorm_fwd": lambda i: mbn.add_rmsnorm_fwd(xs[i], rs[i], w, h=hs[i], y=ys[i], eps=eps),
+              "layernorm_fwd": lambda i: mbn.layernorm_fwd(xs[i], w, bias, y=ys[i], eps=1e-5),
+              "l2norm_fwd": lambda i: mbn.l2norm_fwd(xs[i], y=ys[i], eps=1e-12)}[kname]
+        b = streams * M * N * 2 + {"add_rmsnorm_fwd": 2, "layernorm_fwd": 4, "l2norm_fwd": 0}[kname] * N
+        med, best = timed(fn, nrot)
+        report(f"width_{M}x{N}", kname, nrot, med, best, b, M=M, N=N, algorithmic_bytes=b)
+        del xs, rs, hs, ys, x0
     del x_full, w_full
     torch.cuda.empty_cache()
 

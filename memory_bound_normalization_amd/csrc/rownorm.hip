@@ -530,13 +530,15 @@ struct RowNormCfg {
 // last window use the general entry. An A/B of the library against the
 // tables without windows (GPU kernel durations, both orders, at widths and
 // row counts between the sampled ones too) then shortened the residual-add
-// and L2Norm windows that were slower there. RMSNorm sub-bands
-// (MBN_CFG_UPTO): the band entries are tuned at the band's top width, and
-// between powers of two a configuration with fewer chunks per lane did
-// better; each sub-band entry was nowhere more than 1% slower than the band
-// entry at the widths timed inside it (4352 ... 6144, 8448 ... 15360,
-// 16896 ... 19456, at M * N = 2^26, 2^27 and 2^28, rotated buffers), and 1-9%
-// faster at all but the top width of the first.
+// and L2Norm windows that were slower there. Sub-bands (MBN_CFG_UPTO) and
+// exact widths between powers of two: the band entries are tuned at the
+// band's top width, and between powers of two another geometry often did
+// better. From timing every tight geometry at N = 5120 ... 18432 (M * N =
+// 2^26, 2^27 and 2^28, rotated buffers): each such entry was nowhere more than
+// 1% slower than the band entry at the widths timed inside it and 2-10%
+// faster at most of them (RMSNorm sub-bands also timed at 4352 ... 6144,
+// 8448 ... 15360 and 16896 ... 19456; the RMSNorm one up to 6144 is within
+// 1% at 6144 itself).
 #define MBN_FIRST_BAND(MODE) MBN_CFG(MODE, 1, 4, 1, 1, 0, 0) /* N <= 512 */
 
 const RowNormCfg kRmsTable[] = {
@@ -582,6 +584,7 @@ const RowNormCfg kAddRmsTable[] = {
     MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 2, 1, 64),  // N <= 8192, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 2, 0, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kAddRms, 2048, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 2048
+    MBN_CFG_EXACT(Norm::kAddRms, 2, 2, 1, 5, 2, 4),  // N == 5120: 2 x 128 threads
     MBN_CFG(Norm::kAddRms, 8, 1, 1, 2, 2, 8),   // N <= 8192:  512 threads, 2 WGs/CU
     MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 4, 4, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 4, 0, 0),  // N <= 16384, M <= 512
@@ -608,6 +611,9 @@ const RowNormCfg kLayerTable[] = {
     MBN_CFG(Norm::kLayer, 8, 1, 2, 2, 4, 16),  // N <= 8192:  512 threads x 2 rows
     MBN_CFG_ROWS(Norm::kLayer, 512, 16, 1, 1, 2, 2, 0),  // N <= 16384, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 8, 2, 0),  // N <= 16384, M <= 1024
+    MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 5, 2, 0),  // N == 10240: 256 threads x 2 rows
+    MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 6, 2, 0),  // N == 12288
+    MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 7, 2, 0),  // N == 14336
     MBN_CFG(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
     MBN_CFG_ROWS(Norm::kLayer, 256, 8, 1, 1, 8, 1, 0),  // N <= 32768, M <= 256
     MBN_CFG(Norm::kLayer, 4, 1, 1, 16, 0, 4),  // N <= 32768: 256 threads
@@ -626,6 +632,7 @@ const RowNormCfg kL2Table[] = {
     MBN_CFG(Norm::kL2, 8, 1, 1, 2, 0, 0),   // N <= 8192:  512 threads
     MBN_CFG_ROWS(Norm::kL2, 512, 8, 1, 1, 4, 2, 0),  // N <= 16384, M <= 512
     MBN_CFG_ROWS(Norm::kL2, 2048, 2, 2, 1, 16, 2, 0),  // N <= 16384, M <= 2048
+    MBN_CFG_UPTO(Norm::kL2, 12288, 12, 1, 1, 2, 3, 0),  // 8192 < N <= 12288: 768 threads
     MBN_CFG(Norm::kL2, 4, 1, 1, 8, 3, 4),   // N <= 16384: 256 threads, 3 WGs/CU
     MBN_CFG_ROWS(Norm::kL2, 256, 8, 1, 1, 8, 2, 0),  // N <= 32768, M <= 256
     MBN_CFG_ROWS(Norm::kL2, 1024, 4, 1, 1, 16, 2, 16),  // N <= 32768, M <= 1024
