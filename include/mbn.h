@@ -6,8 +6,9 @@
  *   - Tensors are raw device pointers owned by the caller. bf16 means the raw
  *     16-bit IEEE bfloat16 bit pattern. Arrays are row-major and contiguous.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
- *     is enqueued on it asynchronously; the library never synchronizes and
- *     never allocates device or host memory.
+ *     is enqueued on it asynchronously; the library never synchronizes,
+ *     never allocates device or host memory and issues nothing but kernel
+ *     launches, so its calls may be captured into a HIP graph.
  *   - Every argument is validated on the host before any HIP call. A non-zero
  *     status means nothing was launched (except MBN_EHIP, which reports that
  *     the launch itself failed; the HIP error state is read and cleared with

@@ -1,0 +1,110 @@
+"""HIP graph capture of the library's launches. The entry points allocate
+nothing, never synchronize and launch on the caller's stream, so a sequence of
+them (RMSNorm on the one-shot, persistent and any-width paths, the residual
+add, LayerNorm, L2Norm and the in-place QK-norm + rotary) can be captured into
+one graph (torch.cuda.CUDAGraph) and replayed. Each replay runs on new input
+values copied into the captured buffers, with eager work and synchronizations
+between replays, and must reproduce eager calls of the same entry points bit
+for bit; the first input set is also checked against the fp64 oracle."""
+
+import numpy as np
+import pytest
+
+from parity import assert_parity, from_gpu_bf16, to_gpu_bf16
+from workloads import random_bf16_bits
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+import memory_bound_normalization_amd as mbn  # noqa: E402
+from oracle import l2norm_fwd as o_l2, qk_norm_rope_fwd as o_qk, rmsnorm_fwd as o_rms  # noqa: E402
+
+# (M, N): a row window of the one-shot kernel, the persistent kernel, a width
+# that is not whole 16-byte chunks
+RMS_SHAPES = [(1000, 4096), (3000, 4096), (37, 1001)]
+FAM = (513, 2048)
+T, HQ, HKV, D = 64, 8, 2, 128
+
+
+def _inputs(seed):
+    rng = np.random.default_rng(seed)
+    d = {}
+    for i, (m, n) in enumerate(RMS_SHAPES):
+        d[f"x{i}"] = random_bf16_bits(rng, (m, n))
+        d[f"w{i}"] = random_bf16_bits(rng, (n,), lo=0.5, hi=1.5)
+    m, n = FAM
+    d["fx"] = random_bf16_bits(rng, (m, n))
+    d["fr"] = random_bf16_bits(rng, (m, n))
+    d["fw"] = random_bf16_bits(rng, (n,), lo=0.5, hi=1.5)
+    d["fb"] = random_bf16_bits(rng, (n,), lo=-0.5, hi=0.5)
+    d["qkv"] = random_bf16_bits(rng, (T, (HQ + 2 * HKV) * D))
+    d["qw"] = random_bf16_bits(rng, (D,), lo=0.5, hi=1.5)
+    d["kw"] = random_bf16_bits(rng, (D,), lo=0.5, hi=1.5)
+    d["pos"] = rng.integers(0, 4096, T).astype(np.int64)
+    return d
+
+
+def _to_dev(d):
+    return {k: (torch.from_numpy(v).cuda() if v.dtype == np.int64 else to_gpu_bf16(v)) for k, v in d.items()}
+
+
+def _outputs(inp):
+    out = {f"y{i}": torch.empty_like(inp[f"x{i}"]) for i in range(len(RMS_SHAPES))}
+    for k in ("fh", "fya", "fyl", "fy2"):
+        out[k] = torch.empty_like(inp["fx"])
+    return out
+
+
+def _run_all(inp, out, qkv):
+    for i in range(len(RMS_SHAPES)):
+        mbn.rmsnorm_fwd(inp[f"x{i}"], inp[f"w{i}"], out[f"y{i}"], eps=1e-6)
+    mbn.add_rmsnorm_fwd(inp["fx"], inp["fr"], inp["fw"], h=out["fh"], y=out["fya"], eps=1e-6)
+    mbn.layernorm_fwd(inp["fx"], inp["fw"], inp["fb"], y=out["fyl"], eps=1e-5)
+    mbn.l2norm_fwd(inp["fx"], y=out["fy2"], eps=1e-12)
+    mbn.qk_norm_rope_fwd(qkv, inp["qw"], inp["kw"], inp["pos"], HQ, HKV, D, eps=1e-6, theta=1e6)
+
+
+def test_graph_replays_match_eager():
+    print("[graph] capture and replay", flush=True)
+    inp = _to_dev(_inputs(0))
+    out = _outputs(inp)
+    qkv = inp["qkv"].clone()
+
+    # warm-up on a side stream, then capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _run_all(inp, out, qkv)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _run_all(inp, out, qkv)
+    torch.cuda.synchronize()
+
+    for rep, seed in enumerate((1, 2, 3, 1)):
+        host = _inputs(seed)
+        new = _to_dev(host)
+        # eager reference on buffers of its own
+        ref_out = _outputs(new)
+        ref_qkv = new["qkv"].clone()
+        _run_all(new, ref_out, ref_qkv)
+        torch.cuda.synchronize()
+        # new values into the captured buffers (eager copies), then replay
+        for k in inp:
+            inp[k].copy_(new[k])
+        qkv.copy_(new["qkv"])
+        for t in out.values():
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in out:
+            assert torch.equal(out[k].view(torch.int16), ref_out[k].view(torch.int16)), f"replay {rep}: {k}"
+        assert torch.equal(qkv.view(torch.int16), ref_qkv.view(torch.int16)), f"replay {rep}: qkv"
+        if rep == 0:
+            assert_parity(from_gpu_bf16(out["y0"]), o_rms(host["x0"], host["w0"], 1e-6), "graph y0")
+            assert_parity(from_gpu_bf16(out["fy2"]), o_l2(host["fx"], 1e-12), "graph l2")
+            ref = o_qk(host["qkv"], host["qw"], host["kw"], host["pos"], HQ, HKV, D, 1e-6, 1e6)
+            assert_parity(from_gpu_bf16(qkv), ref, "graph qkv")
+    del g
