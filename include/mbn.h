@@ -75,8 +75,9 @@ extern "C" {
  * N >= 256 with a pointer that is not 8-byte aligned, they copy the 16-byte
  * blocks that hold row elements (so they may read up to 14 bytes before and
  * after a row, inside those blocks, never another page); otherwise they access
- * groups of 4, 2 or 1 elements and read nothing outside the rows. The same holds for add_rmsnorm_fwd (x, r, h and y at one address
- * modulo 16), layernorm_fwd and l2norm_fwd.
+ * groups of 4, 2 or 1 elements and read nothing outside the rows. The same
+ * holds for add_rmsnorm_fwd (x, r, h and y at one address modulo 16),
+ * layernorm_fwd and l2norm_fwd.
  * IEEE behaviour: a NaN in a row makes the row NaN; an infinite element makes
  * the finite elements of its row 0 and itself NaN; a zero row gives 0 when
  * eps > 0 and NaN when eps == 0. Rows whose sum of squares overflows fp32
