@@ -1,12 +1,17 @@
 // Host-side launchers of the gfx950 kernels. Arguments are already validated
-// by the C entry points; each launcher enqueues one kernel on `stream` and
-// returns the launch status.
+// by the C entry points; each launcher enqueues its kernel on `stream` (as
+// several launches over consecutive rows or tokens when one dispatch would
+// exceed kMaxWorkItems) and returns the launch status.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mbn {
+
+// Work-items of one dispatch: the grid size fields of an HSA kernel dispatch
+// packet are 32-bit, so a one-dimensional launch covers at most 2^32 - 1.
+constexpr int64_t kMaxWorkItems = 0xffffffffLL;
 
 // Storage type of every 16-bit tensor of a call.
 enum class Storage : int { kBf16 = 0, kF16 = 1 };

@@ -172,12 +172,20 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
   const int half = rotary_dim / 2;
   for (int i = 0; i < half; ++i)
     inv_freq.v[i] = std::pow((double)theta, -(double)(2 * i) / (double)(2 * half));
-  hipLaunchKernelGGL(dtype == Storage::kF16 ? qk_norm_rope_kernel<F16> : qk_norm_rope_kernel<Bf16>,
-                     dim3((unsigned)T), dim3(64 * waves), 0, stream,
-                     static_cast<uint16_t*>(qkv), static_cast<const uint16_t*>(q_w),
-                     static_cast<const uint16_t*>(k_w), positions, n_q_heads, n_heads, row_stride,
-                     rotary_dim / 16, eps, inv_freq);
-  return hipGetLastError();
+  // One workgroup per token; beyond kMaxWorkItems work-items, several launches
+  // over consecutive token ranges.
+  const int64_t tokens_per_launch = kMaxWorkItems / (64 * waves);
+  for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
+    const int64_t nt = T - t0 < tokens_per_launch ? T - t0 : tokens_per_launch;
+    hipLaunchKernelGGL(dtype == Storage::kF16 ? qk_norm_rope_kernel<F16> : qk_norm_rope_kernel<Bf16>,
+                       dim3((unsigned)nt), dim3(64 * waves), 0, stream,
+                       static_cast<uint16_t*>(qkv) + t0 * row_stride, static_cast<const uint16_t*>(q_w),
+                       static_cast<const uint16_t*>(k_w), positions + t0, n_q_heads, n_heads, row_stride,
+                       rotary_dim / 16, eps, inv_freq);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mbn

@@ -765,14 +765,28 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
   if (!cfg) return hipErrorInvalidValue;
   if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant
   const int rows_per_wg = cfg->rows * cfg->rpl;
-  const int64_t blocks = (args.M + rows_per_wg - 1) / rows_per_wg;
+  const int threads = 64 * cfg->wpr * cfg->rows;
   const size_t lds = rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
   if (nchunk > cfg->full_nchunk) return hipErrorInvalidValue;  // table invariant
   const RowNormKernel kernel = (nchunk == cfg->full_nchunk) ? cfg->full[d] : cfg->ragged[d];
   args.xcd_group = cfg->xcd_group;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * cfg->wpr * cfg->rows), lds, stream,
-                     args);
-  return hipGetLastError();
+  // One dispatch covers at most kMaxWorkItems work-items: larger launches run
+  // as several launches over consecutive row ranges (rows are independent).
+  const int64_t rows_per_launch = (kMaxWorkItems / threads) * rows_per_wg;
+  for (int64_t r0 = 0; r0 < args.M; r0 += rows_per_launch) {
+    RowNormArgs part = args;
+    const int64_t e0 = r0 * N;
+    part.x = args.x + e0;
+    part.y = args.y + e0;
+    if (args.r) part.r = args.r + e0;
+    if (args.h) part.h = args.h + e0;
+    part.M = args.M - r0 < rows_per_launch ? args.M - r0 : rows_per_launch;
+    const int64_t blocks = (part.M + rows_per_wg - 1) / rows_per_wg;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), lds, stream, part);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mbn

@@ -558,9 +558,11 @@ int rownorm_any_group(const RowNormAnyArgs& a) {
   return 1;
 }
 
-hipError_t launch_rownorm_any(Norm mode, Storage dtype, RowNormAnyArgs args, hipStream_t stream) {
-  if (args.n <= 0 || args.M <= 0 || args.M > 0x7fffffffLL) return hipErrorInvalidValue;
-  args.inv_n = 1.0f / (float)args.n;
+namespace {
+
+// One launch of the any-width kernels over rows [0, args.M) of args (one
+// workgroup per row, at most kMaxWorkItems / 1024 rows).
+hipError_t launch_rownorm_any_rows(Norm mode, Storage dtype, RowNormAnyArgs args, hipStream_t stream) {
   const int d = dtype == Storage::kF16 ? 1 : 0;
   // Row tensors at the same address modulo 16 share one chunk grid: the
   // 16-byte staged kernels.
@@ -587,6 +589,30 @@ hipError_t launch_rownorm_any(Norm mode, Storage dtype, RowNormAnyArgs args, hip
   const size_t lds = cfg->stage ? (size_t)args.n * 2 : 0;
   hipLaunchKernelGGL(kernel, dim3((unsigned)args.M), dim3(64 * cfg->waves), lds, stream, args);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rownorm_any(Norm mode, Storage dtype, RowNormAnyArgs args, hipStream_t stream) {
+  if (args.n <= 0 || args.M <= 0 || args.M > 0x7fffffffLL) return hipErrorInvalidValue;
+  args.inv_n = 1.0f / (float)args.n;
+  // One workgroup of at most 1024 lanes per row: beyond kMaxWorkItems / 1024
+  // rows the launch runs as several launches over consecutive row ranges (a
+  // multiple of 8 rows each, so every range starts at the same address modulo
+  // 16 as the tensor and takes the kernel the whole launch would).
+  constexpr int64_t kRowsPerLaunch = (kMaxWorkItems / 1024) & ~(int64_t)7;
+  for (int64_t r0 = 0; r0 < args.M; r0 += kRowsPerLaunch) {
+    RowNormAnyArgs part = args;
+    const int64_t e0 = r0 * args.n;
+    part.x = args.x + e0;
+    part.y = args.y + e0;
+    if (args.r) part.r = args.r + e0;
+    if (args.h) part.h = args.h + e0;
+    part.M = args.M - r0 < kRowsPerLaunch ? args.M - r0 : kRowsPerLaunch;
+    const hipError_t err = launch_rownorm_any_rows(mode, dtype, part, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mbn
