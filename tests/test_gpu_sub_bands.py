@@ -4,8 +4,8 @@ of its own) and exact widths, at the row counts the band's row windows and
 the persistent windows leave. Each sub-band is reached at its lowest width, at
 a ragged width inside it and at its top width, each exact entry at its width,
 with a row count just above every window that would take the launch and not a
-multiple of the rows per workgroup; every output is compared against the fp64
-oracle."""
+multiple of the rows per workgroup, in both storage types; every output is
+compared against the fp64 oracle."""
 
 import pytest
 
@@ -53,7 +53,8 @@ def test_every_entry_reached():
     assert n >= 4 and len(CASES) == n
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("op,M,N", CASES)
-def test_between_powers_of_two(op, M, N):
-    print(f"[between powers of two {op}] M={M} N={N}", flush=True)
-    check_norm(op, M, N, M * 3 + N, f"{op} M={M} N={N}")
+def test_between_powers_of_two(op, M, N, dtype):
+    print(f"[between powers of two {op} {dtype}] M={M} N={N}", flush=True)
+    check_norm(op, M, N, M * 3 + N, f"{op} {dtype} M={M} N={N}", dtype=dtype)

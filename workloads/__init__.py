@@ -3,7 +3,8 @@
 This module is the one thing the CPU oracle and the HIP path have in common:
 it draws the input bit patterns that both sides consume. It holds none of the
 method's arithmetic (no sum of squares, no normalization, no rotation); it only
-draws random numbers and quantizes them to bf16 input bits.
+draws random numbers and quantizes them to bf16 (or, for the fp16 tests,
+binary16) input bits.
 
 Recipe (every workload): a fresh ``numpy.random.default_rng(seed)`` (PCG64),
 values drawn as float32 in the order x -> w -> extras, scaled in float32, then
@@ -43,6 +44,7 @@ __all__ = [
     "make_norm_family_inputs",
     "make_qk_inputs",
     "random_bf16_bits",
+    "random_f16_bits",
 ]
 
 
@@ -198,3 +200,14 @@ def random_bf16_bits(rng: np.random.Generator, shape, scale: float = 1.0, lo=Non
     else:
         v = rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
     return f32_to_bf16_bits(v)
+
+
+def random_f16_bits(rng: np.random.Generator, shape, scale: float = 1.0, lo=None, hi=None):
+    """As random_bf16_bits, for IEEE binary16 storage (numpy's float16 cast,
+    round to nearest even)."""
+    if lo is not None:
+        n = int(np.prod(shape))
+        v = _uniform_f32(rng, n, lo, hi).reshape(shape)
+    else:
+        v = rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    return v.astype(np.float16).view(np.uint16)
