@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mbn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -98,6 +100,25 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, lds_void* lds_wave
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt / lgkmcnt left at max
   __asm__ __volatile__("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(N): vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// f(std::integral_constant<int, I>{}) for I = BEGIN ... END - 1, unrolled at
+// compile time (for per-iteration immediates such as wait_vmcnt_le).
+template <int BEGIN, int END, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (BEGIN < END) {
+    f(std::integral_constant<int, BEGIN>{});
+    static_for<BEGIN + 1, END>(f);
+  }
 }
 
 // Streaming 16-byte store (global_store_dwordx4 ... nt).

@@ -255,12 +255,15 @@ __device__ __forceinline__ void finish_rows(const RowNormArgs& a, u32x4* buf0, f
 // compiler scheduled the LDS reads of the LayerNorm passes less far ahead,
 // 4-6% slower at N >= 16384 on MI355X (RMSNorm, L2Norm and the residual add
 // unchanged).
-template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL>
+template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL, bool CHUNK_WAIT = false>
 __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a) {
   constexpr int TPR = 64 * WPR;  // lanes per lane set
   constexpr bool kHasW = MODE != Norm::kL2;
   constexpr bool kHasB = MODE == Norm::kLayer;
   constexpr bool kHasR = MODE == Norm::kAddRms;
+  // Pass 1 consumes each staged chunk as it lands (see below): full-width
+  // kernels of the table entries that ask for it, not the residual add.
+  constexpr bool kChunkWait = CHUNK_WAIT && FULL && !kHasR;
   extern __shared__ u32x4 lds_rows[];  // ROWS * RPL * nchunk chunks (or more, see launcher)
 
   const int nchunk = a.nchunk;
@@ -273,80 +276,145 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
 
   u32x4* buf0 = lds_rows + (size_t)slot * RPL * nchunk;  // row rr at buf0 + rr * nchunk
 
-  // HBM -> LDS: every row of the lane set, all chunks in flight before any wait.
-#pragma unroll
-  for (int rr = 0; rr < RPL; ++rr) {
-    if (row0 + rr < a.M) {
-      const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + (row0 + rr) * nchunk;
-      u32x4* buf = buf0 + (size_t)rr * nchunk;
-#pragma unroll
-      for (int j = 0; j < MAXC; ++j) {
-        const int k = j * TPR + t;
-        if (FULL || k < nchunk) load_lds_16(xrow + k, (lds_void*)(buf + j * TPR + wave * 64));
-      }
-    }
-  }
-  // Residual chunks go to VGPRs (consumed once); weights and bias to VGPRs
-  // (L2 hits after the first rows), all overlapping the row copy.
   u32x4 rreg[kHasR ? RPL : 1][kHasR ? MAXC : 1], wreg[kHasW ? MAXC : 1], breg[kHasB ? MAXC : 1];
-#pragma unroll
-  for (int j = 0; j < MAXC; ++j) {
-    const int k = j * TPR + t;
-    const bool in = FULL || k < nchunk;
-    if constexpr (kHasR) {
-#pragma unroll
-      for (int rr = 0; rr < RPL; ++rr)
-        rreg[rr][j] = (row0 + rr < a.M && in)
-                          ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r) + (row0 + rr) * nchunk + k)
-                          : u32x4{0u, 0u, 0u, 0u};
-    }
-    if constexpr (kHasW) wreg[j] = in ? reinterpret_cast<const u32x4*>(a.w)[k] : u32x4{0u, 0u, 0u, 0u};
-    if constexpr (kHasB) breg[j] = in ? reinterpret_cast<const u32x4*>(a.b)[k] : u32x4{0u, 0u, 0u, 0u};
-  }
-  wait_vmem();
-
-  // Pass 1 (from LDS): sum of squares, or sum for LayerNorm. For the residual
-  // add, h = bf16(x + r) is formed here, written back over x in LDS and
-  // stored; the norm is taken of the rounded h.
   float s1[RPL];
   u32x4 first[RPL];  // chunk j = 0 of each row, kept for the later passes
-#pragma unroll
-  for (int rr = 0; rr < RPL; ++rr) {
-    u32x4* buf = buf0 + (size_t)rr * nchunk;
-    const bool live = row0 + rr < a.M;
-    float acc0 = 0.f, acc1 = 0.f;
-    first[rr] = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (kChunkWait) {
+    // Weights and bias go to VGPRs (L2 hits after the first rows). With
+    // per-chunk waits they are loaded before the row copy, so that every
+    // vector-memory load issued after a row chunk's copy is a later chunk's copy.
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
       const int k = j * TPR + t;
-      if (FULL || k < nchunk) {
-        u32x4 v = buf[k];
-        if constexpr (kHasR) {
-          u32x4 hv;
+      if constexpr (kHasW) wreg[j] = reinterpret_cast<const u32x4*>(a.w)[k];
+      if constexpr (kHasB) breg[j] = reinterpret_cast<const u32x4*>(a.b)[k];
+    }
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            hv[e] = DT::pack(DT::lo(v[e]) + DT::lo(rreg[rr][j][e]),
-                                DT::hi(v[e]) + DT::hi(rreg[rr][j][e]));
-          v = hv;
-          buf[k] = hv;
-          if (live) store_nt_16(reinterpret_cast<u32x4*>(a.h) + (row0 + rr) * nchunk + k, hv);
+    for (int rr = 0; rr < RPL; ++rr) {
+      if (row0 + rr < a.M) {
+        const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + (row0 + rr) * nchunk;
+        u32x4* buf = buf0 + (size_t)rr * nchunk;
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) load_lds_16(xrow + j * TPR + t, (lds_void*)(buf + j * TPR + wave * 64));
+      }
+    }
+    // Pass 1 (from LDS): sum of squares, or sum for LayerNorm, one chunk at a
+    // time. Vector-memory loads complete in issue order, and with every row of
+    // the lane set copied (no row past M) the RPL * MAXC copies were issued last,
+    // so copy q (row q / MAXC, chunk q % MAXC) has landed once at most
+    // RPL * MAXC - 1 - q loads are outstanding: each chunk is taken as it lands
+    // instead of after the whole row set, in the same order and with the same
+    // arithmetic. In the grid's last row sets it waits for every load.
+    float acc0[RPL], acc1[RPL];
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      acc0[rr] = 0.f;
+      acc1[rr] = 0.f;
+    }
+    auto take = [&](int rr, int j) {
+      const u32x4 v = buf0[(size_t)rr * nchunk + j * TPR + t];
+      if (j == 0) first[rr] = v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = DT::lo(v[e]);
+        const float q = DT::hi(v[e]);
+        if constexpr (MODE == Norm::kLayer) {
+          acc0[rr] += p;
+          acc1[rr] += q;
+        } else {
+          acc0[rr] = __builtin_fmaf(p, p, acc0[rr]);
+          acc1[rr] = __builtin_fmaf(q, q, acc1[rr]);
         }
-        if (j == 0) first[rr] = v;
+      }
+    };
+    if (row0 + RPL <= a.M) {
+      static_for<0, RPL * MAXC>([&](auto q) {
+        constexpr int Q = decltype(q)::value;
+        wait_vmcnt_le<RPL * MAXC - 1 - Q>();
+        take(Q / MAXC, Q % MAXC);
+      });
+    } else {
+      wait_vmem();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = DT::lo(v[e]);
-          const float q = DT::hi(v[e]);
-          if constexpr (MODE == Norm::kLayer) {
-            acc0 += p;
-            acc1 += q;
-          } else {
-            acc0 = __builtin_fmaf(p, p, acc0);
-            acc1 = __builtin_fmaf(q, q, acc1);
-          }
+      for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) take(rr, j);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) s1[rr] = acc0[rr] + acc1[rr];
+  } else {
+    // HBM -> LDS: every row of the lane set, all chunks in flight before any wait.
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      if (row0 + rr < a.M) {
+        const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + (row0 + rr) * nchunk;
+        u32x4* buf = buf0 + (size_t)rr * nchunk;
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+          const int k = j * TPR + t;
+          if (FULL || k < nchunk) load_lds_16(xrow + k, (lds_void*)(buf + j * TPR + wave * 64));
         }
       }
     }
-    s1[rr] = acc0 + acc1;
+    // Residual chunks go to VGPRs (consumed once); weights and bias to VGPRs
+    // (L2 hits after the first rows), all overlapping the row copy.
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * TPR + t;
+      const bool in = FULL || k < nchunk;
+      if constexpr (kHasR) {
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr)
+          rreg[rr][j] = (row0 + rr < a.M && in)
+                            ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r) + (row0 + rr) * nchunk + k)
+                            : u32x4{0u, 0u, 0u, 0u};
+      }
+      if constexpr (kHasW) wreg[j] = in ? reinterpret_cast<const u32x4*>(a.w)[k] : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kHasB) breg[j] = in ? reinterpret_cast<const u32x4*>(a.b)[k] : u32x4{0u, 0u, 0u, 0u};
+    }
+    wait_vmem();
+
+    // Pass 1 (from LDS): sum of squares, or sum for LayerNorm. For the residual
+    // add, h = bf16(x + r) is formed here, written back over x in LDS and
+    // stored; the norm is taken of the rounded h.
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+      u32x4* buf = buf0 + (size_t)rr * nchunk;
+      const bool live = row0 + rr < a.M;
+      float acc0 = 0.f, acc1 = 0.f;
+      first[rr] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int k = j * TPR + t;
+        if (FULL || k < nchunk) {
+          u32x4 v = buf[k];
+          if constexpr (kHasR) {
+            u32x4 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              hv[e] = DT::pack(DT::lo(v[e]) + DT::lo(rreg[rr][j][e]),
+                                  DT::hi(v[e]) + DT::hi(rreg[rr][j][e]));
+            v = hv;
+            buf[k] = hv;
+            if (live) store_nt_16(reinterpret_cast<u32x4*>(a.h) + (row0 + rr) * nchunk + k, hv);
+          }
+          if (j == 0) first[rr] = v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = DT::lo(v[e]);
+            const float q = DT::hi(v[e]);
+            if constexpr (MODE == Norm::kLayer) {
+              acc0 += p;
+              acc1 += q;
+            } else {
+              acc0 = __builtin_fmaf(p, p, acc0);
+              acc1 = __builtin_fmaf(q, q, acc1);
+            }
+          }
+        }
+      }
+      s1[rr] = acc0 + acc1;
+    }
   }
   // Chunk wave * 64 of each row (lane 0's first chunk) is in VGPRs now and is
   // not read from LDS again; the launch tables guarantee nchunk >= 64 * WPR, so
@@ -481,35 +549,58 @@ struct RowNormCfg {
   int wpr, rows, rpl, maxc;
   int wgs_per_cu;    // occupancy cap (0 = as many as LDS, waves and VGPRs allow)
   int xcd_group;     // row blocks per XCD run (0 = dispatch order)
-  RowNormKernel ragged[2];  // any width up to max_nchunk; [bf16, fp16]
-  RowNormKernel full[2];    // width exactly full_nchunk; [bf16, fp16]
+  RowNormKernel ragged[2];   // any width up to max_nchunk; [bf16, fp16]
+  RowNormKernel full[2];     // width exactly full_nchunk; [bf16, fp16]
+  RowNormKernel full_cw[2];  // the same with per-chunk waits in pass 1 (_W entries), else null
 };
 
-#define MBN_CFG_(MODE, MAXCH, EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)       \
+// A grid of at least this many workgroups (four per CU) takes the per-chunk
+// wait kernel of a _W entry: on MI355X it was 1-6% faster there and up to 5%
+// slower on smaller grids (12288 x 1536: 768 workgroups).
+constexpr int64_t kChunkWaitMinBlocks = 1024;
+
+template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool CW>
+constexpr RowNormKernel chunk_wait_kernel() {
+  if constexpr (CW) return &rownorm_kernel<MODE, DT, WPR, ROWS, RPL, MAXC, true, true>;
+  else return nullptr;
+}
+
+#define MBN_CFG_(MODE, MAXCH, EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP, CW)   \
   RowNormCfg {                                                                        \
     MAXCH, 64 * (WPR) * (MAXC), EXACT, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP,     \
         {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, false>,                    \
          &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, false>},                    \
         {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, true>,                     \
-         &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, true>}                      \
+         &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, true>},                     \
+        {chunk_wait_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, CW>(),                   \
+         chunk_wait_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, CW>()}                    \
   }
 // serves every width up to 64 * WPR * MAXC chunks (down to the previous entry)
 #define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
-  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, false)
 // serves only the width 64 * WPR * MAXC chunks; a later entry covers the band
 #define MBN_CFG_EXACT(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
-  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, false)
 // serves the widths of the band that ends at 64 * WPR * MAXC chunks, for
 // launches of at most MAXROWS rows (row windows precede the band's entry for
 // any row count, in increasing MAXROWS)
 #define MBN_CFG_ROWS(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
-  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP, false)
 // sub-band: serves the widths from the band's lower edge (or the previous
 // sub-band) up to MAXN elements, MAXN / 8 <= 64 * WPR * MAXC, at the row
 // counts the band's row windows leave; sub-bands follow the band's windows
 // and precede its entry, in increasing MAXN
 #define MBN_CFG_UPTO(MODE, MAXN, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
-  MBN_CFG_(MODE, (MAXN) / 8, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP)
+  MBN_CFG_(MODE, (MAXN) / 8, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, false)
+// The _W forms: the same entries with a second full-width kernel that takes
+// each staged chunk as it lands (per-chunk waits in pass 1), used for grids of
+// at least kChunkWaitMinBlocks workgroups
+#define MBN_CFG_W(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
+#define MBN_CFG_EXACT_W(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
+#define MBN_CFG_UPTO_W(MODE, MAXN, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, (MAXN) / 8, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
 
 // Per-width launch tables, narrowest first: the first entry that serves the
 // row width is used. Every entry with WPR > 1 serves only widths of at least
@@ -553,7 +644,7 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 2, 0, 0),  // N <= 4096, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 2, 1, 4, 3, 0),  // N <= 4096, M <= 1024
     MBN_CFG_ROWS(Norm::kRms, 4096, 2, 1, 2, 4, 0, 0),  // N <= 4096, M <= 4096
-    MBN_CFG(Norm::kRms, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows, 4 WGs/CU
+    MBN_CFG_W(Norm::kRms, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows, 4 WGs/CU
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 4, 0, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 1024
     MBN_CFG_ROWS(Norm::kRms, 2048, 2, 1, 2, 8, 0, 0),  // N <= 8192, M <= 2048
@@ -561,12 +652,12 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG(Norm::kRms, 4, 1, 1, 4, 4, 8),   // N <= 8192:  256 threads, 4 WGs/CU
     MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 1024, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1024
-    MBN_CFG_UPTO(Norm::kRms, 12288, 12, 1, 2, 2, 0, 0),  // 8192 < N <= 12288: 768 threads x 2 rows
+    MBN_CFG_UPTO_W(Norm::kRms, 12288, 12, 1, 2, 2, 0, 0),  // 8192 < N <= 12288: 768 threads x 2 rows
     MBN_CFG_UPTO(Norm::kRms, 15360, 16, 1, 2, 2, 0, 0),  // 12288 < N <= 15360: 1024 threads x 2 rows
-    MBN_CFG(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
+    MBN_CFG_W(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
     MBN_CFG_UPTO(Norm::kRms, 19456, 8, 1, 1, 5, 3, 0),  // 16384 < N <= 19456: 512 threads
-    MBN_CFG(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N <= 32768: 1024 threads
-    MBN_CFG(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N <= 65536: 1024 threads
+    MBN_CFG_W(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N <= 32768: 1024 threads
+    MBN_CFG_W(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N <= 65536: 1024 threads
 };
 const RowNormCfg kAddRmsTable[] = {
     MBN_FIRST_BAND(Norm::kAddRms),
@@ -604,20 +695,20 @@ const RowNormCfg kLayerTable[] = {
     MBN_CFG_ROWS(Norm::kLayer, 512, 4, 1, 1, 2, 4, 2),  // N <= 4096, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 2, 1, 2, 2, 0),  // N <= 4096, M <= 1024
     MBN_CFG_ROWS(Norm::kLayer, 2048, 1, 4, 1, 8, 2, 0),  // N <= 4096, M <= 2048
-    MBN_CFG(Norm::kLayer, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows
+    MBN_CFG_W(Norm::kLayer, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows
     MBN_CFG_ROWS(Norm::kLayer, 512, 8, 1, 1, 2, 3, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 4, 2, 0),  // N <= 8192, M <= 1024
     MBN_CFG_ROWS(Norm::kLayer, 2048, 8, 1, 4, 2, 2, 0),  // N <= 8192, M <= 2048
-    MBN_CFG(Norm::kLayer, 8, 1, 2, 2, 4, 16),  // N <= 8192:  512 threads x 2 rows
+    MBN_CFG_W(Norm::kLayer, 8, 1, 2, 2, 4, 16),  // N <= 8192:  512 threads x 2 rows
     MBN_CFG_ROWS(Norm::kLayer, 512, 16, 1, 1, 2, 2, 0),  // N <= 16384, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 8, 2, 0),  // N <= 16384, M <= 1024
     MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 5, 2, 0),  // N == 10240: 256 threads x 2 rows
-    MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 6, 2, 0),  // N == 12288
+    MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 6, 2, 0),  // N == 12288
     MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 7, 2, 0),  // N == 14336
-    MBN_CFG(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
+    MBN_CFG_W(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
     MBN_CFG_ROWS(Norm::kLayer, 256, 8, 1, 1, 8, 1, 0),  // N <= 32768, M <= 256
     MBN_CFG(Norm::kLayer, 4, 1, 1, 16, 0, 4),  // N <= 32768: 256 threads
-    MBN_CFG(Norm::kLayer, 8, 1, 1, 16, 1, 0),  // N <= 65536: 512 threads
+    MBN_CFG_W(Norm::kLayer, 8, 1, 1, 16, 1, 0),  // N <= 65536: 512 threads
 };
 const RowNormCfg kL2Table[] = {
     MBN_FIRST_BAND(Norm::kL2),
@@ -768,7 +859,10 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
   const int threads = 64 * cfg->wpr * cfg->rows;
   const size_t lds = rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
   if (nchunk > cfg->full_nchunk) return hipErrorInvalidValue;  // table invariant
-  const RowNormKernel kernel = (nchunk == cfg->full_nchunk) ? cfg->full[d] : cfg->ragged[d];
+  const int64_t all_blocks = (args.M + rows_per_wg - 1) / rows_per_wg;
+  const RowNormKernel kernel = nchunk != cfg->full_nchunk ? cfg->ragged[d]
+                               : cfg->full_cw[d] && all_blocks >= kChunkWaitMinBlocks ? cfg->full_cw[d]
+                                                                                      : cfg->full[d];
   args.xcd_group = cfg->xcd_group;
   // One dispatch covers at most kMaxWorkItems work-items: larger launches run
   // as several launches over consecutive row ranges (rows are independent).

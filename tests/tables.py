@@ -8,12 +8,13 @@ from collections import namedtuple
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "memory_bound_normalization_amd", "csrc", "rownorm.hip")
-CFG = r"MBN_CFG(_EXACT|_ROWS|_UPTO)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
+CFG = r"MBN_CFG(_EXACT|_ROWS|_UPTO)?(_W)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
 
 
-class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto")):
+class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto chunk_wait")):
     """One launch-table entry. `upto` is the widest row (chunks) a sub-band
-    entry (MBN_CFG_UPTO) serves, 0 for the other kinds; `top` is the widest row
+    entry (MBN_CFG_UPTO) serves, 0 for the other kinds; `chunk_wait`: a _W
+    entry (per-chunk waits in its full-width kernel); `top` is the widest row
     any entry serves and `capacity` its kernel's 64 * wpr * maxc chunks."""
 
     @property
@@ -42,7 +43,7 @@ def _tables():
             line = line.strip()
             found = macros.get(line.split("(")[0], None) if line.startswith("MBN_FIRST_BAND") else None
             for e in (found if found is not None else re.findall(CFG, line)):
-                kind, *nums = e
+                kind, w, *nums = e
                 nums = [int(v) for v in nums if v != ""]
                 max_rows = 0
                 upto = 0
@@ -51,7 +52,7 @@ def _tables():
                 elif kind == "_UPTO":
                     assert nums[0] % 8 == 0, line
                     upto, nums = nums[0] // 8, nums[1:]
-                entries.append(Entry(kind == "_EXACT", max_rows, *nums, upto))
+                entries.append(Entry(kind == "_EXACT", max_rows, *nums, upto, w == "_W"))
         out[tname] = entries
     return out
 

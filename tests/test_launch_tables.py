@@ -61,6 +61,20 @@ def test_sub_bands_inside_their_band():
                 assert e.top < band.top, (name, e)
 
 
+def test_chunk_wait_entries():
+    """Per-chunk waits are asked only of entries that serve large launches
+    (never a row window) and never of the residual add, whose first pass
+    also stores."""
+    n = 0
+    for name, entries in TABLES.items():
+        for e in entries:
+            if e.chunk_wait:
+                n += 1
+                assert not e.max_rows and name != "kAddRmsTable", (name, e)
+                assert e.rpl * e.maxc <= 63  # one vmcnt immediate per staged chunk
+    assert n >= 5
+
+
 def test_row_windows_present():
     """Every table has row windows for the small launches of its middle bands."""
     for name, entries in TABLES.items():
