@@ -586,6 +586,10 @@ constexpr RowNormKernel chunk_wait_kernel() {
 // any row count, in increasing MAXROWS)
 #define MBN_CFG_ROWS(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
   MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP, false)
+// a row window that serves only the width 64 * WPR * MAXC chunks (the band's
+// top width), with per-chunk waits
+#define MBN_CFG_ROWS_EXACT_W(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
 // sub-band: serves the widths from the band's lower edge (or the previous
 // sub-band) up to MAXN elements, MAXN / 8 <= 64 * WPR * MAXC, at the row
 // counts the band's row windows leave; sub-bands follow the band's windows
@@ -651,7 +655,8 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_UPTO(Norm::kRms, 6144, 6, 1, 2, 2, 4, 0),  // 4096 < N <= 6144: 384 threads x 2 rows
     MBN_CFG(Norm::kRms, 4, 1, 1, 4, 4, 8),   // N <= 8192:  256 threads, 4 WGs/CU
     MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
-    MBN_CFG_ROWS(Norm::kRms, 1024, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1024
+    MBN_CFG_ROWS(Norm::kRms, 1536, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1536
+    MBN_CFG_ROWS_EXACT_W(Norm::kRms, 6144, 4, 1, 1, 8, 2, 8),  // N == 16384, M <= 6144
     MBN_CFG_UPTO_W(Norm::kRms, 12288, 12, 1, 2, 2, 0, 0),  // 8192 < N <= 12288: 768 threads x 2 rows
     MBN_CFG_UPTO(Norm::kRms, 15360, 16, 1, 2, 2, 0, 0),  // 12288 < N <= 15360: 1024 threads x 2 rows
     MBN_CFG_W(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU

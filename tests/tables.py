@@ -8,7 +8,7 @@ from collections import namedtuple
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "memory_bound_normalization_amd", "csrc", "rownorm.hip")
-CFG = r"MBN_CFG(_EXACT|_ROWS|_UPTO)?(_W)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
+CFG = r"MBN_CFG(_EXACT|_ROWS_EXACT|_ROWS|_UPTO)?(_W)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
 
 
 class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto chunk_wait")):
@@ -47,12 +47,12 @@ def _tables():
                 nums = [int(v) for v in nums if v != ""]
                 max_rows = 0
                 upto = 0
-                if kind == "_ROWS":
+                if kind in ("_ROWS", "_ROWS_EXACT"):
                     max_rows, nums = nums[0], nums[1:]
                 elif kind == "_UPTO":
                     assert nums[0] % 8 == 0, line
                     upto, nums = nums[0] // 8, nums[1:]
-                entries.append(Entry(kind == "_EXACT", max_rows, *nums, upto, w == "_W"))
+                entries.append(Entry(kind in ("_EXACT", "_ROWS_EXACT"), max_rows, *nums, upto, w == "_W"))
         out[tname] = entries
     return out
 

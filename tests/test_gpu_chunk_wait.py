@@ -31,8 +31,12 @@ def _cases():
             windows = [f.max_rows for f in entries if f.max_rows and f.top == band_top]
             pers = [hi for _, _, hi in persistent_windows(op, nchunk)] if op != "add" else []
             rows_per_wg = e.rows * e.rpl
-            M = max(windows + pers + [MIN_BLOCKS * rows_per_wg]) + 1
-            if M % rows_per_wg == 0:
+            if e.max_rows:  # a row window: just below its top row count
+                M = e.max_rows - 1
+                assert M > max([w for w in windows if w < e.max_rows] + pers + [MIN_BLOCKS * rows_per_wg - 1])
+            else:
+                M = max(windows + pers + [MIN_BLOCKS * rows_per_wg]) + 1
+            if M % rows_per_wg == 0 and rows_per_wg > 1:
                 M += 1  # the last workgroup has rows past M
             out.append((op, M, nchunk * 8))
     return out
