@@ -710,6 +710,7 @@ const RowNormCfg kLayerTable[] = {
     MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 5, 2, 0),  // N == 10240: 256 threads x 2 rows
     MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 6, 2, 0),  // N == 12288
     MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 7, 2, 0),  // N == 14336
+    MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 8, 2, 4),  // N == 16384: 256 threads x 2 rows
     MBN_CFG_W(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
     MBN_CFG_ROWS(Norm::kLayer, 256, 8, 1, 1, 8, 1, 0),  // N <= 32768, M <= 256
     MBN_CFG(Norm::kLayer, 4, 1, 1, 16, 0, 4),  // N <= 32768: 256 threads
