@@ -9,7 +9,10 @@
 // only where it is computed on. On gfx950 the row copy is a burst of
 // global_load_lds_dwordx4 (HBM -> LDS without passing through VGPRs), issued
 // for the whole row before the first wait, so a workgroup keeps its entire row
-// in flight.
+// in flight. The first pass either waits for the whole row set or, in the
+// kernels the launch tables ask for it (large grids), takes each chunk as it
+// lands: loads complete in issue order, so s_waitcnt on the number of copies
+// still outstanding marks each chunk's arrival.
 //
 // Work decomposition: a workgroup holds ROWS row slots; each row is served by
 // WPR waves (64 * WPR lanes). Lane t of a row owns the 16-byte chunks
