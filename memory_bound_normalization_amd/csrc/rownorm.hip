@@ -655,7 +655,9 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 4, 0, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 1024
     MBN_CFG_ROWS(Norm::kRms, 2048, 2, 1, 2, 8, 0, 0),  // N <= 8192, M <= 2048
+    MBN_CFG_EXACT_W(Norm::kRms, 4, 1, 2, 3, 2, 0),  // N == 6144: 256 threads x 2 rows
     MBN_CFG_UPTO(Norm::kRms, 6144, 6, 1, 2, 2, 4, 0),  // 4096 < N <= 6144: 384 threads x 2 rows
+    MBN_CFG_EXACT_W(Norm::kRms, 7, 1, 2, 2, 3, 0),  // N == 7168: 448 threads x 2 rows
     MBN_CFG(Norm::kRms, 4, 1, 1, 4, 4, 8),   // N <= 8192:  256 threads, 4 WGs/CU
     MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 1536, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1536
