@@ -709,12 +709,15 @@ const RowNormCfg kLayerTable[] = {
     MBN_CFG_ROWS(Norm::kLayer, 512, 8, 1, 1, 2, 3, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 4, 2, 0),  // N <= 8192, M <= 1024
     MBN_CFG_ROWS(Norm::kLayer, 2048, 8, 1, 4, 2, 2, 0),  // N <= 8192, M <= 2048
+    MBN_CFG_EXACT_W(Norm::kLayer, 2, 2, 2, 5, 3, 0),  // N == 5120: 2 x 128 threads x 2 rows
+    MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 3, 3, 0),  // N == 6144: 256 threads x 2 rows
+    MBN_CFG_EXACT_W(Norm::kLayer, 2, 2, 2, 7, 2, 0),  // N == 7168: 2 x 128 threads x 2 rows
     MBN_CFG_W(Norm::kLayer, 8, 1, 2, 2, 4, 16),  // N <= 8192:  512 threads x 2 rows
     MBN_CFG_ROWS(Norm::kLayer, 512, 16, 1, 1, 2, 2, 0),  // N <= 16384, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 8, 2, 0),  // N <= 16384, M <= 1024
-    MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 5, 2, 0),  // N == 10240: 256 threads x 2 rows
+    MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 5, 3, 8),  // N == 10240: 256 threads x 2 rows
     MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 6, 2, 0),  // N == 12288
-    MBN_CFG_EXACT(Norm::kLayer, 4, 1, 2, 7, 2, 0),  // N == 14336
+    MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 7, 2, 0),  // N == 14336
     MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 8, 2, 4),  // N == 16384: 256 threads x 2 rows
     MBN_CFG_W(Norm::kLayer, 2, 2, 1, 16, 0, 0),  // N <= 16384: 2 x 128 threads
     MBN_CFG_ROWS(Norm::kLayer, 256, 8, 1, 1, 8, 1, 0),  // N <= 32768, M <= 256
