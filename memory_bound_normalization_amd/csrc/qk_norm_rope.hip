@@ -11,8 +11,11 @@
 // bytes, i.e. one DPP row, so a wave holds 4 heads, the head's sum of squares
 // is a 16-lane DPP reduction and the rotary partner of lane j (the chunk 64
 // elements away) is lane j ^ 8 of the same row, fetched with row_ror:8.
-// The inverse frequencies theta^(-2i/R) do not depend on the token: the host
-// evaluates them once per launch in fp64 and passes them as kernel arguments.
+// The inverse frequencies theta^(-2i/R) do not depend on the token. The host
+// evaluates the six powers theta^(-2^(k+1)/R) once per launch in fp64 and
+// passes them as kernel arguments; lane i forms theta^(-2i/R) as the product
+// of the powers whose bit k is set in i. Those are uniform (scalar) loads, so
+// the angle work does not wait for the head loads issued before it.
 // Wave 0 forms the token's 64 angles pos * inv_freq and their sin / cos in
 // fp64 (one per lane) once and shares cos / sin through 1 KiB of LDS; the
 // waves then step over the token's heads 4 at a time. Few tokens: one wave
@@ -44,9 +47,10 @@ constexpr int kHeadDim = 128;
 constexpr int kHalf = kHeadDim / 2;
 constexpr int kHeadsPerWave = 4;
 
-// theta^(-2i/R) for i < R/2 (fp64), filled by the launcher.
-struct InvFreq {
-  double v[kHalf];
+// theta^(-2^(k+1)/R) for k < 6 (fp64), filled by the launcher; pair i < R/2
+// <= 64 has the inverse frequency prod_{bit k of i set} p[k].
+struct InvFreqPowers {
+  double p[6];
 };
 
 template <typename DT>
@@ -54,7 +58,7 @@ __global__ void __launch_bounds__(1024)
 qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w,
                     const uint16_t* __restrict__ k_w, const int64_t* __restrict__ positions,
                     int n_q, int n_heads, int64_t row_stride, int rot_chunks, float eps,
-                    InvFreq inv_freq) {
+                    InvFreqPowers inv_pow) {
   __shared__ double2 cs[kHalf];  // (cos, sin) of the token's rot_chunks * 8 angles
 
   const int lane = threadIdx.x & 63;
@@ -75,9 +79,13 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
   // Angle i = lane: phi = pos * theta^(-2i/R), fp64, R = rotary dimension.
   const int half = 8 * rot_chunks;  // R / 2
   if (wave == 0 && lane < half) {
+    double inv_freq = 1.0;
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+      if ((lane >> k) & 1) inv_freq *= inv_pow.p[k];
     const double pos = (double)positions[token];
     double s, c;
-    sincos(pos * inv_freq.v[lane], &s, &c);
+    sincos(pos * inv_freq, &s, &c);
     cs[lane] = make_double2(c, s);
   }
   __syncthreads();
@@ -165,13 +173,13 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
   const int all = groups < 16 ? groups : 16;
   const int waves = T <= 512 ? all : T <= 1024 ? (all + 1) / 2 : (groups < 4 ? groups : 4);
   const int64_t row_stride = (int64_t)(n_q_heads + 2 * n_kv_heads) * kHeadDim;
-  // The inverse frequency of pair i is theta^(-2i/R): fp64 pow on the host
-  // (the C library's pow, within an ulp), once per launch rather than once per
-  // token on the device (0.4 us of a 3.9 us launch at 256 tokens on MI355X).
-  InvFreq inv_freq{};
-  const int half = rotary_dim / 2;
-  for (int i = 0; i < half; ++i)
-    inv_freq.v[i] = std::pow((double)theta, -(double)(2 * i) / (double)(2 * half));
+  // The inverse frequency of pair i is theta^(-2i/R) = prod over the set bits
+  // k of i of theta^(-2^(k+1)/R): six fp64 pows on the host (the C library's
+  // pow, within an ulp each), at most six fp64 products on the device, so a
+  // relative error of about 1e-15 (an angle error of 1e-15 * phi rad).
+  InvFreqPowers inv_pow{};
+  for (int k = 0; k < 6; ++k)
+    inv_pow.p[k] = std::pow((double)theta, -(double)(2 << k) / (double)rotary_dim);
   // One workgroup per token; beyond kMaxWorkItems work-items, several launches
   // over consecutive token ranges.
   const int64_t tokens_per_launch = kMaxWorkItems / (64 * waves);
@@ -181,7 +189,7 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
                        dim3((unsigned)nt), dim3(64 * waves), 0, stream,
                        static_cast<uint16_t*>(qkv) + t0 * row_stride, static_cast<const uint16_t*>(q_w),
                        static_cast<const uint16_t*>(k_w), positions + t0, n_q_heads, n_heads, row_stride,
-                       rotary_dim / 16, eps, inv_freq);
+                       rotary_dim / 16, eps, inv_pow);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
