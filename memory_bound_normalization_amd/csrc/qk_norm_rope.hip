@@ -17,7 +17,8 @@
 // of the powers whose bit k is set in i. Those are uniform (scalar) loads, so
 // the angle work does not wait for the head loads issued before it.
 // Wave 0 forms the token's 64 angles pos * inv_freq and their sin / cos in
-// fp64 (one per lane) once and shares cos / sin through 1 KiB of LDS; the
+// fp64 (one per lane, sincos_reduced) once and shares cos / sin through 1 KiB
+// of LDS; the
 // waves then step over the token's heads 4 at a time. Few tokens: one wave
 // per 4 heads (a single step, lowest latency); up to 1024 tokens half as many
 // waves, two steps each. Many tokens: 4 waves per token, looping, so the
@@ -53,6 +54,56 @@ struct InvFreqPowers {
   double p[6];
 };
 
+// sin and cos of an fp64 angle for |phi| < 2^40 (else the library's sincos).
+// Cody-Waite reduction: k = rint(phi * 2/pi), r = phi - k * pi/2 with pi/2
+// split into three doubles P1 + P2 + P3 and one FMA per part. phi - k * P1 is
+// a multiple of 2^-53 below 2 in magnitude, hence exact; the other two parts
+// add about one ulp of r. On |r| <= pi/4 (+ a rounding of k), Taylor series
+// to r^15 (sine) and r^16 (cosine), truncation below 5e-17, plus a few ulps of
+// Horner rounding. The quadrant k mod 4 then permutes and negates the pair.
+// About 30 fp64 operations against the library routine's general path; the
+// angle work sits on the critical path of short launches.
+__device__ __forceinline__ void sincos_reduced(double phi, double* s_out, double* c_out) {
+  if (!(__builtin_fabs(phi) < 0x1p40)) {
+    sincos(phi, s_out, c_out);
+    return;
+  }
+  constexpr double kTwoOverPi = 0.6366197723675814;  // fl(2/pi)
+  constexpr double kP1 = 1.5707963267948966;         // fl(pi/2)
+  constexpr double kP2 = 6.123233995736766e-17;      // fl(pi/2 - P1)
+  constexpr double kP3 = -1.4973849048591698e-33;    // fl(pi/2 - P1 - P2)
+  const double k = __builtin_rint(phi * kTwoOverPi);
+  double r = __builtin_fma(-k, kP1, phi);
+  r = __builtin_fma(-k, kP2, r);
+  r = __builtin_fma(-k, kP3, r);
+  const double r2 = r * r;
+  // sin r = r + r^3 * ps, ps = -1/3! + r^2/5! - r^4/7! + ... - r^12/15!
+  double ps = -1.0 / 1307674368000.0;
+  ps = __builtin_fma(ps, r2, 1.0 / 6227020800.0);
+  ps = __builtin_fma(ps, r2, -1.0 / 39916800.0);
+  ps = __builtin_fma(ps, r2, 1.0 / 362880.0);
+  ps = __builtin_fma(ps, r2, -1.0 / 5040.0);
+  ps = __builtin_fma(ps, r2, 1.0 / 120.0);
+  ps = __builtin_fma(ps, r2, -1.0 / 6.0);
+  const double sn = __builtin_fma(ps * r2, r, r);
+  // cos r = 1 - r^2 * pc, pc = 1/2! - r^2/4! + r^4/6! - ... - r^14/16!
+  double pc = -1.0 / 20922789888000.0;
+  pc = __builtin_fma(pc, r2, 1.0 / 87178291200.0);
+  pc = __builtin_fma(pc, r2, -1.0 / 479001600.0);
+  pc = __builtin_fma(pc, r2, 1.0 / 3628800.0);
+  pc = __builtin_fma(pc, r2, -1.0 / 40320.0);
+  pc = __builtin_fma(pc, r2, 1.0 / 720.0);
+  pc = __builtin_fma(pc, r2, -1.0 / 24.0);
+  pc = __builtin_fma(pc, r2, 0.5);
+  const double cs = __builtin_fma(-pc, r2, 1.0);
+  // phi = k pi/2 + r: quadrant q = k mod 4 (two's complement for k < 0)
+  const int q = (int)((long long)k & 3);
+  const double s = (q & 1) ? cs : sn;
+  const double c = (q & 1) ? sn : cs;
+  *s_out = (q & 2) ? -s : s;
+  *c_out = ((q + 1) & 2) ? -c : c;
+}
+
 template <typename DT>
 __global__ void __launch_bounds__(1024)
 qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w,
@@ -68,14 +119,22 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
   const int j = lane & 15;  // 16-byte chunk of the head: elements [8j, 8j + 8)
   uint16_t* const trow = qkv + token * row_stride;
 
+  // The token's position: a uniform (scalar) load, issued with the head loads
+  // and kept there (see below) rather than moved into wave 0's angle branch
+  // behind further argument loads.
+  const int64_t pos_i = positions[token];
   // Issue the first head load before the angle computation so the two overlap.
   int head = wave * kHeadsPerWave + (lane >> 4);
-  u32x4 xv = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-  if (head < n_heads) {
-    xv = *reinterpret_cast<const u32x4*>(trow + (int64_t)head * kHeadDim + 8 * j);
-    wv = *reinterpret_cast<const u32x4*>((head < n_q ? q_w : k_w) + 8 * j);
-  }
+  // Unconditional (no branch around the first loads, so the position's scalar
+  // load is scheduled among them): lanes past the last head (n_heads >= 1)
+  // read that head, and the loop zeroes them.
+  const int h0 = head < n_heads ? head : n_heads - 1;
+  u32x4 xv = *reinterpret_cast<const u32x4*>(trow + (int64_t)h0 * kHeadDim + 8 * j);
+  u32x4 wv = *reinterpret_cast<const u32x4*>((h0 < n_q ? q_w : k_w) + 8 * j);
 
+  // Using the position here keeps its load ahead of this point; the wait
+  // counts scalar loads only, so the head loads stay in flight.
+  asm volatile("" ::"s"(pos_i));
   // Angle i = lane: phi = pos * theta^(-2i/R), fp64, R = rotary dimension.
   const int half = 8 * rot_chunks;  // R / 2
   if (wave == 0 && lane < half) {
@@ -83,9 +142,9 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
 #pragma unroll
     for (int k = 0; k < 6; ++k)
       if ((lane >> k) & 1) inv_freq *= inv_pow.p[k];
-    const double pos = (double)positions[token];
+    const double pos = (double)pos_i;
     double s, c;
-    sincos(pos * inv_freq, &s, &c);
+    sincos_reduced(pos * inv_freq, &s, &c);
     cs[lane] = make_double2(c, s);
   }
   __syncthreads();
@@ -180,12 +239,13 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
   InvFreqPowers inv_pow{};
   for (int k = 0; k < 6; ++k)
     inv_pow.p[k] = std::pow((double)theta, -(double)(2 << k) / (double)rotary_dim);
+  const auto kernel = dtype == Storage::kF16 ? qk_norm_rope_kernel<F16> : qk_norm_rope_kernel<Bf16>;
   // One workgroup per token; beyond kMaxWorkItems work-items, several launches
   // over consecutive token ranges.
   const int64_t tokens_per_launch = kMaxWorkItems / (64 * waves);
   for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
     const int64_t nt = T - t0 < tokens_per_launch ? T - t0 : tokens_per_launch;
-    hipLaunchKernelGGL(dtype == Storage::kF16 ? qk_norm_rope_kernel<F16> : qk_norm_rope_kernel<Bf16>,
+    hipLaunchKernelGGL(kernel,
                        dim3((unsigned)nt), dim3(64 * waves), 0, stream,
                        static_cast<uint16_t*>(qkv) + t0 * row_stride, static_cast<const uint16_t*>(q_w),
                        static_cast<const uint16_t*>(k_w), positions + t0, n_q_heads, n_heads, row_stride,
