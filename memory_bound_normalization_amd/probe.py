@@ -12,6 +12,17 @@ known (x's bytes read and written), give the factor that converts each counter
 reading into bytes. `summarize` prints the per-launch HBM traffic of the
 RMSNorm kernel from the two runs' counter CSV files.
 
+    rocprofv3 --pmc FETCH_SIZE -d <dir> -o run -- python -m memory_bound_normalization_amd.probe qk-run
+    rocprofv3 --pmc WRITE_SIZE -d <dir> -o run -- python -m memory_bound_normalization_amd.probe qk-run
+    python -m memory_bound_normalization_amd.probe qk-summarize <fetch_dir> <write_dir>
+
+`qk-run` does the same for qk_norm_rope_fwd on 65536 tokens of 32 q + 8 k + 8 v
+heads of 128 (768 MiB, more than the Infinity Cache), calibrated by torch's
+device copy of a separate 512 MiB buffer (the RMSNorm runs' calibration
+kernel and size);
+`qk-summarize` prints its per-launch traffic beside the
+algorithmic bytes (q and k heads read and written, v heads untouched).
+
     rocprofv3 --kernel-trace --stats -d <dir> -o run -- python -m memory_bound_normalization_amd.probe ceiling
     python -m memory_bound_normalization_amd.probe ceiling-summary <dir>
 
@@ -73,6 +84,66 @@ def run(workload: str = DEFAULT_WORKLOAD) -> None:
         z.copy_(x)
         torch.cuda.synchronize()
         print(f"copy launch {i} done", flush=True)
+
+
+QK_TOKENS, QK_HQ, QK_HKV, QK_D = 65536, 32, 8, 128
+
+
+def qk_algorithmic_bytes(T: int = QK_TOKENS) -> int:
+    """q and k heads read and written, the two weights and the positions."""
+    return 2 * T * (QK_HQ + QK_HKV) * QK_D * 2 + 2 * QK_D * 2 + 8 * T
+
+
+def qk_run() -> None:
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    width = (QK_HQ + 2 * QK_HKV) * QK_D
+    # the calibration copy's source (512 MiB), created before qkv
+    n = COPY_BYTES // 2
+    src = torch.randn(n, device=dev, generator=g).to(torch.bfloat16)
+    qkv = torch.randn(QK_TOKENS, width, device=dev, generator=g).to(torch.bfloat16)
+    q_w = (torch.rand(QK_D, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    k_w = (torch.rand(QK_D, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    pos = torch.arange(QK_TOKENS, device=dev, dtype=torch.int64)
+    torch.cuda.synchronize()
+    for i in range(LAUNCHES):
+        mbn.qk_norm_rope_fwd(qkv, q_w, k_w, pos, QK_HQ, QK_HKV, QK_D, eps=1e-6, theta=1e6)
+        torch.cuda.synchronize()
+        print(f"qk_norm_rope launch {i} done", flush=True)
+    # calibration: torch's device copy of 512 MiB, the kernel and footprint of
+    # the RMSNorm calibration
+    z = torch.empty(n, dtype=src.dtype, device=dev)
+    for i in range(LAUNCHES):
+        z.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy launch {i} done", flush=True)
+
+
+def qk_summarize(fetch_dir: str, write_dir: str) -> None:
+    copy_bytes = COPY_BYTES  # the calibration copy's bytes, each way
+    # torch's input set-up launches elementwise kernels too: only the copy counts
+    f = _per_kernel(fetch_dir, "FETCH_SIZE", "qk_norm_rope", "copyBuffer")
+    w = _per_kernel(write_dir, "WRITE_SIZE", "qk_norm_rope", "copyBuffer")
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    f_k, f_c = mean(f["rmsnorm"]), mean(f["copy"])
+    w_k, w_c = mean(w["rmsnorm"]), mean(w["copy"])
+    fetch_b = f_k * copy_bytes / f_c
+    write_b = w_k * copy_bytes / w_c
+    qk = QK_TOKENS * (QK_HQ + QK_HKV) * QK_D * 2
+    print(f"qk_norm_rope FETCH_SIZE per launch (raw): {f_k:.1f}  over {len(f['rmsnorm'])} launches")
+    print(f"qk_norm_rope WRITE_SIZE per launch (raw): {w_k:.1f}  over {len(w['rmsnorm'])} launches")
+    print(f"tokens {QK_TOKENS}, heads {QK_HQ} q + {QK_HKV} k + {QK_HKV} v of {QK_D}")
+    print(f"copy    FETCH_SIZE per launch (raw): {f_c:.1f}   WRITE_SIZE: {w_c:.1f}   true bytes each way: {copy_bytes}")
+    print(f"calibration factors (bytes per counter unit): fetch {copy_bytes / f_c:.3f}  write {copy_bytes / w_c:.3f}")
+    print(f"fetch_bytes_per_launch: {fetch_b:.0f}  (q and k heads: {qk}, x{fetch_b / qk:.4f})")
+    print(f"write_bytes_per_launch: {write_b:.0f}  (q and k heads: {qk}, x{write_b / qk:.4f})")
+    print(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}  algorithmic_bytes_per_launch: {qk_algorithmic_bytes()}"
+          f"  (x{(fetch_b + write_b) / qk_algorithmic_bytes():.4f})")
 
 
 CEIL_REPS = 20
@@ -324,8 +395,11 @@ def _rows(d: str):
     return out
 
 
-def _per_kernel(d: str, counter: str):
-    """{'rmsnorm': [values...], 'copy': [values...]} for one counter (summed over its instances)."""
+def _per_kernel(d: str, counter: str, kernel: str = "rownorm_kernel", copy: str | None = None):
+    """{'rmsnorm': [values...], 'copy': [values...]} for one counter (summed over
+    its instances); 'rmsnorm' holds the kernels whose name contains `kernel`,
+    'copy' those whose name contains `copy` (default: torch's copy or
+    elementwise kernels)."""
     acc = {}
     for r in _rows(d):
         if r.get("Counter_Name") != counter:
@@ -334,9 +408,9 @@ def _per_kernel(d: str, counter: str):
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
     res = {"rmsnorm": [], "copy": []}
     for (_, name), v in sorted(acc.items(), key=lambda kv: int(kv[0][0])):
-        if "rownorm_kernel" in name:
+        if kernel in name:
             res["rmsnorm"].append(v)
-        elif "copy" in name.lower() or "elementwise" in name.lower():
+        elif (copy in name) if copy else ("copy" in name.lower() or "elementwise" in name.lower()):
             res["copy"].append(v)
     return res
 
@@ -377,6 +451,10 @@ if __name__ == "__main__":
         small_summary(sys.argv[2])
     elif len(sys.argv) in (2, 3) and sys.argv[1] == "run":
         run(*sys.argv[2:])
+    elif len(sys.argv) == 2 and sys.argv[1] == "qk-run":
+        qk_run()
+    elif len(sys.argv) == 4 and sys.argv[1] == "qk-summarize":
+        qk_summarize(sys.argv[2], sys.argv[3])
     elif len(sys.argv) in (4, 5) and sys.argv[1] == "summarize":
         summarize(*sys.argv[2:])
     else:
