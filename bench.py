@@ -20,7 +20,6 @@ workload (row blocks of 1024), single-threaded.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -31,26 +30,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from memory_bound_normalization_amd.timing import HipTimingEvents  # noqa: E402
+from probe import HipTimingEvents, kernel_source_hash  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 RMS_WORKLOAD = "rms_16384x16384"
 QK_WORKLOAD = "qk_256"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_16384x16384_hbm_traffic.txt")
-KERNEL_SOURCES = [
-    os.path.join(ROOT, "memory_bound_normalization_amd", "csrc", f)
-    for f in ("rownorm.hip", "device.h")
-]
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(algorithmic_bytes: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none or the kernel source changed since it was taken."""
@@ -80,10 +65,10 @@ def streaming_copy_reference(x, y, stream, steps: int, warmup: int):
     hand-written copy of libmbn_stream.so with 4 KiB per workgroup (16-byte
     non-temporal loads and stores, the row-norm kernels' accesses) -- timed
     the same way as the RMSNorm (timing events around each launch) on the same
-    512 MiB buffers: the reference roofline.frac is read against. None when
-    libmbn_stream.so is not built."""
+    512 MiB buffers: the reference roofline.frac is read against. probe.py
+    compiles libmbn_stream.so when it is missing; None when that fails."""
     try:
-        from memory_bound_normalization_amd.probe import stream_lib
+        from probe import stream_lib
 
         sl = stream_lib()
     except (RuntimeError, OSError):
@@ -227,7 +212,7 @@ def suite(steps: int, warmup: int) -> int:
     def report(workload, kernel, nrot, med, best, b, **shape):
         """One JSON line: the median and best per-launch times and the batch
         mean against b algorithmic bytes per launch."""
-        print(json.dumps({"workload": workload, "kernel": kernel, **shape,
+        print(json.dumps({"workload": workload, "kernel": kernel, **shape, "algorithmic_bytes": b,
                           "rotating_sets": nrot, "median_us": round(med, 2), "best_us": round(best, 2),
                           "GBps_median": round(b / med / 1e3, 1),
                           "pct_of_8TBps_median": round(b / med / 1e3 / 80.0, 2),
@@ -351,7 +336,7 @@ def suite(steps: int, warmup: int) -> int:
               "l2norm_fwd": lambda i: mbn.l2norm_fwd(xs[i], y=ys[i], eps=1e-12)}[kname]
         b = streams * M * N * 2 + {"add_rmsnorm_fwd": 2, "layernorm_fwd": 4, "l2norm_fwd": 0}[kname] * N
         med, best = timed(fn, nrot)
-        report(f"width_{M}x{N}", kname, nrot, med, best, b, M=M, N=N, algorithmic_bytes=b)
+        report(f"width_{M}x{N}", kname, nrot, med, best, b, M=M, N=N)
         del xs, rs, hs, ys, x0
     del x_full, w_full
     torch.cuda.empty_cache()
@@ -376,8 +361,7 @@ def suite(steps: int, warmup: int) -> int:
         ]
         for kname, b, fn in cases:
             med, best = timed(fn, nrot)
-            report(name.replace("rms_", "family_"), kname, nrot, med, best, b, M=wl.M, N=wl.N,
-                   algorithmic_bytes=b)
+            report(name.replace("rms_", "family_"), kname, nrot, med, best, b, M=wl.M, N=wl.N)
         del xs, rs, hs, ys, x, r
         torch.cuda.empty_cache()
     for name, wl in QK_WORKLOADS.items():

@@ -164,7 +164,15 @@ MBN_API int l2norm_fwd(const void* x, void* y, int64_t M, int64_t N, float eps, 
  *              n_kv_heads k heads, then n_kv_heads v heads; v is never read
  *              or written.
  *   q_w, k_w   device, bf16 [head_dim] each, shared by all q (k) heads
- *   positions  device, int64 [T] (|position| < 2^53)
+ *   positions  device, int64 [T]. Any value is accepted; it is converted to
+ *              fp64 (exact for |position| <= 2^53). Parity with the fp64
+ *              reference above (one bf16 ulp plus 1e-6) is established for
+ *              |position| <= 1.23e8, i.e. angles up to ~1.2e8 rad. Beyond
+ *              that the fp64 angle is itself uncertain by half an ulp of phi
+ *              (7e-9 rad at 1e8 rad, 6e-8 rad near 1e9) on both sides, so the
+ *              1e-6 absolute floor can no longer judge near-cancelling
+ *              outputs; angles with |phi| >= 2^40 take the device library's
+ *              sine and cosine.
  *   T          tokens, >= 0 (T == 0 returns MBN_OK); at most 2^31 - 1
  *   n_q_heads, n_kv_heads  >= 0
  *   head_dim   must equal MBN_QK_HEAD_DIM (odd values are MBN_EINVAL)

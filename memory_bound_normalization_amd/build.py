@@ -4,10 +4,10 @@
 
 Compiles every ``csrc/*.hip`` file with hipcc into one shared library next to
 this file. No fast-math: the kernels rely on IEEE fp32/fp64 behaviour.
-``build_stream()`` compiles ``probe_csrc/*.hip`` into libmbn_stream.so, the
-plain streaming kernels the measurement tools time beside the norms (not part
-of the normalization path). ``build_c_client()`` compiles the plain C client
-of the C ABI the tests use (``tests/c_abi``) with gcc.
+``build_c_client()`` compiles the plain C client of the C ABI the tests use
+(``tests/c_abi``) with gcc, and ``build_rope_host()`` a host build of the
+kernels' rotary-angle functions (``csrc/rope_math.h``) for the CPU tests. (The measurement tools next to bench.py build
+their own streaming reference kernels with ``build(out=..., sources_=...)``.)
 """
 
 from __future__ import annotations
@@ -24,8 +24,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmbn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-PROBE_CSRC = os.path.join(PKG, "probe_csrc")
-STREAM_LIB_PATH = os.path.join(PKG, "libmbn_stream.so")
 ARCH = "gfx950"
 
 
@@ -40,7 +38,7 @@ def sources(src_dir: str = CSRC) -> list[str]:
     return sorted(glob.glob(os.path.join(src_dir, "*.hip")))
 
 
-def compile_command(out: str, extra: list[str] | None = None, src_dir: str = CSRC) -> list[str]:
+def compile_command(out: str, extra: list[str] | None = None, srcs: list[str] | None = None) -> list[str]:
     return [
         hipcc(),
         f"--offload-arch={ARCH}",
@@ -55,15 +53,16 @@ def compile_command(out: str, extra: list[str] | None = None, src_dir: str = CSR
         "-I", INCLUDE,
         *(extra or []),
         "-o", out,
-        *sources(src_dir),
+        *(srcs if srcs is not None else sources()),
     ]
 
 
 def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = None,
-          src_dir: str = CSRC) -> str:
-    """Compile the library; always rebuilds. Returns the path of the .so."""
+          sources_: list[str] | None = None) -> str:
+    """Compile the library (or, with ``sources_``, those HIP files with the
+    same flags); always rebuilds. Returns the path of the .so."""
     tmp = out + ".tmp"
-    cmd = compile_command(tmp, extra, src_dir)
+    cmd = compile_command(tmp, extra, sources_)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -97,12 +96,17 @@ def build_c_client(verbose: bool = False) -> str:
     return C_CLIENT_LIB
 
 
-def build_stream(verbose: bool = False) -> str:
-    """Compile libmbn_stream.so (the streaming reference kernels); always rebuilds."""
-    return build(verbose=verbose, out=STREAM_LIB_PATH, src_dir=PROBE_CSRC)
+ROPE_HOST_SRC = os.path.join(ROOT, "tests", "c_abi", "rope_math_host.hip")
+ROPE_HOST_LIB = os.path.join(ROOT, "tests", "c_abi", "librope_math_host.so")
+
+
+def build_rope_host(verbose: bool = False) -> str:
+    """Compile tests/c_abi/librope_math_host.so: the QK kernel's sincos and
+    inverse-frequency functions built for the host; always rebuilds."""
+    return build(verbose=verbose, out=ROPE_HOST_LIB, sources_=[ROPE_HOST_SRC])
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
-    print(build_stream(verbose=True))
     print(build_c_client(verbose=True))
+    print(build_rope_host(verbose=True))

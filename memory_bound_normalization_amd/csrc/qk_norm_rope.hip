@@ -40,6 +40,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "rope_math.h"
 
 namespace mbn {
 namespace {
@@ -47,62 +48,6 @@ namespace {
 constexpr int kHeadDim = 128;
 constexpr int kHalf = kHeadDim / 2;
 constexpr int kHeadsPerWave = 4;
-
-// theta^(-2^(k+1)/R) for k < 6 (fp64), filled by the launcher; pair i < R/2
-// <= 64 has the inverse frequency prod_{bit k of i set} p[k].
-struct InvFreqPowers {
-  double p[6];
-};
-
-// sin and cos of an fp64 angle for |phi| < 2^40 (else the library's sincos).
-// Cody-Waite reduction: k = rint(phi * 2/pi), r = phi - k * pi/2 with pi/2
-// split into three doubles P1 + P2 + P3 and one FMA per part. phi - k * P1 is
-// a multiple of 2^-53 below 2 in magnitude, hence exact; the other two parts
-// add about one ulp of r. On |r| <= pi/4 (+ a rounding of k), Taylor series
-// to r^15 (sine) and r^16 (cosine), truncation below 5e-17, plus a few ulps of
-// Horner rounding. The quadrant k mod 4 then permutes and negates the pair.
-// About 30 fp64 operations against the library routine's general path; the
-// angle work sits on the critical path of short launches.
-__device__ __forceinline__ void sincos_reduced(double phi, double* s_out, double* c_out) {
-  if (!(__builtin_fabs(phi) < 0x1p40)) {
-    sincos(phi, s_out, c_out);
-    return;
-  }
-  constexpr double kTwoOverPi = 0.6366197723675814;  // fl(2/pi)
-  constexpr double kP1 = 1.5707963267948966;         // fl(pi/2)
-  constexpr double kP2 = 6.123233995736766e-17;      // fl(pi/2 - P1)
-  constexpr double kP3 = -1.4973849048591698e-33;    // fl(pi/2 - P1 - P2)
-  const double k = __builtin_rint(phi * kTwoOverPi);
-  double r = __builtin_fma(-k, kP1, phi);
-  r = __builtin_fma(-k, kP2, r);
-  r = __builtin_fma(-k, kP3, r);
-  const double r2 = r * r;
-  // sin r = r + r^3 * ps, ps = -1/3! + r^2/5! - r^4/7! + ... - r^12/15!
-  double ps = -1.0 / 1307674368000.0;
-  ps = __builtin_fma(ps, r2, 1.0 / 6227020800.0);
-  ps = __builtin_fma(ps, r2, -1.0 / 39916800.0);
-  ps = __builtin_fma(ps, r2, 1.0 / 362880.0);
-  ps = __builtin_fma(ps, r2, -1.0 / 5040.0);
-  ps = __builtin_fma(ps, r2, 1.0 / 120.0);
-  ps = __builtin_fma(ps, r2, -1.0 / 6.0);
-  const double sn = __builtin_fma(ps * r2, r, r);
-  // cos r = 1 - r^2 * pc, pc = 1/2! - r^2/4! + r^4/6! - ... - r^14/16!
-  double pc = -1.0 / 20922789888000.0;
-  pc = __builtin_fma(pc, r2, 1.0 / 87178291200.0);
-  pc = __builtin_fma(pc, r2, -1.0 / 479001600.0);
-  pc = __builtin_fma(pc, r2, 1.0 / 3628800.0);
-  pc = __builtin_fma(pc, r2, -1.0 / 40320.0);
-  pc = __builtin_fma(pc, r2, 1.0 / 720.0);
-  pc = __builtin_fma(pc, r2, -1.0 / 24.0);
-  pc = __builtin_fma(pc, r2, 0.5);
-  const double cs = __builtin_fma(-pc, r2, 1.0);
-  // phi = k pi/2 + r: quadrant q = k mod 4 (two's complement for k < 0)
-  const int q = (int)((long long)k & 3);
-  const double s = (q & 1) ? cs : sn;
-  const double c = (q & 1) ? sn : cs;
-  *s_out = (q & 2) ? -s : s;
-  *c_out = ((q + 1) & 2) ? -c : c;
-}
 
 template <typename DT>
 __global__ void __launch_bounds__(1024)
@@ -138,10 +83,7 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
   // Angle i = lane: phi = pos * theta^(-2i/R), fp64, R = rotary dimension.
   const int half = 8 * rot_chunks;  // R / 2
   if (wave == 0 && lane < half) {
-    double inv_freq = 1.0;
-#pragma unroll
-    for (int k = 0; k < 6; ++k)
-      if ((lane >> k) & 1) inv_freq *= inv_pow.p[k];
+    const double inv_freq = rope_inv_freq(inv_pow, lane);
     const double pos = (double)pos_i;
     double s, c;
     sincos_reduced(pos * inv_freq, &s, &c);
@@ -236,9 +178,7 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
   // k of i of theta^(-2^(k+1)/R): six fp64 pows on the host (the C library's
   // pow, within an ulp each), at most six fp64 products on the device, so a
   // relative error of about 1e-15 (an angle error of 1e-15 * phi rad).
-  InvFreqPowers inv_pow{};
-  for (int k = 0; k < 6; ++k)
-    inv_pow.p[k] = std::pow((double)theta, -(double)(2 << k) / (double)rotary_dim);
+  const InvFreqPowers inv_pow = rope_inv_freq_powers(theta, rotary_dim);
   const auto kernel = dtype == Storage::kF16 ? qk_norm_rope_kernel<F16> : qk_norm_rope_kernel<Bf16>;
   // One workgroup per token; beyond kMaxWorkItems work-items, several launches
   // over consecutive token ranges.

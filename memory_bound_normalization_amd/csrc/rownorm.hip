@@ -35,6 +35,16 @@
 #include "device.h"
 #include "kernels.h"
 
+// Timeline marks of the one-shot kernel: workgroup start, rows landed and
+// reduced, last store issued and completed. The measurement tools compile this
+// file with them defined (wall clock per workgroup); in the library they are
+// empty and the kernel is unchanged.
+#ifndef MBN_TL_START
+#define MBN_TL_START()
+#define MBN_TL_LANDED()
+#define MBN_TL_END()
+#endif
+
 namespace mbn {
 namespace {
 
@@ -258,8 +268,11 @@ __device__ __forceinline__ void finish_rows(const RowNormArgs& a, u32x4* buf0, f
 // compiler scheduled the LDS reads of the LayerNorm passes less far ahead,
 // 4-6% slower at N >= 16384 on MI355X (RMSNorm, L2Norm and the residual add
 // unchanged).
-template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL, bool CHUNK_WAIT = false>
-__global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a) {
+//
+// rownorm_block is that body for one row block (ROWS * RPL rows starting at
+// block * ROWS * RPL); rownorm_kernel runs it for its own block.
+template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL, bool CHUNK_WAIT>
+__device__ __forceinline__ void rownorm_block(const RowNormArgs& a, int64_t block) {
   constexpr int TPR = 64 * WPR;  // lanes per lane set
   constexpr bool kHasW = MODE != Norm::kL2;
   constexpr bool kHasB = MODE == Norm::kLayer;
@@ -268,13 +281,13 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
   // kernels of the table entries that ask for it, not the residual add.
   constexpr bool kChunkWait = CHUNK_WAIT && FULL && !kHasR;
   extern __shared__ u32x4 lds_rows[];  // ROWS * RPL * nchunk chunks (or more, see launcher)
+  MBN_TL_START();
 
   const int nchunk = a.nchunk;
   const int tid = threadIdx.x;
   const int slot = tid / TPR;
   const int t = tid - slot * TPR;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t block = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group);
   const int64_t row0 = (block * ROWS + slot) * RPL;
 
   u32x4* buf0 = lds_rows + (size_t)slot * RPL * nchunk;  // row rr at buf0 + rr * nchunk
@@ -292,6 +305,19 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
       if constexpr (kHasW) wreg[j] = reinterpret_cast<const u32x4*>(a.w)[k];
       if constexpr (kHasB) breg[j] = reinterpret_cast<const u32x4*>(a.b)[k];
     }
+    // The per-chunk waits below count the copies issued after chunk q. Their
+    // immediates assume the weight / bias loads were all issued before the
+    // first copy: a weight load sunk below a copy would make the wait for an
+    // earlier chunk also wait for it (correct, but it puts an L2 round trip
+    // back on pass 1's path), and nothing else keeps them apart (the loads
+    // read global memory, the copies write LDS). The empty asm with a memory
+    // clobber keeps the IR order, the scheduling barrier keeps the machine
+    // scheduler from interleaving the two groups. Correctness rests on the
+    // copies themselves staying in program order (each writes LDS through
+    // M0; the compiler keeps them in order), so that exactly the later copies
+    // are outstanding after chunk q's.
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rr = 0; rr < RPL; ++rr) {
       if (row0 + rr < a.M) {
@@ -423,6 +449,7 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
   // not read from LDS again; the launch tables guarantee nchunk >= 64 * WPR, so
   // every wave owns such a chunk to park its partial sums in.
   rows_sum<WPR, RPL>(s1, buf0, nullptr, nchunk, t, wave, 0);
+  MBN_TL_LANDED();
 
   float mu[RPL], scale[RPL];
   if constexpr (MODE == Norm::kLayer) {
@@ -498,6 +525,12 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
       }
     }
   }
+  MBN_TL_END();
+}
+
+template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL, bool CHUNK_WAIT = false>
+__global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a) {
+  rownorm_block<MODE, DT, WPR, ROWS, RPL, MAXC, FULL, CHUNK_WAIT>(a, xcd_remap(blockIdx.x, gridDim.x, a.xcd_group));
 }
 
 // Persistent kernel ("[Inductor] Codegen Gluon", section 3.3: copies of the

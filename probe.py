@@ -1,0 +1,1333 @@
+"""Short GPU program for hardware-counter runs, and the summarizer of their output.
+
+    rocprofv3 --pmc FETCH_SIZE -d <dir> -o run -- python probe.py run
+    rocprofv3 --pmc WRITE_SIZE -d <dir> -o run -- python probe.py run
+    python probe.py summarize <fetch_dir> <write_dir> [workload]
+
+`run [workload]` launches rmsnorm_fwd on x[16384, 16384] (the benchmark
+workload; or another RMSNorm workload of `workloads`, e.g. rms_4096x32768) a
+few times, then a plain device-to-device copy of the same x (torch's copy
+kernel) as the calibration: the counters of the copy, whose true HBM traffic is
+known (x's bytes read and written), give the factor that converts each counter
+reading into bytes. `summarize` prints the per-launch HBM traffic of the
+RMSNorm kernel from the two runs' counter CSV files.
+
+    rocprofv3 --pmc FETCH_SIZE -d <dir> -o run -- python probe.py qk-run
+    rocprofv3 --pmc WRITE_SIZE -d <dir> -o run -- python probe.py qk-run
+    python probe.py qk-summarize <fetch_dir> <write_dir>
+
+`qk-run` does the same for qk_norm_rope_fwd on 65536 tokens of 32 q + 8 k + 8 v
+heads of 128 (768 MiB, more than the Infinity Cache), calibrated by torch's
+device copy of a separate 512 MiB buffer (the RMSNorm runs' calibration
+kernel and size);
+`qk-summarize` prints its per-launch traffic beside the
+algorithmic bytes (q and k heads read and written, v heads untouched).
+
+    rocprofv3 --kernel-trace --stats -d <dir> -o run -- python probe.py ceiling
+    python probe.py ceiling-summary <dir>
+
+    rocprofv3 --kernel-trace -d <dir> -o run -- python probe.py small
+    python probe.py small-summary <dir>
+
+`small` launches the two small workloads (RMSNorm on x[1024, 4096], QK-norm +
+RoPE on 256 tokens) beside plain copies of the same bytes and a one-workgroup
+write; `small-summary` gives their GPU durations, the floor such launches sit
+on.
+
+`ceiling` times plain streaming kernels on the same 512 MiB buffers beside
+rmsnorm_fwd: torch's (read only: a sum; write only: a fill; read + write: a
+copy and a scale) and the hand-written ones of libmbn_stream.so (read only,
+write only and copy with the row-norm kernels' 16-byte non-temporal accesses,
+at per-workgroup footprints of 4 to 64 KiB), each over two alternating buffer
+sets (1 GiB apart, so nothing is served from the 256 MiB Infinity Cache);
+`ceiling-summary` turns the kernel trace into GB/s per kernel. It measures what
+the memory system gives a pure-read, a pure-write and a 50/50 read/write stream
+on this part, the reference for the RMSNorm kernel's fraction of peak.
+"""
+
+from __future__ import annotations
+
+import csv
+import ctypes
+import glob
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROBE_CSRC = os.path.join(ROOT, "probe_csrc")
+STREAM_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_stream.so")
+LAUNCHES = 5
+COPY_BYTES = 16384 * 16384 * 2
+
+
+DEFAULT_WORKLOAD = "rms_16384x16384"
+
+
+class HipTimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence.
+
+    A default event record performs a system-scope release (an L2 writeback and
+    invalidate) when it completes; the HIP header documents this flag for
+    events used only to measure time, to avoid that cost and its effect on
+    the following work. Measured on MI355X around each 170 us RMSNorm launch:
+    default events (torch's) read 170.8 us, these 169.1 us, the rocprofv3
+    kernel trace 166.4 us. Recorded on the stream the kernels run on.
+    """
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, stream):
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")  # already loaded by torch
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(stream.cuda_stream)
+        self.events = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        self.events.append(e)
+        return e
+
+    def record(self, e):
+        rc = self.hip.hipEventRecord(e, self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def run(workload: str = DEFAULT_WORKLOAD) -> None:
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+    from workloads import RMS_WORKLOADS, make_rms_inputs
+
+    wl = RMS_WORKLOADS[workload]
+    x_bits, w_bits, eps = make_rms_inputs(wl)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for i in range(LAUNCHES):
+        mbn.rmsnorm_fwd(x, w, y, eps=eps)
+        torch.cuda.synchronize()
+        print(f"rmsnorm launch {i} done", flush=True)
+    z = torch.empty_like(x)
+    for i in range(LAUNCHES):
+        z.copy_(x)
+        torch.cuda.synchronize()
+        print(f"copy launch {i} done", flush=True)
+
+
+QK_TOKENS, QK_HQ, QK_HKV, QK_D = 65536, 32, 8, 128
+
+
+def qk_algorithmic_bytes(T: int = QK_TOKENS) -> int:
+    """q and k heads read and written, the two weights and the positions."""
+    return 2 * T * (QK_HQ + QK_HKV) * QK_D * 2 + 2 * QK_D * 2 + 8 * T
+
+
+def qk_run() -> None:
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    width = (QK_HQ + 2 * QK_HKV) * QK_D
+    # the calibration copy's source (512 MiB), created before qkv
+    n = COPY_BYTES // 2
+    src = torch.randn(n, device=dev, generator=g).to(torch.bfloat16)
+    qkv = torch.randn(QK_TOKENS, width, device=dev, generator=g).to(torch.bfloat16)
+    q_w = (torch.rand(QK_D, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    k_w = (torch.rand(QK_D, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    pos = torch.arange(QK_TOKENS, device=dev, dtype=torch.int64)
+    torch.cuda.synchronize()
+    for i in range(LAUNCHES):
+        mbn.qk_norm_rope_fwd(qkv, q_w, k_w, pos, QK_HQ, QK_HKV, QK_D, eps=1e-6, theta=1e6)
+        torch.cuda.synchronize()
+        print(f"qk_norm_rope launch {i} done", flush=True)
+    # calibration: torch's device copy of 512 MiB, the kernel and footprint of
+    # the RMSNorm calibration
+    z = torch.empty(n, dtype=src.dtype, device=dev)
+    for i in range(LAUNCHES):
+        z.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy launch {i} done", flush=True)
+
+
+def qk_summarize(fetch_dir: str, write_dir: str) -> None:
+    copy_bytes = COPY_BYTES  # the calibration copy's bytes, each way
+    # torch's input set-up launches elementwise kernels too: only the copy counts
+    f = _per_kernel(fetch_dir, "FETCH_SIZE", "qk_norm_rope", "copyBuffer")
+    w = _per_kernel(write_dir, "WRITE_SIZE", "qk_norm_rope", "copyBuffer")
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    f_k, f_c = mean(f["rmsnorm"]), mean(f["copy"])
+    w_k, w_c = mean(w["rmsnorm"]), mean(w["copy"])
+    fetch_b = f_k * copy_bytes / f_c
+    write_b = w_k * copy_bytes / w_c
+    qk = QK_TOKENS * (QK_HQ + QK_HKV) * QK_D * 2
+    print(f"qk_norm_rope FETCH_SIZE per launch (raw): {f_k:.1f}  over {len(f['rmsnorm'])} launches")
+    print(f"qk_norm_rope WRITE_SIZE per launch (raw): {w_k:.1f}  over {len(w['rmsnorm'])} launches")
+    print(f"tokens {QK_TOKENS}, heads {QK_HQ} q + {QK_HKV} k + {QK_HKV} v of {QK_D}")
+    print(f"copy    FETCH_SIZE per launch (raw): {f_c:.1f}   WRITE_SIZE: {w_c:.1f}   true bytes each way: {copy_bytes}")
+    print(f"calibration factors (bytes per counter unit): fetch {copy_bytes / f_c:.3f}  write {copy_bytes / w_c:.3f}")
+    print(f"fetch_bytes_per_launch: {fetch_b:.0f}  (q and k heads: {qk}, x{fetch_b / qk:.4f})")
+    print(f"write_bytes_per_launch: {write_b:.0f}  (q and k heads: {qk}, x{write_b / qk:.4f})")
+    print(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}  algorithmic_bytes_per_launch: {qk_algorithmic_bytes()}"
+          f"  (x{(fetch_b + write_b) / qk_algorithmic_bytes():.4f})")
+
+
+CEIL_REPS = 20
+
+# (case, bytes moved per launch, kind, lanes, chunks): kind "torch-*" is one of
+# torch's kernels, "read" / "write" / "copy" a libmbn_stream.so kernel with
+# workgroups of `lanes` lanes moving `chunks` 16-byte chunks each.
+CEILING_CASES = [
+    ("read only (torch sum)", COPY_BYTES, "torch-sum", 0, 0),
+    ("write only (torch fill)", COPY_BYTES, "torch-fill", 0, 0),
+    ("copy (torch copy_)", 2 * COPY_BYTES, "torch-copy", 0, 0),
+    ("read + write (torch scale)", 2 * COPY_BYTES, "torch-scale", 0, 0),
+    ("read only, 4 KiB/WG", COPY_BYTES, "read", 256, 1),
+    ("read only, 32 KiB/WG", COPY_BYTES, "read", 256, 8),
+    ("write only, 4 KiB/WG", COPY_BYTES, "write", 256, 1),
+    ("write only, 32 KiB/WG", COPY_BYTES, "write", 256, 8),
+    ("copy, 4 KiB/WG", 2 * COPY_BYTES, "copy", 256, 1),
+    ("copy, 8 KiB/WG", 2 * COPY_BYTES, "copy", 512, 1),
+    ("copy, 16 KiB/WG", 2 * COPY_BYTES, "copy", 1024, 1),
+    ("copy, 16 KiB/WG (4 per lane)", 2 * COPY_BYTES, "copy", 256, 4),
+    ("copy, 32 KiB/WG", 2 * COPY_BYTES, "copy", 256, 8),
+    ("copy, 32 KiB/WG (1024 lanes)", 2 * COPY_BYTES, "copy", 1024, 2),
+    ("copy, 64 KiB/WG", 2 * COPY_BYTES, "copy", 256, 16),
+    ("rmsnorm_fwd", 2 * COPY_BYTES + 2 * 16384, "rmsnorm", 0, 0),
+]
+
+
+def build_stream(verbose: bool = False) -> str:
+    """Compile probe_csrc/stream.hip into probe_csrc/libmbn_stream.so (the
+    streaming reference kernels; not part of the library); always rebuilds."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=STREAM_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "stream.hip")])
+
+
+def stream_lib():
+    """ctypes handle of libmbn_stream.so (the streaming reference kernels),
+    compiled first when it is not there."""
+    import ctypes
+
+    if not os.path.exists(STREAM_LIB_PATH):
+        build_stream()
+    h = ctypes.CDLL(STREAM_LIB_PATH)
+    vp, sz, i32, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32
+    h.mbn_stream_copy.argtypes = [vp, vp, sz, i32, i32, vp]
+    h.mbn_stream_read.argtypes = [vp, vp, sz, i32, i32, vp]
+    h.mbn_stream_write.argtypes = [vp, sz, i32, i32, u32, vp]
+    for f in (h.mbn_stream_copy, h.mbn_stream_read, h.mbn_stream_write):
+        f.restype = i32
+    return h
+
+
+def ceiling() -> None:
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+    from workloads import RMS_WORKLOADS, make_rms_inputs
+
+    wl = RMS_WORKLOADS["rms_16384x16384"]
+    x_bits, w_bits, eps = make_rms_inputs(wl)
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xs = [x0, x0.clone()]
+    ys = [torch.empty_like(x0), torch.empty_like(x0)]
+    sink = torch.empty(1024 * 16, dtype=torch.uint8, device=dev)
+    sl = stream_lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"libmbn_stream status {rc}")
+
+    def fn_for(kind, lanes, chunks):
+        if kind == "torch-sum":
+            return lambda i: xs[i].sum(dtype=torch.float32)
+        if kind == "torch-fill":
+            return lambda i: ys[i].fill_(1.0)
+        if kind == "torch-copy":
+            return lambda i: ys[i].copy_(xs[i])
+        if kind == "torch-scale":
+            return lambda i: torch.mul(xs[i], 2.0, out=ys[i])
+        if kind == "read":
+            return lambda i: ok(sl.mbn_stream_read(xs[i].data_ptr(), sink.data_ptr(), COPY_BYTES, lanes, chunks, sp))
+        if kind == "write":
+            return lambda i: ok(sl.mbn_stream_write(ys[i].data_ptr(), COPY_BYTES, lanes, chunks, 0x3F803F80, sp))
+        if kind == "copy":
+            return lambda i: ok(sl.mbn_stream_copy(xs[i].data_ptr(), ys[i].data_ptr(), COPY_BYTES, lanes, chunks, sp))
+        return lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps)
+
+    # the copy kernel copies (checked before the timed cases)
+    ok(sl.mbn_stream_copy(xs[0].data_ptr(), ys[0].data_ptr(), COPY_BYTES, 256, 8, sp))
+    torch.cuda.synchronize()
+    if not torch.equal(ys[0].view(torch.int16), xs[0].view(torch.int16)):
+        raise RuntimeError("stream copy produced a different buffer")
+
+    timer = HipTimingEvents(stream)
+    for name, nbytes, kind, lanes, chunks in CEILING_CASES:
+        fn = fn_for(kind, lanes, chunks)
+        for i in range(3):
+            fn(i % 2)
+        torch.cuda.synchronize()
+        ev = [(timer.new(), timer.new()) for _ in range(CEIL_REPS)]
+        for i, (a, b) in enumerate(ev):
+            timer.record(a)
+            fn(i % 2)
+            timer.record(b)
+        torch.cuda.synchronize()
+        us = sorted(timer.elapsed_ms(a, b) * 1e3 for a, b in ev)
+        timer.close()
+        med = us[len(us) // 2]
+        print(json.dumps({"case": name, "bytes": nbytes, "median_us": round(med, 2),
+                          "GBps": round(nbytes / med / 1e3, 1), "pct_of_8TBps": round(nbytes / med / 1e3 / 80, 2)}),
+              flush=True)
+
+
+def ceiling_summary(d: str) -> None:
+    """GB/s per kernel from a rocprofv3 kernel trace of `ceiling`."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # dispatches of >= 20 us are the 512 MiB kernels: the last ones come in
+    # blocks of 3 warm-up + CEIL_REPS per case, in the order of CEILING_CASES
+    # (before them: the clone that makes the second buffer set and the check
+    # of the copy kernel)
+    big = [r for r in rows if int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) > 20000]
+    per = 3 + CEIL_REPS
+    n = len(CEILING_CASES)
+    if len(big) < per * n:
+        raise SystemExit(f"expected {per * n} large dispatches, found {len(big)}")
+    big = big[len(big) - per * n :]
+    for k, (name, nb, *_rest) in enumerate(CEILING_CASES):
+        grp = big[k * per + 3 : (k + 1) * per]
+        d_us = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+        med = d_us[len(d_us) // 2]
+        kname = grp[0]["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        kname = kname.removeprefix("void ")[:60]
+        print(f"{name:<30} {med:9.2f} us {nb / med / 1e3:8.0f} GB/s {nb / med / 1e3 / 80:6.1f}%   {kname}")
+
+
+# The small workloads beside a plain copy of the same bytes: (case, bytes per
+# launch, kind, lanes, chunks) as in CEILING_CASES; "rms-small" is rmsnorm_fwd
+# on x[1024, 4096], "qk" qk_norm_rope_fwd on 256 tokens of 32 + 8 + 8 heads.
+SMALL_RMS_BYTES = 1024 * 4096 * 2
+SMALL_QK_BYTES = 256 * 40 * 128 * 2
+SMALL_CASES = [
+    ("copy 8 MiB, 4 KiB/WG", 2 * SMALL_RMS_BYTES, "copy", 256, 1),
+    ("copy 8 MiB, 8 KiB/WG", 2 * SMALL_RMS_BYTES, "copy", 512, 1),
+    ("copy 8 MiB, 16 KiB/WG", 2 * SMALL_RMS_BYTES, "copy", 1024, 1),
+    ("rmsnorm_fwd 1024x4096", 2 * SMALL_RMS_BYTES + 2 * 4096, "rms-small", 0, 0),
+    ("copy 2.5 MiB, 4 KiB/WG", 2 * SMALL_QK_BYTES, "copy", 256, 1),
+    ("copy 2.5 MiB, 8 KiB/WG", 2 * SMALL_QK_BYTES, "copy", 512, 1),
+    ("qk_norm_rope_fwd 256 tokens", 2 * SMALL_QK_BYTES + 512 + 8 * 256, "qk", 0, 0),
+    ("write 4 KiB (one workgroup)", 4096, "write-tiny", 256, 1),
+]
+SMALL_REPS = 200
+
+
+def small() -> None:
+    """Times the small workloads and plain copies of their bytes, buffers
+    rotated over >= 1 GiB (cold) except the in-place QK tensor set (64 copies,
+    160 MiB); read the durations from a kernel trace (`small-summary`)."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+    from workloads import QK_WORKLOADS, RMS_WORKLOADS, make_qk_inputs, make_rms_inputs
+
+    dev = torch.device("cuda:0")
+    sl = stream_lib()
+    sp = torch.cuda.current_stream(dev).cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"libmbn_stream status {rc}")
+
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    x_bits, w_bits, eps = make_rms_inputs(RMS_WORKLOADS["rms_1024x4096"])
+    nrot = (1 << 30) // (2 * SMALL_RMS_BYTES)
+    xs = [up(x_bits) for _ in range(nrot)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+    w = up(w_bits)
+    qwl = QK_WORKLOADS["qk_256"]
+    qkv_bits, qw_bits, kw_bits, pos, qeps, theta = make_qk_inputs(qwl)
+    qs = [up(qkv_bits) for _ in range(64)]
+    qw, kw = up(qw_bits), up(kw_bits)
+    posg = torch.from_numpy(pos).to(dev)
+    qrot = 64
+    # the copies of the QK case move the q and k heads' bytes, one tensor per launch
+    qk_src = [torch.empty(SMALL_QK_BYTES // 2, dtype=torch.bfloat16, device=dev) for _ in range(qrot)]
+    qk_dst = [torch.empty_like(qk_src[0]) for _ in range(qrot)]
+    torch.cuda.synchronize()
+    for name, nbytes, kind, lanes, chunks in SMALL_CASES:
+        for i in range(SMALL_REPS + 20):
+            if kind == "copy" and nbytes == 2 * SMALL_RMS_BYTES:
+                ok(sl.mbn_stream_copy(xs[i % nrot].data_ptr(), ys[i % nrot].data_ptr(), SMALL_RMS_BYTES, lanes, chunks, sp))
+            elif kind == "copy":
+                ok(sl.mbn_stream_copy(qk_src[i % qrot].data_ptr(), qk_dst[i % qrot].data_ptr(), SMALL_QK_BYTES, lanes,
+                                      chunks, sp))
+            elif kind == "rms-small":
+                mbn.rmsnorm_fwd(xs[i % nrot], w, ys[i % nrot], eps=eps)
+            elif kind == "qk":
+                mbn.qk_norm_rope_fwd(qs[i % qrot], qw, kw, posg, qwl.n_q_heads, qwl.n_kv_heads, qwl.head_dim,
+                                     eps=qeps, theta=theta)
+            else:
+                ok(sl.mbn_stream_write(ys[0].data_ptr(), 4096, lanes, chunks, 0, sp))
+        torch.cuda.synchronize()
+        print(f"{name}: {SMALL_REPS + 20} launches", flush=True)
+
+
+def small_summary(d: str) -> None:
+    """Median GPU duration of each `small` case (its last SMALL_REPS launches)."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ours = [r for r in rows if any(k in r["Kernel_Name"] for k in ("stream_", "rownorm", "qk_norm_rope"))]
+    per = SMALL_REPS + 20
+    if len(ours) < per * len(SMALL_CASES):
+        raise SystemExit(f"expected {per * len(SMALL_CASES)} dispatches, found {len(ours)}")
+    ours = ours[len(ours) - per * len(SMALL_CASES):]
+    for k, (name, nb, *_rest) in enumerate(SMALL_CASES):
+        grp = ours[k * per + 20 : (k + 1) * per]
+        d_us = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+        med = d_us[len(d_us) // 2]
+        kname = grp[0]["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        kname = kname.removeprefix("void ").replace("mbn::", "")[:48]
+        print(f"{name:<30} {med:8.2f} us  p10 {d_us[len(d_us) // 10]:7.2f}  {nb / med / 1e3:7.0f} GB/s "
+              f"{nb / med / 1e3 / 80:6.1f}%   {kname}")
+
+
+def _rows(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = []
+    for f in files:
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def _per_kernel(d: str, counter: str, kernel: str = "rownorm_kernel", copy: str | None = None):
+    """{'rmsnorm': [values...], 'copy': [values...]} for one counter (summed over
+    its instances); 'rmsnorm' holds the kernels whose name contains `kernel`,
+    'copy' those whose name contains `copy` (default: torch's copy or
+    elementwise kernels)."""
+    acc = {}
+    for r in _rows(d):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    res = {"rmsnorm": [], "copy": []}
+    for (_, name), v in sorted(acc.items(), key=lambda kv: int(kv[0][0])):
+        if kernel in name:
+            res["rmsnorm"].append(v)
+        elif (copy in name) if copy else ("copy" in name.lower() or "elementwise" in name.lower()):
+            res["copy"].append(v)
+    return res
+
+
+KERNEL_SOURCES = [os.path.join(ROOT, "memory_bound_normalization_amd", "csrc", f) for f in ("rownorm.hip", "device.h")]
+
+
+def kernel_source_hash() -> str:
+    """First 16 hex digits of sha256(csrc/rownorm.hip + csrc/device.h): the
+    row-norm kernels' source, recorded with their counter summaries."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize(fetch_dir: str, write_dir: str, workload: str = DEFAULT_WORKLOAD) -> None:
+    """Print the HBM-traffic summary of rmsnorm_fwd on `workload` from the
+    FETCH_SIZE and WRITE_SIZE runs of `run` (the text committed under
+    profiles/)."""
+    sys.path.insert(0, ROOT)
+    from workloads import RMS_WORKLOADS
+
+    wl = RMS_WORKLOADS[workload]
+    copy_bytes = wl.M * wl.N * 2  # the calibration copy moves x once each way
+    f = _per_kernel(fetch_dir, "FETCH_SIZE")
+    w = _per_kernel(write_dir, "WRITE_SIZE")
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    f_r, f_c = mean(f["rmsnorm"]), mean(f["copy"])
+    w_r, w_c = mean(w["rmsnorm"]), mean(w["copy"])
+    f_scale = copy_bytes / f_c
+    w_scale = copy_bytes / w_c
+    fetch_b = f_r * f_scale
+    write_b = w_r * w_scale
+    rd = wl.M * wl.N * 2 + 2 * wl.N
+    wr = wl.M * wl.N * 2
+    arg = "" if workload == DEFAULT_WORKLOAD else f" {workload}"
+    title = f"rmsnorm_fwd HBM traffic per launch, x[{wl.M}, {wl.N}] bf16, MI355X (gfx950)"
+    print(title)
+    print("=" * len(title))
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp), one counter per run:")
+    print(f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- \\")
+    print(f"      python -u probe.py run{arg}")
+    print(f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- \\")
+    print(f"      python -u probe.py run{arg}")
+    print(f"  python probe.py summarize {fetch_dir} {write_dir}{arg}")
+    print()
+    print(f"The probe launches rmsnorm_fwd {LAUNCHES} times on the workload, then torch's device copy")
+    print(f"of the same {copy_bytes:,} B {LAUNCHES} times (the calibration kernel: true traffic")
+    print(f"{copy_bytes:,} B read and {copy_bytes:,} B written per launch). The figures are")
+    print("therefore relative to that copy: an over-fetch a plain copy shares would not show.")
+    print()
+    print("Raw counters (mean per dispatch, as rocprofv3 reports them):")
+    print(f"  rmsnorm  FETCH_SIZE {f_r:.1f}   WRITE_SIZE {w_r:.1f}   ({len(f['rmsnorm'])} / {len(w['rmsnorm'])} dispatches)")
+    print(f"  copy     FETCH_SIZE {f_c:.1f}   WRITE_SIZE {w_c:.1f}   ({len(f['copy'])} / {len(w['copy'])} dispatches)")
+    print(f"Calibration (true bytes / copy counter): fetch x{f_scale:.3f}, write x{w_scale:.3f}")
+    print()
+    print("Per rmsnorm launch:")
+    print(f"  fetch_bytes_per_launch: {fetch_b:.0f}   (algorithmic read {rd:,}: {100 * (fetch_b / rd - 1):+.3f}%)")
+    print(f"  write_bytes_per_launch: {write_b:.0f}   (algorithmic write {wr:,}: {100 * (write_b / wr - 1):+.3f}%)")
+    print(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
+    print(f"algorithmic_bytes_per_launch: {wl.algorithmic_bytes}   (traffic / algorithmic = "
+          f"{(fetch_b + write_b) / wl.algorithmic_bytes:.4f})")
+    print()
+    print(f"kernel_source_sha256_16: {kernel_source_hash()}")
+    print("(sha256 of csrc/rownorm.hip + csrc/device.h, first 16 hex digits; bench.py")
+    print("reports roofline.traffic only while this matches the current source.)")
+
+
+TL_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_tl.so")
+TL_MAGIC = 0x74696D65
+TICKS_PER_US = 100.0  # s_memrealtime: 100 MHz constant-rate clock
+
+
+def build_timeline(verbose: bool = False) -> str:
+    """Compile probe_csrc/timeline.hip (the library's row-norm source with its
+    timeline marks defined, and a marked copy) into probe_csrc/libmbn_tl.so."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=TL_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "timeline.hip")])
+
+
+def timeline_lib():
+    import ctypes
+
+    if not os.path.exists(TL_LIB_PATH):
+        build_timeline()
+    h = ctypes.CDLL(TL_LIB_PATH)
+    vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    h.mbn_tl_rmsnorm.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp]
+    h.mbn_tl_copy.argtypes = [vp, vp, sz, i32, vp]
+    h.mbn_tl_clear.argtypes = [i64]
+    h.mbn_tl_fetch.argtypes = [vp, i64]
+    for f in (h.mbn_tl_rmsnorm, h.mbn_tl_copy, h.mbn_tl_clear, h.mbn_tl_fetch, h.mbn_tl_max_blocks):
+        f.restype = i32
+    return h
+
+
+def timeline_metrics(rec, total_bytes: float) -> dict:
+    """Launch metrics from per-workgroup records [nblocks, 8] (start, landed,
+    last store issued, stores done, XCC_ID, HW_ID, block, magic).
+
+    Reads are counted when a workgroup's data has landed, writes when its
+    stores have completed; `steady` is the rate between 20% and 80% of the
+    launch's bytes, `head` / `tail` the time lost before / after that
+    stretch against the steady rate, `xcd_end_spread` the gap between the first
+    and the last XCD to finish.
+    """
+    import numpy as np
+
+    ok = rec[:, 7] == TL_MAGIC
+    r = rec[ok].astype(np.float64)
+    n = int(ok.sum())
+    t0 = r[:, 0].min()
+    start, landed, issued, done = ((r[:, i] - t0) / TICKS_PER_US for i in range(4))
+    xcc = rec[ok, 4].astype(np.int64) & 0xF
+    span = float(done.max())
+    half = total_bytes / 2 / n
+    ev_t = np.concatenate([landed, done])
+    order = np.argsort(ev_t, kind="stable")
+    cum = np.cumsum(np.full(2 * n, half))
+    ts = ev_t[order]
+
+    def t_at(frac):
+        return float(ts[np.searchsorted(cum, frac * total_bytes)])
+
+    t20, t80 = t_at(0.2), t_at(0.8)
+    steady = 0.6 * total_bytes / (t80 - t20) / 1e3  # GB/s (bytes per us / 1e3)
+    ideal = total_bytes / steady / 1e3
+    xcd_end = {int(k): float(done[xcc == k].max()) for k in np.unique(xcc)}
+    ends = np.array(list(xcd_end.values()))
+    # resident workgroups over time
+    edges = np.concatenate([start, done])
+    delta = np.concatenate([np.ones(n), -np.ones(n)])
+    occ = np.cumsum(delta[np.argsort(edges, kind="stable")])
+    # end of a workgroup -> start of the next one on the same CU (HW_ID: CU
+    # bits 11:8, SH bit 12, SE bits 15:13; with the XCD that names the CU)
+    hw = rec[ok, 5].astype(np.int64)
+    cu = xcc * 4096 + ((hw >> 13) & 7) * 256 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 15)
+    gaps = []
+    for k in np.unique(cu):
+        m = cu == k
+        ss = np.sort(start[m])
+        j = np.searchsorted(ss, done[m])
+        gaps.append((ss[j[j < len(ss)]] - done[m][j < len(ss)]))
+    gaps = np.concatenate(gaps) if gaps else np.zeros(1)
+    return {
+        "blocks": n,
+        "cus": int(len(np.unique(cu))),
+        "gap_us_median": round(float(np.median(gaps)), 2),
+        "gap_us_p90": round(float(np.percentile(gaps, 90)), 2),
+        "span_us": round(span, 2),
+        "GBps_span": round(total_bytes / span / 1e3, 1),
+        "steady_GBps": round(steady, 1),
+        "steady_pct": round(100 * steady / 8000.0, 2),
+        "ideal_us_at_steady": round(ideal, 2),
+        "overhead_us": round(span - ideal, 2),
+        "head_us": round(t20 - 0.2 * ideal, 2),
+        "tail_us": round(span - t80 - 0.2 * ideal, 2),
+        "last_start_us": round(float(start.max()), 2),
+        "drain_us": round(span - float(start.max()), 2),
+        "first_end_us": round(float(done.min()), 2),
+        "xcd_end_us": {k: round(v, 2) for k, v in sorted(xcd_end.items())},
+        "xcd_end_spread_us": round(float(ends.max() - ends.min()), 2),
+        "xcd_blocks": {int(k): int((xcc == k).sum()) for k in np.unique(xcc)},
+        "max_resident_wgs": int(occ.max()),
+        "wg_life_us_median": round(float(np.median(done - start)), 2),
+        "wg_land_us_median": round(float(np.median(landed - start)), 2),
+        "wg_store_us_median": round(float(np.median(done - landed)), 2),
+    }
+
+
+def _timeline_total(name: str) -> int:
+    """Algorithmic bytes of a timeline case: rmsnorm_MxN or a copy of 512 MiB."""
+    if name.startswith("rmsnorm_"):
+        m, n = (int(v) for v in name.split("_")[1].split("x"))
+        return 2 * m * n * 2 + 2 * n
+    return 2 * 16384 * 16384 * 2
+
+
+TIMELINE_SHAPES = [(16384, 16384), (8192, 8192), (4096, 32768)]
+
+
+def timeline(out_dir: str = "gpurun_out/timeline", launches: int = 4) -> None:
+    """Per-workgroup timelines of rmsnorm_fwd (the library's kernel with its
+    marks compiled in) at x[16384, 16384], x[8192, 8192] and x[4096, 32768],
+    and of the streaming copy of 512 MiB (4 KiB and 32 KiB per workgroup).
+    Records are saved per traced launch (.npz, times relative to the launch's
+    first workgroup start).
+    Before each traced launch the part runs ~40 ms of back-to-back library
+    launches at 16384 x 16384 (1 GiB each, so the traced launch's data is not
+    in the 256 MiB Infinity Cache); records saved as .npy, one JSON line of
+    metrics per traced launch."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    os.makedirs(out_dir, exist_ok=True)
+    tl = timeline_lib()
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    bufs = {}
+    for M, N in TIMELINE_SHAPES:
+        x = torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16)
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        bufs[(M, N)] = (x, w, torch.empty_like(x))
+    x, w, y = bufs[(16384, 16384)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    nbytes = x.numel() * 2
+    for _ in range(2400):
+        mbn.rmsnorm_fwd(x, w, y, eps=1e-6)
+    torch.cuda.synchronize()
+    timer = HipTimingEvents(stream)
+    ev = [(timer.new(), timer.new()) for _ in range(200)]
+    for a, b in ev:
+        timer.record(a)
+        mbn.rmsnorm_fwd(x, w, y, eps=1e-6)
+        timer.record(b)
+    torch.cuda.synchronize()
+    lib_us = [timer.elapsed_ms(a, b) * 1e3 for a, b in ev]
+    print(json.dumps({"kernel": "library rmsnorm_fwd 16384x16384 (no marks)", "launches": len(lib_us),
+                      "mean_us": round(sum(lib_us) / len(lib_us), 2), "min_us": round(min(lib_us), 2)}), flush=True)
+    rmax = tl.mbn_tl_max_blocks()
+
+    def rms_case(M, N):
+        xm, wm, ym = bufs[(M, N)]
+        return lambda: tl.mbn_tl_rmsnorm(xm.data_ptr(), wm.data_ptr(), ym.data_ptr(), M, N, 1e-6, sp)
+
+    cases = [(f"rmsnorm_{M}x{N}", rms_case(M, N)) for M, N in TIMELINE_SHAPES]
+    cases += [("copy_4KiB_per_wg", lambda: tl.mbn_tl_copy(x.data_ptr(), y.data_ptr(), nbytes, 1, sp)),
+              ("copy_32KiB_per_wg", lambda: tl.mbn_tl_copy(x.data_ptr(), y.data_ptr(), nbytes, 8, sp))]
+    for name, fn in cases:
+        total = _timeline_total(name)
+        for i in range(launches):
+            for _ in range(240):
+                mbn.rmsnorm_fwd(x, w, y, eps=1e-6)
+            torch.cuda.synchronize()
+            if tl.mbn_tl_clear(rmax) != 0:
+                raise RuntimeError("mbn_tl_clear failed")
+            a, b = timer.new(), timer.new()
+            timer.record(a)
+            rc = fn()
+            timer.record(b)
+            if rc != 0:
+                raise RuntimeError(f"{name}: launch status {rc}")
+            torch.cuda.synchronize()
+            rec = np.zeros((rmax, 8), dtype=np.uint64)
+            if tl.mbn_tl_fetch(rec.ctypes.data, rmax) != 0:
+                raise RuntimeError("mbn_tl_fetch failed")
+            rec = rec[rec[:, 7] == TL_MAGIC]
+            rec[:, :4] -= rec[:, 0].min()  # times relative to the first start (compresses well)
+            np.savez_compressed(os.path.join(out_dir, f"{name}_{i}.npz"), rec=rec)
+            m = timeline_metrics(rec, total)
+            m.update({"case": name, "launch": i, "event_us": round(timer.elapsed_ms(a, b) * 1e3, 2)})
+            print(json.dumps(m), flush=True)
+    timer.close()
+
+
+def timeline_summary(d: str) -> None:
+    """Median metrics per case over the saved launches, and the bandwidth over
+    time (4 us bins) of the median-span launch of rmsnorm_16384x16384 and
+    copy_4KiB_per_wg."""
+    import numpy as np
+
+    names = sorted({os.path.basename(f).rsplit("_", 1)[0] for f in glob.glob(os.path.join(d, "*_*.npz"))})
+    for name in names:
+        total = _timeline_total(name)
+        files = sorted(glob.glob(os.path.join(d, f"{name}_*.npz")))
+        if not files:
+            continue
+        recs = [np.load(f)["rec"] for f in files]
+        ms = [timeline_metrics(r, total) for r in recs]
+        keys = ["span_us", "GBps_span", "steady_GBps", "steady_pct", "overhead_us", "head_us", "tail_us",
+                "gap_us_median", "gap_us_p90",
+                "drain_us", "xcd_end_spread_us", "max_resident_wgs", "wg_life_us_median", "wg_land_us_median",
+                "wg_store_us_median", "first_end_us"]
+        print(f"{name}: {len(ms)} launches, {ms[0]['blocks']} workgroups")
+        for k in keys:
+            v = [m[k] for m in ms]
+            print(f"  {k:22s} median {np.median(v):9.2f}   min {min(v):9.2f}   max {max(v):9.2f}")
+        print("  XCD finish times (us after the first workgroup start), per launch:")
+        for m in ms:
+            e = m["xcd_end_us"]
+            print("    " + " ".join(f"{e[k]:7.2f}" for k in sorted(e)) + f"   spread {m['xcd_end_spread_us']:.2f}")
+        if name not in ("rmsnorm_16384x16384", "copy_4KiB_per_wg"):
+            continue
+        med = sorted(range(len(ms)), key=lambda i: ms[i]["span_us"])[len(ms) // 2]
+        r = recs[med][recs[med][:, 7] == TL_MAGIC].astype(np.float64)
+        t0 = r[:, 0].min()
+        landed, done = (r[:, 1] - t0) / TICKS_PER_US, (r[:, 3] - t0) / TICKS_PER_US
+        n = len(r)
+        half = total / 2 / n
+        bins = np.arange(0.0, done.max() + 4.0, 4.0)
+        rd = np.histogram(landed, bins)[0] * half / 4.0 / 1e3
+        wr = np.histogram(done, bins)[0] * half / 4.0 / 1e3
+        print(f"  GB/s per 4 us bin (launch {med}): rows landed + rows written = total, % of 8 TB/s")
+        for i in range(len(bins) - 1):
+            tot = rd[i] + wr[i]
+            print(f"    {bins[i]:6.1f}-{bins[i + 1]:6.1f} us  {rd[i]:7.0f} + {wr[i]:7.0f} = {tot:7.0f}  {100 * tot / 8000:5.1f}%")
+
+
+def sizes(out: str | None = None) -> None:
+    """Kernel time against size at N = 16384: the library's rmsnorm_fwd and the
+    4 KiB-per-workgroup streaming copy of the same bytes, M = 8192 ... 131072
+    (event mean of 100 launches after 50), and a least-squares line per kernel:
+    its slope is the steady-state rate, its intercept the per-launch overhead."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    N = 16384
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    sl = stream_lib()
+    timer = HipTimingEvents(stream)
+    Ms = [8192, 16384, 32768, 65536, 131072]
+    xbig = torch.empty(max(Ms), N, dtype=torch.bfloat16, device=dev).normal_()
+    ybig = torch.empty_like(xbig)
+    w = torch.ones(N, dtype=torch.bfloat16, device=dev)
+    for _ in range(2400):
+        mbn.rmsnorm_fwd(xbig[:16384], w, ybig[:16384], eps=1e-6)
+    torch.cuda.synchronize()
+    res = {"rmsnorm": [], "copy": []}
+    for M in Ms:
+        x, y = xbig[:M], ybig[:M]
+        fns = {"rmsnorm": lambda: mbn.rmsnorm_fwd(x, w, y, eps=1e-6),
+               "copy": lambda: sl.mbn_stream_copy(x.data_ptr(), y.data_ptr(), M * N * 2, 256, 1, sp)}
+        for name, fn in fns.items():
+            for _ in range(50):
+                fn()
+            ev = [(timer.new(), timer.new()) for _ in range(100)]
+            for a, b in ev:
+                timer.record(a)
+                fn()
+                timer.record(b)
+            torch.cuda.synchronize()
+            us = float(np.mean([timer.elapsed_ms(a, b) * 1e3 for a, b in ev]))
+            nb = 2 * M * N * 2 + (2 * N if name == "rmsnorm" else 0)
+            res[name].append((nb, us))
+            print(json.dumps({"kernel": name, "M": M, "N": N, "bytes": nb, "mean_us": round(us, 2),
+                              "pct": round(100 * nb / us / 1e3 / 8000, 2)}), flush=True)
+            timer.close()
+    for name, pts in res.items():
+        b = np.array([p[0] for p in pts], dtype=np.float64)
+        t = np.array([p[1] for p in pts])
+        slope, icpt = np.polyfit(b, t, 1)
+        print(json.dumps({"fit": name, "steady_GBps": round(1 / slope / 1e3, 1),
+                          "steady_pct": round(100 / slope / 1e3 / 8000, 2), "intercept_us": round(icpt, 2)}),
+              flush=True)
+
+
+VARIANTS = {
+    0: "N=16384: 2 lane sets x 128 lanes, 1 row each, cap 2, XCD group 4 (the table's entry)",
+    1: "N=16384: 128 lanes, 1 row, cap 4, group 4",
+    2: "N=16384: 128 lanes, 1 row, cap 2, group 4",
+    3: "N=16384: 256 lanes, 1 row, cap 4, group 4",
+    4: "N=16384: 2 x 128 lanes, cap 2, group 0",
+    5: "N=16384: 128 lanes, 1 row, cap 5, group 4",
+    6: "N=16384: 2 x 128 lanes, cap 2, group 8",
+    7: "N=16384: 128 lanes, 2 rows per lane set, cap 2, group 4",
+    8: "N=16384: 256 lanes, 1 row, cap 3, group 4",
+    9: "N=16384: 2 x 128 lanes, cap 1, group 4",
+    10: "N=32768: 1024 lanes, 1 row, no cap, group 0 (the table's entry)",
+    11: "N=32768: 512 lanes, cap 2, group 0",
+    12: "N=32768: 256 lanes, cap 2, group 0",
+    13: "N=32768: 512 lanes, cap 2, group 4",
+    14: "N=32768: 1024 lanes, no cap, group 4",
+    15: "N=32768: 256 lanes, cap 2, group 4",
+}
+
+
+def variants(out_dir: str = "gpurun_out/variants", rounds: int = 3, launches: int = 60) -> None:
+    """Geometry variants of the library's one-shot RMSNorm kernel (timeline
+    marks compiled in) at x[16384, 16384] (variants 0-9) and x[4096, 32768]
+    (10-15): event median over `launches` launches per round, rounds
+    interleaved, plus one traced launch per variant (saved as .npz)."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    os.makedirs(out_dir, exist_ok=True)
+    tl = timeline_lib()
+    tl.mbn_tl_rmsnorm_variant.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                                                  ctypes.c_void_p, ctypes.c_int]
+    tl.mbn_tl_rmsnorm_variant.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(12)
+    shapes = {16384: (16384, 16384), 32768: (4096, 32768)}
+    bufs = {}
+    for n, (M, N) in shapes.items():
+        x = torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16)
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        bufs[n] = (M, N, x, w, torch.empty_like(x), torch.empty_like(x))
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    M0, N0, x0, w0, y0, _ = bufs[16384]
+    for _ in range(2400):
+        mbn.rmsnorm_fwd(x0, w0, y0, eps=1e-6)
+    torch.cuda.synchronize()
+    for v in VARIANTS:  # first launch of each kernel (module load) outside the timing
+        M, N, x, w, y, y2 = bufs[16384 if v < 10 else 32768]
+        if tl.mbn_tl_rmsnorm_variant(x.data_ptr(), w.data_ptr(), y.data_ptr(), M, N, 1e-6, sp, v) != 0:
+            raise RuntimeError(f"variant {v}: launch failed")
+    torch.cuda.synchronize()
+    timer = HipTimingEvents(stream)
+    res = {v: [] for v in VARIANTS}
+    lib_res = {16384: [], 32768: []}
+    for rnd in range(rounds):
+        for n in (16384, 32768):
+            M, N, x, w, y, y2 = bufs[n]
+            ev = [(timer.new(), timer.new()) for _ in range(launches)]
+            for i, (a, b) in enumerate(ev):
+                timer.record(a)
+                mbn.rmsnorm_fwd(x, w, y if i % 2 else y2, eps=1e-6)
+                timer.record(b)
+            torch.cuda.synchronize()
+            lib_res[n] += [timer.elapsed_ms(a, b) * 1e3 for a, b in ev]
+            timer.close()
+        for v in VARIANTS:
+            M, N, x, w, y, y2 = bufs[16384 if v < 10 else 32768]
+            ev = [(timer.new(), timer.new()) for _ in range(launches)]
+            for i, (a, b) in enumerate(ev):
+                timer.record(a)
+                rc = tl.mbn_tl_rmsnorm_variant(x.data_ptr(), w.data_ptr(), (y if i % 2 else y2).data_ptr(), M, N,
+                                               1e-6, sp, v)
+                timer.record(b)
+                if rc != 0:
+                    raise RuntimeError(f"variant {v}: status {rc}")
+            torch.cuda.synchronize()
+            res[v] += [timer.elapsed_ms(a, b) * 1e3 for a, b in ev]
+            timer.close()
+        print(f"round {rnd} done", flush=True)
+    rmax = tl.mbn_tl_max_blocks()
+    for n in (16384, 32768):
+        M, N = shapes[n]
+        nb = 2 * M * N * 2 + 2 * N
+        us = float(np.median(lib_res[n]))
+        print(json.dumps({"variant": "library", "N": n, "median_us": round(us, 2),
+                          "pct": round(100 * nb / us / 1e3 / 8000, 2)}), flush=True)
+    for v, desc in VARIANTS.items():
+        M, N, x, w, y, y2 = bufs[16384 if v < 10 else 32768]
+        nb = 2 * M * N * 2 + 2 * N
+        us = float(np.median(res[v]))
+        for _ in range(100):
+            mbn.rmsnorm_fwd(x0, w0, y0, eps=1e-6)
+        torch.cuda.synchronize()
+        tl.mbn_tl_clear(rmax)
+        if tl.mbn_tl_rmsnorm_variant(x.data_ptr(), w.data_ptr(), y.data_ptr(), M, N, 1e-6, sp, v) != 0:
+            raise RuntimeError(f"variant {v}: launch failed")
+        torch.cuda.synchronize()
+        rec = np.zeros((rmax, 8), dtype=np.uint64)
+        tl.mbn_tl_fetch(rec.ctypes.data, rmax)
+        rec = rec[rec[:, 7] == TL_MAGIC]
+        rec[:, :4] -= rec[:, 0].min()
+        np.savez_compressed(os.path.join(out_dir, f"variant{v}.npz"), rec=rec)
+        m = timeline_metrics(rec, nb)
+        keep = {k: m[k] for k in ("span_us", "steady_pct", "overhead_us", "gap_us_median", "gap_us_p90",
+                                  "xcd_end_spread_us", "max_resident_wgs", "wg_land_us_median",
+                                  "wg_store_us_median")}
+        print(json.dumps({"variant": v, "desc": desc, "median_us": round(us, 2),
+                          "pct": round(100 * nb / us / 1e3 / 8000, 2), **keep}), flush=True)
+
+
+STREAM_VARIANTS = {
+    0: (16384, "128 lanes/row, 2 buffers, 2 WGs/CU"),
+    1: (16384, "256 lanes/row, 2 buffers, 2 WGs/CU"),
+    2: (16384, "256 lanes/row, 3 buffers, 1 WG/CU"),
+    3: (16384, "256 lanes/row, 4 buffers, 1 WG/CU"),
+    4: (16384, "512 lanes/row, 4 buffers, 1 WG/CU"),
+    5: (16384, "128 lanes/row, 2 buffers, 1 WG/CU"),
+    6: (16384, "256 lanes/row, 2 buffers, 1 WG/CU"),
+    10: (32768, "512 lanes/row, 2 buffers, 1 WG/CU"),
+    11: (32768, "256 lanes/row, 2 buffers, 1 WG/CU"),
+    12: (32768, "1024 lanes/row, 2 buffers, 1 WG/CU"),
+    20: (8192, "128 lanes/row, 2 buffers, 4 WGs/CU"),
+    21: (8192, "128 lanes/row, 3 buffers, 3 WGs/CU"),
+    22: (8192, "64 lanes/row, 2 buffers, 4 WGs/CU"),
+    23: (8192, "256 lanes/row, 4 buffers, 2 WGs/CU"),
+}
+STREAM_SHAPES = {16384: (16384, 16384), 32768: (4096, 32768), 8192: (8192, 8192)}
+
+
+def stream_variants(rounds: int = 3, launches: int = 60) -> None:
+    """The pipelined persistent RMSNorm experiment (probe_csrc/timeline.hip)
+    against the library's rmsnorm_fwd at the same shapes: every output compared
+    with the library's (at most one bf16 ulp apart: the reduction order may
+    differ), then event medians over interleaved rounds. Inputs rotate over
+    buffer sets of >= 1 GiB so no launch is served from the Infinity Cache."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    tl = timeline_lib()
+    tl.mbn_tl_rmsnorm_stream.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                                                 ctypes.c_void_p, ctypes.c_int]
+    tl.mbn_tl_rmsnorm_stream.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(13)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    sets = {}
+    for n, (M, N) in STREAM_SHAPES.items():
+        nset = max(1, -(-(1 << 30) // (2 * M * N * 2)))
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        sets[n] = [(torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16), w,
+                    torch.empty(M, N, dtype=torch.bfloat16, device=dev)) for _ in range(nset)]
+    x0, w0, y0 = sets[16384][0]
+    for _ in range(2400):
+        mbn.rmsnorm_fwd(x0, w0, y0, eps=1e-6)
+    torch.cuda.synchronize()
+
+    def run_stream(v, x, w, y):
+        M, N = x.shape
+        rc = tl.mbn_tl_rmsnorm_stream(x.data_ptr(), w.data_ptr(), y.data_ptr(), M, N, 1e-6, sp, v)
+        if rc != 0:
+            raise RuntimeError(f"stream variant {v}: status {rc}")
+
+    # correctness against the library, every output
+    for v, (n, desc) in STREAM_VARIANTS.items():
+        x, w, y = sets[n][0]
+        ref = mbn.rmsnorm_fwd(x, w, eps=1e-6)
+        y.fill_(0)
+        run_stream(v, x, w, y)
+        torch.cuda.synchronize()
+        d = (y.float() - ref.float()).abs()
+        tol = ref.float().abs() * 2.0 ** -7 + 1e-6
+        bad = int((d > tol).sum())
+        same = float((y.view(torch.int16) == ref.view(torch.int16)).float().mean())
+        print(json.dumps({"check": v, "outside_1ulp": bad, "bit_equal_frac": round(same, 6)}), flush=True)
+        if bad:
+            raise RuntimeError(f"stream variant {v}: {bad} outputs differ from the library by more than 1 ulp")
+    timer = HipTimingEvents(stream)
+    res = {("lib", n): [] for n in STREAM_SHAPES}
+    res.update({v: [] for v in STREAM_VARIANTS})
+
+    def timed(key, fn, n):
+        ev = [(timer.new(), timer.new()) for _ in range(launches)]
+        for i, (a, b) in enumerate(ev):
+            x, w, y = sets[n][i % len(sets[n])]
+            timer.record(a)
+            fn(x, w, y)
+            timer.record(b)
+        torch.cuda.synchronize()
+        res[key] += [timer.elapsed_ms(a, b) * 1e3 for a, b in ev]
+        timer.close()
+
+    for rnd in range(rounds):
+        for n in STREAM_SHAPES:
+            timed(("lib", n), lambda x, w, y: mbn.rmsnorm_fwd(x, w, y, eps=1e-6), n)
+            for v, (vn, _) in STREAM_VARIANTS.items():
+                if vn == n:
+                    timed(v, lambda x, w, y, v=v: run_stream(v, x, w, y), n)
+        print(f"round {rnd} done", flush=True)
+    for key, us in res.items():
+        n = key[1] if isinstance(key, tuple) else STREAM_VARIANTS[key][0]
+        M, N = STREAM_SHAPES[n]
+        nb = 2 * M * N * 2 + 2 * N
+        med = float(np.median(us))
+        print(json.dumps({"kernel": "library" if isinstance(key, tuple) else key, "shape": f"{M}x{N}",
+                          "desc": "rmsnorm_fwd" if isinstance(key, tuple) else STREAM_VARIANTS[key][1],
+                          "median_us": round(med, 2), "mean_us": round(float(np.mean(us)), 2),
+                          "pct_median": round(100 * nb / med / 1e3 / 8000, 2)}), flush=True)
+
+
+CLAIM_CASES = [(0, 512), (256, 512), (512, 512), (1024, 512), (512, 256), (1024, 1024), (2048, 512)]
+
+
+def claim_variants(rounds: int = 4, launches: int = 50) -> None:
+    """The claimed-tail experiment (probe_csrc/timeline.hip, tl_claim_kernel)
+    at x[16384, 16384]: (dynamic blocks, claiming workgroups) cases against the
+    same geometry without claims (variant 0) and the library's rmsnorm_fwd;
+    every output compared with the library's, then event medians over
+    interleaved rounds."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    tl = timeline_lib()
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    tl.mbn_tl_rmsnorm_claim.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp, ctypes.c_uint, ctypes.c_uint]
+    tl.mbn_tl_rmsnorm_claim.restype = ctypes.c_int
+    tl.mbn_tl_rmsnorm_variant.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp, ctypes.c_int]
+    tl.mbn_tl_rmsnorm_variant.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(14)
+    M = N = 16384
+    x = torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16)
+    w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    for _ in range(2400):
+        mbn.rmsnorm_fwd(x, w, y, eps=1e-6)
+    torch.cuda.synchronize()
+    ref = mbn.rmsnorm_fwd(x, w, eps=1e-6)
+
+    def claim(c):
+        rc = tl.mbn_tl_rmsnorm_claim(x.data_ptr(), w.data_ptr(), y.data_ptr(), M, N, 1e-6, sp, c[0], c[1])
+        if rc != 0:
+            raise RuntimeError(f"claim {c}: status {rc}")
+
+    for c in CLAIM_CASES:
+        for rep in range(2):
+            y.fill_(0)
+            claim(c)
+            torch.cuda.synchronize()
+            same = bool(torch.equal(y.view(torch.int16), ref.view(torch.int16)))
+            print(json.dumps({"check": list(c), "rep": rep, "bit_equal_to_library": same}), flush=True)
+            if not same:
+                raise RuntimeError(f"claim {c}: output differs from the library's")
+    timer = HipTimingEvents(stream)
+    keys = ["library", "variant0"] + [tuple(c) for c in CLAIM_CASES]
+    res = {k: [] for k in keys}
+
+    def fn_of(k):
+        if k == "library":
+            return lambda: mbn.rmsnorm_fwd(x, w, y, eps=1e-6)
+        if k == "variant0":
+            return lambda: tl.mbn_tl_rmsnorm_variant(x.data_ptr(), w.data_ptr(), y.data_ptr(), M, N, 1e-6, sp, 0)
+        return lambda: claim(k)
+
+    for rnd in range(rounds):
+        for k in keys:
+            fn = fn_of(k)
+            ev = [(timer.new(), timer.new()) for _ in range(launches)]
+            for a, b in ev:
+                timer.record(a)
+                fn()
+                timer.record(b)
+            torch.cuda.synchronize()
+            res[k] += [timer.elapsed_ms(a, b) * 1e3 for a, b in ev]
+            timer.close()
+        print(f"round {rnd} done", flush=True)
+    nb = 2 * M * N * 2 + 2 * N
+    for k in keys:
+        med = float(np.median(res[k]))
+        print(json.dumps({"kernel": k if isinstance(k, str) else {"ndyn": k[0], "nclaim": k[1]},
+                          "median_us": round(med, 2), "mean_us": round(float(np.mean(res[k])), 2),
+                          "pct_median": round(100 * nb / med / 1e3 / 8000, 2)}), flush=True)
+
+
+def _short_kernel(n: str) -> str:
+    n = n.replace("mbn::(anonymous namespace)::", "").replace("void ", "")
+    n = re.sub(r"\(mbn::RowNormArgs\)|\(mbn::RowNormAnyArgs\)|\(RowNormAnyArgs\)|\(unsigned short\*.*", "", n)
+    return n.replace("(mbn::Norm)", "").replace("mbn::Bf16, ", "").replace("mbn::", "")
+
+
+def trace_summary(d: str, bench_json: str, timed: int = 200) -> None:
+    """The headline kernel-trace summary: rocprofv3 --kernel-trace --stats of
+    `python -u bench.py --no-cpu-baseline` (files in d), beside that run's JSON
+    line (bench_json: a file holding it)."""
+    import json
+    import statistics
+
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
+    stats = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    rms = sorted((r for r in rows if "rownorm_kernel" in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rms][-timed:]
+    b = [json.loads(line) for line in open(bench_json) if line.startswith("{")][-1]
+    algo = b["roofline"]["algorithmic_bytes_per_launch"]
+    r0 = rms[0]
+    title = "rmsnorm_fwd, x[16384, 16384] bf16 -> y (bench workload), MI355X (gfx950), one GPU"
+    print(title)
+    print("=" * len(title))
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp):")
+    print(f"  rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- \\")
+    print(f"      python -u bench.py --no-cpu-baseline > {bench_json}")
+    print(f"      (defaults: {b['warmup']} warm-up + {b['steps']} timed steps)")
+    print(f"  python probe.py trace-summary {d} {bench_json}")
+    print()
+    print(f"Kernel statistics (run_kernel_stats.csv, every dispatch of the run, warm-up included):")
+    print()
+    print(f"  {'kernel':<66} {'calls':>5} {'avg_us':>8} {'min_us':>8} {'max_us':>8} {'sd_us':>7}")
+    for st in stats:
+        kn = _short_kernel(st["Name"])[:66]
+        print(f"  {kn:<66} {int(st['Calls']):>5} {float(st['AverageNs']) / 1e3:>8.2f} "
+              f"{float(st['MinNs']) / 1e3:>8.2f} {float(st['MaxNs']) / 1e3:>8.2f} {float(st['StdDev']) / 1e3:>7.2f}")
+    print()
+    print(f"{_short_kernel(r0['Kernel_Name'])}: workgroup {r0['Workgroup_Size_X']} threads, grid "
+          f"{int(r0['Grid_Size_X']) // int(r0['Workgroup_Size_X'])} workgroups, VGPR {r0['VGPR_Count']}, "
+          f"SGPR {r0['SGPR_Count']}, LDS {r0.get('LDS_Block_Size', r0.get('Lds_Size', '?'))} B")
+    print()
+    m = statistics.mean(dur)
+    print(f"Algorithmic bytes per launch: 2*M*N*2 + 2*N = {algo:,} B.")
+    print(f"Mean over the last {len(dur)} dispatches (the timed steps), trace: {m:.2f} us -> "
+          f"{algo / m / 1e3:.1f} GB/s = {100 * algo / m / 1e3 / 8000:.2f}% of 8 TB/s.")
+    print(f"The same run's bench.py line (HIP events around each launch): mean {b['roofline']['mean_us']} us, "
+          f"best {b['roofline']['best_us']} us -> {b['value']} GB/s ({100 * b['roofline']['frac']:.2f}%); "
+          f"the means differ by {100 * (b['roofline']['mean_us'] - m) / m:+.2f}%.")
+    cr = b["roofline"].get("streaming_copy_reference")
+    if cr:
+        print(f"Streaming copy of the same buffers in the same run (stream_copy<256, 1>): "
+              f"{cr['mean_us']} us, {cr['GBps']} GB/s ({100 * cr['frac']:.2f}%); rmsnorm / copy = "
+              f"{cr['rmsnorm_over_copy']}.")
+
+
+def suite_summary(d: str, suite_log: str, warm: int = 3000) -> None:
+    """The all-workloads table from rocprofv3 --kernel-trace of
+    `python -u bench.py --suite --steps 50 --warmup 5` (files in d) and that
+    run's JSON lines (suite_log). The first `warm` dispatches (the suite's
+    initial load) are skipped; each workload then owns an equal run of
+    dispatches in order."""
+    import json
+    import statistics
+
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ks = [r for r in rows if "rownorm" in r["Kernel_Name"] or "qk_norm_rope" in r["Kernel_Name"]][warm:]
+    cases = [json.loads(line) for line in open(suite_log) if line.startswith("{")]
+    per, rem = divmod(len(ks), len(cases))
+    if rem:
+        raise SystemExit(f"{len(ks)} dispatches do not split into {len(cases)} workloads")
+    title = "Every workload, GPU-side kernel durations, MI355X (gfx950), one GPU"
+    print(title)
+    print("=" * len(title))
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp):")
+    print(f"  rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- \\")
+    print(f"      python -u bench.py --suite --steps 50 --warmup 5 > {suite_log}")
+    print(f"  python probe.py suite-summary {d} {suite_log}")
+    print()
+    print("bench.py --suite rotates over buffer sets of >= 1 GiB per workload, so no launch")
+    print("finds its inputs in the 256 MiB Infinity Cache. Durations are kernel start to")
+    print(f"end from the trace ({per} dispatches per workload: warm-up, per-launch-event and")
+    print("batch phases); bytes are the algorithmic bytes of one launch; % is of 8 TB/s.")
+    print("grid_MxN: the RMSNorm shape grid of the normalization pages (the leading M x N")
+    print("block of the 16384 x 16384 input). Template arguments: rownorm_kernel<mode, WPR,")
+    print("ROWS, RPL, MAXC, full, chunk wait>, rownorm_persistent_kernel<mode, WPR, RPL,")
+    print("MAXC, full> (mode 0 RMSNorm, 1 residual add + RMSNorm, 2 LayerNorm, 3 L2Norm),")
+    print("rownorm_any_kernel / rownorm_s16_kernel (widths that are not whole 16-byte")
+    print("chunks). WGs is the grid size (the persistent grid loops over the rows).")
+    print()
+    print(f"  {'workload':<22} {'op':<20} {'kernel instantiation':<56} {'WGs':>6} {'median_us':>9} {'min_us':>8} "
+          f"{'GB/s':>7} {'%':>6}")
+    for i, c in enumerate(cases):
+        grp = ks[i * per:(i + 1) * per]
+        names = {_short_kernel(r["Kernel_Name"]) for r in grp}
+        if len(names) != 1:
+            raise SystemExit(f"workload {c['workload']}: kernels {names}")
+        du = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+        med = statistics.median(du)
+        b = c["algorithmic_bytes"]
+        wg = int(grp[0]["Grid_Size_X"]) // int(grp[0]["Workgroup_Size_X"])
+        print(f"  {c['workload']:<22} {c['kernel']:<20} {names.pop()[:56]:<56} {wg:>6} {med:>9.2f} {du[0]:>8.2f} "
+              f"{b / med / 1e3:>7.0f} {b / med / 1e3 / 80:>6.1f}")
+
+
+def experiments_summary(sizes_log: str, variants_log: str, claim_log: str, stream_log: str) -> None:
+    """Tables of the size sweep, the geometry variants, the claimed-tail and the
+    pipelined persistent experiments from their JSON-line outputs."""
+    import json
+
+    def lines(p):
+        return [json.loads(x) for x in open(p) if x.startswith("{")]
+
+    print("Size sweep at N = 16384 (event mean of 100 launches after 50; copy = stream_copy<256, 1>):")
+    print(f"  {'kernel':<8} {'M':>7} {'bytes':>12} {'mean_us':>9} {'% of 8 TB/s':>12}")
+    for r in lines(sizes_log):
+        if "fit" in r:
+            print(f"  least-squares line, {r['fit']}: slope -> {r['steady_GBps']} GB/s ({r['steady_pct']}%), "
+                  f"intercept {r['intercept_us']} us")
+        else:
+            print(f"  {r['kernel']:<8} {r['M']:>7} {r['bytes']:>12} {r['mean_us']:>9.2f} {r['pct']:>12.2f}")
+    print()
+    print("Geometry variants of the one-shot kernel (timeline marks compiled in; event median of 180")
+    print("launches in interleaved rounds; the trace columns are from one traced launch):")
+    print(f"  {'variant':<82} {'med_us':>7} {'%':>6} {'steady%':>7} {'gap':>5} {'gap90':>5} {'xcd':>5} {'land':>5}")
+    for r in lines(variants_log):
+        if r["variant"] == "library":
+            print(f"  {'library rmsnorm_fwd, N = ' + str(r['N']) + ' (no marks)':<82} {r['median_us']:>7.2f} {r['pct']:>6.2f}")
+            continue
+        print(f"  {str(r['variant']) + ': ' + r['desc']:<82} {r['median_us']:>7.2f} {r['pct']:>6.2f} "
+              f"{r['steady_pct']:>7.2f} {r['gap_us_median']:>5.2f} {r['gap_us_p90']:>5.2f} "
+              f"{r['xcd_end_spread_us']:>5.2f} {r['wg_land_us_median']:>5.2f}")
+    print("  (gap: us from a workgroup's end to the next start on its CU, median / p90; xcd: spread of")
+    print("  the XCD finish times; land: median us from a workgroup's start until its rows are reduced)")
+    print()
+    print("Claimed tail at x[16384, 16384] (the table's geometry; ndyn row blocks claimed from a device")
+    print("counter by nclaim workgroups dispatched after the static ones; event median of 200 launches):")
+    for r in lines(claim_log):
+        if "check" in r:
+            continue
+        k = r["kernel"]
+        name = k if isinstance(k, str) else f"ndyn {k['ndyn']}, nclaim {k['nclaim']}"
+        print(f"  {name:<28} {r['median_us']:>8.2f} us  {r['pct_median']:>6.2f}%")
+    print()
+    print("Pipelined persistent kernel (rows g, g + G, ... per workgroup, NB LDS row buffers in a ring,")
+    print("the next row's copy issued as soon as pass 2 has read a buffer; event median of 180 launches):")
+    for r in lines(stream_log):
+        if "check" in r:
+            continue
+        name = "library rmsnorm_fwd" if r["kernel"] == "library" else f"{r['kernel']}: {r['desc']}"
+        print(f"  {r['shape']:<12} {name:<50} {r['median_us']:>8.2f} us  {r['pct_median']:>6.2f}%")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 2 and sys.argv[1] == "ceiling":
+        ceiling()
+    elif len(sys.argv) >= 3 and sys.argv[1] == "ceiling-summary":
+        ceiling_summary(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "small":
+        small()
+    elif len(sys.argv) == 3 and sys.argv[1] == "small-summary":
+        small_summary(sys.argv[2])
+    elif len(sys.argv) in (2, 3) and sys.argv[1] == "run":
+        run(*sys.argv[2:])
+    elif len(sys.argv) == 2 and sys.argv[1] == "qk-run":
+        qk_run()
+    elif len(sys.argv) == 4 and sys.argv[1] == "qk-summarize":
+        qk_summarize(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) in (2, 3) and sys.argv[1] == "timeline":
+        timeline(*sys.argv[2:])
+    elif len(sys.argv) == 3 and sys.argv[1] == "timeline-summary":
+        timeline_summary(sys.argv[2])
+    elif len(sys.argv) in (2, 3) and sys.argv[1] == "variants":
+        variants(*sys.argv[2:])
+    elif len(sys.argv) == 4 and sys.argv[1] == "trace-summary":
+        trace_summary(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 4 and sys.argv[1] == "suite-summary":
+        suite_summary(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 6 and sys.argv[1] == "experiments-summary":
+        experiments_summary(*sys.argv[2:])
+    elif len(sys.argv) == 2 and sys.argv[1] == "claim":
+        claim_variants()
+    elif len(sys.argv) == 2 and sys.argv[1] == "stream":
+        stream_variants()
+    elif len(sys.argv) == 2 and sys.argv[1] == "sizes":
+        sizes()
+    elif len(sys.argv) in (4, 5) and sys.argv[1] == "summarize":
+        summarize(*sys.argv[2:])
+    else:
+        raise SystemExit(__doc__)

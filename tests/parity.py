@@ -67,3 +67,37 @@ def ulp_stats(got_bits, ref_bits) -> dict:
     fin = np.isfinite(r) & np.isfinite(g)
     same = int(np.count_nonzero((got_bits == ref_bits) & fin))
     return {"compared": int(fin.sum()), "bit_equal": same, "frac_bit_equal": same / max(1, int(fin.sum()))}
+
+
+def host_threads() -> int:
+    """Threads for host-side oracle work: the CPUs this process may use, at most 16."""
+    import os
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def assert_parity_rows(got_bits, ref_rows, what: str = "", dtype="bf16", block: int = 512):
+    """Compare every row of ``got_bits`` [M, ...] with the oracle.
+
+    ``ref_rows(lo, hi)`` returns the oracle's output bits for rows [lo, hi).
+    The oracle runs in row blocks (bounded float64 temporaries) on host threads
+    (NumPy releases the GIL inside its array operations); every block is checked
+    with the same elementwise tolerance as assert_parity. Returns the number of
+    outputs compared.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    got_bits = np.asarray(got_bits)
+    m = got_bits.shape[0]
+
+    def one(lo):
+        hi = min(m, lo + block)
+        assert_parity(got_bits[lo:hi], ref_rows(lo, hi), f"{what} rows [{lo}, {hi})", dtype)
+        return got_bits[lo:hi].size
+
+    with ThreadPoolExecutor(host_threads()) as pool:
+        return sum(pool.map(one, range(0, m, block)))

@@ -260,12 +260,9 @@ def test_stream_reference_library_loads_and_validates():
     exports its three entry points and rejects, before any launch, sizes that
     are not whole workgroups, unknown workgroup shapes and misaligned or null
     pointers."""
-    from memory_bound_normalization_amd import build as b
-    from memory_bound_normalization_amd.probe import stream_lib
+    from probe import stream_lib
 
-    if not os.path.exists(b.STREAM_LIB_PATH):
-        b.build_stream()
-    h = stream_lib()
+    h = stream_lib()  # compiled on first use
     assert h.mbn_stream_copy(FAKE, FAKE + (1 << 30), 4096 + 16, 256, 1, None) == 1  # ragged
     assert h.mbn_stream_copy(FAKE, FAKE + (1 << 30), 4096, 256, 3, None) == 1  # no such shape
     assert h.mbn_stream_copy(FAKE + 8, FAKE + (1 << 30), 4096, 256, 1, None) == 1  # misaligned

@@ -1,4 +1,4 @@
-"""CPU tests of the hardware-counter summarizers of memory_bound_normalization_amd.probe.
+"""CPU tests of the hardware-counter summarizers of probe.py (the measurement tools next to bench.py).
 
 The summarizers turn rocprofv3 counter CSV files into bytes per launch, with a
 device copy of known size as the calibration. These tests feed them small
@@ -11,7 +11,7 @@ import os
 
 import pytest
 
-from memory_bound_normalization_amd import probe
+import probe
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 
@@ -60,3 +60,41 @@ def test_default_copy_filter_keeps_torch_copies(tmp_path):
 def test_qk_algorithmic_bytes():
     T = probe.QK_TOKENS
     assert probe.qk_algorithmic_bytes() == 2 * T * 40 * 128 * 2 + 512 + 8 * T == 1342702080
+
+
+def test_timing_events_bind_without_a_gpu():
+    """bench.py's timing events bind the HIP runtime's event calls (no call is
+    made until an event is created)."""
+
+    class _Stream:
+        cuda_stream = 0
+
+    t = probe.HipTimingEvents(_Stream())
+    assert t.events == [] and t.hip.hipEventRecord is not None
+
+
+def test_timeline_metrics_on_a_synthetic_schedule():
+    """Workgroups started every 0.1 us, landing 5 us and finishing 10 us
+    later, on 8 XCDs round robin: the steady rate is one workgroup's bytes per
+    0.1 us, the overhead one workgroup lifetime, the XCD finish spread 0.7 us."""
+    import numpy as np
+
+    n, per_wg = 800, 65536 * 2
+    rec = np.zeros((n, 8), dtype=np.uint64)
+    for i in range(n):
+        s = 1000 + 10 * i  # ticks of 10 ns
+        rec[i] = [s, s + 500, s + 990, s + 1000, i % 8, 0, i, probe.TL_MAGIC]
+    rec[5, 7] = 0  # a record that was not written is ignored ...
+    m = probe.timeline_metrics(rec, (n - 1) * per_wg)
+    assert m["blocks"] == n - 1
+    rec[5, 7] = probe.TL_MAGIC
+    m = probe.timeline_metrics(rec, n * per_wg)
+    assert m["blocks"] == n
+    assert m["steady_GBps"] == pytest.approx(per_wg / 0.1 / 1e3, rel=1e-3)
+    assert m["ideal_us_at_steady"] == pytest.approx(80.0, rel=1e-3)
+    assert m["span_us"] == pytest.approx(89.9)
+    assert m["overhead_us"] == pytest.approx(9.9, abs=0.05)
+    assert m["xcd_end_spread_us"] == pytest.approx(0.7)
+    assert m["xcd_blocks"] == {k: 100 for k in range(8)}
+    assert m["max_resident_wgs"] == 101
+    assert m["wg_land_us_median"] == pytest.approx(5.0) and m["wg_store_us_median"] == pytest.approx(5.0)
