@@ -1137,6 +1137,27 @@ def claim_variants(rounds: int = 4, launches: int = 50) -> None:
         print(json.dumps({"kernel": k if isinstance(k, str) else {"ndyn": k[0], "nclaim": k[1]},
                           "median_us": round(med, 2), "mean_us": round(float(np.mean(res[k])), 2),
                           "pct_median": round(100 * nb / med / 1e3 / 8000, 2)}), flush=True)
+    # XCD finish times without and with the claimed tail (timeline records: a
+    # claiming workgroup's record is that of the last block it served)
+    rmax = tl.mbn_tl_max_blocks()
+    for k in ("variant0", (2048, 512)):
+        for rep in range(4):
+            for _ in range(240):
+                mbn.rmsnorm_fwd(x, w, y, eps=1e-6)
+            torch.cuda.synchronize()
+            tl.mbn_tl_clear(rmax)
+            fn_of(k)()
+            torch.cuda.synchronize()
+            rec = np.zeros((rmax, 8), dtype=np.uint64)
+            tl.mbn_tl_fetch(rec.ctypes.data, rmax)
+            rec = rec[rec[:, 7] == TL_MAGIC].astype(np.float64)
+            t0 = rec[:, 0].min()
+            done = (rec[:, 3] - t0) / TICKS_PER_US
+            xcc = rec[:, 4].astype(np.int64) & 0xF
+            ends = [float(done[xcc == c].max()) for c in range(8)]
+            print(json.dumps({"xcd_ends": k if isinstance(k, str) else {"ndyn": k[0], "nclaim": k[1]}, "rep": rep,
+                              "span_us": round(max(ends), 2), "xcd_end_us": [round(e, 2) for e in ends],
+                              "spread_us": round(max(ends) - min(ends), 2)}), flush=True)
 
 
 def _short_kernel(n: str) -> str:
@@ -1280,6 +1301,12 @@ def experiments_summary(sizes_log: str, variants_log: str, claim_log: str, strea
     print("counter by nclaim workgroups dispatched after the static ones; event median of 200 launches):")
     for r in lines(claim_log):
         if "check" in r:
+            continue
+        if "xcd_ends" in r:
+            k = r["xcd_ends"]
+            name = k if isinstance(k, str) else f"ndyn {k['ndyn']}, nclaim {k['nclaim']}"
+            print(f"  traced {name:<21} span {r['span_us']:7.2f} us  XCD finish spread {r['spread_us']:5.2f} us  "
+                  f"(" + " ".join(f"{e:.1f}" for e in r["xcd_end_us"]) + ")")
             continue
         k = r["kernel"]
         name = k if isinstance(k, str) else f"ndyn {k['ndyn']}, nclaim {k['nclaim']}"
