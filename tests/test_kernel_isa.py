@@ -41,7 +41,12 @@ def _disassemble(tmp_path):
     if not os.path.exists(mbn_build.LIB_PATH):
         mbn_build.build()
     fat = tmp_path / "fatbin.bin"
-    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", mbn_build.LIB_PATH], check=True)
+    # objcopy rewrites the file it reads when given no output file: work on a
+    # copy, and write the copy's result to another scratch file
+    lib = tmp_path / "libmbn_copy.so"
+    shutil.copyfile(mbn_build.LIB_PATH, lib)
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", str(lib), str(tmp_path / "stripped.so")],
+                   check=True)
     data = fat.read_bytes()
     starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
     text = []
