@@ -38,13 +38,17 @@ QK_WORKLOAD = "qk_256"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_16384x16384_hbm_traffic.txt")
 def measured_traffic(algorithmic_bytes: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
+    when there is none, it covers another workload, or the kernel source changed
+    since it was taken."""
     if not os.path.exists(PMC_SUMMARY):
         return None
     text = open(PMC_SUMMARY).read()
     src = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
     tot = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not tot or src.group(1) != kernel_source_hash():
+    algo = re.search(r"algorithmic_bytes_per_launch:\s*(\d+)", text)
+    if not src or not tot or not algo or src.group(1) != kernel_source_hash():
+        return None
+    if int(algo.group(1)) != algorithmic_bytes:
         return None
     return float(tot.group(1))
 

@@ -782,7 +782,7 @@ def timeline_summary(d: str) -> None:
             print(f"    {bins[i]:6.1f}-{bins[i + 1]:6.1f} us  {rd[i]:7.0f} + {wr[i]:7.0f} = {tot:7.0f}  {100 * tot / 8000:5.1f}%")
 
 
-def sizes(out: str | None = None) -> None:
+def sizes() -> None:
     """Kernel time against size at N = 16384: the library's rmsnorm_fwd and the
     4 KiB-per-workgroup streaming copy of the same bytes, M = 8192 ... 131072
     (event mean of 100 launches after 50), and a least-squares line per kernel:
