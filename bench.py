@@ -500,6 +500,9 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_calibration": "FETCH_SIZE and WRITE_SIZE per launch, each scaled by the same counter's "
+                                   "reading for a plain 512 MiB device copy (copy-relative, not absolute); "
+                                   "profiles/rmsnorm_16384x16384_hbm_traffic.txt",
             "kernel": "rmsnorm_fwd",
             "algorithmic_bytes_per_launch": rms_bytes,
             "mean_us": round(rms_mean_s * 1e6, 2),
