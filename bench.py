@@ -400,7 +400,7 @@ def main() -> int:
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(
             "bench.py measures one GPU only: the kernels run on one MI355X's share of the "
-            "rows; multi-GPU runs are not part of this build.",
+            "rows; multi-GPU runs are not supported.",
             file=sys.stderr,
         )
         return 2

@@ -659,7 +659,7 @@ def _timeline_total(name: str) -> int:
 TIMELINE_SHAPES = [(16384, 16384), (8192, 8192), (4096, 32768)]
 
 
-def timeline(out_dir: str = "gpurun_out/timeline", launches: int = 4) -> None:
+def timeline(out_dir: str = "probe_out/timeline", launches: int = 4) -> None:
     """Per-workgroup timelines of rmsnorm_fwd (the library's kernel with its
     marks compiled in) at x[16384, 16384], x[8192, 8192] and x[4096, 32768],
     and of the streaming copy of 512 MiB (4 KiB and 32 KiB per workgroup).
@@ -857,7 +857,7 @@ VARIANTS = {
 }
 
 
-def variants(out_dir: str = "gpurun_out/variants", rounds: int = 3, launches: int = 60) -> None:
+def variants(out_dir: str = "probe_out/variants", rounds: int = 3, launches: int = 60) -> None:
     """Geometry variants of the library's one-shot RMSNorm kernel (timeline
     marks compiled in) at x[16384, 16384] (variants 0-9) and x[4096, 32768]
     (10-15): event median over `launches` launches per round, rounds
