@@ -1166,7 +1166,7 @@ def _short_kernel(n: str) -> str:
     return n.replace("(mbn::Norm)", "").replace("mbn::Bf16, ", "").replace("mbn::", "")
 
 
-def trace_summary(d: str, bench_json: str, timed: int = 200) -> None:
+def trace_summary(d: str, bench_json: str) -> None:
     """The headline kernel-trace summary: rocprofv3 --kernel-trace --stats of
     `python -u bench.py --no-cpu-baseline` (files in d), beside that run's JSON
     line (bench_json: a file holding it)."""
@@ -1176,8 +1176,8 @@ def trace_summary(d: str, bench_json: str, timed: int = 200) -> None:
     rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
     stats = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
     rms = sorted((r for r in rows if "rownorm_kernel" in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
-    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rms][-timed:]
     b = [json.loads(line) for line in open(bench_json) if line.startswith("{")][-1]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rms][-b["steps"]:]
     algo = b["roofline"]["algorithmic_bytes_per_launch"]
     r0 = rms[0]
     title = "rmsnorm_fwd, x[16384, 16384] bf16 -> y (bench workload), MI355X (gfx950), one GPU"
@@ -1186,8 +1186,9 @@ def trace_summary(d: str, bench_json: str, timed: int = 200) -> None:
     print()
     print("Commands (from the repository root, TMPDIR=/tmp):")
     print(f"  rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- \\")
-    print(f"      python -u bench.py --no-cpu-baseline > {bench_json}")
-    print(f"      (defaults: {b['warmup']} warm-up + {b['steps']} timed steps)")
+    extra = "" if (b["warmup"], b["steps"]) == (2000, 200) else f" --steps {b['steps']} --warmup {b['warmup']}"
+    print(f"      python -u bench.py --no-cpu-baseline{extra} > {bench_json}")
+    print(f"      ({b['warmup']} warm-up + {b['steps']} timed steps)")
     print(f"  python probe.py trace-summary {d} {bench_json}")
     print()
     print(f"Kernel statistics (run_kernel_stats.csv, every dispatch of the run, warm-up included):")
