@@ -42,7 +42,23 @@ at per-workgroup footprints of 4 to 64 KiB), each over two alternating buffer
 sets (1 GiB apart, so nothing is served from the 256 MiB Infinity Cache);
 `ceiling-summary` turns the kernel trace into GB/s per kernel. It measures what
 the memory system gives a pure-read, a pure-write and a 50/50 read/write stream
-on this part, the reference for the RMSNorm kernel's fraction of peak.
+on this part, the reference for the RMSNorm kernel's fraction of peak. The
+copies are also timed with other cache policies on their stores (nt sc1, sc1,
+sc0 sc1).
+
+    python probe.py store-policy > <log>
+    python probe.py store-policy-summary <log>
+
+`store-policy` times the library's RMSNorm on x[16384, 16384] against the same
+kernel compiled with those store policies on its output stores
+(probe_csrc/store_policy.hip, built on first use), after checking that every
+variant's output equals the library's bit for bit.
+
+The other commands, each the source of a committed summary: `timeline`,
+`timeline-summary` (per-workgroup timelines), `variants`, `claim`, `stream`,
+`sizes`, `experiments-summary` (the geometry, claimed-tail, pipelined-kernel
+and size experiments), `trace-summary`, `suite-summary` (kernel-trace
+summaries of the bench commands).
 """
 
 from __future__ import annotations
@@ -220,6 +236,12 @@ CEILING_CASES = [
     ("copy, 32 KiB/WG", 2 * COPY_BYTES, "copy", 256, 8),
     ("copy, 32 KiB/WG (1024 lanes)", 2 * COPY_BYTES, "copy", 1024, 2),
     ("copy, 64 KiB/WG", 2 * COPY_BYTES, "copy", 256, 16),
+    ("copy, 4 KiB/WG, stores nt (inline asm)", 2 * COPY_BYTES, "copy-pol0", 256, 1),
+    ("copy, 4 KiB/WG, stores nt sc1", 2 * COPY_BYTES, "copy-pol1", 256, 1),
+    ("copy, 4 KiB/WG, stores sc1", 2 * COPY_BYTES, "copy-pol2", 256, 1),
+    ("copy, 4 KiB/WG, stores sc0 sc1", 2 * COPY_BYTES, "copy-pol3", 256, 1),
+    ("copy, 32 KiB/WG, stores nt (inline asm)", 2 * COPY_BYTES, "copy-pol0", 256, 8),
+    ("copy, 32 KiB/WG, stores nt sc1", 2 * COPY_BYTES, "copy-pol1", 256, 8),
     ("rmsnorm_fwd", 2 * COPY_BYTES + 2 * 16384, "rmsnorm", 0, 0),
 ]
 
@@ -245,7 +267,8 @@ def stream_lib():
     h.mbn_stream_copy.argtypes = [vp, vp, sz, i32, i32, vp]
     h.mbn_stream_read.argtypes = [vp, vp, sz, i32, i32, vp]
     h.mbn_stream_write.argtypes = [vp, sz, i32, i32, u32, vp]
-    for f in (h.mbn_stream_copy, h.mbn_stream_read, h.mbn_stream_write):
+    h.mbn_stream_copy_policy.argtypes = [vp, vp, sz, i32, i32, vp]
+    for f in (h.mbn_stream_copy, h.mbn_stream_read, h.mbn_stream_write, h.mbn_stream_copy_policy):
         f.restype = i32
     return h
 
@@ -291,13 +314,22 @@ def ceiling() -> None:
             return lambda i: ok(sl.mbn_stream_write(ys[i].data_ptr(), COPY_BYTES, lanes, chunks, 0x3F803F80, sp))
         if kind == "copy":
             return lambda i: ok(sl.mbn_stream_copy(xs[i].data_ptr(), ys[i].data_ptr(), COPY_BYTES, lanes, chunks, sp))
+        if kind.startswith("copy-pol"):
+            pol = int(kind[len("copy-pol"):])
+            return lambda i: ok(sl.mbn_stream_copy_policy(xs[i].data_ptr(), ys[i].data_ptr(), COPY_BYTES, chunks, pol,
+                                                          sp))
         return lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps)
 
-    # the copy kernel copies (checked before the timed cases)
-    ok(sl.mbn_stream_copy(xs[0].data_ptr(), ys[0].data_ptr(), COPY_BYTES, 256, 8, sp))
-    torch.cuda.synchronize()
-    if not torch.equal(ys[0].view(torch.int16), xs[0].view(torch.int16)):
-        raise RuntimeError("stream copy produced a different buffer")
+    # the copy kernels copy (checked before the timed cases)
+    copies = [lambda: ok(sl.mbn_stream_copy(xs[0].data_ptr(), ys[0].data_ptr(), COPY_BYTES, 256, 8, sp))]
+    copies += [lambda c=c, p=p: ok(sl.mbn_stream_copy_policy(xs[0].data_ptr(), ys[0].data_ptr(), COPY_BYTES, c, p, sp))
+               for c in (1, 8) for p in range(4)]
+    for copy in copies:
+        ys[0].zero_()
+        copy()
+        torch.cuda.synchronize()
+        if not torch.equal(ys[0].view(torch.int16), xs[0].view(torch.int16)):
+            raise RuntimeError("stream copy produced a different buffer")
 
     timer = HipTimingEvents(stream)
     for name, nbytes, kind, lanes, chunks in CEILING_CASES:
@@ -345,7 +377,7 @@ def ceiling_summary(d: str) -> None:
         med = d_us[len(d_us) // 2]
         kname = grp[0]["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
         kname = kname.removeprefix("void ")[:60]
-        print(f"{name:<30} {med:9.2f} us {nb / med / 1e3:8.0f} GB/s {nb / med / 1e3 / 80:6.1f}%   {kname}")
+        print(f"{name:<40} {med:9.2f} us {nb / med / 1e3:8.0f} GB/s {nb / med / 1e3 / 80:6.1f}%   {kname}")
 
 
 # The small workloads beside a plain copy of the same bytes: (case, bytes per
@@ -953,6 +985,144 @@ def variants(out_dir: str = "probe_out/variants", rounds: int = 3, launches: int
                           "pct": round(100 * nb / us / 1e3 / 8000, 2), **keep}), flush=True)
 
 
+SP_POLICIES = {0: "nt (inline asm)", 1: "nt sc1", 2: "sc1", 3: "sc0 sc1"}
+
+
+def sp_lib_path(policy: int) -> str:
+    return os.path.join(PROBE_CSRC, f"libmbn_sp{policy}.so")
+
+
+def store_policy_source() -> str:
+    """The library's csrc/rownorm.hip with the one-shot kernel's output store
+    (pass 2 of rownorm_block: the only store_nt_16 of y from there to the end)
+    replaced by MBN_STORE_Y, which probe_csrc/store_policy.hip defines."""
+    with open(os.path.join(ROOT, "memory_bound_normalization_amd", "csrc", "rownorm.hip")) as f:
+        text = f.read()
+    start = text.index("rownorm_block(const RowNormArgs")
+    store = "store_nt_16(yrow + k, o);"
+    if text.count(store, start) != 1:
+        raise RuntimeError("rownorm.hip: expected exactly one output store in rownorm_block and after it")
+    i = text.index(store, start)
+    return text[:i] + "MBN_STORE_Y(yrow + k, o);" + text[i + len(store):]
+
+
+def build_store_policy(verbose: bool = False) -> None:
+    """Compile probe_csrc/store_policy.hip once per store policy (the library's
+    row-norm source with another cache policy on pass 2's stores) into
+    probe_csrc/libmbn_sp<policy>.so; always rebuilds."""
+    sys.path.insert(0, ROOT)
+    from concurrent.futures import ThreadPoolExecutor
+
+    from memory_bound_normalization_amd.build import build
+
+    csrc = os.path.join(ROOT, "memory_bound_normalization_amd", "csrc")
+    gen = os.path.join(PROBE_CSRC, "gen")
+    os.makedirs(gen, exist_ok=True)
+    with open(os.path.join(gen, "rownorm_store_policy.hip"), "w") as f:
+        f.write(store_policy_source())
+    src = [os.path.join(PROBE_CSRC, "store_policy.hip")]
+    with ThreadPoolExecutor(len(SP_POLICIES)) as ex:
+        list(ex.map(lambda p: build(verbose=verbose, out=sp_lib_path(p),
+                                    extra=["-I", gen, "-I", csrc, f"-DMBN_PROBE_POLICY={p}"], sources_=src),
+                    SP_POLICIES))
+
+
+def store_policy(rounds: int = 4, launches: int = 60) -> None:
+    """The library's RMSNorm at x[16384, 16384] against the same kernel with
+    other cache policies on its output stores (libmbn_sp<policy>.so): every
+    output checked bit for bit against the library's, then event medians over
+    `launches` launches per round, rounds interleaved (order reversed every
+    other round), two buffer sets alternating."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import numpy as np
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    if not all(os.path.exists(sp_lib_path(p)) for p in SP_POLICIES):
+        build_store_policy()
+    libs = {}
+    for p in SP_POLICIES:
+        h = ctypes.CDLL(sp_lib_path(p))
+        h.mbn_sp_rmsnorm.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                                             ctypes.c_void_p]
+        h.mbn_sp_rmsnorm.restype = ctypes.c_int
+        libs[p] = h
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(21)
+    M = N = 16384
+    xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(2)]
+    w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    ys = [torch.empty_like(xs[0]) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    nb = 2 * M * N * 2 + 2 * N
+
+    def call(k, i):
+        if k == "library":
+            mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=1e-6)
+            return
+        rc = libs[k].mbn_sp_rmsnorm(xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, N, 1e-6, sp)
+        if rc != 0:
+            raise RuntimeError(f"store policy {k}: status {rc}")
+
+    kinds = ["library", *SP_POLICIES]
+    call("library", 0)
+    torch.cuda.synchronize()
+    ref = ys[0].clone()
+    for k in SP_POLICIES:
+        ys[0].zero_()
+        call(k, 0)
+        torch.cuda.synchronize()
+        if not torch.equal(ys[0].view(torch.int16), ref.view(torch.int16)):
+            raise RuntimeError(f"store policy {k}: output differs from the library's")
+    del ref
+    print(json.dumps({"check": "every policy's output equals the library's bit for bit"}), flush=True)
+    for _ in range(2400):
+        call("library", 0)
+    torch.cuda.synchronize()
+    timer = HipTimingEvents(stream)
+    res = {k: [] for k in kinds}
+    for rnd in range(rounds):
+        for k in (kinds if rnd % 2 == 0 else kinds[::-1]):
+            for i in range(6):
+                call(k, i % 2)
+            torch.cuda.synchronize()
+            ev = [(timer.new(), timer.new()) for _ in range(launches)]
+            for i, (a, b) in enumerate(ev):
+                timer.record(a)
+                call(k, i % 2)
+                timer.record(b)
+            torch.cuda.synchronize()
+            res[k].append(float(np.median([timer.elapsed_ms(a, b) * 1e3 for a, b in ev])))
+            timer.close()
+        print(f"round {rnd} done", flush=True)
+    for k in kinds:
+        us = float(np.median(res[k]))
+        print(json.dumps({"kernel": k if k == "library" else f"policy {k}",
+                          "stores": "nt (compiler)" if k == "library" else SP_POLICIES[k],
+                          "median_us": round(us, 2), "pct": round(100 * nb / us / 1e3 / 8000, 2),
+                          "rounds_us": [round(t, 2) for t in res[k]]}), flush=True)
+
+
+def store_policy_summary(log: str) -> None:
+    import json
+
+    rows = [json.loads(x) for x in open(log) if x.startswith("{")]
+    print("RMSNorm x[16384, 16384], the library's kernel with other cache policies on its output stores")
+    print("(event medians; per round: median of 60 launches; reported: median of the round medians):")
+    print(f"  {'kernel':<12} {'stores':<18} {'median_us':>9} {'% of 8 TB/s':>12}  rounds")
+    for r in rows:
+        if "check" in r:
+            continue
+        print(f"  {r['kernel']:<12} {r['stores']:<18} {r['median_us']:>9.2f} {r['pct']:>12.2f}  "
+              + " ".join(f"{t:.1f}" for t in r["rounds_us"]))
+    if any("check" in r for r in rows):
+        print("  every policy's output equals the library's bit for bit")
+
+
 STREAM_VARIANTS = {
     0: (16384, "128 lanes/row, 2 buffers, 2 WGs/CU"),
     1: (16384, "256 lanes/row, 2 buffers, 2 WGs/CU"),
@@ -1355,6 +1525,10 @@ if __name__ == "__main__":
         stream_variants()
     elif len(sys.argv) == 2 and sys.argv[1] == "sizes":
         sizes()
+    elif len(sys.argv) == 2 and sys.argv[1] == "store-policy":
+        store_policy()
+    elif len(sys.argv) == 3 and sys.argv[1] == "store-policy-summary":
+        store_policy_summary(sys.argv[2])
     elif len(sys.argv) in (4, 5) and sys.argv[1] == "summarize":
         summarize(*sys.argv[2:])
     else:

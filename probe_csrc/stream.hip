@@ -46,6 +46,40 @@ __global__ void __launch_bounds__(LANES) stream_write(u32x4* __restrict__ dst, u
   for (int j = 0; j < CHUNKS; ++j) __builtin_nontemporal_store(v, dst + base + (size_t)j * LANES + threadIdx.x);
 }
 
+// Copy whose 16-byte stores carry a chosen cache policy: global_store_dwordx4
+// with the nt / sc0 / sc1 bits of POL (0: nt, 1: nt sc1, 2: sc1, 3: sc0 sc1),
+// 256 lanes and CHUNKS chunks per lane. The loads are the compiler's (so its
+// waits cover the stores' data operands); the stores are inline assembly, each
+// followed by two wait states: on gfx950 a VALU instruction may overwrite the
+// data registers of a store wider than 8 bytes only two wait states after it
+// (the compiler inserts them after its own stores, not after inline assembly).
+template <int CHUNKS, int POL>
+__global__ void __launch_bounds__(256) stream_copy_policy(const u32x4* __restrict__ src, u32x4* __restrict__ dst) {
+  const size_t base = (size_t)blockIdx.x * 256 * CHUNKS;
+  u32x4 v[CHUNKS];
+#pragma unroll
+  for (int j = 0; j < CHUNKS; ++j) v[j] = __builtin_nontemporal_load(src + base + (size_t)j * 256 + threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < CHUNKS; ++j) {
+    u32x4* p = dst + base + (size_t)j * 256 + threadIdx.x;
+    if constexpr (POL == 0) {
+      __asm__ __volatile__("global_store_dwordx4 %0, %1, off nt\n\ts_nop 1" ::"v"(p), "v"(v[j]) : "memory");
+    } else if constexpr (POL == 1) {
+      __asm__ __volatile__("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" ::"v"(p), "v"(v[j]) : "memory");
+    } else if constexpr (POL == 2) {
+      __asm__ __volatile__("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v[j]) : "memory");
+    } else {
+      __asm__ __volatile__("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(p), "v"(v[j]) : "memory");
+    }
+  }
+}
+
+typedef void (*PolicyCopy)(const u32x4*, u32x4*);
+const PolicyCopy kPolicyCopies[2][4] = {
+    {&stream_copy_policy<1, 0>, &stream_copy_policy<1, 1>, &stream_copy_policy<1, 2>, &stream_copy_policy<1, 3>},
+    {&stream_copy_policy<8, 0>, &stream_copy_policy<8, 1>, &stream_copy_policy<8, 2>, &stream_copy_policy<8, 3>},
+};
+
 struct Shape {
   int lanes, chunks;
   void (*copy)(const u32x4*, u32x4*);
@@ -90,6 +124,20 @@ __attribute__((visibility("default"))) int mbn_stream_copy(const void* src, void
   if (rc) return rc;
   const size_t grid = bytes / ((size_t)lanes * chunks * 16);
   hipLaunchKernelGGL(s->copy, dim3((unsigned)grid), dim3(lanes), 0, (hipStream_t)stream,
+                     (const u32x4*)src, (u32x4*)dst);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// The store-policy copy (stream_copy_policy): chunks 1 or 8 per lane of 256
+// lanes, policy 0-3 as listed there.
+__attribute__((visibility("default"))) int mbn_stream_copy_policy(const void* src, void* dst, size_t bytes,
+                                                                  int chunks, int policy, void* stream) {
+  const Shape* s;
+  int rc = check(src, bytes, 256, chunks, &s);
+  if (rc == 0) rc = check(dst, bytes, 256, chunks, &s);
+  if (rc || (chunks != 1 && chunks != 8) || policy < 0 || policy > 3) return rc ? rc : 1;
+  const size_t grid = bytes / ((size_t)256 * chunks * 16);
+  hipLaunchKernelGGL(kPolicyCopies[chunks == 8][policy], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4*)src, (u32x4*)dst);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }

@@ -269,6 +269,9 @@ def test_stream_reference_library_loads_and_validates():
     assert h.mbn_stream_copy(FAKE, 0, 4096, 256, 1, None) == 1  # null
     assert h.mbn_stream_read(FAKE, 0, 4096, 256, 1, None) == 1  # null sink
     assert h.mbn_stream_write(FAKE, 0, 256, 1, 0, None) == 1  # empty
+    assert h.mbn_stream_copy_policy(FAKE, FAKE + (1 << 30), 4096, 1, 4, None) == 1  # no such policy
+    assert h.mbn_stream_copy_policy(FAKE, FAKE + (1 << 30), 4096, 2, 1, None) == 1  # no such shape
+    assert h.mbn_stream_copy_policy(FAKE, FAKE + (1 << 30), 4096 + 16, 1, 1, None) == 1  # ragged
 
 
 def test_c_client_builds_and_sees_host_validation():

@@ -98,3 +98,52 @@ def test_timeline_metrics_on_a_synthetic_schedule():
     assert m["xcd_blocks"] == {k: 100 for k in range(8)}
     assert m["max_resident_wgs"] == 101
     assert m["wg_land_us_median"] == pytest.approx(5.0) and m["wg_store_us_median"] == pytest.approx(5.0)
+
+
+def test_store_policy_source_replaces_only_the_one_shot_output_store():
+    src = probe.store_policy_source()
+    with open(os.path.join(probe.ROOT, "memory_bound_normalization_amd", "csrc", "rownorm.hip")) as f:
+        lib = f.read()
+    assert src.count("MBN_STORE_Y(yrow + k, o);") == 1
+    assert src.replace("MBN_STORE_Y(yrow + k, o);", "store_nt_16(yrow + k, o);") == lib
+    # the replaced store is pass 2 of the one-shot body, not the persistent kernel's
+    assert src.index("MBN_STORE_Y") > src.index("rownorm_block(const RowNormArgs")
+
+
+def test_ceiling_summary_groups_dispatches_per_case(tmp_path, capsys):
+    d = tmp_path / "trace"
+    d.mkdir()
+    per = 3 + probe.CEIL_REPS
+    rows, t = [], 0
+    # a short set-up dispatch, then per case: 3 warm-up + CEIL_REPS timed launches
+    for k in range(len(probe.CEILING_CASES)):
+        for j in range(per):
+            dur = 100_000 + 1000 * k + (50_000 if j < 3 else 0)  # warm-ups slower, excluded
+            rows.append({"Kernel_Name": f"void k{k}(int)", "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 10
+    rows.insert(0, {"Kernel_Name": "setup", "Start_Timestamp": -5000, "End_Timestamp": -4000})
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    probe.ceiling_summary(str(d))
+    out = capsys.readouterr().out.strip().split("\n")
+    assert len(out) == len(probe.CEILING_CASES)
+    for k, (line, (name, nb, *_)) in enumerate(zip(out, probe.CEILING_CASES)):
+        assert line.startswith(name) and f"k{k}" in line
+        us = (100_000 + 1000 * k) / 1e3
+        assert f"{us:9.2f} us" in line
+
+
+def test_store_policy_summary_table(tmp_path, capsys):
+    log = tmp_path / "sp.log"
+    log.write_text(
+        '{"check": "every policy\'s output equals the library\'s bit for bit"}\n'
+        "round 0 done\n"
+        '{"kernel": "library", "stores": "nt (compiler)", "median_us": 164.7, "pct": 81.49, "rounds_us": [165.1, 164.4]}\n'
+        '{"kernel": "policy 1", "stores": "nt sc1", "median_us": 165.2, "pct": 81.26, "rounds_us": [164.9, 165.3]}\n')
+    probe.store_policy_summary(str(log))
+    out = capsys.readouterr().out
+    assert "library      nt (compiler)         164.70        81.49  165.1 164.4" in out
+    assert "policy 1     nt sc1                165.20        81.26  164.9 165.3" in out
+    assert "bit for bit" in out
