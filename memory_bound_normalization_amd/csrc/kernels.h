@@ -66,6 +66,7 @@ int rownorm_any_group(const RowNormAnyArgs& args);
 
 // Dynamic LDS bytes a row-norm launch requests (exposed for tuning tools).
 size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu);
+size_t rownorm_regs_lds_bytes(int wgs_per_cu);
 
 // rotary_dim: a multiple of 16 in [16, 128]; 128 is the full-rotary case.
 hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const void* k_w,

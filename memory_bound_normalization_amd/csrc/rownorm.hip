@@ -533,6 +533,137 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
   rownorm_block<MODE, DT, WPR, ROWS, RPL, MAXC, FULL, CHUNK_WAIT>(a, xcd_remap(blockIdx.x, gridDim.x, a.xcd_group));
 }
 
+// Register-resident rows: the same one-shot method with each lane's chunks of
+// the row held in VGPRs instead of LDS ("[Inductor] Codegen Gluon", section 2
+// and 3.1 keep the reused row in on-chip memory; here that memory is the
+// register file). Each row is still read from HBM once, with the same 16-byte
+// non-temporal loads and the same lane-to-chunk mapping, kept narrow (packed
+// 16-bit) in the registers and widened where it is computed on; both passes
+// read those registers, so only the cross-wave partial sums use LDS (a small
+// static array). The compiler's waits take each chunk as it lands (loads
+// complete in issue order). The launch tables use it for the widths where it
+// measured faster on MI355X: no LDS staging means no LDS write and two fewer
+// LDS reads per chunk on each workgroup's critical path, at the same number of
+// rows in flight (waves or VGPRs, not LDS, bound the residency there).
+// Arithmetic, order and rounding are those of rownorm_block, so a row gives
+// the same output bits through either kernel at the same WPR.
+template <Norm MODE, typename DT, int WPR, int ROWS, int MAXC, bool FULL>
+__global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_regs_kernel(RowNormArgs a) {
+  constexpr int TPR = 64 * WPR;  // lanes per row
+  constexpr bool kHasW = Regs<MODE>::kHasW;
+  constexpr bool kHasB = Regs<MODE>::kHasB;
+  constexpr bool kHasR = Regs<MODE>::kHasR;
+  __shared__ float part[ROWS][2][WPR];  // [row slot][reduction][wave]
+
+  const int nchunk = a.nchunk;
+  const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x / TPR);  // TPR is whole waves
+  const int t = threadIdx.x - slot * TPR;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t row = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group) * ROWS + slot;
+  const bool live = row < a.M;
+  const int64_t base = row * nchunk;
+
+  // The row (and residual) chunks first (HBM), then weight and bias (L2 hits).
+  u32x4 xv[MAXC], rv[kHasR ? MAXC : 1];
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * TPR + t;
+    const bool in = live && (FULL || k < nchunk);
+    xv[j] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x) + base + k)
+               : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kHasR)
+      rv[j] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r) + base + k)
+                 : u32x4{0u, 0u, 0u, 0u};
+  }
+  u32x4 wreg[kHasW ? MAXC : 1], breg[kHasB ? MAXC : 1];
+  load_affine<MODE, WPR, MAXC, FULL>(a, t, wreg, breg);
+
+  // Pass 1: sum of squares (LayerNorm: sum). The residual add forms
+  // h = round(x + r), stores it and continues with h.
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * TPR + t;
+    if constexpr (kHasR) {
+      u32x4 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hv[e] = DT::pack(DT::lo(xv[j][e]) + DT::lo(rv[j][e]), DT::hi(xv[j][e]) + DT::hi(rv[j][e]));
+      xv[j] = hv;
+      if (live && (FULL || k < nchunk)) store_nt_16(reinterpret_cast<u32x4*>(a.h) + base + k, hv);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = DT::lo(xv[j][e]);
+      const float q = DT::hi(xv[j][e]);
+      if constexpr (MODE == Norm::kLayer) {
+        acc0 += p;
+        acc1 += q;
+      } else {
+        acc0 = __builtin_fmaf(p, p, acc0);
+        acc1 = __builtin_fmaf(q, q, acc1);
+      }
+    }
+  }
+  float s1[1] = {acc0 + acc1};
+  rows_sum<WPR, 1>(s1, nullptr, &part[slot][0][0], nchunk, t, wave, 0);
+
+  float mu = 0.f, scale;
+  if constexpr (MODE == Norm::kLayer) {
+    // Pass 1b: centred second moment.
+    mu = s1[0] * a.inv_n;
+    float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * TPR + t;
+      if (FULL || k < nchunk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = DT::lo(xv[j][e]) - mu;
+          const float q = DT::hi(xv[j][e]) - mu;
+          c0 = __builtin_fmaf(p, p, c0);
+          c1 = __builtin_fmaf(q, q, c1);
+        }
+      }
+    }
+    float s2[1] = {c0 + c1};
+    rows_sum<WPR, 1>(s2, nullptr, &part[slot][0][0], nchunk, t, wave, 1);
+    scale = __builtin_amdgcn_rsqf(s2[0] * a.inv_n + a.eps);
+  } else if constexpr (MODE == Norm::kL2) {
+    const float nrm = __builtin_sqrtf(s1[0]);
+    scale = 1.0f / ((nrm < a.eps) ? a.eps : nrm);  // NaN norms stay NaN
+  } else {
+    scale = __builtin_amdgcn_rsqf(__builtin_fmaf(s1[0], a.inv_n, a.eps));
+  }
+
+  // Pass 2: normalize, weight, round, streaming stores.
+  if (!live) return;
+  u32x4* yrow = reinterpret_cast<u32x4*>(a.y) + base;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int k = j * TPR + t;
+    if (FULL || k < nchunk) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p = DT::lo(xv[j][e]), q = DT::hi(xv[j][e]);
+        if constexpr (MODE == Norm::kLayer) {
+          p = __builtin_fmaf((p - mu) * scale, DT::lo(wreg[j][e]), DT::lo(breg[j][e]));
+          q = __builtin_fmaf((q - mu) * scale, DT::hi(wreg[j][e]), DT::hi(breg[j][e]));
+        } else if constexpr (MODE == Norm::kL2) {
+          p *= scale;
+          q *= scale;
+        } else {
+          p = (p * scale) * DT::lo(wreg[j][e]);
+          q = (q * scale) * DT::hi(wreg[j][e]);
+        }
+        o[e] = DT::pack(p, q);
+      }
+      store_nt_16(yrow + k, o);
+    }
+  }
+}
+
 // Persistent kernel ("[Inductor] Codegen Gluon", section 3.3: copies of the
 // next tile in flight while the current one is computed): a grid of at most
 // a few workgroups per CU, each looping over row sets g, g + G, g + 2G, ...
@@ -588,6 +719,7 @@ struct RowNormCfg {
   RowNormKernel ragged[2];   // any width up to max_nchunk; [bf16, fp16]
   RowNormKernel full[2];     // width exactly full_nchunk; [bf16, fp16]
   RowNormKernel full_cw[2];  // the same with per-chunk waits in pass 1 (_W entries), else null
+  bool regs;                 // register-resident rows (rownorm_regs_kernel, _R entries)
 };
 
 // A grid of at least this many workgroups (four per CU) takes the per-chunk
@@ -609,7 +741,8 @@ constexpr RowNormKernel chunk_wait_kernel() {
         {&rownorm_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, true>,                     \
          &rownorm_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, true>},                     \
         {chunk_wait_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, CW>(),                   \
-         chunk_wait_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, CW>()}                    \
+         chunk_wait_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, CW>()},                   \
+        false                                                                         \
   }
 // serves every width up to 64 * WPR * MAXC chunks (down to the previous entry)
 #define MBN_CFG(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
@@ -641,6 +774,20 @@ constexpr RowNormKernel chunk_wait_kernel() {
   MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
 #define MBN_CFG_UPTO_W(MODE, MAXN, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
   MBN_CFG_(MODE, (MAXN) / 8, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
+
+// The _R form: an exact-width entry with register-resident rows
+// (rownorm_regs_kernel: one row per lane set, RPL = 1, no LDS staging; CAP
+// still caps the resident workgroups per CU through the dynamic LDS request).
+// Only exact widths: at widths below a kernel's capacity it measured 10-12%
+// slower than the staged kernel.
+#define MBN_CFG_EXACT_R(MODE, WPR, ROWS, MAXC, CAP, GROUP)                             \
+  RowNormCfg {                                                                       \
+    64 * (WPR) * (MAXC), 64 * (WPR) * (MAXC), true, 0, WPR, ROWS, 1, MAXC, CAP, GROUP, \
+        {nullptr, nullptr},                                                          \
+        {&rownorm_regs_kernel<MODE, Bf16, WPR, ROWS, MAXC, true>,                    \
+         &rownorm_regs_kernel<MODE, F16, WPR, ROWS, MAXC, true>},                    \
+        {nullptr, nullptr}, true                                                     \
+  }
 
 // Per-width launch tables, narrowest first: the first entry that serves the
 // row width is used. Every entry with WPR > 1 serves only widths of at least
@@ -698,8 +845,10 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_UPTO_W(Norm::kRms, 12288, 12, 1, 2, 2, 0, 0),  // 8192 < N <= 12288: 768 threads x 2 rows
     MBN_CFG_UPTO(Norm::kRms, 15360, 16, 1, 2, 2, 0, 0),  // 12288 < N <= 15360: 1024 threads x 2 rows
     MBN_CFG_W(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
+    MBN_CFG_EXACT_R(Norm::kRms, 16, 1, 4, 4, 4),  // N == 32768: 1024 threads, rows in VGPRs
     MBN_CFG_UPTO(Norm::kRms, 19456, 8, 1, 1, 5, 3, 0),  // 16384 < N <= 19456: 512 threads
     MBN_CFG_W(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N <= 32768: 1024 threads
+    MBN_CFG_EXACT_R(Norm::kRms, 8, 1, 16, 4, 4),  // N == 65536: 512 threads, rows in VGPRs
     MBN_CFG_W(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N <= 65536: 1024 threads
 };
 const RowNormCfg kAddRmsTable[] = {
@@ -864,6 +1013,14 @@ size_t rownorm_lds_bytes(int rows, int64_t N, int wgs_per_cu) {
   return lds;
 }
 
+// Dynamic LDS of a register-resident launch: none, or enough to hold the
+// resident workgroups per CU to the cap (kLdsPerCU / cap, less room for the
+// kernel's static partial sums, at most 512 bytes).
+size_t rownorm_regs_lds_bytes(int wgs_per_cu) {
+  if (wgs_per_cu <= 0) return 0;
+  return ((kLdsPerCU / (size_t)wgs_per_cu) & ~(size_t)511) - 1024;
+}
+
 hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_t stream,
                           RowNormPath path, int grid) {
   const int nchunk = args.nchunk;
@@ -904,12 +1061,14 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
   if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant
   const int rows_per_wg = cfg->rows * cfg->rpl;
   const int threads = 64 * cfg->wpr * cfg->rows;
-  const size_t lds = rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
+  const size_t lds = cfg->regs ? rownorm_regs_lds_bytes(cfg->wgs_per_cu)
+                                : rownorm_lds_bytes(rows_per_wg, N, cfg->wgs_per_cu);
   if (nchunk > cfg->full_nchunk) return hipErrorInvalidValue;  // table invariant
   const int64_t all_blocks = (args.M + rows_per_wg - 1) / rows_per_wg;
   const RowNormKernel kernel = nchunk != cfg->full_nchunk ? cfg->ragged[d]
                                : cfg->full_cw[d] && all_blocks >= kChunkWaitMinBlocks ? cfg->full_cw[d]
                                                                                       : cfg->full[d];
+  if (!kernel) return hipErrorInvalidValue;  // table invariant (exact _R entries have no ragged kernel)
   args.xcd_group = cfg->xcd_group;
   // One dispatch covers at most kMaxWorkItems work-items: larger launches run
   // as several launches over consecutive row ranges (rows are independent).

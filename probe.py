@@ -54,6 +54,13 @@ kernel compiled with those store policies on its output stores
 (probe_csrc/store_policy.hip, built on first use), after checking that every
 variant's output equals the library's bit for bit.
 
+    python probe.py staging > <log>
+    python probe.py staging-summary <log>
+
+`staging` times rmsnorm_fwd where its launch tables hold each lane's chunks
+of the row in VGPRs (N = 32768 and 65536) against the staged-row (LDS) kernel
+those widths used before (probe_csrc/lds_rows.hip), on the same data.
+
 The other commands, each the source of a committed summary: `timeline`,
 `timeline-summary` (per-workgroup timelines), `variants`, `claim`, `stream`,
 `sizes`, `experiments-summary` (the geometry, claimed-tail, pipelined-kernel
@@ -487,11 +494,16 @@ def _rows(d: str):
     return out
 
 
-def _per_kernel(d: str, counter: str, kernel: str = "rownorm_kernel", copy: str | None = None):
+# The one-shot row-norm kernels (staged rows, rows in VGPRs) by name.
+ROW_KERNELS = ("rownorm_kernel", "rownorm_regs_kernel")
+
+
+def _per_kernel(d: str, counter: str, kernel: str | tuple = ROW_KERNELS, copy: str | None = None):
     """{'rmsnorm': [values...], 'copy': [values...]} for one counter (summed over
-    its instances); 'rmsnorm' holds the kernels whose name contains `kernel`,
-    'copy' those whose name contains `copy` (default: torch's copy or
-    elementwise kernels)."""
+    its instances); 'rmsnorm' holds the kernels whose name contains `kernel`
+    (or one of them), 'copy' those whose name contains `copy` (default: torch's
+    copy or elementwise kernels)."""
+    kernels = (kernel,) if isinstance(kernel, str) else kernel
     acc = {}
     for r in _rows(d):
         if r.get("Counter_Name") != counter:
@@ -500,7 +512,7 @@ def _per_kernel(d: str, counter: str, kernel: str = "rownorm_kernel", copy: str 
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
     res = {"rmsnorm": [], "copy": []}
     for (_, name), v in sorted(acc.items(), key=lambda kv: int(kv[0][0])):
-        if kernel in name:
+        if any(k in name for k in kernels):
             res["rmsnorm"].append(v)
         elif (copy in name) if copy else ("copy" in name.lower() or "elementwise" in name.lower()):
             res["copy"].append(v)
@@ -994,15 +1006,16 @@ def sp_lib_path(policy: int) -> str:
 
 def store_policy_source() -> str:
     """The library's csrc/rownorm.hip with the one-shot kernel's output store
-    (pass 2 of rownorm_block: the only store_nt_16 of y from there to the end)
-    replaced by MBN_STORE_Y, which probe_csrc/store_policy.hip defines."""
+    (pass 2 of rownorm_block: its only store_nt_16 of y) replaced by
+    MBN_STORE_Y, which probe_csrc/store_policy.hip defines."""
     with open(os.path.join(ROOT, "memory_bound_normalization_amd", "csrc", "rownorm.hip")) as f:
         text = f.read()
     start = text.index("rownorm_block(const RowNormArgs")
+    end = text.index(") rownorm_kernel(RowNormArgs a)", start)  # the body ends before the kernel that calls it
     store = "store_nt_16(yrow + k, o);"
-    if text.count(store, start) != 1:
-        raise RuntimeError("rownorm.hip: expected exactly one output store in rownorm_block and after it")
-    i = text.index(store, start)
+    if text.count(store, start, end) != 1:
+        raise RuntimeError("rownorm.hip: expected exactly one output store in rownorm_block")
+    i = text.index(store, start, end)
     return text[:i] + "MBN_STORE_Y(yrow + k, o);" + text[i + len(store):]
 
 
@@ -1121,6 +1134,135 @@ def store_policy_summary(log: str) -> None:
               + " ".join(f"{t:.1f}" for t in r["rounds_us"]))
     if any("check" in r for r in rows):
         print("  every policy's output equals the library's bit for bit")
+
+
+LDS_ROWS_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_lds_rows.so")
+STAGING_SHAPES = [(4096, 32768), (8192, 32768), (2048, 65536), (4096, 65536)]
+
+
+def build_lds_rows(verbose: bool = False) -> str:
+    """Compile probe_csrc/lds_rows.hip (the staged-row kernel at the entries
+    N = 32768 and 65536 used before their rows moved to VGPRs) into
+    probe_csrc/libmbn_lds_rows.so; always rebuilds."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=LDS_ROWS_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "lds_rows.hip")])
+
+
+def staging(rounds: int = 6, launches: int = 60) -> None:
+    """rmsnorm_fwd (rows held in VGPRs at N = 32768 and 65536) against the
+    staged-row kernel at the entries those widths used before
+    (libmbn_lds_rows.so), on the same data: outputs compared bit for bit,
+    then, per round and in alternating order, the median of `launches`
+    individually timed launches and the mean over about 0.2 s of back-to-back
+    launches, over buffer sets rotated through >= 1 GiB."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    if not os.path.exists(LDS_ROWS_LIB_PATH):
+        build_lds_rows()
+    h = ctypes.CDLL(LDS_ROWS_LIB_PATH)
+    h.mbn_lds_rmsnorm.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                                          ctypes.c_void_p]
+    h.mbn_lds_rmsnorm.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    g = torch.Generator(device=dev).manual_seed(23)
+    for M, N in STAGING_SHAPES:
+        n = max(2, -(-(1 << 30) // (M * N * 4)))
+        xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+        ys = [torch.empty_like(xs[0]) for _ in range(n)]
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+
+        def lds(i):
+            rc = h.mbn_lds_rmsnorm(xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, N, 1e-5, sp)
+            if rc != 0:
+                raise RuntimeError(f"staged-row kernel: status {rc}")
+
+        fns = {"registers (library)": lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=1e-5), "LDS (before)": lds}
+        outs = []
+        for fn in fns.values():
+            ys[0].zero_()
+            fn(0)
+            torch.cuda.synchronize()
+            outs.append(ys[0].clone())
+        # N = 32768: both kernels use 1024 lanes per row (the same sums in the
+        # same order, so the same bits); N = 65536: 512 against 1024 lanes, so
+        # the partial sums differ in order and the outputs agree to one ulp
+        a, b2 = outs[0].float(), outs[1].float()
+        if not bool(((a - b2).abs() <= b2.abs() * 2.0 ** -7 + 1e-6).all()):
+            raise RuntimeError(f"{M}x{N}: the two kernels' outputs differ by more than one bf16 ulp")
+        same = float((outs[0].view(torch.int16) == outs[1].view(torch.int16)).float().mean())
+        if N == 32768 and same != 1.0:
+            raise RuntimeError(f"{M}x{N}: the two kernels' outputs differ")
+        del outs, a, b2
+        nb = 2 * M * N * 2 + 2 * N
+        sustained_n = max(200, int(0.2e6 / (nb / 6.4e6)))
+        res = {(k, m): [] for k in fns for m in ("events", "sustained")}
+        for _ in range(200):
+            fns["registers (library)"](0)
+        torch.cuda.synchronize()
+        for rnd in range(rounds):
+            for k in (list(fns) if rnd % 2 == 0 else list(fns)[::-1]):
+                fn = fns[k]
+                for i in range(20):
+                    fn(i % n)
+                torch.cuda.synchronize()
+                ev = [(timer.new(), timer.new()) for _ in range(launches)]
+                for i, (a, b) in enumerate(ev):
+                    timer.record(a)
+                    fn(i % n)
+                    timer.record(b)
+                torch.cuda.synchronize()
+                us = sorted(timer.elapsed_ms(a, b) * 1e3 for a, b in ev)
+                timer.close()
+                res[(k, "events")].append(us[len(us) // 2])
+                e0, e1 = timer.new(), timer.new()
+                timer.record(e0)
+                for i in range(sustained_n):
+                    fn(i % n)
+                timer.record(e1)
+                torch.cuda.synchronize()
+                res[(k, "sustained")].append(timer.elapsed_ms(e0, e1) * 1e3 / sustained_n)
+                timer.close()
+        for (k, m), t in res.items():
+            us = sorted(t)[len(t) // 2]
+            print(json.dumps({"M": M, "N": N, "kernel": k, "timing": m, "buffer_sets": n, "median_us": round(us, 2),
+                              "pct": round(100 * nb / us / 1e3 / 8000, 2), "rounds_us": [round(v, 2) for v in t]}),
+                  flush=True)
+        print(json.dumps({"check": f"{M}x{N}: outputs within one bf16 ulp, {100 * same:.4f}% bit-identical"}),
+              flush=True)
+        del xs, ys
+        torch.cuda.empty_cache()
+
+
+def staging_summary(log: str) -> None:
+    import json
+
+    rows = [json.loads(x) for x in open(log) if x.startswith("{")]
+    print("RMSNorm, rows held in VGPRs (the library at N = 32768 and 65536) against the staged-row LDS kernel")
+    print("those widths used before, same data; median over rounds (events: per-launch median of 60; sustained:")
+    print("mean per launch over ~0.2 s of back-to-back launches):")
+    print(f"  {'shape':<14} {'timing':<10} {'registers us':>12} {'%':>6} {'LDS us':>9} {'%':>6} {'ratio':>6}")
+    by = {}
+    for r in rows:
+        if "check" in r:
+            continue
+        by.setdefault((r["M"], r["N"], r["timing"]), {})[r["kernel"]] = r
+    for (M, N, m), d in by.items():
+        a, b = d["registers (library)"], d["LDS (before)"]
+        print(f"  {str(M) + 'x' + str(N):<14} {m:<10} {a['median_us']:>12.2f} {a['pct']:>6.2f} {b['median_us']:>9.2f} "
+              f"{b['pct']:>6.2f} {a['median_us'] / b['median_us']:>6.3f}")
+    for r in rows:
+        if "check" in r:
+            print("  " + r["check"])
 
 
 STREAM_VARIANTS = {
@@ -1345,7 +1487,8 @@ def trace_summary(d: str, bench_json: str) -> None:
 
     rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
     stats = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
-    rms = sorted((r for r in rows if "rownorm_kernel" in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    rms = sorted((r for r in rows if any(k in r["Kernel_Name"] for k in ROW_KERNELS)),
+                 key=lambda r: int(r["Start_Timestamp"]))
     b = [json.loads(line) for line in open(bench_json) if line.startswith("{")][-1]
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rms][-b["steps"]:]
     algo = b["roofline"]["algorithmic_bytes_per_launch"]
@@ -1418,8 +1561,9 @@ def suite_summary(d: str, suite_log: str, warm: int = 3000) -> None:
     print("batch phases); bytes are the algorithmic bytes of one launch; % is of 8 TB/s.")
     print("grid_MxN: the RMSNorm shape grid of the normalization pages (the leading M x N")
     print("block of the 16384 x 16384 input). Template arguments: rownorm_kernel<mode, WPR,")
-    print("ROWS, RPL, MAXC, full, chunk wait>, rownorm_persistent_kernel<mode, WPR, RPL,")
-    print("MAXC, full> (mode 0 RMSNorm, 1 residual add + RMSNorm, 2 LayerNorm, 3 L2Norm),")
+    print("ROWS, RPL, MAXC, full, chunk wait>, rownorm_regs_kernel<mode, WPR, ROWS, MAXC,")
+    print("full> (rows in VGPRs), rownorm_persistent_kernel<mode, WPR, RPL, MAXC, full>")
+    print("(mode 0 RMSNorm, 1 residual add + RMSNorm, 2 LayerNorm, 3 L2Norm),")
     print("rownorm_any_kernel / rownorm_s16_kernel (widths that are not whole 16-byte")
     print("chunks). WGs is the grid size (the persistent grid loops over the rows).")
     print()
@@ -1525,6 +1669,10 @@ if __name__ == "__main__":
         stream_variants()
     elif len(sys.argv) == 2 and sys.argv[1] == "sizes":
         sizes()
+    elif len(sys.argv) == 2 and sys.argv[1] == "staging":
+        staging()
+    elif len(sys.argv) == 3 and sys.argv[1] == "staging-summary":
+        staging_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "store-policy":
         store_policy()
     elif len(sys.argv) == 3 and sys.argv[1] == "store-policy-summary":

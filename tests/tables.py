@@ -9,13 +9,17 @@ from collections import namedtuple
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "memory_bound_normalization_amd", "csrc", "rownorm.hip")
 CFG = r"MBN_CFG(_EXACT|_ROWS_EXACT|_ROWS|_UPTO)?(_W)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
+# exact-width entries with register-resident rows: WPR, ROWS, MAXC, CAP, GROUP (RPL = 1)
+CFG_R = r"MBN_CFG_EXACT_R\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
 
 
-class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto chunk_wait")):
+class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto chunk_wait regs",
+                       defaults=(False,))):
     """One launch-table entry. `upto` is the widest row (chunks) a sub-band
     entry (MBN_CFG_UPTO) serves, 0 for the other kinds; `chunk_wait`: a _W
-    entry (per-chunk waits in its full-width kernel); `top` is the widest row
-    any entry serves and `capacity` its kernel's 64 * wpr * maxc chunks."""
+    entry (per-chunk waits in its full-width kernel); `regs`: an _R entry
+    (register-resident rows, exact width only); `top` is the widest row any
+    entry serves and `capacity` its kernel's 64 * wpr * maxc chunks."""
 
     @property
     def capacity(self):
@@ -42,6 +46,10 @@ def _tables():
         for line in body.split("\n"):
             line = line.strip()
             found = macros.get(line.split("(")[0], None) if line.startswith("MBN_FIRST_BAND") else None
+            for wpr, rows, maxc, cap, grp in re.findall(CFG_R, line):
+                entries.append(Entry(True, 0, int(wpr), int(rows), 1, int(maxc), int(cap), int(grp), 0, False, True))
+            if re.search(CFG_R, line):
+                continue
             for e in (found if found is not None else re.findall(CFG, line)):
                 kind, w, *nums = e
                 nums = [int(v) for v in nums if v != ""]

@@ -106,8 +106,9 @@ def test_store_policy_source_replaces_only_the_one_shot_output_store():
         lib = f.read()
     assert src.count("MBN_STORE_Y(yrow + k, o);") == 1
     assert src.replace("MBN_STORE_Y(yrow + k, o);", "store_nt_16(yrow + k, o);") == lib
-    # the replaced store is pass 2 of the one-shot body, not the persistent kernel's
-    assert src.index("MBN_STORE_Y") > src.index("rownorm_block(const RowNormArgs")
+    # the replaced store is pass 2 of the one-shot body, not another kernel's
+    assert src.index("rownorm_block(const RowNormArgs") < src.index("MBN_STORE_Y") < src.index(
+        ") rownorm_kernel(RowNormArgs a)")
 
 
 def test_ceiling_summary_groups_dispatches_per_case(tmp_path, capsys):
@@ -147,3 +148,14 @@ def test_store_policy_summary_table(tmp_path, capsys):
     assert "library      nt (compiler)         164.70        81.49  165.1 164.4" in out
     assert "policy 1     nt sc1                165.20        81.26  164.9 165.3" in out
     assert "bit for bit" in out
+
+
+def test_counter_summary_counts_both_row_kernels(tmp_path):
+    """The row-norm kernels of either kind (staged rows, rows in VGPRs) count as
+    the measured kernel; torch's copy as the calibration."""
+    d = tmp_path / "fetch"
+    _write(str(d), "FETCH_SIZE", [("void mbn::(anonymous namespace)::rownorm_regs_kernel<(mbn::Norm)0, mbn::Bf16, 16, 1, 4, true>(mbn::RowNormArgs)", 10.0),
+                                  ("void mbn::(anonymous namespace)::rownorm_kernel<(mbn::Norm)0, mbn::Bf16, 2, 2, 1, 16, true, true>(mbn::RowNormArgs)", 12.0),
+                                  ("__amd_rocclr_copyBuffer", 20.0)])
+    res = probe._per_kernel(str(d), "FETCH_SIZE")
+    assert res == {"rmsnorm": [10.0, 12.0], "copy": [20.0]}
