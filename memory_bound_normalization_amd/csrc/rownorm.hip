@@ -1,6 +1,8 @@
 // Row-wise norms for gfx950 with each row staged in LDS: RMSNorm, residual add
 // + RMSNorm, LayerNorm and L2Norm, on bf16 or fp16 data (fp16 is among the
-// broadened inputs of "[Inductor] Codegen Gluon", section 3.2).
+// broadened inputs of "[Inductor] Codegen Gluon", section 3.2). RMSNorm rows
+// of exactly 32768 and 65536 elements are held in VGPRs instead
+// (rownorm_regs_kernel, below).
 //
 // The method ("[Inductor] Codegen Gluon", section 3.1, RMSNorm as the reference
 // workload; section 3.2 for the rest of the family): the input row is needed
@@ -270,8 +272,16 @@ __device__ __forceinline__ void finish_rows(const RowNormArgs& a, u32x4* buf0, f
 // unchanged).
 //
 // rownorm_block is that body for one row block (ROWS * RPL rows starting at
-// block * ROWS * RPL); rownorm_kernel runs it for its own block.
-template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL, bool CHUNK_WAIT>
+// block * ROWS * RPL); rownorm_kernel runs it for its own block. LATE_W
+// (rownorm_lw_kernel) loads the weight (and bias) only once the row is
+// reduced, just before pass 2, instead of alongside the row copy: on MI355X
+// the weight loads issued with the copy slowed the 512-lane, one-row
+// workgroups of the N <= 8192 band by 3-8% (L2Norm, which reads no weight,
+// ran that much faster on the same geometry), while waiting for them after
+// the reduction costs less. Not with per-chunk waits, whose kernels load the
+// weight first.
+template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL, bool CHUNK_WAIT,
+          bool LATE_W = false>
 __device__ __forceinline__ void rownorm_block(const RowNormArgs& a, int64_t block) {
   constexpr int TPR = 64 * WPR;  // lanes per lane set
   constexpr bool kHasW = MODE != Norm::kL2;
@@ -280,6 +290,7 @@ __device__ __forceinline__ void rownorm_block(const RowNormArgs& a, int64_t bloc
   // Pass 1 consumes each staged chunk as it lands (see below): full-width
   // kernels of the table entries that ask for it, not the residual add.
   constexpr bool kChunkWait = CHUNK_WAIT && FULL && !kHasR;
+  static_assert(!(LATE_W && CHUNK_WAIT), "late weights are for kernels without per-chunk waits");
   extern __shared__ u32x4 lds_rows[];  // ROWS * RPL * nchunk chunks (or more, see launcher)
   MBN_TL_START();
 
@@ -398,8 +409,8 @@ __device__ __forceinline__ void rownorm_block(const RowNormArgs& a, int64_t bloc
                             ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r) + (row0 + rr) * nchunk + k)
                             : u32x4{0u, 0u, 0u, 0u};
       }
-      if constexpr (kHasW) wreg[j] = in ? reinterpret_cast<const u32x4*>(a.w)[k] : u32x4{0u, 0u, 0u, 0u};
-      if constexpr (kHasB) breg[j] = in ? reinterpret_cast<const u32x4*>(a.b)[k] : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kHasW && !LATE_W) wreg[j] = in ? reinterpret_cast<const u32x4*>(a.w)[k] : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kHasB && !LATE_W) breg[j] = in ? reinterpret_cast<const u32x4*>(a.b)[k] : u32x4{0u, 0u, 0u, 0u};
     }
     wait_vmem();
 
@@ -494,6 +505,8 @@ __device__ __forceinline__ void rownorm_block(const RowNormArgs& a, int64_t bloc
     }
   }
 
+  if constexpr (LATE_W) load_affine<MODE, WPR, MAXC, FULL>(a, t, wreg, breg);
+
   // Pass 2 (from LDS): normalize, weight, round to bf16, streaming stores.
 #pragma unroll
   for (int rr = 0; rr < RPL; ++rr) {
@@ -533,8 +546,15 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_kernel(RowNormArgs a)
   rownorm_block<MODE, DT, WPR, ROWS, RPL, MAXC, FULL, CHUNK_WAIT>(a, xcd_remap(blockIdx.x, gridDim.x, a.xcd_group));
 }
 
+// The same one-shot kernel with the weight (and bias) loaded after the
+// reduction (rownorm_block's LATE_W).
+template <Norm MODE, typename DT, int WPR, int ROWS, int RPL, int MAXC, bool FULL>
+__global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_lw_kernel(RowNormArgs a) {
+  rownorm_block<MODE, DT, WPR, ROWS, RPL, MAXC, FULL, false, true>(a, xcd_remap(blockIdx.x, gridDim.x, a.xcd_group));
+}
+
 // Register-resident rows: the same one-shot method with each lane's chunks of
-// the row held in VGPRs instead of LDS ("[Inductor] Codegen Gluon", section 2
+// the row held in VGPRs instead of LDS ("[Inductor] Codegen Gluon", sections 2
 // and 3.1 keep the reused row in on-chip memory; here that memory is the
 // register file). Each row is still read from HBM once, with the same 16-byte
 // non-temporal loads and the same lane-to-chunk mapping, kept narrow (packed
@@ -775,11 +795,25 @@ constexpr RowNormKernel chunk_wait_kernel() {
 #define MBN_CFG_UPTO_W(MODE, MAXN, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
   MBN_CFG_(MODE, (MAXN) / 8, false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
 
+// The _LW form: a band's entry whose kernels load the weight (and bias) after
+// the reduction (rownorm_lw_kernel), for grids of any size.
+#define MBN_CFG_LW(MODE, WPR, ROWS, RPL, MAXC, CAP, GROUP)                              \
+  RowNormCfg {                                                                        \
+    64 * (WPR) * (MAXC), 64 * (WPR) * (MAXC), false, 0, WPR, ROWS, RPL, MAXC, CAP, GROUP, \
+        {&rownorm_lw_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, false>,                 \
+         &rownorm_lw_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, false>},                 \
+        {&rownorm_lw_kernel<MODE, Bf16, WPR, ROWS, RPL, MAXC, true>,                  \
+         &rownorm_lw_kernel<MODE, F16, WPR, ROWS, RPL, MAXC, true>},                  \
+        {nullptr, nullptr}, false                                                     \
+  }
+
 // The _R form: an exact-width entry with register-resident rows
 // (rownorm_regs_kernel: one row per lane set, RPL = 1, no LDS staging; CAP
 // still caps the resident workgroups per CU through the dynamic LDS request).
 // Only exact widths: at widths below a kernel's capacity it measured 10-12%
-// slower than the staged kernel.
+// slower than the staged kernel; and only past a row window that keeps the
+// staged kernel for launches of up to 1536-2048 rows, where it was 3-9%
+// slower.
 #define MBN_CFG_EXACT_R(MODE, WPR, ROWS, MAXC, CAP, GROUP)                             \
   RowNormCfg {                                                                       \
     64 * (WPR) * (MAXC), 64 * (WPR) * (MAXC), true, 0, WPR, ROWS, 1, MAXC, CAP, GROUP, \
@@ -838,18 +872,20 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_EXACT_W(Norm::kRms, 4, 1, 2, 3, 2, 0),  // N == 6144: 256 threads x 2 rows
     MBN_CFG_UPTO(Norm::kRms, 6144, 6, 1, 2, 2, 4, 0),  // 4096 < N <= 6144: 384 threads x 2 rows
     MBN_CFG_EXACT_W(Norm::kRms, 7, 1, 2, 2, 3, 0),  // N == 7168: 448 threads x 2 rows
-    MBN_CFG(Norm::kRms, 4, 1, 1, 4, 4, 8),   // N <= 8192:  256 threads, 4 WGs/CU
+    MBN_CFG_LW(Norm::kRms, 8, 1, 1, 2, 0, 0),  // N <= 8192:  512 threads, weight after the reduction
     MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 1536, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1536
     MBN_CFG_ROWS_EXACT_W(Norm::kRms, 6144, 4, 1, 1, 8, 2, 8),  // N == 16384, M <= 6144
     MBN_CFG_UPTO_W(Norm::kRms, 12288, 12, 1, 2, 2, 0, 0),  // 8192 < N <= 12288: 768 threads x 2 rows
     MBN_CFG_UPTO(Norm::kRms, 15360, 16, 1, 2, 2, 0, 0),  // 12288 < N <= 15360: 1024 threads x 2 rows
     MBN_CFG_W(Norm::kRms, 2, 2, 1, 16, 2, 4),  // N <= 16384: 2 x 128 threads, 2 WGs/CU
+    MBN_CFG_ROWS_EXACT_W(Norm::kRms, 2048, 16, 1, 1, 4, 0, 0),  // N == 32768, M <= 2048: rows in LDS
     MBN_CFG_EXACT_R(Norm::kRms, 16, 1, 4, 4, 4),  // N == 32768: 1024 threads, rows in VGPRs
     MBN_CFG_UPTO(Norm::kRms, 19456, 8, 1, 1, 5, 3, 0),  // 16384 < N <= 19456: 512 threads
-    MBN_CFG_W(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N <= 32768: 1024 threads
+    MBN_CFG(Norm::kRms, 16, 1, 1, 4, 0, 0),  // N < 32768: 1024 threads (the top width: the two entries above)
+    MBN_CFG_ROWS_EXACT_W(Norm::kRms, 1536, 16, 1, 1, 8, 0, 0),  // N == 65536, M <= 1536: rows in LDS
     MBN_CFG_EXACT_R(Norm::kRms, 8, 1, 16, 4, 4),  // N == 65536: 512 threads, rows in VGPRs
-    MBN_CFG_W(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N <= 65536: 1024 threads
+    MBN_CFG(Norm::kRms, 16, 1, 1, 8, 0, 0),  // N < 65536: 1024 threads (the top width: the two entries above)
 };
 const RowNormCfg kAddRmsTable[] = {
     MBN_FIRST_BAND(Norm::kAddRms),

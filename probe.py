@@ -56,10 +56,15 @@ variant's output equals the library's bit for bit.
 
     python probe.py staging > <log>
     python probe.py staging-summary <log>
+    python probe.py late-weights > <log>
+    python probe.py late-weights-summary <log>
 
 `staging` times rmsnorm_fwd where its launch tables hold each lane's chunks
 of the row in VGPRs (N = 32768 and 65536) against the staged-row (LDS) kernel
-those widths used before (probe_csrc/lds_rows.hip), on the same data.
+those widths used before; `late-weights` the N <= 8192 band's entry, which
+loads the weight after the reduction, against the band's previous entry. The
+prior entries are the library's own kernels, compiled from its source by
+probe_csrc/prior_entries.hip; same data, outputs compared first.
 
 The other commands, each the source of a committed summary: `timeline`,
 `timeline-summary` (per-workgroup timelines), `variants`, `claim`, `stream`,
@@ -892,7 +897,7 @@ VARIANTS = {
     7: "N=16384: 128 lanes, 2 rows per lane set, cap 2, group 4",
     8: "N=16384: 256 lanes, 1 row, cap 3, group 4",
     9: "N=16384: 2 x 128 lanes, cap 1, group 4",
-    10: "N=32768: 1024 lanes, 1 row, no cap, group 0 (the table's entry)",
+    10: "N=32768: 1024 lanes, 1 row, no cap, group 0 (the staged-row entry)",
     11: "N=32768: 512 lanes, cap 2, group 0",
     12: "N=32768: 256 lanes, cap 2, group 0",
     13: "N=32768: 512 lanes, cap 2, group 4",
@@ -1136,27 +1141,39 @@ def store_policy_summary(log: str) -> None:
         print("  every policy's output equals the library's bit for bit")
 
 
-LDS_ROWS_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_lds_rows.so")
-STAGING_SHAPES = [(4096, 32768), (8192, 32768), (2048, 65536), (4096, 65536)]
+PRIOR_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_prior.so")
+STAGING_SHAPES = [(1024, 32768), (4096, 32768), (8192, 32768), (512, 65536), (2048, 65536), (4096, 65536)]
 
 
-def build_lds_rows(verbose: bool = False) -> str:
-    """Compile probe_csrc/lds_rows.hip (the staged-row kernel at the entries
-    N = 32768 and 65536 used before their rows moved to VGPRs) into
-    probe_csrc/libmbn_lds_rows.so; always rebuilds."""
+def build_prior(verbose: bool = False) -> str:
+    """Compile probe_csrc/prior_entries.hip (launch-table entries the library
+    used before: the staged-row kernel at N = 32768 and 65536, the N <= 8192
+    band's early-weight entry) into probe_csrc/libmbn_prior.so; always
+    rebuilds."""
     sys.path.insert(0, ROOT)
     from memory_bound_normalization_amd.build import build
 
-    return build(verbose=verbose, out=LDS_ROWS_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "lds_rows.hip")])
+    return build(verbose=verbose, out=PRIOR_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "prior_entries.hip")])
 
 
-def staging(rounds: int = 6, launches: int = 60) -> None:
-    """rmsnorm_fwd (rows held in VGPRs at N = 32768 and 65536) against the
-    staged-row kernel at the entries those widths used before
-    (libmbn_lds_rows.so), on the same data: outputs compared bit for bit,
-    then, per round and in alternating order, the median of `launches`
-    individually timed launches and the mean over about 0.2 s of back-to-back
-    launches, over buffer sets rotated through >= 1 GiB."""
+def prior_lib():
+    if not os.path.exists(PRIOR_LIB_PATH):
+        build_prior()
+    h = ctypes.CDLL(PRIOR_LIB_PATH)
+    for f in (h.mbn_lds_rmsnorm, h.mbn_early_w_rmsnorm):
+        f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+    return h
+
+
+def _ab_prior(shapes, new_name, old_name, old_fn, eps, same_bits, seed, rounds=6, launches=60) -> None:
+    """rmsnorm_fwd against a prior launch-table entry (old_fn(h, x, w, y, M,
+    N, eps, stream) through libmbn_prior.so) on the same data: outputs
+    compared (within one bf16 ulp; bit for bit where same_bits(N)), then, per
+    round and in alternating order, the median of `launches` individually
+    timed launches and the mean over about 0.2 s of back-to-back launches,
+    over buffer sets rotated through >= 1 GiB. One JSON line per shape,
+    kernel and timing."""
     sys.path.insert(0, ROOT)
     import json
 
@@ -1164,50 +1181,42 @@ def staging(rounds: int = 6, launches: int = 60) -> None:
 
     import memory_bound_normalization_amd as mbn
 
-    if not os.path.exists(LDS_ROWS_LIB_PATH):
-        build_lds_rows()
-    h = ctypes.CDLL(LDS_ROWS_LIB_PATH)
-    h.mbn_lds_rmsnorm.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
-                                                          ctypes.c_void_p]
-    h.mbn_lds_rmsnorm.restype = ctypes.c_int
+    h = prior_lib()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     timer = HipTimingEvents(stream)
-    g = torch.Generator(device=dev).manual_seed(23)
-    for M, N in STAGING_SHAPES:
+    g = torch.Generator(device=dev).manual_seed(seed)
+    for M, N in shapes:
         n = max(2, -(-(1 << 30) // (M * N * 4)))
         xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
         ys = [torch.empty_like(xs[0]) for _ in range(n)]
         w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
 
-        def lds(i):
-            rc = h.mbn_lds_rmsnorm(xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, N, 1e-5, sp)
+        def old(i):
+            rc = old_fn(h, xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, N, eps, sp)
             if rc != 0:
-                raise RuntimeError(f"staged-row kernel: status {rc}")
+                raise RuntimeError(f"{old_name}: status {rc}")
 
-        fns = {"registers (library)": lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=1e-5), "LDS (before)": lds}
+        fns = {new_name: lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps), old_name: old}
         outs = []
         for fn in fns.values():
             ys[0].zero_()
             fn(0)
             torch.cuda.synchronize()
             outs.append(ys[0].clone())
-        # N = 32768: both kernels use 1024 lanes per row (the same sums in the
-        # same order, so the same bits); N = 65536: 512 against 1024 lanes, so
-        # the partial sums differ in order and the outputs agree to one ulp
         a, b2 = outs[0].float(), outs[1].float()
         if not bool(((a - b2).abs() <= b2.abs() * 2.0 ** -7 + 1e-6).all()):
             raise RuntimeError(f"{M}x{N}: the two kernels' outputs differ by more than one bf16 ulp")
         same = float((outs[0].view(torch.int16) == outs[1].view(torch.int16)).float().mean())
-        if N == 32768 and same != 1.0:
+        if same_bits(N) and same != 1.0:
             raise RuntimeError(f"{M}x{N}: the two kernels' outputs differ")
         del outs, a, b2
         nb = 2 * M * N * 2 + 2 * N
         sustained_n = max(200, int(0.2e6 / (nb / 6.4e6)))
         res = {(k, m): [] for k in fns for m in ("events", "sustained")}
         for _ in range(200):
-            fns["registers (library)"](0)
+            fns[new_name](0)
         torch.cuda.synchronize()
         for rnd in range(rounds):
             for k in (list(fns) if rnd % 2 == 0 else list(fns)[::-1]):
@@ -1243,22 +1252,49 @@ def staging(rounds: int = 6, launches: int = 60) -> None:
         torch.cuda.empty_cache()
 
 
-def staging_summary(log: str) -> None:
+def staging() -> None:
+    """rmsnorm_fwd, rows held in VGPRs at N = 32768 and 65536, against the
+    staged-row kernel those widths used before. At 32768 both use 1024 lanes
+    per row (same sums in the same order: same bits); at 65536 512 against
+    1024 lanes, so the outputs agree to one ulp."""
+    _ab_prior(STAGING_SHAPES, "registers (library)", "LDS (before)",
+              lambda h, *args: h.mbn_lds_rmsnorm(*args), 1e-5, lambda N: N == 32768, 23)
+
+
+LATE_W_SHAPES = [(M, N) for N in (8192, 7680, 6656) for M in (4096, 8192, 16384, 32768)]
+
+
+def late_weights() -> None:
+    """rmsnorm_fwd in the N <= 8192 band (512 lanes per row, weight loaded
+    after the reduction) against the band's previous entry (256 lanes, weight
+    loaded with the row copy); the lane mappings differ, so the outputs agree
+    to one ulp."""
+    _ab_prior(LATE_W_SHAPES, "late weight (library)", "early weight (before)",
+              lambda h, *args: h.mbn_early_w_rmsnorm(*args), 1e-6, lambda N: False, 29)
+
+
+def ab_summary(log: str) -> None:
+    """Table of a staging / late-weights log: the library against the prior
+    entry, per shape and timing."""
     import json
 
     rows = [json.loads(x) for x in open(log) if x.startswith("{")]
-    print("RMSNorm, rows held in VGPRs (the library at N = 32768 and 65536) against the staged-row LDS kernel")
-    print("those widths used before, same data; median over rounds (events: per-launch median of 60; sustained:")
-    print("mean per launch over ~0.2 s of back-to-back launches):")
-    print(f"  {'shape':<14} {'timing':<10} {'registers us':>12} {'%':>6} {'LDS us':>9} {'%':>6} {'ratio':>6}")
+    kinds = []
+    for r in rows:
+        if "kernel" in r and r["kernel"] not in kinds:
+            kinds.append(r["kernel"])
+    new, old = kinds
+    print(f"{new} against {old}, same data; median over rounds (events: per-launch median of 60;")
+    print("sustained: mean per launch over ~0.2 s of back-to-back launches):")
+    print(f"  {'shape':<14} {'timing':<10} {'library us':>10} {'%':>6} {'before us':>9} {'%':>6} {'ratio':>6}")
     by = {}
     for r in rows:
         if "check" in r:
             continue
         by.setdefault((r["M"], r["N"], r["timing"]), {})[r["kernel"]] = r
     for (M, N, m), d in by.items():
-        a, b = d["registers (library)"], d["LDS (before)"]
-        print(f"  {str(M) + 'x' + str(N):<14} {m:<10} {a['median_us']:>12.2f} {a['pct']:>6.2f} {b['median_us']:>9.2f} "
+        a, b = d[new], d[old]
+        print(f"  {str(M) + 'x' + str(N):<14} {m:<10} {a['median_us']:>10.2f} {a['pct']:>6.2f} {b['median_us']:>9.2f} "
               f"{b['pct']:>6.2f} {a['median_us'] / b['median_us']:>6.3f}")
     for r in rows:
         if "check" in r:
@@ -1671,8 +1707,10 @@ if __name__ == "__main__":
         sizes()
     elif len(sys.argv) == 2 and sys.argv[1] == "staging":
         staging()
-    elif len(sys.argv) == 3 and sys.argv[1] == "staging-summary":
-        staging_summary(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "late-weights":
+        late_weights()
+    elif len(sys.argv) == 3 and sys.argv[1] in ("staging-summary", "late-weights-summary"):
+        ab_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "store-policy":
         store_policy()
     elif len(sys.argv) == 3 and sys.argv[1] == "store-policy-summary":

@@ -351,7 +351,7 @@ __attribute__((visibility("default"))) int mbn_tl_rmsnorm_variant(const void* x,
     case 7: return tl_variant<2, 1, 2, 16>(x, w, y, M, N, eps, s, 2, 4);
     case 8: return tl_variant<4, 1, 1, 8>(x, w, y, M, N, eps, s, 3, 4);
     case 9: return tl_variant<2, 2, 1, 16>(x, w, y, M, N, eps, s, 1, 4);
-    case 10: return tl_variant<16, 1, 1, 4>(x, w, y, M, N, eps, s, 0, 0);  // the table's entry
+    case 10: return tl_variant<16, 1, 1, 4>(x, w, y, M, N, eps, s, 0, 0);  // the staged-row entry (rows in VGPRs now past 2048 rows)
     case 11: return tl_variant<8, 1, 1, 8>(x, w, y, M, N, eps, s, 2, 0);
     case 12: return tl_variant<4, 1, 1, 16>(x, w, y, M, N, eps, s, 2, 0);
     case 13: return tl_variant<8, 1, 1, 8>(x, w, y, M, N, eps, s, 2, 4);

@@ -8,18 +8,19 @@ from collections import namedtuple
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "memory_bound_normalization_amd", "csrc", "rownorm.hip")
-CFG = r"MBN_CFG(_EXACT|_ROWS_EXACT|_ROWS|_UPTO)?(_W)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
+CFG = r"MBN_CFG(_EXACT|_ROWS_EXACT|_ROWS|_UPTO)?(_W|_LW)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
 # exact-width entries with register-resident rows: WPR, ROWS, MAXC, CAP, GROUP (RPL = 1)
 CFG_R = r"MBN_CFG_EXACT_R\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
 
 
-class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto chunk_wait regs",
-                       defaults=(False,))):
+class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto chunk_wait regs late_w",
+                       defaults=(False, False))):
     """One launch-table entry. `upto` is the widest row (chunks) a sub-band
     entry (MBN_CFG_UPTO) serves, 0 for the other kinds; `chunk_wait`: a _W
     entry (per-chunk waits in its full-width kernel); `regs`: an _R entry
-    (register-resident rows, exact width only); `top` is the widest row any
-    entry serves and `capacity` its kernel's 64 * wpr * maxc chunks."""
+    (register-resident rows, exact width only); `late_w`: an _LW entry (weight
+    loaded after the reduction); `top` is the widest row any entry serves and
+    `capacity` its kernel's 64 * wpr * maxc chunks."""
 
     @property
     def capacity(self):
@@ -60,7 +61,8 @@ def _tables():
                 elif kind == "_UPTO":
                     assert nums[0] % 8 == 0, line
                     upto, nums = nums[0] // 8, nums[1:]
-                entries.append(Entry(kind in ("_EXACT", "_ROWS_EXACT"), max_rows, *nums, upto, w == "_W"))
+                entries.append(Entry(kind in ("_EXACT", "_ROWS_EXACT"), max_rows, *nums, upto, w == "_W", False,
+                                     w == "_LW"))
         out[tname] = entries
     return out
 

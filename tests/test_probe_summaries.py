@@ -159,3 +159,21 @@ def test_counter_summary_counts_both_row_kernels(tmp_path):
                                   ("__amd_rocclr_copyBuffer", 20.0)])
     res = probe._per_kernel(str(d), "FETCH_SIZE")
     assert res == {"rmsnorm": [10.0, 12.0], "copy": [20.0]}
+
+
+def test_ab_summary_table(tmp_path, capsys):
+    import json
+
+    log = tmp_path / "ab.log"
+    lines = []
+    for k, us in (("late weight (library)", 44.0), ("early weight (before)", 46.0)):
+        for m in ("events", "sustained"):
+            lines.append(json.dumps({"M": 8192, "N": 8192, "kernel": k, "timing": m, "buffer_sets": 4,
+                                     "median_us": us, "pct": 1.0, "rounds_us": [us]}))
+    lines.append(json.dumps({"check": "8192x8192: outputs within one bf16 ulp, 99.0000% bit-identical"}))
+    log.write_text("\n".join(lines) + "\n")
+    probe.ab_summary(str(log))
+    out = capsys.readouterr().out
+    assert "late weight (library) against early weight (before)" in out
+    assert "8192x8192      events          44.00   1.00     46.00   1.00  0.957" in out
+    assert "99.0000% bit-identical" in out
