@@ -1,8 +1,8 @@
 """HIP graph capture of the library's launches. The entry points allocate
 nothing, never synchronize and launch on the caller's stream, so a sequence of
-them (RMSNorm on the one-shot, persistent and any-width paths, the residual
-add, LayerNorm, L2Norm and the in-place QK-norm + rotary) can be captured into
-one graph (torch.cuda.CUDAGraph) and replayed. Each replay runs on new input
+them (RMSNorm on the one-shot, register-row, late-weight, persistent and
+any-width paths, the residual add, LayerNorm, L2Norm and the in-place QK-norm +
+rotary) can be captured into one graph (torch.cuda.CUDAGraph) and replayed. Each replay runs on new input
 values copied into the captured buffers, with eager work and synchronizations
 between replays, and must reproduce eager calls of the same entry points bit
 for bit; the first input set is also checked against the fp64 oracle."""
@@ -10,7 +10,7 @@ for bit; the first input set is also checked against the fp64 oracle."""
 import numpy as np
 import pytest
 
-from parity import assert_parity, from_gpu_bf16, to_gpu_bf16
+from parity import assert_parity, assert_parity_rows, from_gpu_bf16, to_gpu_bf16
 from workloads import random_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -20,8 +20,9 @@ import memory_bound_normalization_amd as mbn  # noqa: E402
 from oracle import l2norm_fwd as o_l2, qk_norm_rope_fwd as o_qk, rmsnorm_fwd as o_rms  # noqa: E402
 
 # (M, N): a row window of the one-shot kernel, the persistent kernel, a width
-# that is not whole 16-byte chunks
-RMS_SHAPES = [(1000, 4096), (3000, 4096), (37, 1001)]
+# that is not whole 16-byte chunks, rows held in VGPRs, the weight loaded after
+# the reduction
+RMS_SHAPES = [(1000, 4096), (3000, 4096), (37, 1001), (2100, 32768), (4000, 8192)]
 FAM = (513, 2048)
 T, HQ, HKV, D = 64, 8, 2, 128
 
@@ -104,6 +105,10 @@ def test_graph_replays_match_eager():
         assert torch.equal(qkv.view(torch.int16), ref_qkv.view(torch.int16)), f"replay {rep}: qkv"
         if rep == 0:
             assert_parity(from_gpu_bf16(out["y0"]), o_rms(host["x0"], host["w0"], 1e-6), "graph y0")
+            for i in (3, 4):  # rows in VGPRs, weight after the reduction
+                x, w = host[f"x{i}"], host[f"w{i}"]
+                assert assert_parity_rows(from_gpu_bf16(out[f"y{i}"]), lambda lo, hi: o_rms(x[lo:hi], w, 1e-6),
+                                          f"graph y{i}") == x.size
             assert_parity(from_gpu_bf16(out["fy2"]), o_l2(host["fx"], 1e-12), "graph l2")
             ref = o_qk(host["qkv"], host["qw"], host["kw"], host["pos"], HQ, HKV, D, 1e-6, 1e6)
             assert_parity(from_gpu_bf16(qkv), ref, "graph qkv")
