@@ -24,6 +24,18 @@
 // waves, two steps each. Many tokens: 4 waves per token, looping, so the
 // per-token angle work is not repeated in every wave.
 //
+// Each wave issues the loads of a group of up to KMAX of its steps before the
+// arithmetic of the first (the first group's before the angle work), so KMAX
+// head rows per wave are in flight: KMAX = 3 with 4 waves per token (all of a
+// wave's steps for up to 48 heads), 2 with two steps per wave, else 1; with
+// KMAX > 1 the lane's cos / sin stay in registers across the steps. The
+// token's q and k heads are addressed through a buffer resource that ends at
+// the last head: lanes past it (head counts not a multiple of 4, steps past a
+// wave's last) load zeros and their stores are dropped by the hardware's
+// range check, so every load and store is unconditional and the compiler's
+// wait before a step covers that step's row only. The head rows are read
+// once and written once: their loads and stores are non-temporal.
+//
 // Partial rotary (rotary_dim R < 128, a multiple of 16; the page keeps the
 // full-head norm for it since the tail must still be normalized): the RMS and
 // the weight cover the whole head, chunks [0, R/8) rotate with the partner
@@ -49,7 +61,12 @@ constexpr int kHeadDim = 128;
 constexpr int kHalf = kHeadDim / 2;
 constexpr int kHeadsPerWave = 4;
 
-template <typename DT>
+// Cache-policy bits of a buffer access: non-temporal.
+constexpr int kBufferNT = 2;
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <typename DT, int KMAX>
 __global__ void __launch_bounds__(1024)
 qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w,
                     const uint16_t* __restrict__ k_w, const int64_t* __restrict__ positions,
@@ -63,19 +80,37 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
   const int64_t token = blockIdx.x;
   const int j = lane & 15;  // 16-byte chunk of the head: elements [8j, 8j + 8)
   uint16_t* const trow = qkv + token * row_stride;
+  // Step s of this wave covers heads wave0 + s * step_heads + [0, 4); lane
+  // row r = lane >> 4 takes head wave0 + s * step_heads + r.
+  const int wave0 = wave * kHeadsPerWave;
+  const int step_heads = waves * kHeadsPerWave;
 
   // The token's position: a uniform (scalar) load, issued with the head loads
   // and kept there (see below) rather than moved into wave 0's angle branch
   // behind further argument loads.
   const int64_t pos_i = positions[token];
-  // Issue the first head load before the angle computation so the two overlap.
-  int head = wave * kHeadsPerWave + (lane >> 4);
-  // Unconditional (no branch around the first loads, so the position's scalar
-  // load is scheduled among them): lanes past the last head (n_heads >= 1)
-  // read that head, and the loop zeroes them.
-  const int h0 = head < n_heads ? head : n_heads - 1;
-  u32x4 xv = *reinterpret_cast<const u32x4*>(trow + (int64_t)h0 * kHeadDim + 8 * j);
-  u32x4 wv = *reinterpret_cast<const u32x4*>((h0 < n_q ? q_w : k_w) + 8 * j);
+  // Both weight chunks of the lane, loaded ahead of the head rows so that
+  // waiting for them never waits for a head row. A weight with no heads may be
+  // null: its chunk is then read from the other weight and never used.
+  const uint16_t* const qwp = n_q > 0 ? q_w : k_w;
+  const uint16_t* const kwp = n_heads > n_q ? k_w : q_w;
+  const u32x4 qwv = *reinterpret_cast<const u32x4*>(qwp + 8 * j);
+  const u32x4 kwv = *reinterpret_cast<const u32x4*>(kwp + 8 * j);
+  // The token's q and k heads, n_heads * 256 bytes: accesses at or past the
+  // end read zeros or write nothing.
+  const __amdgpu_buffer_rsrc_t heads =
+      __builtin_amdgcn_make_buffer_rsrc(trow, (short)0, n_heads * kHeadDim * 2, kBufferWord3);
+  // Loads of steps s0 ... s0 + KMAX - 1, issued before the angle computation
+  // (first group) or the group's arithmetic.
+  u32x4 xs[KMAX];
+  auto load_group = [&](int s0) {
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      const int head = wave0 + (s0 + s) * step_heads + (lane >> 4);
+      xs[s] = __builtin_amdgcn_raw_buffer_load_b128(heads, head * kHeadDim * 2 + 16 * j, 0, kBufferNT);
+    }
+  };
+  load_group(0);
 
   // Using the position here keeps its load ahead of this point; the wait
   // counts scalar loads only, so the head loads stay in flight.
@@ -100,61 +135,79 @@ qk_norm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w
   const double sgn = first_half ? -1.0 : 1.0;
   const int i0 = 8 * (first_half ? j : j - rot_chunks);
   const int partner = (lane & ~15) | (rotated ? (first_half ? j + rot_chunks : j - rot_chunks) : j);
-  // Every lane of a wave runs the same number of steps (the DPP exchanges need
-  // the whole row of 16 lanes): the loop bound is the wave's first head.
-  for (int base = wave * kHeadsPerWave; base < n_heads; base += waves * kHeadsPerWave) {
-    head = base + (lane >> 4);
-    const bool live = head < n_heads;
-    if (base != wave * kHeadsPerWave && live) {
-      xv = *reinterpret_cast<const u32x4*>(trow + (int64_t)head * kHeadDim + 8 * j);
-      wv = *reinterpret_cast<const u32x4*>((head < n_q ? q_w : k_w) + 8 * j);
-    } else if (!live) {
-      xv = u32x4{0u, 0u, 0u, 0u};
-      wv = u32x4{0u, 0u, 0u, 0u};
+  // With several steps per group the lane's 8 (cos, +/-sin) pairs stay in
+  // registers; a single step reads them from LDS where they are used (fewer
+  // registers, more waves resident).
+  constexpr bool kHoist = KMAX > 1;
+  double hc[kHoist ? 8 : 1], hs[kHoist ? 8 : 1];
+  if constexpr (kHoist) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double2 a = rotated ? cs[i0 + e] : make_double2(1.0, 0.0);
+      hc[e] = a.x;
+      hs[e] = sgn * a.y;
     }
-    float x[8], xw[8];
+  }
+  // Every lane of a wave runs the same steps (the DPP exchanges need the
+  // whole row of 16 lanes): a step runs while the wave's first head in it
+  // exists.
+  for (int s0 = 0;; s0 += KMAX) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = DT::lo(xv[e]);
-      x[2 * e + 1] = DT::hi(xv[e]);
-      xw[2 * e] = x[2 * e] * DT::lo(wv[e]);
-      xw[2 * e + 1] = x[2 * e + 1] * DT::hi(wv[e]);
-    }
-    float acc = 0.f;
+    for (int s = 0; s < KMAX; ++s) {
+      const int base = wave0 + (s0 + s) * step_heads;
+      if (base >= n_heads) return;
+      const int head = base + (lane >> 4);
+      const u32x4 xv = xs[s];
+      const u32x4 wv = head < n_q ? qwv : kwv;
+      float x[8], xw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
-    const float ss = row16_sum(acc);
-    const float rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, 1.0f / kHeadDim, eps));
-
-    float xwp[8];  // partner chunk (R/2 elements away), same head
-    if (full) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xwp[e] = dpp<kDppRowRor8>(xw[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        xwp[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(partner << 2, __float_as_int(xw[e])));
-    }
-
-    // first half: o_i = u_i cos - u_{i+R/2} sin; second half: o = u cos + u_{i-R/2} sin
-    float o[8];
-    if (rotated) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double2 a = cs[i0 + e];
-        const double r = __builtin_fma((double)xwp[e], sgn * a.y, (double)xw[e] * a.x);
-        o[e] = (float)r * rstd;
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = DT::lo(xv[e]);
+        x[2 * e + 1] = DT::hi(xv[e]);
+        xw[2 * e] = x[2 * e] * DT::lo(wv[e]);
+        xw[2 * e + 1] = x[2 * e + 1] * DT::hi(wv[e]);
       }
-    } else {
+      float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = xw[e] * rstd;
-    }
-    if (live) {
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
+      const float ss = row16_sum(acc);
+      const float rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, 1.0f / kHeadDim, eps));
+
+      float xwp[8];  // partner chunk (R/2 elements away), same head
+      if (full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xwp[e] = dpp<kDppRowRor8>(xw[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          xwp[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(partner << 2, __float_as_int(xw[e])));
+      }
+
+      // first half: o_i = u_i cos - u_{i+R/2} sin; second half: o = u cos + u_{i-R/2} sin
+      float o[8];
+      if (rotated) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          double r;
+          if constexpr (kHoist) {
+            r = __builtin_fma((double)xwp[e], hs[e], (double)xw[e] * hc[e]);
+          } else {
+            const double2 a = cs[i0 + e];
+            r = __builtin_fma((double)xwp[e], sgn * a.y, (double)xw[e] * a.x);
+          }
+          o[e] = (float)r * rstd;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = xw[e] * rstd;
+      }
       u32x4 out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e] = DT::pack(o[2 * e], o[2 * e + 1]);
-      *reinterpret_cast<u32x4*>(trow + (int64_t)head * kHeadDim + 8 * j) = out;
+      __builtin_amdgcn_raw_buffer_store_b128(out, heads, head * kHeadDim * 2 + 16 * j, 0, kBufferNT);
     }
+    if (wave0 + (s0 + KMAX) * step_heads >= n_heads) return;
+    load_group(s0 + KMAX);
   }
 }
 
@@ -168,9 +221,11 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
   const int groups = (n_heads + kHeadsPerWave - 1) / kHeadsPerWave;
   // Up to 512 tokens: one wave per 4-head group (at most 16 waves, a single
   // step); up to 1024, half as many waves (two steps); beyond, 4 waves per
-  // token. Chosen on MI355X for 32 q + 8 k heads, back to back: T = 256 3.4 us
-  // with 10 waves against 4.1 us with 4; T = 1024 8.6 us with 5 waves against
-  // 9.6 us with 10; T = 65536 249 us with 4 waves against 363 us with 10.
+  // token. Chosen on MI355X for 32 q + 8 k heads: back to back, T = 256 3.4 us
+  // with 10 waves against 4.1 us with 4; per launch, T = 1024 6.0 us with 5
+  // waves against 6.6 us with 4, T = 4096 16.3 us with 4 waves against 17.1
+  // with 5 and 17.0 with 2, T = 65536 217 us with 4 against 224 with 5 and 222
+  // with 2.
   const int all = groups < 16 ? groups : 16;
   const int waves = T <= 512 ? all : T <= 1024 ? (all + 1) / 2 : (groups < 4 ? groups : 4);
   const int64_t row_stride = (int64_t)(n_q_heads + 2 * n_kv_heads) * kHeadDim;
@@ -179,7 +234,16 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
   // pow, within an ulp each), at most six fp64 products on the device, so a
   // relative error of about 1e-15 (an angle error of 1e-15 * phi rad).
   const InvFreqPowers inv_pow = rope_inv_freq_powers(theta, rotary_dim);
-  const auto kernel = dtype == Storage::kF16 ? qk_norm_rope_kernel<F16> : qk_norm_rope_kernel<Bf16>;
+  // Head rows in flight per wave (KMAX): all of a wave's steps, at most 3.
+  // Measured on MI355X for 32 q + 8 k heads, per launch, against one row in
+  // flight: 65536 tokens 215 us against 223, 16384 54.2 us against 58.5, 4096
+  // 16.3 us against 17.6, 1024 6.0 us against 6.7, 768 5.0 us against 6.0.
+  const int steps = (groups + waves - 1) / waves;
+  const int kmax = steps < 3 ? steps : 3;
+  const auto kernel =
+      dtype == Storage::kF16
+          ? (kmax == 3 ? qk_norm_rope_kernel<F16, 3> : kmax == 2 ? qk_norm_rope_kernel<F16, 2> : qk_norm_rope_kernel<F16, 1>)
+          : (kmax == 3 ? qk_norm_rope_kernel<Bf16, 3> : kmax == 2 ? qk_norm_rope_kernel<Bf16, 2> : qk_norm_rope_kernel<Bf16, 1>);
   // One workgroup per token; beyond kMaxWorkItems work-items, several launches
   // over consecutive token ranges.
   const int64_t tokens_per_launch = kMaxWorkItems / (64 * waves);

@@ -66,6 +66,12 @@ loads the weight after the reduction, against the band's previous entry. The
 prior entries are the library's own kernels, compiled from its source by
 probe_csrc/prior_entries.hip; same data, outputs compared first.
 
+    python probe.py qk-pattern > <log>
+    python probe.py qk-pattern-summary <log>
+
+`qk-pattern` times qk_norm_rope_fwd against its memory access pattern with no
+arithmetic (the q and k bytes of each token read and written back in place).
+
 The other commands, each the source of a committed summary: `timeline`,
 `timeline-summary` (per-workgroup timelines), `variants`, `claim`, `stream`,
 `sizes`, `experiments-summary` (the geometry, claimed-tail, pipelined-kernel
@@ -280,7 +286,9 @@ def stream_lib():
     h.mbn_stream_read.argtypes = [vp, vp, sz, i32, i32, vp]
     h.mbn_stream_write.argtypes = [vp, sz, i32, i32, u32, vp]
     h.mbn_stream_copy_policy.argtypes = [vp, vp, sz, i32, i32, vp]
-    for f in (h.mbn_stream_copy, h.mbn_stream_read, h.mbn_stream_write, h.mbn_stream_copy_policy):
+    h.mbn_stream_qk_pattern.argtypes = [vp, ctypes.c_int64, i32, i32, vp]
+    for f in (h.mbn_stream_copy, h.mbn_stream_read, h.mbn_stream_write, h.mbn_stream_copy_policy,
+              h.mbn_stream_qk_pattern):
         f.restype = i32
     return h
 
@@ -1301,6 +1309,85 @@ def ab_summary(log: str) -> None:
             print("  " + r["check"])
 
 
+QK_PATTERN_TOKENS = (65536, 4096)
+
+
+def qk_pattern(rounds: int = 6, launches: int = 40) -> None:
+    """qk_norm_rope_fwd (32 q + 8 k + 8 v heads of 128) against its memory
+    access pattern with no arithmetic (stream_qk_pattern: the q and k bytes of
+    each token read and written back in place, every load before the first
+    store), per token count: per-launch event medians, rounds interleaved."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    sl = stream_lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    g = torch.Generator(device=dev).manual_seed(67)
+    hq, hkv, d = 32, 8, 128
+    for T in QK_PATTERN_TOKENS:
+        row = (hq + 2 * hkv) * d
+        n = max(2, -(-(1 << 30) // (T * row * 2)))
+        qkv = [torch.randn(T, row, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+        qw = (torch.rand(d, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        kw = (torch.rand(d, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        pos = torch.arange(T, device=dev, dtype=torch.int64)
+
+        def bare(i):
+            rc = sl.mbn_stream_qk_pattern(qkv[i].data_ptr(), T, row // 8, (hq + hkv) * d // 8, sp)
+            if rc != 0:
+                raise RuntimeError(f"qk pattern: status {rc}")
+
+        fns = {"qk_norm_rope_fwd": lambda i: mbn.qk_norm_rope_fwd(qkv[i], qw, kw, pos, hq, hkv, d, eps=1e-6,
+                                                                  theta=1e6),
+               "access pattern only": bare}
+        nb = 2 * T * (hq + hkv) * d * 2
+        res = {k: [] for k in fns}
+        # the GPU's first sustained load of the process runs slower for a while
+        for fn in fns.values():
+            for i in range(40):
+                fn(i % n)
+        torch.cuda.synchronize()
+        for rnd in range(rounds):
+            for k in (list(fns) if rnd % 2 == 0 else list(fns)[::-1]):
+                fn = fns[k]
+                for i in range(10):
+                    fn(i % n)
+                torch.cuda.synchronize()
+                ev = [(timer.new(), timer.new()) for _ in range(launches)]
+                for i, (a, b) in enumerate(ev):
+                    timer.record(a)
+                    fn(i % n)
+                    timer.record(b)
+                torch.cuda.synchronize()
+                us = sorted(timer.elapsed_ms(a, b) * 1e3 for a, b in ev)
+                timer.close()
+                res[k].append(us[len(us) // 2])
+        for k, t in res.items():
+            us = sorted(t)[len(t) // 2]
+            print(json.dumps({"T": T, "kernel": k, "median_us": round(us, 2), "pct": round(100 * nb / us / 1e3 / 8000, 2),
+                              "rounds_us": [round(v, 2) for v in t]}), flush=True)
+        del qkv
+        torch.cuda.empty_cache()
+
+
+def qk_pattern_summary(log: str) -> None:
+    import json
+
+    rows = [json.loads(x) for x in open(log) if x.startswith("{")]
+    print("qk_norm_rope_fwd against its access pattern with no arithmetic (q and k bytes of each token read")
+    print("and written back in place; % of 8 TB/s on 2 x T x 40 x 128 x 2 B):")
+    for r in rows:
+        print(f"  T={r['T']:<6} {r['kernel']:<22} {r['median_us']:>8.2f} us {r['pct']:>6.2f}%  rounds "
+              + " ".join(f"{v:.1f}" for v in r["rounds_us"]))
+
+
 STREAM_VARIANTS = {
     0: (16384, "128 lanes/row, 2 buffers, 2 WGs/CU"),
     1: (16384, "256 lanes/row, 2 buffers, 2 WGs/CU"),
@@ -1707,6 +1794,10 @@ if __name__ == "__main__":
         sizes()
     elif len(sys.argv) == 2 and sys.argv[1] == "staging":
         staging()
+    elif len(sys.argv) == 2 and sys.argv[1] == "qk-pattern":
+        qk_pattern()
+    elif len(sys.argv) == 3 and sys.argv[1] == "qk-pattern-summary":
+        qk_pattern_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "late-weights":
         late_weights()
     elif len(sys.argv) == 3 and sys.argv[1] in ("staging-summary", "late-weights-summary"):

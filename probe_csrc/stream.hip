@@ -74,6 +74,28 @@ __global__ void __launch_bounds__(256) stream_copy_policy(const u32x4* __restric
   }
 }
 
+// The QK-norm + RoPE kernel's memory access pattern with no arithmetic: for
+// each token row of `row` 16-byte chunks, the first `qk` chunks (the q and k
+// heads) are read and written back in place (v untouched), one workgroup of
+// 256 lanes per token, every load issued before the first store, loads and
+// stores non-temporal as in the kernel. The xor with `key` (0 from the host)
+// keeps the stores from being folded away.
+__global__ void __launch_bounds__(256) stream_qk_pattern(u32x4* __restrict__ qkv, int row, int qk, uint32_t key) {
+  u32x4* t = qkv + (size_t)blockIdx.x * row;
+  constexpr int kMax = 4;  // up to 4 * 256 chunks (16 KiB) of q and k per token
+  u32x4 v[kMax];
+#pragma unroll
+  for (int j = 0; j < kMax; ++j) {
+    const int k = j * 256 + threadIdx.x;
+    if (k < qk) v[j] = __builtin_nontemporal_load(t + k);
+  }
+#pragma unroll
+  for (int j = 0; j < kMax; ++j) {
+    const int k = j * 256 + threadIdx.x;
+    if (k < qk) __builtin_nontemporal_store(v[j] ^ key, t + k);
+  }
+}
+
 typedef void (*PolicyCopy)(const u32x4*, u32x4*);
 const PolicyCopy kPolicyCopies[2][4] = {
     {&stream_copy_policy<1, 0>, &stream_copy_policy<1, 1>, &stream_copy_policy<1, 2>, &stream_copy_policy<1, 3>},
@@ -139,6 +161,17 @@ __attribute__((visibility("default"))) int mbn_stream_copy_policy(const void* sr
   const size_t grid = bytes / ((size_t)256 * chunks * 16);
   hipLaunchKernelGGL(kPolicyCopies[chunks == 8][policy], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4*)src, (u32x4*)dst);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// stream_qk_pattern over T token rows of `row` chunks, the first `qk` of them
+// read and written back (qk <= 1024 <= row). 0 = ok, 1 = invalid, 3 = launch
+// failed.
+__attribute__((visibility("default"))) int mbn_stream_qk_pattern(void* qkv, int64_t T, int row, int qk,
+                                                                 void* stream) {
+  if (!qkv || ((uintptr_t)qkv & 15) != 0 || T <= 0 || T > 0x7fffffff || qk <= 0 || qk > 1024 || row < qk) return 1;
+  hipLaunchKernelGGL(stream_qk_pattern, dim3((unsigned)T), dim3(256), 0, (hipStream_t)stream, (u32x4*)qkv, row, qk,
+                     0u);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

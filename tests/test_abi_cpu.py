@@ -272,6 +272,9 @@ def test_stream_reference_library_loads_and_validates():
     assert h.mbn_stream_copy_policy(FAKE, FAKE + (1 << 30), 4096, 1, 4, None) == 1  # no such policy
     assert h.mbn_stream_copy_policy(FAKE, FAKE + (1 << 30), 4096, 2, 1, None) == 1  # no such shape
     assert h.mbn_stream_copy_policy(FAKE, FAKE + (1 << 30), 4096 + 16, 1, 1, None) == 1  # ragged
+    assert h.mbn_stream_qk_pattern(FAKE, 16, 768, 1025, None) == 1  # more q/k chunks than the kernel holds
+    assert h.mbn_stream_qk_pattern(FAKE, 16, 600, 640, None) == 1  # row shorter than its q/k part
+    assert h.mbn_stream_qk_pattern(FAKE + 8, 16, 768, 640, None) == 1  # misaligned
 
 
 def test_c_client_builds_and_sees_host_validation():

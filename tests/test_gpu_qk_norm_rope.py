@@ -9,7 +9,7 @@ import pytest
 import memory_bound_normalization_amd as mbn
 from oracle import qk_norm_rope_fwd as oracle_qk
 from parity import assert_parity, assert_parity_rows, from_gpu_bf16, to_gpu_bf16
-from workloads import QK_WORKLOADS, make_qk_inputs, random_bf16_bits
+from workloads import QK_WORKLOADS, make_qk_inputs, random_bf16_bits, random_f16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -159,3 +159,58 @@ def test_many_tokens():
                                                           1e-6, 1e6), "large T", block=1024)
     assert n == after.size
     assert np.array_equal(after[:, (hq + hk) * D:], before[:, (hq + hk) * D:])
+
+
+# Launch shapes that keep several head rows of a wave in flight: 5 waves of two
+# steps (513 ... 1024 tokens), 4 waves of three (more tokens), and more heads
+# than 48, where a wave loads a second group of rows after the first three.
+@pytest.mark.parametrize("T,hq,hk,rot,dtype", [
+    (700, 32, 8, 128, "bf16"),  # 5 waves x 2 steps
+    (700, 30, 3, 64, "f16"),  # 33 heads: the last step of one wave holds 1 live head
+    (1500, 32, 8, 48, "bf16"),  # 4 waves x 3 steps, partial rotary
+    (1500, 70, 9, 128, "bf16"),  # 79 heads: 5 steps per wave, two load groups, ragged
+    (2500, 61, 2, 112, "f16"),  # 63 heads, partial rotary
+    (9000, 32, 8, 128, "bf16"),
+])
+def test_rows_in_flight(T, hq, hk, rot, dtype):
+    label = f"T={T} hq={hq} hk={hk} rot={rot} {dtype}"
+    print(f"[qk rows in flight] {label}", flush=True)
+    rng = np.random.default_rng(T + 7 * hq + hk)
+    gen = random_f16_bits if dtype == "f16" else random_bf16_bits
+    qkv = gen(rng, (T, (hq + 2 * hk) * D))
+    q_w = gen(rng, (D,), lo=0.5, hi=1.5)
+    k_w = gen(rng, (D,), lo=0.5, hi=1.5)
+    pos = rng.integers(0, 1 << 20, T).astype(np.int64)
+    g = to_gpu_bf16(qkv, dtype=dtype)
+    mbn.qk_norm_rope_fwd(g, to_gpu_bf16(q_w, dtype=dtype), to_gpu_bf16(k_w, dtype=dtype),
+                         torch.from_numpy(pos).cuda(), hq, hk, D, eps=1e-6, theta=1e6,
+                         rotary_dim=None if rot == D else rot)
+    torch.cuda.synchronize()
+    got = from_gpu_bf16(g)
+    nk = (hq + hk) * D
+    assert np.array_equal(got[:, nk:], qkv[:, nk:]), "v heads changed"
+    ref = oracle_qk(qkv, q_w, k_w, pos, hq, hk, D, 1e-6, 1e6, rotary_dim=rot, dtype=dtype)
+    assert_parity(got, ref, label, dtype=dtype)
+
+
+@pytest.mark.parametrize("T", [7, 700, 1500])
+@pytest.mark.parametrize("hq,hk", [(0, 5), (9, 0)])
+def test_null_weight_of_absent_heads(T, hq, hk):
+    """The C ABI takes a null q_w when there are no q heads (null k_w when
+    there are no kv heads); the kernel must not read it."""
+    print(f"[qk null weight] T={T} hq={hq} hk={hk}", flush=True)
+    rng = np.random.default_rng(31 * T + hq)
+    qkv = random_bf16_bits(rng, (T, (hq + 2 * hk) * D))
+    w = random_bf16_bits(rng, (D,), lo=0.5, hi=1.5)
+    pos = rng.integers(0, 1 << 20, T).astype(np.int64)
+    g = to_gpu_bf16(qkv)
+    wg = to_gpu_bf16(w)
+    p = torch.from_numpy(pos).cuda()
+    q_ptr = wg.data_ptr() if hq else None
+    k_ptr = wg.data_ptr() if hk else None
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = mbn.lib().qk_norm_rope_fwd(g.data_ptr(), q_ptr, k_ptr, p.data_ptr(), T, hq, hk, D, 1e-6, 1e6, stream)
+    assert rc == mbn.MBN_OK
+    torch.cuda.synchronize()
+    ref = oracle_qk(qkv, w, w, pos, hq, hk, D, 1e-6, 1e6)
+    assert_parity(from_gpu_bf16(g), ref, f"null weight T={T} hq={hq} hk={hk}")

@@ -177,3 +177,26 @@ def test_ab_summary_table(tmp_path, capsys):
     assert "late weight (library) against early weight (before)" in out
     assert "8192x8192      events          44.00   1.00     46.00   1.00  0.957" in out
     assert "99.0000% bit-identical" in out
+
+
+def test_qk_pattern_summary_table(tmp_path, capsys):
+    log = tmp_path / "qkpat.log"
+    log.write_text(
+        "noise line\n"
+        '{"T": 65536, "kernel": "qk_norm_rope_fwd", "median_us": 215.0, "pct": 78.07, "rounds_us": [215.3, 214.9]}\n'
+        '{"T": 65536, "kernel": "access pattern only", "median_us": 214.5, "pct": 78.25, "rounds_us": [214.5]}\n')
+    probe.qk_pattern_summary(str(log))
+    out = capsys.readouterr().out
+    assert "T=65536  qk_norm_rope_fwd         215.00 us  78.07%  rounds 215.3 214.9" in out
+    assert "T=65536  access pattern only      214.50 us  78.25%  rounds 214.5" in out
+
+
+def test_qk_counter_summary_matches_every_kmax_instance(tmp_path):
+    """The QK kernel is a template over the rows a wave keeps in flight; each
+    instance counts as the measured kernel."""
+    d = tmp_path / "fetch"
+    _write(str(d), "FETCH_SIZE", [("void mbn::(anonymous namespace)::qk_norm_rope_kernel<mbn::Bf16, 3>(unsigned short*)", 7.0),
+                                  ("void mbn::(anonymous namespace)::qk_norm_rope_kernel<mbn::Bf16, 1>(unsigned short*)", 5.0),
+                                  ("__amd_rocclr_copyBuffer", 20.0)])
+    res = probe._per_kernel(str(d), "FETCH_SIZE", "qk_norm_rope", "copyBuffer")
+    assert res == {"rmsnorm": [7.0, 5.0], "copy": [20.0]}
