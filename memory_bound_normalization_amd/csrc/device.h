@@ -121,6 +121,20 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b mod 8). With group = G > 0, XCD x is given runs of G consecutive row
+// blocks instead of every 8th one, which changes how the concurrent HBM
+// traffic of the XCDs interleaves; G = 0 keeps the identity. The remap is a
+// bijection on the leading blocks that fill whole groups of 8*G; the rest keep
+// their own index.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nblocks, int group) {
+  if (group <= 0) return b;
+  const int64_t span = 8 * (int64_t)group;
+  if (b >= (nblocks / span) * span) return b;
+  const int64_t xcd = b & 7, i = b >> 3;
+  return (i / group) * span + xcd * group + (i % group);
+}
+
 // Streaming 16-byte store (global_store_dwordx4 ... nt).
 __device__ __forceinline__ void store_nt_16(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));

@@ -53,9 +53,10 @@ struct RowNormAnyArgs {
   uint16_t* h;
   uint16_t* y;
   int64_t M;
-  int n;        // N
-  float inv_n;  // set by the launcher
+  int n;          // N
+  float inv_n;    // set by the launcher
   float eps;
+  int xcd_group;  // set by the launcher (row blocks per XCD run, 16-byte staged kernels)
 };
 
 hipError_t launch_rownorm_any(Norm mode, Storage dtype, RowNormAnyArgs args, hipStream_t stream);

@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_any_kernel(RowNormAnyArgs 
   const int N = a.n;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t e0 = (int64_t)blockIdx.x * N;  // first element of this row
+  const int64_t e0 = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group) * N;  // first element of this row
   // Groups start `head` elements into the row; `tail` elements follow them.
   int head = 0, ng = N / G, tail = 0;
   if constexpr (SHIFT) {
@@ -277,25 +277,38 @@ __device__ __forceinline__ u32x4 window16(u32x4 lo, u32x4 hi, int sh) {
 // Element e (0 ... 7) of a 16-byte chunk, as raw 16-bit bits.
 __device__ __forceinline__ uint32_t chunk_elem(u32x4 v, int e) { return (v[e >> 1] >> (16 * (e & 1))) & 0xffffu; }
 
-// Elements [p0, p0 + 8) of the N-element vector p as one chunk: the 16 bytes
-// straddle two aligned chunks of p (uniform shift per row). `whole`: all eight
-// are elements of p (the interior chunks), else only those in [0, N) are read
-// and the rest are zero.
-__device__ __forceinline__ u32x4 vec_chunk(const uint16_t* p, int64_t p0, int N, bool whole) {
-  if (whole) {
-    const uintptr_t wa = reinterpret_cast<uintptr_t>(p) + 2 * p0;
-    const u32x4* A = reinterpret_cast<const u32x4*>(wa & ~(uintptr_t)15);
-    const int sh = (int)(wa & 15);
-    const u32x4 lo = A[0];
-    return sh ? window16(lo, A[1], sh) : lo;
+// A vector p of N elements (the weight or the bias, 2-byte aligned) on the
+// chunk grid of a row whose first element sits h elements into its 16-byte
+// block: output chunk k holds row elements [8k - h, 8k - h + 8), whose p
+// elements are bytes [sh, sh + 16) of the aligned blocks k and k + 1, counted
+// from the block that holds the address of element -h. Both block indices are
+// clamped into [b0, b1], the blocks that hold elements of p, so nothing
+// outside them is read. Clamping changes only bytes of elements outside
+// [0, N), which in the first and last chunk of a row belong to no row element:
+// a row element's byte lies in block k or k + 1, and that block holds an
+// element of p, hence lies in [b0, b1] and is left unclamped.
+struct VecGrid {
+  typedef const __attribute__((address_space(1))) u32x4* gvec;
+  gvec base;
+  int sh, b0, b1;
+  __device__ __forceinline__ VecGrid(const uint16_t* p, int h, int N) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t a0 = pa - 2 * (uintptr_t)h;
+    base = (gvec)(a0 & ~(uintptr_t)15);
+    sh = (int)(a0 & 15);
+    b0 = (int)((pa >> 4) - (a0 >> 4));
+    b1 = (int)(((pa + 2 * (uintptr_t)N - 2) >> 4) - (a0 >> 4));
   }
-  u32x4 o = {0u, 0u, 0u, 0u};
-  for (int e = 0; e < 8; ++e) {
-    const int64_t q = p0 + e;
-    if (q >= 0 && q < N) o[e >> 1] |= (uint32_t)p[q] << (16 * (e & 1));
+  // The two blocks of chunk k (the second repeats the first when the window
+  // is block-aligned).
+  __device__ __forceinline__ void load(int k, u32x4& lo, u32x4& hi) const {
+    const int l = k > b0 ? k : b0;
+    const int u = sh ? (k + 1 < b1 ? k + 1 : b1) : l;
+    lo = base[l];
+    hi = base[u];
   }
-  return o;
-}
+  __device__ __forceinline__ u32x4 window(u32x4 lo, u32x4 hi) const { return window16(lo, hi, sh); }
+};
 
 // Row norms whose rows start anywhere inside a 16-byte block (N % 8 != 0, or
 // element-aligned base pointers), with x, y (and r, h) at the same address
@@ -307,9 +320,11 @@ __device__ __forceinline__ u32x4 vec_chunk(const uint16_t* p, int64_t p0, int N,
 // every interior chunk is one 16-byte store; the two edge chunks store their
 // row elements one by one. The weight (bias) chunk of an output chunk starts
 // h elements before the chunk (h = the row's offset in its first block): two
-// aligned 16-byte loads from L2, shifted by a byte count that is uniform over
-// the row.
-template <Norm MODE, typename DT, int WAVES, int MAXC>
+// aligned 16-byte loads from L2 (VecGrid), shifted by a byte count that is
+// uniform over the row. The loads of all the lane's chunks are issued after
+// pass 1, ahead of the reduction, and waited for once before pass 2.
+// Workgroup b serves row xcd_remap(b) (runs of xcd_group rows per XCD).
+template <Norm MODE, typename DT, int WAVES, int MAXC, bool BATCH>
 __global__ void __launch_bounds__(64 * WAVES) rownorm_s16_kernel(RowNormAnyArgs a) {
   constexpr int T = 64 * WAVES;
   constexpr bool kHasR = MODE == Norm::kAddRms;
@@ -318,7 +333,7 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_s16_kernel(RowNormAnyArgs 
   const int N = a.n;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t e0 = (int64_t)blockIdx.x * N;  // first element of this row
+  const int64_t e0 = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group) * N;  // first element of this row
   const uintptr_t xs = reinterpret_cast<uintptr_t>(a.x + e0);
   const int h = (int)((xs & 15) >> 1);  // elements of the first block before the row
   const int nck = (h + N + 7) >> 3;     // chunks covering the row
@@ -379,6 +394,24 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_s16_kernel(RowNormAnyArgs 
       }
     }
   }
+  // BATCH: the weight (bias) blocks of every chunk of the lane, issued
+  // before the reduction (lanes past the row's last chunk load that chunk's
+  // blocks); else each chunk's blocks are loaded in pass 2 where it is
+  // computed (fewer registers: 8 per chunk and vector).
+  constexpr bool kHasW = MODE != Norm::kL2;
+  constexpr bool kHasB = MODE == Norm::kLayer;
+  constexpr int kHeld = BATCH ? MAXC : 1;
+  const VecGrid wg(a.w, h, N), bg(a.b, h, N);
+  u32x4 wlo[kHasW ? kHeld : 1], whi[kHasW ? kHeld : 1];
+  u32x4 blo[kHasB ? kHeld : 1], bhi[kHasB ? kHeld : 1];
+  if constexpr (BATCH) {
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int k = j * T + t < nck ? j * T + t : nck - 1;
+      if constexpr (kHasW) wg.load(k, wlo[j], whi[j]);
+      if constexpr (kHasB) bg.load(k, blo[j], bhi[j]);
+    }
+  }
   const float s1 = group_sum<WAVES>(acc, part[0], wave);
 
   float mu = 0.f, scale;
@@ -409,6 +442,9 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_s16_kernel(RowNormAnyArgs 
   }
 
   u32x4* yc = const_cast<u32x4*>(chunk_ptr(a.y));
+  // The batched weight (bias) blocks: one wait here, none between the stores
+  // below.
+  if constexpr (BATCH) wait_vmem();
 
   // Pass 2 (from LDS): normalize, weight (and bias), round, store.
 #pragma unroll
@@ -419,8 +455,12 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_s16_kernel(RowNormAnyArgs 
       const bool edge = is_edge(k);
       const int64_t p0 = 8 * (int64_t)k - h;
       u32x4 wv{}, bv{};
-      if constexpr (MODE != Norm::kL2) wv = vec_chunk(a.w, p0, N, !edge);
-      if constexpr (MODE == Norm::kLayer) bv = vec_chunk(a.b, p0, N, !edge);
+      if constexpr (!BATCH) {
+        if constexpr (kHasW) wg.load(k, wlo[0], whi[0]);
+        if constexpr (kHasB) bg.load(k, blo[0], bhi[0]);
+      }
+      if constexpr (kHasW) wv = wg.window(wlo[BATCH ? j : 0], whi[BATCH ? j : 0]);
+      if constexpr (kHasB) bv = bg.window(blo[BATCH ? j : 0], bhi[BATCH ? j : 0]);
       u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -502,31 +542,48 @@ const AnyCfg kAny4[] = {
 struct S16Cfg {
   int max_nck;
   int waves;
-  RowNormAnyKernel k[4][2];  // [mode][bf16, fp16]
+  int xcd_group;
+  RowNormAnyKernel k[2];  // [bf16, fp16]
 };
-#define MBN_S16_MODE(MODE, W, C) \
-  { &rownorm_s16_kernel<MODE, Bf16, W, C>, &rownorm_s16_kernel<MODE, F16, W, C> }
-#define MBN_S16(W, C)                                                                        \
-  S16Cfg {                                                                                   \
-    64 * (W) * (C), W, {                                                                     \
-      MBN_S16_MODE(Norm::kRms, W, C), MBN_S16_MODE(Norm::kAddRms, W, C),                     \
-          MBN_S16_MODE(Norm::kLayer, W, C), MBN_S16_MODE(Norm::kL2, W, C)                    \
-    }                                                                                        \
-  }
-// Eight chunks per lane throughout; the lanes per row follow the width (a
-// sweep of 1-16 waves x 1-32 chunks x occupancy caps on MI355X at N = 2047,
-// 4095, 8191, 16380, 16383, 16384 (element offset 1) and 32767: these were
-// the fastest or within 2% of it, without caps).
-const S16Cfg kS16[] = {
-    MBN_S16(1, 1),   // N <= 498:   64 lanes
-    MBN_S16(1, 2),   // N <= 1010
-    MBN_S16(1, 4),   // N <= 2034
-    MBN_S16(1, 8),   // N <= 4082
-    MBN_S16(2, 8),   // N <= 8178:  128 lanes
-    MBN_S16(4, 8),   // N <= 16370: 256 lanes
-    MBN_S16(8, 8),   // N <= 32754: 512 lanes
-    MBN_S16(16, 8),  // N <= 65522: 1024 lanes
+#define MBN_S16(MODE, W, C, G, B) \
+  S16Cfg { 64 * (W) * (C), W, G, {&rownorm_s16_kernel<MODE, Bf16, W, C, B>, &rownorm_s16_kernel<MODE, F16, W, C, B>} }
+// Bands by the widest chunk count of the launch (64 * waves * chunks per
+// lane), from a sweep on MI355X of 1-16 waves x 1-8 chunks x XCD runs of 0, 8
+// and 16 rows x batched or per-chunk weight loads at N = 511 and 1023
+// (element offset 1), 1535, 2047, 3071, 4095, 8191, 16383, 32767 and 65521
+// (about 256 MiB per launch): the fastest entry or one within 1.5% of it.
+// RMSNorm (also the residual add, and L2Norm, which has no weight):
+#define MBN_S16_RMS_BANDS(MODE)                                                                  \
+  MBN_S16(MODE, 1, 2, 8, true),       /* N <= 1010:  64 lanes */                                  \
+      MBN_S16(MODE, 1, 3, 8, true),   /* N <= 1522 */                                             \
+      MBN_S16(MODE, 2, 2, 8, true),   /* N <= 2034:  128 lanes */                                 \
+      MBN_S16(MODE, 2, 3, 8, false),  /* N <= 3058 */                                             \
+      MBN_S16(MODE, 4, 2, 8, true),   /* N <= 4082:  256 lanes */                                 \
+      MBN_S16(MODE, 4, 4, 8, false),  /* N <= 8178 */                                             \
+      MBN_S16(MODE, 8, 4, 8, false),  /* N <= 16370: 512 lanes */                                 \
+      MBN_S16(MODE, 16, 3, 8, true),  /* N <= 24562: 1024 lanes */                                \
+      MBN_S16(MODE, 16, 8, 8, false)  /* N <= 65522 */
+const S16Cfg kS16Rms[] = {MBN_S16_RMS_BANDS(Norm::kRms)};
+const S16Cfg kS16AddRms[] = {MBN_S16_RMS_BANDS(Norm::kAddRms)};
+const S16Cfg kS16L2[] = {MBN_S16_RMS_BANDS(Norm::kL2)};
+// LayerNorm (weight and bias: fewer lanes, more chunks per lane, per-chunk
+// loads):
+const S16Cfg kS16Layer[] = {
+    MBN_S16(Norm::kLayer, 1, 2, 0, true),    // N <= 1010:  64 lanes
+    MBN_S16(Norm::kLayer, 1, 4, 8, false),   // N <= 2034
+    MBN_S16(Norm::kLayer, 1, 8, 8, false),   // N <= 4082
+    MBN_S16(Norm::kLayer, 2, 8, 8, false),   // N <= 8178:  128 lanes
+    MBN_S16(Norm::kLayer, 4, 8, 8, false),   // N <= 16370: 256 lanes
+    MBN_S16(Norm::kLayer, 8, 8, 8, false),   // N <= 32754: 512 lanes
+    MBN_S16(Norm::kLayer, 16, 8, 8, false),  // N <= 65522: 1024 lanes
 };
+
+template <size_t K>
+const S16Cfg* pick_s16(const S16Cfg (&table)[K], int max_nck) {
+  for (const S16Cfg& c : table)
+    if (max_nck <= c.max_nck) return &c;
+  return nullptr;
+}
 // From kS16MinN on, the staged kernels serve every width except rows of whole
 // 4-element groups on 8-byte aligned pointers (N % 4 == 0), where the group
 // kernels measured faster (16384 x 16380: 195 against 207 us); from
@@ -572,12 +629,14 @@ hipError_t launch_rownorm_any_rows(Norm mode, Storage dtype, RowNormAnyArgs args
   const bool s16 = args.n >= kS16MinN ? !(args.n % 4 == 0 && g4 == 4) : (args.n >= kS16MinNarrow && g4 < 4);
   if (s16 && same16(args.y) && same16(args.r) && same16(args.h)) {
     const int max_nck = (args.n + 14) >> 3;
-    for (const S16Cfg& c : kS16) {
-      if (max_nck <= c.max_nck) {
-        hipLaunchKernelGGL(c.k[(int)mode][d], dim3((unsigned)args.M), dim3(64 * c.waves), (size_t)max_nck * 16,
-                           stream, args);
-        return hipGetLastError();
-      }
+    const S16Cfg* c = mode == Norm::kLayer    ? pick_s16(kS16Layer, max_nck)
+                      : mode == Norm::kAddRms ? pick_s16(kS16AddRms, max_nck)
+                      : mode == Norm::kL2     ? pick_s16(kS16L2, max_nck)
+                                              : pick_s16(kS16Rms, max_nck);
+    if (c) {
+      args.xcd_group = c->xcd_group;
+      hipLaunchKernelGGL(c->k[d], dim3((unsigned)args.M), dim3(64 * c->waves), (size_t)max_nck * 16, stream, args);
+      return hipGetLastError();
     }
   }
   const int g = rownorm_any_group(args);

@@ -68,9 +68,13 @@ probe_csrc/prior_entries.hip; same data, outputs compared first.
 
     python probe.py qk-pattern > <log>
     python probe.py qk-pattern-summary <log>
+    python probe.py any-width-ab > <log>
+    python probe.py any-width-summary <log>
 
 `qk-pattern` times qk_norm_rope_fwd against its memory access pattern with no
 arithmetic (the q and k bytes of each token read and written back in place).
+`any-width-ab` times the any-width row norms against the prior any-width path
+(probe_csrc/prior_any_width.hip).
 
 The other commands, each the source of a committed summary: `timeline`,
 `timeline-summary` (per-workgroup timelines), `variants`, `claim`, `stream`,
@@ -1281,6 +1285,149 @@ def late_weights() -> None:
               lambda h, *args: h.mbn_early_w_rmsnorm(*args), 1e-6, lambda N: False, 29)
 
 
+PRIOR_ANY_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_prior_any.so")
+
+
+def build_prior_any(verbose: bool = False) -> str:
+    """Compile probe_csrc/prior_any_width.hip (the any-width launch path
+    before the staged kernels' weight windows became unconditional loads and
+    their tables were re-swept) into probe_csrc/libmbn_prior_any.so; always
+    rebuilds."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=PRIOR_ANY_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "prior_any_width.hip")])
+
+
+def prior_any_lib():
+    if not os.path.exists(PRIOR_ANY_LIB_PATH):
+        build_prior_any()
+    h = ctypes.CDLL(PRIOR_ANY_LIB_PATH)
+    h.mbn_prior_any_rownorm.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 6 + [
+        ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    h.mbn_prior_any_rownorm.restype = ctypes.c_int
+    return h
+
+
+# (N, element offset of every row tensor): widths that take the 16-byte staged
+# kernels (N % 8 != 0 from 1024 on; below, pointers that are not 8-byte
+# aligned), one per band of the tables and a view of an aligned width.
+ANY_AB_SHAPES = [(300, 1), (511, 1), (777, 3), (1023, 1), (1523, 0), (2047, 0), (3059, 0), (4095, 0), (8191, 0),
+                 (16383, 0), (16384, 1), (24563, 0), (32767, 0), (65521, 0)]
+ANY_AB_OPS = ("rms", "add", "layer", "l2")
+
+
+def any_width_ab(rounds: int = 6, launches: int = 40) -> None:
+    """The any-width row norms of the library against the prior any-width
+    path (libmbn_prior_any.so) on the same data, per width and op: outputs
+    compared (one bf16 ulp, or 2^-14 absolute), then per round, in
+    alternating order, the median of `launches` individually timed launches
+    over buffer sets rotated through >= 1 GiB (about 256 MiB of rows each).
+    One JSON line per width, op and kernel."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    h = prior_any_lib()
+    lib = mbn.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    g = torch.Generator(device=dev).manual_seed(37)
+    mode = {"rms": 0, "add": 1, "layer": 2, "l2": 3}
+    for N, off in ANY_AB_SHAPES:
+        M = max(1, (1 << 27) // N)
+        n = max(2, -(-(1 << 30) // (M * N * 2)))
+        size = M * N + off + 8
+        xs = [torch.randn(size, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+        rs = [torch.randn(size, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+        hs = [torch.empty_like(xs[0]) for _ in range(n)]
+        ys = [torch.empty_like(xs[0]) for _ in range(n)]
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        b = (torch.rand(N, device=dev, generator=g) - 0.5).to(torch.bfloat16)
+
+        def ptr(t, i):
+            return t[i].data_ptr() + 2 * off
+
+        for op in ANY_AB_OPS:
+            def new(i, op=op):
+                x, y = ptr(xs, i), ptr(ys, i)
+                if op == "rms":
+                    rc = lib.rmsnorm_fwd(x, w.data_ptr(), y, M, N, 1e-6, sp)
+                elif op == "add":
+                    rc = lib.add_rmsnorm_fwd(x, ptr(rs, i), w.data_ptr(), ptr(hs, i), y, M, N, 1e-6, sp)
+                elif op == "layer":
+                    rc = lib.layernorm_fwd(x, w.data_ptr(), b.data_ptr(), y, M, N, 1e-6, sp)
+                else:
+                    rc = lib.l2norm_fwd(x, y, M, N, 1e-6, sp)
+                if rc != 0:
+                    raise RuntimeError(f"{op} N={N}: status {rc}")
+
+            def old(i, op=op):
+                rc = h.mbn_prior_any_rownorm(mode[op], 0, ptr(xs, i), ptr(rs, i), w.data_ptr(), b.data_ptr(),
+                                             ptr(hs, i), ptr(ys, i), M, N, 1e-6, sp)
+                if rc != 0:
+                    raise RuntimeError(f"prior {op} N={N}: status {rc}")
+
+            fns = {"library": new, "before": old}
+            outs = []
+            for fn in fns.values():
+                ys[0].zero_()
+                fn(0)
+                torch.cuda.synchronize()
+                outs.append(ys[0][off:off + M * N].float().clone())
+            a, b2 = outs
+            if not bool(((a - b2).abs() <= b2.abs() * 2.0 ** -7 + 2.0 ** -14).all()):
+                raise RuntimeError(f"{op} N={N}: the two paths' outputs differ by more than one bf16 ulp")
+            del outs, a, b2
+            nb = (4 if op == "add" else 2) * M * N * 2
+            res = {k: [] for k in fns}
+            for fn in fns.values():
+                for i in range(20):
+                    fn(i % n)
+            torch.cuda.synchronize()
+            for rnd in range(rounds):
+                for k in (list(fns) if rnd % 2 == 0 else list(fns)[::-1]):
+                    ev = [(timer.new(), timer.new()) for _ in range(launches)]
+                    for i, (e0, e1) in enumerate(ev):
+                        timer.record(e0)
+                        fns[k](i % n)
+                        timer.record(e1)
+                    torch.cuda.synchronize()
+                    us = sorted(timer.elapsed_ms(e0, e1) * 1e3 for e0, e1 in ev)
+                    timer.close()
+                    res[k].append(us[len(us) // 2])
+            for k, t in res.items():
+                us = sorted(t)[len(t) // 2]
+                print(json.dumps({"N": N, "M": M, "offset": off, "op": op, "kernel": k, "median_us": round(us, 2),
+                                  "pct": round(100 * nb / us / 1e3 / 8000, 2), "rounds_us": [round(v, 2) for v in t]}),
+                      flush=True)
+        del xs, rs, hs, ys
+        torch.cuda.empty_cache()
+
+
+def any_width_summary(log: str) -> None:
+    """Table of an any-width-ab log: library against the prior path per width
+    and op, with the ratio before / library."""
+    import json
+
+    rows = [json.loads(x) for x in open(log) if x.startswith("{")]
+    by = {}
+    for r in rows:
+        by.setdefault((r["N"], r["offset"], r["M"], r["op"]), {})[r["kernel"]] = r
+    print("Any-width row norms: library against the prior any-width path, same data, per-launch median")
+    print("of 40 launches, median over rounds; % of 8 TB/s on the algorithmic bytes:")
+    print(f"  {'N':>6} {'off':>3} {'M':>6} {'op':<6} {'library us':>10} {'%':>6} {'before us':>9} {'%':>6} {'speedup':>7}")
+    for (N, off, M, op), d in by.items():
+        new, old = d["library"], d["before"]
+        print(f"  {N:>6} {off:>3} {M:>6} {op:<6} {new['median_us']:>10.2f} {new['pct']:>6.1f} "
+              f"{old['median_us']:>9.2f} {old['pct']:>6.1f} {old['median_us'] / new['median_us']:>7.3f}")
+
+
 def ab_summary(log: str) -> None:
     """Table of a staging / late-weights log: the library against the prior
     entry, per shape and timing."""
@@ -1794,6 +1941,10 @@ if __name__ == "__main__":
         sizes()
     elif len(sys.argv) == 2 and sys.argv[1] == "staging":
         staging()
+    elif len(sys.argv) == 2 and sys.argv[1] == "any-width-ab":
+        any_width_ab()
+    elif len(sys.argv) == 3 and sys.argv[1] == "any-width-summary":
+        any_width_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "qk-pattern":
         qk_pattern()
     elif len(sys.argv) == 3 and sys.argv[1] == "qk-pattern-summary":

@@ -38,7 +38,8 @@ WIDTHS = [
     1, 3, 7, 9, 511, 513, 2047, 2049, 8191, 8193, 12345, 32767, 32769, 40001, 65535,  # odd: 1 element
     2, 6, 1002, 1026, 4094, 4098, 8190, 8194, 32766, 32770, 65534,  # N % 4 == 2: 2 elements
     12, 100, 1004, 1028, 4092, 4100, 8188, 8196, 32764, 32772, 40000, 65532,  # N % 8 == 4: 4 elements
-    4082, 4083, 8178, 8179, 16370, 16371, 32754, 32755, 65522, 65523,  # staged-kernel band edges
+    1522, 1523, 3058, 3059, 4082, 4083, 8178, 8179, 16370, 16371, 24562, 24563, 32754, 32755,  # staged-kernel
+    65522, 65523,  # band edges
 ]
 GUARD = 8  # guard elements around an output view (16 bytes: keeps the view's alignment)
 FILL = 0x4B00  # bf16 / fp16 bit pattern the guards hold
@@ -72,15 +73,28 @@ def _guards_intact_at(buf, M, N, guard):
     return bool(np.all(g == FILL))
 
 
-def _check(op, M, N, seed, dtype="bf16", eps=1e-6, offset=0, out_offset=None):
+def _vec_view(bits, off, dtype):
+    """A GPU copy of the vector `bits` starting `off` elements into a fresh
+    allocation (off % 8 != 0: inside a 16-byte block)."""
+    g = to_gpu_bf16(bits, dtype=dtype)
+    if not off:
+        return g
+    buf = torch.zeros(g.numel() + off, dtype=g.dtype, device="cuda")
+    buf[off:] = g
+    return buf[off:]
+
+
+def _check(op, M, N, seed, dtype="bf16", eps=1e-6, offset=0, out_offset=None, w_off=0, b_off=0):
     """`offset` (elements) places x and r at that offset from an aligned
     address, `out_offset` (default: the same) the outputs: element-aligned
-    pointers (2- or 1-element groups, or staged chunks at a block offset)."""
+    pointers (2- or 1-element groups, or staged chunks at a block offset);
+    `w_off` and `b_off` the weight and the bias."""
     out_offset = offset if out_offset is None else out_offset
-    print(f"[any-width {op} {dtype}] M={M} N={N} offset={offset} out_offset={out_offset}", flush=True)
+    print(f"[any-width {op} {dtype}] M={M} N={N} offset={offset} out_offset={out_offset} w_off={w_off} "
+          f"b_off={b_off}", flush=True)
     x, r, w, b = _inputs(M, N, seed, dtype)
     xg, rg = to_gpu_bf16(x, dtype=dtype), to_gpu_bf16(r, dtype=dtype)
-    wg, bg = to_gpu_bf16(w, dtype=dtype), to_gpu_bf16(b, dtype=dtype)
+    wg, bg = _vec_view(w, w_off, dtype), _vec_view(b, b_off, dtype)
     if offset:
         xb = torch.zeros(M * N + offset, dtype=xg.dtype, device="cuda")
         xb[offset:] = xg.view(-1)
@@ -145,6 +159,16 @@ def test_any_width_mixed_offsets(op, N):
 @pytest.mark.parametrize("op", ["rms", "add", "layer", "l2"])
 def test_any_width_f16(op, N):
     _check(op, _rows(N), N, seed=N + 1, dtype="f16", eps=1e-5)
+
+
+# Weight and bias views that start inside a 16-byte block: the staged kernels
+# read each weight (bias) chunk as a shifted window of the two aligned blocks
+# under it, clamped to the blocks that hold the vector's elements.
+@pytest.mark.parametrize("N,w_off,b_off", [(1011, 3, 3), (1523, 7, 3), (2049, 1, 6), (3059, 4, 1), (8193, 2, 0),
+                                           (16383, 5, 2), (24563, 2, 7), (40001, 3, 3), (65535, 6, 5)])
+@pytest.mark.parametrize("op", ["rms", "add", "layer"])
+def test_staged_weight_offsets(op, N, w_off, b_off):
+    _check(op, _rows(N), N, seed=N + 11, offset=1 if N < 1024 else 0, w_off=w_off, b_off=b_off)
 
 
 @pytest.mark.parametrize("M", [1, 2, 65, 20000])

@@ -200,3 +200,15 @@ def test_qk_counter_summary_matches_every_kmax_instance(tmp_path):
                                   ("__amd_rocclr_copyBuffer", 20.0)])
     res = probe._per_kernel(str(d), "FETCH_SIZE", "qk_norm_rope", "copyBuffer")
     assert res == {"rmsnorm": [7.0, 5.0], "copy": [20.0]}
+
+
+def test_any_width_summary_table(tmp_path, capsys):
+    import json
+
+    log = tmp_path / "any.log"
+    lines = [json.dumps({"N": 16383, "M": 8192, "offset": 0, "op": "rms", "kernel": k, "median_us": us, "pct": p,
+                         "rounds_us": [us]}) for k, us, p in (("library", 98.0, 68.5), ("before", 104.0, 64.5))]
+    log.write_text("noise\n" + "\n".join(lines) + "\n")
+    probe.any_width_summary(str(log))
+    out = capsys.readouterr().out
+    assert "   16383   0   8192 rms         98.00   68.5    104.00   64.5   1.061" in out
