@@ -90,22 +90,14 @@ __device__ __forceinline__ float group_sum(float v, float* part, int wave) {
   return v;
 }
 
-// Weight (or bias) elements [head + 4 g, head + 4 g + 4) of the N-element
-// vector at p (8-byte aligned) as one group: the aligned group g shifted down
-// by `head` elements, filled from group g + 1, whose elements past N (only
-// for the last groups) are not read.
-__device__ __forceinline__ u32x2 shifted_group(const uint16_t* p, int g, int head, int N) {
-  const u32x2* q = reinterpret_cast<const u32x2*>(p);
-  if (head == 0) return q[g];
-  const uint64_t lo = __builtin_bit_cast(uint64_t, q[g]);
-  uint64_t hi = 0;
-  if (4 * g + 8 <= N) {
-    hi = __builtin_bit_cast(uint64_t, q[g + 1]);
-  } else {
-    for (int i = 0; i < head; ++i) hi |= (uint64_t)p[4 * g + 4 + i] << (16 * i);
-  }
+// Weight (or bias) elements [head + 4 g, head + 4 g + 4) of a vector (8-byte
+// aligned) from its aligned 4-element groups g (lo) and g + 1 (hi): lo
+// shifted down by `head` elements, filled from hi.
+__device__ __forceinline__ u32x2 shift_pair(u32x2 lo, u32x2 hi, int head) {
+  if (head == 0) return lo;
+  const uint64_t l = __builtin_bit_cast(uint64_t, lo), h = __builtin_bit_cast(uint64_t, hi);
   const int sh = 16 * head;  // 16, 32 or 48
-  return __builtin_bit_cast(u32x2, (lo >> sh) | (hi << (64 - sh)));
+  return __builtin_bit_cast(u32x2, (l >> sh) | (h << (64 - sh)));
 }
 
 template <Norm MODE, typename DT, int G, int WAVES, int MAXG, bool STAGE, bool SHIFT>
@@ -124,7 +116,7 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_any_kernel(RowNormAnyArgs 
   const int N = a.n;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t e0 = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group) * N;  // first element of this row
+  const int64_t e0 = (int64_t)blockIdx.x * N;  // first element of this row
   // Groups start `head` elements into the row; `tail` elements follow them.
   int head = 0, ng = N / G, tail = 0;
   if constexpr (SHIFT) {
@@ -187,6 +179,8 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_any_kernel(RowNormAnyArgs 
     }
     acc = MODE == Norm::kLayer ? acc + v : __builtin_fmaf(v, v, acc);
   }
+  constexpr bool kHasW = MODE != Norm::kL2;
+  constexpr bool kHasB = MODE == Norm::kLayer;
   const float s1 = group_sum<WAVES>(acc, part[0], wave);
 
   // The later passes visit this lane's groups (value, index) in order: from
@@ -233,15 +227,21 @@ __global__ void __launch_bounds__(64 * WAVES) rownorm_any_kernel(RowNormAnyArgs 
     else if constexpr (MODE == Norm::kL2) return p * scale;
     else return (p * scale) * wv;
   };
+  // Shifted rows: the weight (bias) window of group g spans the vector's
+  // aligned groups g and g + 1; the second is clamped to the group that
+  // holds element N - 1 (its elements past N - 1 belong to no row element),
+  // so both loads are unconditional.
+  const int glast = (N - 1) / G;
   for_each([&](greg v, int g) {
     float o[G];
     greg wv{}, bv{};
     if constexpr (SHIFT) {
-      if constexpr (MODE != Norm::kL2) wv = shifted_group(a.w, g, head, N);
-      if constexpr (MODE == Norm::kLayer) bv = shifted_group(a.b, g, head, N);
+      const int g1 = g + 1 < glast ? g + 1 : glast;
+      if constexpr (kHasW) wv = shift_pair(GR::from(w[g]), GR::from(w[g1]), head);
+      if constexpr (kHasB) bv = shift_pair(GR::from(bb[g]), GR::from(bb[g1]), head);
     } else {
-      if constexpr (MODE != Norm::kL2) wv = GR::from(w[g]);
-      if constexpr (MODE == Norm::kLayer) bv = GR::from(bb[g]);
+      if constexpr (kHasW) wv = GR::from(w[g]);
+      if constexpr (kHasB) bv = GR::from(bb[g]);
     }
 #pragma unroll
     for (int i = 0; i < G; ++i)

@@ -68,7 +68,7 @@ probe_csrc/prior_entries.hip; same data, outputs compared first.
 
     python probe.py qk-pattern > <log>
     python probe.py qk-pattern-summary <log>
-    python probe.py any-width-ab > <log>
+    python probe.py any-width-ab [N:offset,...] > <log>
     python probe.py any-width-summary <log>
 
 `qk-pattern` times qk_norm_rope_fwd against its memory access pattern with no
@@ -1941,7 +1941,9 @@ if __name__ == "__main__":
         sizes()
     elif len(sys.argv) == 2 and sys.argv[1] == "staging":
         staging()
-    elif len(sys.argv) == 2 and sys.argv[1] == "any-width-ab":
+    elif len(sys.argv) in (2, 3) and sys.argv[1] == "any-width-ab":
+        if len(sys.argv) == 3:  # N:offset,... instead of the default widths
+            ANY_AB_SHAPES[:] = [tuple(int(v) for v in c.split(":")) for c in sys.argv[2].split(",")]
         any_width_ab()
     elif len(sys.argv) == 3 and sys.argv[1] == "any-width-summary":
         any_width_summary(sys.argv[2])
