@@ -1750,8 +1750,8 @@ def _short_kernel(n: str) -> str:
 
 def trace_summary(d: str, bench_json: str) -> None:
     """The headline kernel-trace summary: rocprofv3 --kernel-trace --stats of
-    `python -u bench.py --no-cpu-baseline` (files in d), beside that run's JSON
-    line (bench_json: a file holding it)."""
+    a bench.py run (files in d), beside that run's JSON line (bench_json: a
+    file holding it)."""
     import json
     import statistics
 
@@ -1769,8 +1769,12 @@ def trace_summary(d: str, bench_json: str) -> None:
     print()
     print("Commands (from the repository root, TMPDIR=/tmp):")
     print(f"  rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- \\")
-    extra = "" if (b["warmup"], b["steps"]) == (2000, 200) else f" --steps {b['steps']} --warmup {b['warmup']}"
-    print(f"      python -u bench.py --no-cpu-baseline{extra} > {bench_json}")
+    # the command as it was run: the CPU baseline leg is in the JSON unless it
+    # was switched off
+    flags = "" if "cpu_baseline" in b else " --no-cpu-baseline"
+    if (b["warmup"], b["steps"]) != (2000, 200):
+        flags = f" --gpus 1 --steps {b['steps']} --warmup {b['warmup']}" + flags
+    print(f"      python -u bench.py{flags} > {bench_json}")
     print(f"      ({b['warmup']} warm-up + {b['steps']} timed steps)")
     print(f"  python probe.py trace-summary {d} {bench_json}")
     print()
