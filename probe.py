@@ -68,11 +68,15 @@ probe_csrc/prior_entries.hip; same data, outputs compared first.
 
     python probe.py qk-pattern > <log>
     python probe.py qk-pattern-summary <log>
+    python probe.py qk-ab > <log>
+    python probe.py qk-ab-summary <log>
     python probe.py any-width-ab [N:offset,...] > <log>
     python probe.py any-width-summary <log>
 
 `qk-pattern` times qk_norm_rope_fwd against its memory access pattern with no
 arithmetic (the q and k bytes of each token read and written back in place).
+`qk-ab` times qk_norm_rope_fwd against the prior QK kernel
+(probe_csrc/prior_qk_norm_rope.hip) over token and head counts.
 `any-width-ab` times the any-width row norms against the prior any-width path
 (probe_csrc/prior_any_width.hip).
 
@@ -1524,6 +1528,128 @@ def qk_pattern(rounds: int = 6, launches: int = 40) -> None:
         torch.cuda.empty_cache()
 
 
+PRIOR_QK_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_prior_qk.so")
+
+
+def build_prior_qk(verbose: bool = False) -> str:
+    """Compile probe_csrc/prior_qk_norm_rope.hip (the QK kernel before each
+    wave kept all of its head rows in flight) into
+    probe_csrc/libmbn_prior_qk.so; always rebuilds."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=PRIOR_QK_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "prior_qk_norm_rope.hip")])
+
+
+def prior_qk_lib():
+    if not os.path.exists(PRIOR_QK_LIB_PATH):
+        build_prior_qk()
+    h = ctypes.CDLL(PRIOR_QK_LIB_PATH)
+    h.mbn_prior_qk_norm_rope.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                                 ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    h.mbn_prior_qk_norm_rope.restype = ctypes.c_int
+    return h
+
+
+# (tokens, q heads, kv heads): the bench workload's head counts over the
+# launch shapes (one step per wave up to 512 tokens, two up to 1024, three
+# beyond), and other head counts.
+QK_AB_CASES = [(256, 32, 8), (768, 32, 8), (1024, 32, 8), (4096, 32, 8), (16384, 32, 8), (65536, 32, 8),
+               (256, 64, 8), (4096, 64, 8), (16384, 64, 8), (600, 28, 4), (5000, 28, 4), (3000, 96, 8),
+               (20000, 96, 8), (4096, 8, 1), (65536, 8, 1), (32768, 16, 4)]
+
+
+def qk_ab(rounds: int = 6, launches: int = 40) -> None:
+    """qk_norm_rope_fwd against the prior QK kernel (libmbn_prior_qk.so) on
+    the same data (bf16, full rotary, theta 1e6, random positions below 2^17):
+    outputs compared bit for bit, then per round, in alternating order, the
+    median of `launches` individually timed launches over buffer sets rotated
+    through >= 1 GiB. One JSON line per case and kernel."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import torch
+
+    h = prior_qk_lib()
+    lib = __import__("memory_bound_normalization_amd").lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    g = torch.Generator(device=dev).manual_seed(41)
+    for T, hq, hk in QK_AB_CASES:
+        width = (hq + 2 * hk) * 128
+        n = max(2, -(-(1 << 30) // (T * width * 2)))
+        qkv = [torch.randn(T, width, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+        qw = (torch.rand(128, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        kw = (torch.rand(128, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        pos = torch.randint(0, 1 << 17, (T,), device=dev, dtype=torch.int64, generator=g)
+
+        def new(i):
+            rc = lib.qk_norm_rope_fwd(qkv[i].data_ptr(), qw.data_ptr(), kw.data_ptr(), pos.data_ptr(), T, hq, hk, 128,
+                                      1e-6, 1e6, sp)
+            if rc != 0:
+                raise RuntimeError(f"qk_norm_rope_fwd: status {rc}")
+
+        def old(i):
+            rc = h.mbn_prior_qk_norm_rope(qkv[i].data_ptr(), qw.data_ptr(), kw.data_ptr(), pos.data_ptr(), T, hq, hk,
+                                          1e-6, 1e6, sp)
+            if rc != 0:
+                raise RuntimeError(f"prior qk: status {rc}")
+
+        fns = {"library": new, "before": old}
+        src = qkv[0].clone()
+        outs = []
+        for fn in fns.values():
+            qkv[0].copy_(src)
+            fn(0)
+            torch.cuda.synchronize()
+            outs.append(qkv[0].clone())
+        if not torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)):
+            raise RuntimeError(f"T={T} hq={hq} hk={hk}: the two kernels' outputs differ")
+        del src, outs
+        nb = 2 * T * (hq + hk) * 128 * 2
+        res = {k: [] for k in fns}
+        for fn in fns.values():
+            for i in range(20):
+                fn(i % n)
+        torch.cuda.synchronize()
+        for rnd in range(rounds):
+            for k in (list(fns) if rnd % 2 == 0 else list(fns)[::-1]):
+                ev = [(timer.new(), timer.new()) for _ in range(launches)]
+                for i, (e0, e1) in enumerate(ev):
+                    timer.record(e0)
+                    fns[k](i % n)
+                    timer.record(e1)
+                torch.cuda.synchronize()
+                us = sorted(timer.elapsed_ms(e0, e1) * 1e3 for e0, e1 in ev)
+                timer.close()
+                res[k].append(us[len(us) // 2])
+        for k, t in res.items():
+            us = sorted(t)[len(t) // 2]
+            print(json.dumps({"T": T, "n_q": hq, "n_kv": hk, "kernel": k, "median_us": round(us, 2),
+                              "pct": round(100 * nb / us / 1e3 / 8000, 2), "rounds_us": [round(v, 2) for v in t]}),
+                  flush=True)
+        del qkv
+        torch.cuda.empty_cache()
+
+
+def qk_ab_summary(log: str) -> None:
+    import json
+
+    rows = [json.loads(x) for x in open(log) if x.startswith("{")]
+    by = {}
+    for r in rows:
+        by.setdefault((r["T"], r["n_q"], r["n_kv"]), {})[r["kernel"]] = r
+    print("qk_norm_rope_fwd against the prior QK kernel, same data, outputs bit-identical; per-launch median")
+    print("of 40 launches, median over rounds; % of 8 TB/s on 2 x T x (q + kv heads) x 256 B:")
+    print(f"  {'T':>6} {'q':>3} {'kv':>3} {'library us':>10} {'%':>6} {'before us':>9} {'%':>6} {'speedup':>7}")
+    for (T, hq, hk), d in by.items():
+        new, old = d["library"], d["before"]
+        print(f"  {T:>6} {hq:>3} {hk:>3} {new['median_us']:>10.2f} {new['pct']:>6.1f} {old['median_us']:>9.2f} "
+              f"{old['pct']:>6.1f} {old['median_us'] / new['median_us']:>7.3f}")
+
+
 def qk_pattern_summary(log: str) -> None:
     import json
 
@@ -1951,6 +2077,10 @@ if __name__ == "__main__":
         any_width_ab()
     elif len(sys.argv) == 3 and sys.argv[1] == "any-width-summary":
         any_width_summary(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "qk-ab":
+        qk_ab()
+    elif len(sys.argv) == 3 and sys.argv[1] == "qk-ab-summary":
+        qk_ab_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "qk-pattern":
         qk_pattern()
     elif len(sys.argv) == 3 and sys.argv[1] == "qk-pattern-summary":

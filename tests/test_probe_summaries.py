@@ -212,3 +212,15 @@ def test_any_width_summary_table(tmp_path, capsys):
     probe.any_width_summary(str(log))
     out = capsys.readouterr().out
     assert "   16383   0   8192 rms         98.00   68.5    104.00   64.5   1.061" in out
+
+
+def test_qk_ab_summary_table(tmp_path, capsys):
+    import json
+
+    log = tmp_path / "qkab.log"
+    lines = [json.dumps({"T": 65536, "n_q": 32, "n_kv": 8, "kernel": k, "median_us": us, "pct": p, "rounds_us": [us]})
+             for k, us, p in (("library", 215.0, 78.1), ("before", 255.0, 65.8))]
+    log.write_text("\n".join(lines) + "\n")
+    probe.qk_ab_summary(str(log))
+    out = capsys.readouterr().out
+    assert "   65536  32   8     215.00   78.1    255.00   65.8   1.186" in out
