@@ -68,9 +68,10 @@ def streaming_copy_reference(x, y, stream, steps: int, warmup: int):
     """The best 50/50 read/write stream measured on this part -- the
     hand-written copy of libmbn_stream.so with 4 KiB per workgroup (16-byte
     non-temporal loads and stores, the row-norm kernels' accesses) -- timed
-    the same way as the RMSNorm (timing events around each launch) on the same
-    512 MiB buffers: the reference roofline.frac is read against. probe.py
-    compiles libmbn_stream.so when it is missing; None when that fails."""
+    the same way as the RMSNorm (the kernel's own start and end, recorded in
+    events by hipExtLaunchKernel) on the same 512 MiB buffers: the reference
+    roofline.frac is read against. probe.py compiles libmbn_stream.so when it
+    is missing; None when that fails."""
     try:
         from probe import stream_lib
 
@@ -80,19 +81,19 @@ def streaming_copy_reference(x, y, stream, steps: int, warmup: int):
     nbytes = x.numel() * x.element_size()
     sp = stream.cuda_stream
 
-    def launch():
-        rc = sl.mbn_stream_copy(x.data_ptr(), y.data_ptr(), nbytes, 256, 1, sp)
-        if rc != 0:
-            raise RuntimeError(f"mbn_stream_copy status {rc}")
-
-    for _ in range(warmup):
-        launch()
     timer = HipTimingEvents(stream)
+
+    def launch(a, b):
+        rc = sl.mbn_stream_copy_timed(x.data_ptr(), y.data_ptr(), nbytes, 256, 1, sp, a, b)
+        if rc != 0:
+            raise RuntimeError(f"mbn_stream_copy_timed status {rc}")
+
+    spare = (timer.new(), timer.new())
+    for _ in range(warmup):
+        launch(*spare)
     ev = [(timer.new(), timer.new()) for _ in range(steps)]
     for a, b in ev:
-        timer.record(a)
-        launch()
-        timer.record(b)
+        launch(a, b)
     import torch
 
     torch.cuda.synchronize()
@@ -223,6 +224,23 @@ def suite(steps: int, warmup: int) -> int:
                           "batch_mean_us": round(timed.batch_us, 2),
                           "pct_of_8TBps_batch": round(b / timed.batch_us / 1e3 / 80.0, 2)}), flush=True)
 
+    # The plain 4 KiB-per-workgroup streaming copy (libmbn_stream.so) of the
+    # same bytes between the same rotating buffers follows each RMSNorm
+    # workload ("<workload>_copy"): what a 50/50 stream of that size reaches
+    # on this part, launch ramp and drain included.
+    try:
+        from probe import stream_lib
+
+        sl = stream_lib()
+    except (RuntimeError, OSError):
+        sl = None
+    sp = stream.cuda_stream
+
+    def copy(src, dst):
+        rc = sl.mbn_stream_copy(src.data_ptr(), dst.data_ptr(), src.numel() * 2, 256, 1, sp)
+        if rc != 0:
+            raise RuntimeError(f"mbn_stream_copy status {rc}")
+
     for name, wl in RMS_WORKLOADS.items():
         x_bits, w_bits, eps = make_rms_inputs(wl)
         x0, w = to_dev(x_bits), to_dev(w_bits)
@@ -233,6 +251,9 @@ def suite(steps: int, warmup: int) -> int:
         med, best = timed(lambda i: mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps), nrot)
         b = wl.algorithmic_bytes
         report(name, "rmsnorm_fwd", nrot, med, best, b, M=wl.M, N=wl.N)
+        if sl is not None:
+            med, best = timed(lambda i: copy(xs[i], ys[i]), nrot)
+            report(name + "_copy", "stream_copy", nrot, med, best, pair, M=wl.M, N=wl.N)
         del xs, ys, x0
         torch.cuda.empty_cache()
     # The RMSNorm benchmark grid of "[Inductor] Codegen Gluon", section 3.1
@@ -440,31 +461,34 @@ def main() -> int:
 
     timer = HipTimingEvents(stream)
 
-    def step(ev=None):
-        if ev is not None:
-            timer.record(ev[0])
-        mbn.rmsnorm_fwd(x, w, y, eps=eps)
-        if ev is not None:
-            timer.record(ev[1])
-        mbn.qk_norm_rope_fwd(qkv, q_w, k_w, positions, qwl.n_q_heads, qwl.n_kv_heads,
-                             qwl.head_dim, eps=qeps, theta=theta)
-        if ev is not None:
-            timer.record(ev[2])
+    # One step: the RMSNorm, then the QK-norm + RoPE, each through its timed
+    # entry point, which records the kernel's own start and end in the step's
+    # events (ev[0], ev[1]: RMSNorm; ev[2], ev[3]: QK). Warm-up steps take the
+    # same path with a spare set of events.
+    def step(ev):
+        mbn.rmsnorm_fwd_timed(x, w, ev[0], ev[1], y=y, eps=eps)
+        mbn.qk_norm_rope_fwd_timed(qkv, q_w, k_w, positions, qwl.n_q_heads, qwl.n_kv_heads,
+                                   ev[2], ev[3], head_dim=qwl.head_dim, eps=qeps, theta=theta)
 
+    spare = [timer.new() for _ in range(4)]
     for _ in range(args.warmup):
-        step()
+        step(spare)
     torch.cuda.synchronize()
 
-    evs = [[timer.new() for _ in range(3)] for _ in range(args.steps)]
+    evs = [[timer.new() for _ in range(4)] for _ in range(args.steps)]
+    region = (timer.new(), timer.new())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    timer.record(region[0])
     for i in range(args.steps):
         step(evs[i])
+    timer.record(region[1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     rms_ms = [timer.elapsed_ms(e[0], e[1]) for e in evs]
-    qk_ms = [timer.elapsed_ms(e[1], e[2]) for e in evs]
+    qk_ms = [timer.elapsed_ms(e[2], e[3]) for e in evs]
+    region_us = timer.elapsed_ms(*region) * 1e3 / args.steps
     timer.close()
     rms_mean_s = sum(rms_ms) / len(rms_ms) / 1e3
     qk_mean_s = sum(qk_ms) / len(qk_ms) / 1e3
@@ -507,6 +531,9 @@ def main() -> int:
             "algorithmic_bytes_per_launch": rms_bytes,
             "mean_us": round(rms_mean_s * 1e6, 2),
             "best_us": round(min(rms_ms) * 1e3, 2),
+            "timing": "kernel start to end, recorded in HIP events by hipExtLaunchKernel "
+                      "(rmsnorm_fwd_timed) on the launch stream; mean over the timed steps",
+            "timed_region_us_per_step": round(region_us, 2),
         },
         "qk_norm_rope": {
             "mean_us": round(qk_mean_s * 1e6, 2),

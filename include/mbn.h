@@ -13,7 +13,8 @@
  *     status means nothing was launched (except MBN_EHIP, which reports that
  *     the launch itself failed; the HIP error state is read and cleared with
  *     hipGetLastError).
- *   - The library is stateless and may be called from several host threads.
+ *   - The library keeps no state between calls and may be called from several
+ *     host threads.
  *   - Results are deterministic: a fixed reduction order, no atomics.
  */
 #ifndef MBN_H
@@ -233,6 +234,34 @@ MBN_API int qk_norm_rope_partial_fwd_f16(void* qkv, const void* q_w, const void*
                                          const int64_t* positions, int64_t T, int32_t n_q_heads,
                                          int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
                                          float eps, float theta, void* stream);
+
+/*
+ * Timed variants -- rmsnorm_fwd and qk_norm_rope_fwd with kernel-execution
+ * timestamps.
+ *
+ * The operation, arguments, validation and status codes are exactly those of
+ * the entry point without the suffix. In addition, the call's first kernel
+ * records start_event when it starts executing on the GPU and its last kernel
+ * records stop_event when it has finished (hipExtLaunchKernel), so that
+ * hipEventElapsedTime(start_event, stop_event) is the duration of the call's
+ * own kernels: what a bandwidth figure of the operation divides its bytes by,
+ * the same interval a kernel trace reports. A hipEventRecord before and after
+ * the plain call measures more: the queue packets of the two records and the
+ * kernel's dispatch after the first.
+ *
+ *   start_event, stop_event  hipEvent_t (as void*), created by the caller on
+ *              the stream's device, both non-NULL (else MBN_EINVAL). They are
+ *              left unrecorded when the call launches nothing (an empty input)
+ *              or returns an error.
+ * Meant for eager timing: the events are attached to the dispatches, which a
+ * HIP graph capture need not support; capture the plain entry points.
+ */
+MBN_API int rmsnorm_fwd_timed(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                              float eps, void* stream, void* start_event, void* stop_event);
+MBN_API int qk_norm_rope_fwd_timed(void* qkv, const void* q_w, const void* k_w,
+                                   const int64_t* positions, int64_t T, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
+                                   void* stream, void* start_event, void* stop_event);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 MBN_API const char* mbn_strerror(int status);

@@ -18,6 +18,11 @@ Functions with the C names take torch tensors, all bfloat16 or all float16
 * ``qk_norm_rope_fwd(qkv, q_w, k_w, positions, n_q_heads, n_kv_heads,
   head_dim=128, eps=1e-6, theta=1e6, stream=None)`` -- modifies qkv in place
   and returns it.
+* ``rmsnorm_fwd_timed(x, w, start_event, stop_event, y=None, eps=1e-6,
+  stream=None)`` and ``qk_norm_rope_fwd_timed(qkv, q_w, k_w, positions,
+  n_q_heads, n_kv_heads, start_event, stop_event, ...)`` -- bf16 only; the
+  same calls, with the kernels' own start and end recorded into two
+  caller-created hipEvent_t handles (ints or ctypes.c_void_p).
 * ``mbn_strerror(status)``.
 
 ``lib()`` returns the raw ctypes handle (C signatures of include/mbn.h).
@@ -43,7 +48,9 @@ __all__ = [
     "lib_path",
     "mbn_strerror",
     "qk_norm_rope_fwd",
+    "qk_norm_rope_fwd_timed",
     "rmsnorm_fwd",
+    "rmsnorm_fwd_timed",
 ]
 
 MBN_OK = 0
@@ -95,6 +102,10 @@ def lib() -> ctypes.CDLL:
             f16 = getattr(h, name + "_f16")
             f16.argtypes = getattr(h, name).argtypes
             f16.restype = ctypes.c_int
+        h.rmsnorm_fwd_timed.argtypes = h.rmsnorm_fwd.argtypes + [vp, vp]
+        h.rmsnorm_fwd_timed.restype = ctypes.c_int
+        h.qk_norm_rope_fwd_timed.argtypes = h.qk_norm_rope_fwd.argtypes + [vp, vp]
+        h.qk_norm_rope_fwd_timed.restype = ctypes.c_int
         h.mbn_strerror.argtypes = [ctypes.c_int]
         h.mbn_strerror.restype = ctypes.c_char_p
         _LIB = h
@@ -161,6 +172,27 @@ def rmsnorm_fwd(x, w, y=None, eps: float = 1e-6, stream=None):
     )
     if rc != MBN_OK:
         raise MbnError(rc, "rmsnorm_fwd")
+    return y
+
+
+def _event_handle(e):
+    return e.value if isinstance(e, ctypes.c_void_p) else int(e)
+
+
+def rmsnorm_fwd_timed(x, w, start_event, stop_event, y=None, eps: float = 1e-6, stream=None):
+    """rmsnorm_fwd (bf16) with the kernels' own start / end recorded in two hipEvent_t."""
+    import torch
+
+    _check_bf16_cuda("x", x, torch.bfloat16)
+    m, n = _rows_of(x)
+    _check_vec("w", w, n, x.dtype)
+    y = _out_like(x, y, "y")
+    rc = lib().rmsnorm_fwd_timed(
+        x.data_ptr(), w.data_ptr(), y.data_ptr(), m, n, float(eps), _stream_handle(stream, x.device),
+        _event_handle(start_event), _event_handle(stop_event),
+    )
+    if rc != MBN_OK:
+        raise MbnError(rc, "rmsnorm_fwd_timed")
     return y
 
 
@@ -266,4 +298,31 @@ def qk_norm_rope_fwd(
         where = "qk_norm_rope_partial_fwd" + ("_f16" if qkv.dtype == torch.float16 else "")
     if rc != MBN_OK:
         raise MbnError(rc, where)
+    return qkv
+
+
+def qk_norm_rope_fwd_timed(
+    qkv, q_w, k_w, positions, n_q_heads: int, n_kv_heads: int, start_event, stop_event,
+    head_dim: int = MBN_QK_HEAD_DIM, eps: float = 1e-6, theta: float = 1e6, stream=None,
+):
+    """qk_norm_rope_fwd (bf16, full rotary) with the kernels' own start / end in two hipEvent_t."""
+    import torch
+
+    _check_bf16_cuda("qkv", qkv, torch.bfloat16)
+    _check_bf16_cuda("q_w", q_w, qkv.dtype)
+    _check_bf16_cuda("k_w", k_w, qkv.dtype)
+    if positions.dtype != torch.int64 or not positions.is_cuda or not positions.is_contiguous():
+        raise TypeError("positions must be a contiguous int64 GPU tensor")
+    t = qkv.shape[0] if qkv.dim() else 0
+    if qkv.dim() != 2 or qkv.shape[1] != (n_q_heads + 2 * n_kv_heads) * head_dim:
+        raise ValueError("qkv must have shape [T, (n_q_heads + 2 * n_kv_heads) * head_dim]")
+    if positions.numel() != t:
+        raise ValueError("positions must have T entries")
+    rc = lib().qk_norm_rope_fwd_timed(
+        qkv.data_ptr(), q_w.data_ptr(), k_w.data_ptr(), positions.data_ptr(), t,
+        int(n_q_heads), int(n_kv_heads), int(head_dim), float(eps), float(theta),
+        _stream_handle(stream, qkv.device), _event_handle(start_event), _event_handle(stop_event),
+    )
+    if rc != MBN_OK:
+        raise MbnError(rc, "qk_norm_rope_fwd_timed")
     return qkv

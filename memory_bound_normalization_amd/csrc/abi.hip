@@ -162,7 +162,32 @@ int qk_impl(mbn::Storage dt, void* qkv, const void* q_w, const void* k_w,
 constexpr mbn::Storage kBf16 = mbn::Storage::kBf16;
 constexpr mbn::Storage kF16 = mbn::Storage::kF16;
 
+// Points the calling thread's timing slot at a call's events for the duration
+// of that call (the *_timed entry points).
+class TimedCall {
+ public:
+  TimedCall(void* start, void* stop)
+      : t_{static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)},
+        prev_(mbn::launch_timing()) {
+    mbn::launch_timing() = &t_;
+  }
+  ~TimedCall() { mbn::launch_timing() = prev_; }
+  TimedCall(const TimedCall&) = delete;
+  TimedCall& operator=(const TimedCall&) = delete;
+
+ private:
+  mbn::LaunchTiming t_;
+  mbn::LaunchTiming* prev_;
+};
+
 }  // namespace
+
+namespace mbn {
+LaunchTiming*& launch_timing() {
+  static thread_local LaunchTiming* slot = nullptr;
+  return slot;
+}
+}  // namespace mbn
 
 extern "C" {
 
@@ -226,6 +251,23 @@ MBN_API int qk_norm_rope_partial_fwd_f16(void* qkv, const void* q_w, const void*
                                          int32_t n_kv_heads, int32_t head_dim, int32_t rotary_dim,
                                          float eps, float theta, void* stream) {
   return qk_impl(kF16, qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads, head_dim, rotary_dim,
+                 eps, theta, stream);
+}
+
+MBN_API int rmsnorm_fwd_timed(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                              float eps, void* stream, void* start_event, void* stop_event) {
+  if (!start_event || !stop_event) return MBN_EINVAL;
+  TimedCall timed(start_event, stop_event);
+  return rmsnorm_impl(kBf16, x, w, y, M, N, eps, stream);
+}
+
+MBN_API int qk_norm_rope_fwd_timed(void* qkv, const void* q_w, const void* k_w,
+                                   const int64_t* positions, int64_t T, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, float eps, float theta,
+                                   void* stream, void* start_event, void* stop_event) {
+  if (!start_event || !stop_event) return MBN_EINVAL;
+  TimedCall timed(start_event, stop_event);
+  return qk_impl(kBf16, qkv, q_w, k_w, positions, T, n_q_heads, n_kv_heads, head_dim, head_dim,
                  eps, theta, stream);
 }
 

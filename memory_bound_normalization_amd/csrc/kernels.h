@@ -4,10 +4,39 @@
 // exceed kMaxWorkItems) and returns the launch status.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mbn {
+
+// Kernel-execution timestamps for one entry-point call. While a call of a
+// *_timed entry point runs, the calling thread's slot points at its events:
+// the call's first dispatch records `start` when its kernel starts and every
+// dispatch records `stop` when its kernel ends (hipExtLaunchKernel), so that
+// stop - start spans exactly the call's kernels, without the queue packets a
+// hipEventRecord before and after the call would add to the interval. Null
+// (every other call): plain launches.
+struct LaunchTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchTiming*& launch_timing();
+
+// Every kernel launch of the library goes through here; returns the launch status.
+template <typename... KArgs, typename... Args>
+hipError_t dispatch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                    Args... args) {
+  LaunchTiming* t = launch_timing();
+  if (!t) {
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, static_cast<KArgs>(args)...);
+  } else {
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, stream, t->start, t->stop, 0u,
+                          static_cast<KArgs>(args)...);
+    t->start = nullptr;  // later dispatches of the same call only move `stop`
+  }
+  return hipGetLastError();
+}
 
 // Work-items of one dispatch: the grid size fields of an HSA kernel dispatch
 // packet are 32-bit, so a one-dimensional launch covers at most 2^32 - 1.

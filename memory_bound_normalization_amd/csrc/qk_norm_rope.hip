@@ -249,12 +249,11 @@ hipError_t launch_qk_norm_rope(Storage dtype, void* qkv, const void* q_w, const 
   const int64_t tokens_per_launch = kMaxWorkItems / (64 * waves);
   for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
     const int64_t nt = T - t0 < tokens_per_launch ? T - t0 : tokens_per_launch;
-    hipLaunchKernelGGL(kernel,
-                       dim3((unsigned)nt), dim3(64 * waves), 0, stream,
-                       static_cast<uint16_t*>(qkv) + t0 * row_stride, static_cast<const uint16_t*>(q_w),
-                       static_cast<const uint16_t*>(k_w), positions + t0, n_q_heads, n_heads, row_stride,
-                       rotary_dim / 16, eps, inv_pow);
-    const hipError_t err = hipGetLastError();
+    const hipError_t err =
+        dispatch(kernel, dim3((unsigned)nt), dim3(64 * waves), 0, stream,
+                 static_cast<uint16_t*>(qkv) + t0 * row_stride, static_cast<const uint16_t*>(q_w),
+                 static_cast<const uint16_t*>(k_w), positions + t0, n_q_heads, n_heads, row_stride,
+                 rotary_dim / 16, eps, inv_pow);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

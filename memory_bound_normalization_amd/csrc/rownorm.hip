@@ -1066,9 +1066,8 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
       int64_t g = grid > 0 ? grid : pc->grid;
       if (g > sets) g = sets;
       const RowNormKernel kernel = (nchunk == 64 * pc->wpr * pc->maxc) ? pc->full[d] : pc->ragged[d];
-      hipLaunchKernelGGL(kernel, dim3((unsigned)g), dim3(64 * pc->wpr), persistent_lds_bytes(*pc, nchunk),
-                         stream, args);
-      return hipGetLastError();
+      return dispatch(kernel, dim3((unsigned)g), dim3(64 * pc->wpr), persistent_lds_bytes(*pc, nchunk),
+                      stream, args);
     }
   }
 
@@ -1104,8 +1103,7 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
     if (args.h) part.h = args.h + e0;
     part.M = args.M - r0 < rows_per_launch ? args.M - r0 : rows_per_launch;
     const int64_t blocks = (part.M + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), lds, stream, part);
-    const hipError_t err = hipGetLastError();
+    const hipError_t err = dispatch(kernel, dim3((unsigned)blocks), dim3(threads), lds, stream, part);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

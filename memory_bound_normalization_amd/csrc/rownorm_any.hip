@@ -635,8 +635,7 @@ hipError_t launch_rownorm_any_rows(Norm mode, Storage dtype, RowNormAnyArgs args
                                               : pick_s16(kS16Rms, max_nck);
     if (c) {
       args.xcd_group = c->xcd_group;
-      hipLaunchKernelGGL(c->k[d], dim3((unsigned)args.M), dim3(64 * c->waves), (size_t)max_nck * 16, stream, args);
-      return hipGetLastError();
+      return dispatch(c->k[d], dim3((unsigned)args.M), dim3(64 * c->waves), (size_t)max_nck * 16, stream, args);
     }
   }
   const int g = rownorm_any_group(args);
@@ -646,8 +645,7 @@ hipError_t launch_rownorm_any_rows(Norm mode, Storage dtype, RowNormAnyArgs args
   if (!cfg) return hipErrorInvalidValue;
   const RowNormAnyKernel kernel = cfg->k[shift ? 1 : 0][(int)mode][d];
   const size_t lds = cfg->stage ? (size_t)args.n * 2 : 0;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)args.M), dim3(64 * cfg->waves), lds, stream, args);
-  return hipGetLastError();
+  return dispatch(kernel, dim3((unsigned)args.M), dim3(64 * cfg->waves), lds, stream, args);
 }
 
 }  // namespace

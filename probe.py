@@ -294,9 +294,10 @@ def stream_lib():
     h.mbn_stream_read.argtypes = [vp, vp, sz, i32, i32, vp]
     h.mbn_stream_write.argtypes = [vp, sz, i32, i32, u32, vp]
     h.mbn_stream_copy_policy.argtypes = [vp, vp, sz, i32, i32, vp]
+    h.mbn_stream_copy_timed.argtypes = [vp, vp, sz, i32, i32, vp, vp, vp]
     h.mbn_stream_qk_pattern.argtypes = [vp, ctypes.c_int64, i32, i32, vp]
     for f in (h.mbn_stream_copy, h.mbn_stream_read, h.mbn_stream_write, h.mbn_stream_copy_policy,
-              h.mbn_stream_qk_pattern):
+              h.mbn_stream_qk_pattern, h.mbn_stream_copy_timed):
         f.restype = i32
     return h
 
@@ -1869,6 +1870,9 @@ def claim_variants(rounds: int = 4, launches: int = 50) -> None:
 
 
 def _short_kernel(n: str) -> str:
+    m = re.search(r"stream_copy<[^>]*>", n)
+    if m:
+        return m.group(0)
     n = n.replace("mbn::(anonymous namespace)::", "").replace("void ", "")
     n = re.sub(r"\(mbn::RowNormArgs\)|\(mbn::RowNormAnyArgs\)|\(RowNormAnyArgs\)|\(unsigned short\*.*", "", n)
     return n.replace("(mbn::Norm)", "").replace("mbn::Bf16, ", "").replace("mbn::", "")
@@ -1920,7 +1924,9 @@ def trace_summary(d: str, bench_json: str) -> None:
     print(f"Algorithmic bytes per launch: 2*M*N*2 + 2*N = {algo:,} B.")
     print(f"Mean over the last {len(dur)} dispatches (the timed steps), trace: {m:.2f} us -> "
           f"{algo / m / 1e3:.1f} GB/s = {100 * algo / m / 1e3 / 8000:.2f}% of 8 TB/s.")
-    print(f"The same run's bench.py line (HIP events around each launch): mean {b['roofline']['mean_us']} us, "
+    how = ("the kernel's own start and end in HIP events" if "timing" in b["roofline"]
+           else "HIP events around each launch")
+    print(f"The same run's bench.py line ({how}): mean {b['roofline']['mean_us']} us, "
           f"best {b['roofline']['best_us']} us -> {b['value']} GB/s ({100 * b['roofline']['frac']:.2f}%); "
           f"the means differ by {100 * (b['roofline']['mean_us'] - m) / m:+.2f}%.")
     cr = b["roofline"].get("streaming_copy_reference")
@@ -1941,7 +1947,8 @@ def suite_summary(d: str, suite_log: str, warm: int = 3000) -> None:
 
     rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    ks = [r for r in rows if "rownorm" in r["Kernel_Name"] or "qk_norm_rope" in r["Kernel_Name"]][warm:]
+    ks = [r for r in rows if any(k in r["Kernel_Name"] for k in ("rownorm", "qk_norm_rope", "stream_copy"))]
+    ks = ks[warm:]
     cases = [json.loads(line) for line in open(suite_log) if line.startswith("{")]
     per, rem = divmod(len(ks), len(cases))
     if rem:
@@ -1967,8 +1974,18 @@ def suite_summary(d: str, suite_log: str, warm: int = 3000) -> None:
     print("rownorm_any_kernel / rownorm_s16_kernel (widths that are not whole 16-byte")
     print("chunks). WGs is the grid size (the persistent grid loops over the rows).")
     print()
+    if any(c["kernel"] == "stream_copy" for c in cases):
+        print("<workload>_copy: the plain streaming copy (stream_copy<256, 1> of libmbn_stream.so,")
+        print("4 KiB per workgroup, 16-byte non-temporal loads and stores) of the same input bytes")
+        print("between the same buffers; 'of copy' = the copy's median time / the workload's.")
+    print()
     print(f"  {'workload':<22} {'op':<20} {'kernel instantiation':<56} {'WGs':>6} {'median_us':>9} {'min_us':>8} "
-          f"{'GB/s':>7} {'%':>6}")
+          f"{'GB/s':>7} {'%':>6} {'of copy':>7}")
+    meds = {}
+    for i, c in enumerate(cases):
+        grp = ks[i * per:(i + 1) * per]
+        meds[c["workload"]] = statistics.median(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
     for i, c in enumerate(cases):
         grp = ks[i * per:(i + 1) * per]
         names = {_short_kernel(r["Kernel_Name"]) for r in grp}
@@ -1978,8 +1995,10 @@ def suite_summary(d: str, suite_log: str, warm: int = 3000) -> None:
         med = statistics.median(du)
         b = c["algorithmic_bytes"]
         wg = int(grp[0]["Grid_Size_X"]) // int(grp[0]["Workgroup_Size_X"])
+        cm = meds.get(c["workload"] + "_copy")
+        vs = f"{cm / med:>7.3f}" if cm and c["kernel"] != "stream_copy" else f"{'':>7}"
         print(f"  {c['workload']:<22} {c['kernel']:<20} {names.pop()[:56]:<56} {wg:>6} {med:>9.2f} {du[0]:>8.2f} "
-              f"{b / med / 1e3:>7.0f} {b / med / 1e3 / 80:>6.1f}")
+              f"{b / med / 1e3:>7.0f} {b / med / 1e3 / 80:>6.1f} {vs}")
 
 
 def experiments_summary(sizes_log: str, variants_log: str, claim_log: str, stream_log: str) -> None:

@@ -8,6 +8,7 @@
 // chunks j * LANES + t), with the same non-temporal 16-byte loads and stores
 // as the row-norm kernels: every chunk of a workgroup is in flight before the
 // first one is consumed.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -147,6 +148,23 @@ __attribute__((visibility("default"))) int mbn_stream_copy(const void* src, void
   const size_t grid = bytes / ((size_t)lanes * chunks * 16);
   hipLaunchKernelGGL(s->copy, dim3((unsigned)grid), dim3(lanes), 0, (hipStream_t)stream,
                      (const u32x4*)src, (u32x4*)dst);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// mbn_stream_copy with the kernel's own start and end recorded in two
+// caller-created events (hipExtLaunchKernel), as the library's timed entry
+// points do, so the copy and the row norm are timed alike.
+__attribute__((visibility("default"))) int mbn_stream_copy_timed(const void* src, void* dst, size_t bytes,
+                                                                 int lanes, int chunks, void* stream,
+                                                                 void* start, void* stop) {
+  const Shape* s;
+  int rc = check(src, bytes, lanes, chunks, &s);
+  if (rc == 0) rc = check(dst, bytes, lanes, chunks, &s);
+  if (rc == 0 && (!start || !stop)) rc = 1;
+  if (rc) return rc;
+  const size_t grid = bytes / ((size_t)lanes * chunks * 16);
+  hipExtLaunchKernelGGL(s->copy, dim3((unsigned)grid), dim3(lanes), 0, (hipStream_t)stream,
+                        (hipEvent_t)start, (hipEvent_t)stop, 0, (const u32x4*)src, (u32x4*)dst);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

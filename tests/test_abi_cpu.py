@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {
         "rmsnorm_fwd", "add_rmsnorm_fwd", "layernorm_fwd", "l2norm_fwd", "qk_norm_rope_fwd",
         "qk_norm_rope_partial_fwd", "rmsnorm_fwd_f16", "add_rmsnorm_fwd_f16", "layernorm_fwd_f16",
-        "l2norm_fwd_f16", "qk_norm_rope_partial_fwd_f16", "mbn_strerror"}
+        "l2norm_fwd_f16", "qk_norm_rope_partial_fwd_f16", "rmsnorm_fwd_timed",
+        "qk_norm_rope_fwd_timed", "mbn_strerror"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -253,6 +254,30 @@ def test_f16_entry_points_validate_like_bf16(lib):
         a = getattr(lib, name)(*args)
         b = getattr(lib, name + "_f16")(*args)
         assert a == b and a != mbn.MBN_OK, (name, args, a, b)
+
+
+def test_timed_entry_points_validate_like_the_plain_ones(lib):
+    """The timed variants run the plain entry point's checks (same status, no
+    HIP call for a rejected or empty input) and reject null events first."""
+    ev = FAKE + 0x30000000  # never dereferenced: every call below fails or is empty on the host
+    rms_cases = [
+        (FAKE, FAKE + B, FAKE + 16, 4, 64, 1e-6, None),      # y overlaps x
+        (FAKE, FAKE + B, FAKE + 2 * B, 4, 64, -1.0, None),   # eps < 0
+        (FAKE + 1, FAKE + B, FAKE + 2 * B, 4, 64, 1e-6, None),  # odd address
+        (None, None, None, 0, 64, 1e-6, None),               # empty: MBN_OK, nothing launched
+    ]
+    for args in rms_cases:
+        assert lib.rmsnorm_fwd_timed(*args, ev, ev + 8) == lib.rmsnorm_fwd(*args), args
+    qk_cases = [
+        (FAKE, FAKE + B, FAKE + B + 4096, FAKE + B + 8192, 4, 4, 2, 64, 1e-6, 1e6, None),   # head_dim
+        (None, FAKE + B, FAKE + B + 4096, FAKE + B + 8192, 4, 4, 2, 128, 1e-6, 1e6, None),  # null qkv
+        (FAKE, FAKE + B, FAKE + B + 4096, FAKE + B + 8192, 0, 4, 2, 128, 1e-6, 1e6, None),  # empty
+    ]
+    for args in qk_cases:
+        assert lib.qk_norm_rope_fwd_timed(*args, ev, ev + 8) == lib.qk_norm_rope_fwd(*args), args
+    assert lib.rmsnorm_fwd_timed(*rms_cases[0][:7], None, ev) == mbn.MBN_EINVAL
+    assert lib.rmsnorm_fwd_timed(*rms_cases[0][:7], ev, None) == mbn.MBN_EINVAL
+    assert lib.qk_norm_rope_fwd_timed(*qk_cases[0], None, None) == mbn.MBN_EINVAL
 
 
 def test_stream_reference_library_loads_and_validates():
