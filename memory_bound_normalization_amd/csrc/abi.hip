@@ -182,13 +182,6 @@ class TimedCall {
 
 }  // namespace
 
-namespace mbn {
-LaunchTiming*& launch_timing() {
-  static thread_local LaunchTiming* slot = nullptr;
-  return slot;
-}
-}  // namespace mbn
-
 extern "C" {
 
 MBN_API int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps,

@@ -21,7 +21,10 @@ struct LaunchTiming {
   hipEvent_t start;
   hipEvent_t stop;
 };
-LaunchTiming*& launch_timing();
+inline LaunchTiming*& launch_timing() {
+  static thread_local LaunchTiming* slot = nullptr;
+  return slot;
+}
 
 // Every kernel launch of the library goes through here; returns the launch status.
 template <typename... KArgs, typename... Args>
