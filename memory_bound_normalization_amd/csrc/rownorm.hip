@@ -567,6 +567,13 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_regs_kernel(RowNormAr
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t row = xcd_remap(blockIdx.x, gridDim.x, a.xcd_group) * ROWS + slot;
   const bool live = row < a.M;
+  // With one row per workgroup, a workgroup past the last row has no barrier
+  // to join: it leaves here, and the row loads below need no row predicate
+  // (on MI355X predicated loads made 4096 x 32768 about 1% slower).
+  if constexpr (ROWS == 1) {
+    if (!live) return;
+  }
+  const bool row_live = ROWS == 1 || live;
   const int64_t base = row * nchunk;
 
   // The row (and residual) chunks first (HBM), then weight and bias (L2 hits).
@@ -574,7 +581,7 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_regs_kernel(RowNormAr
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
     const int k = j * TPR + t;
-    const bool in = live && (FULL || k < nchunk);
+    const bool in = row_live && (FULL || k < nchunk);
     xv[j] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x) + base + k)
                : u32x4{0u, 0u, 0u, 0u};
     if constexpr (kHasR)
@@ -596,7 +603,7 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_regs_kernel(RowNormAr
       for (int e = 0; e < 4; ++e)
         hv[e] = DT::pack(DT::lo(xv[j][e]) + DT::lo(rv[j][e]), DT::hi(xv[j][e]) + DT::hi(rv[j][e]));
       xv[j] = hv;
-      if (live && (FULL || k < nchunk)) store_nt_16(reinterpret_cast<u32x4*>(a.h) + base + k, hv);
+      if (row_live && (FULL || k < nchunk)) store_nt_16(reinterpret_cast<u32x4*>(a.h) + base + k, hv);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -643,7 +650,7 @@ __global__ void __launch_bounds__(64 * WPR * ROWS) rownorm_regs_kernel(RowNormAr
   }
 
   // Pass 2: normalize, weight, round, streaming stores.
-  if (!live) return;
+  if (!row_live) return;
   u32x4* yrow = reinterpret_cast<u32x4*>(a.y) + base;
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {

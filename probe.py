@@ -1290,6 +1290,302 @@ def late_weights() -> None:
               lambda h, *args: h.mbn_early_w_rmsnorm(*args), 1e-6, lambda N: False, 29)
 
 
+WIDE_ROWS_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_wide.so")
+# probe_csrc/wide_rows.hip, variant: (lanes per row, occupancy cap, XCD row run,
+# when the weight is loaded); variant 1 is the launch table's entry.
+WIDE_ROW_VARIANTS = {
+    1: (1024, 4, 4, "with the row"),
+    2: (1024, 4, 4, "after the reduction"),
+    3: (1024, 4, 0, "after the reduction"),
+    4: (1024, 4, 8, "after the reduction"),
+    5: (512, 4, 4, "with the row"),
+    6: (512, 2, 4, "with the row"),
+    7: (512, 4, 4, "after the reduction"),
+    8: (512, 3, 4, "after the reduction"),
+    9: (512, 0, 4, "after the reduction"),
+    10: (512, 4, 0, "after the reduction"),
+    11: (256, 4, 4, "after the reduction"),
+    12: (256, 8, 4, "after the reduction"),
+}
+WIDE_ROW_SHAPES = [(4096, 32768), (8192, 32768)]
+
+
+def build_wide_rows(verbose: bool = False) -> str:
+    """Compile probe_csrc/wide_rows.hip (register-row RMSNorm geometries at
+    N = 32768, with the library's row-norm source) into
+    probe_csrc/libmbn_wide.so; always rebuilds."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=WIDE_ROWS_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "wide_rows.hip")])
+
+
+def wide_rows_lib():
+    if not os.path.exists(WIDE_ROWS_LIB_PATH):
+        build_wide_rows()
+    h = ctypes.CDLL(WIDE_ROWS_LIB_PATH)
+    h.mbn_wide_rows_variant.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_float, ctypes.c_int] + [
+        ctypes.c_void_p] * 3
+    h.mbn_wide_rows_variant.restype = ctypes.c_int
+    return h
+
+
+def _timed_rounds(cases, nrot, timer, rounds, launches):
+    """Median per round of `launches` launches of each case (f(i, start, stop)
+    records the kernel's own start and end), rounds in alternating order.
+    Destroys every event the timer holds (the caller's too) as it goes."""
+    import statistics
+
+    import torch
+
+    spare = (timer.new(), timer.new())
+    res = {k: [] for k, _ in cases}
+    for rnd in range(rounds):
+        for k, f in (cases if rnd % 2 == 0 else cases[::-1]):
+            for i in range(4):
+                f(i % nrot, *spare)
+            ev = [(timer.new(), timer.new()) for _ in range(launches)]
+            for i, (a, b) in enumerate(ev):
+                f(i % nrot, a, b)
+            torch.cuda.synchronize()
+            res[k].append(statistics.median(timer.elapsed_ms(a, b) * 1e3 for a, b in ev))
+            timer.close()
+            spare = (timer.new(), timer.new())
+    return res
+
+
+def wide_rows(rounds: int = 6, launches: int = 40) -> None:
+    """rmsnorm_fwd at N = 32768 (rows in VGPRs) against the register-row
+    geometries of probe_csrc/wide_rows.hip on the same data (x ~ 0.5 N(0, 1),
+    w ~ U(0.5, 1.5), eps 1e-5, buffer sets rotated through >= 1 GiB). Each
+    variant's output is compared with the library's (same lanes per row: same
+    bits; otherwise within one ulp); then per round, in alternating order, the
+    median of `launches` launches timed by the kernels' own start and end.
+    One JSON line per shape and case."""
+    sys.path.insert(0, ROOT)
+    import json
+    import statistics
+
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    h = wide_rows_lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    g = torch.Generator(device=dev).manual_seed(3)
+    for M, N in WIDE_ROW_SHAPES:
+        spare = (timer.new(), timer.new())  # _timed_rounds destroys the timer's events
+        nrot = max(2, -(-(1 << 30) // (2 * M * N * 2)))
+        xs = [(torch.randn(M, N, device=dev, generator=g) * 0.5).to(torch.bfloat16) for _ in range(nrot)]
+        ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        ref = mbn.rmsnorm_fwd(xs[0], w, eps=1e-5)
+
+        def variant(v):
+            def f(i, a, b):
+                rc = h.mbn_wide_rows_variant(xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, 1e-5, v, sp, a, b)
+                if rc != 0:
+                    raise RuntimeError(f"wide-row variant {v}: status {rc}")
+            return f
+
+        def library(i, a, b):
+            mbn.rmsnorm_fwd_timed(xs[i], w, a, b, y=ys[i], eps=1e-5)
+
+        for v in WIDE_ROW_VARIANTS:
+            variant(v)(0, *spare)
+            torch.cuda.synchronize()
+            d = (ys[0].view(torch.int16).int() - ref.view(torch.int16).int()).abs()
+            print(json.dumps({"check": v, "M": M, "N": N, "bit_identical": float((d == 0).float().mean()),
+                              "max_bits": int(d.max())}), flush=True)
+            if int(d.max()) > 1:
+                raise RuntimeError(f"wide-row variant {v}: outputs differ from the library's by more than one ulp")
+        for i in range(2000 * 4096 // M):
+            library(i % nrot, *spare)
+        torch.cuda.synchronize()
+        cases = [("library", library)] + [(v, variant(v)) for v in WIDE_ROW_VARIANTS]
+        res = _timed_rounds(cases, nrot, timer, rounds, launches)
+        nb = 2 * M * N * 2 + 2 * N
+        for k, _ in cases:
+            med = statistics.median(res[k])
+            print(json.dumps({"kernel": k, "M": M, "N": N, "median_us": round(med, 2),
+                              "pct": round(nb / med / 1e3 / 80, 2), "rounds": [round(r, 2) for r in res[k]]}),
+                  flush=True)
+        del xs, ys
+        torch.cuda.empty_cache()
+
+
+def wide_rows_summary(log: str) -> None:
+    import json
+
+    rows = [json.loads(x) for x in open(log) if x.startswith("{")]
+    print("rmsnorm_fwd at N = 32768 (rows in VGPRs) against register-row geometries, MI355X (gfx950), one GPU")
+    print("=" * 98)
+    print()
+    print("Commands (from the repository root; probe.py builds probe_csrc/libmbn_wide.so from")
+    print("probe_csrc/wide_rows.hip on first use):")
+    print(f"  python -u probe.py wide-rows > {log}")
+    print(f"  python probe.py wide-rows-summary {log}")
+    print()
+    print("Each variant holds the row in VGPRs as the library's rownorm_regs_kernel does (16-byte")
+    print("non-temporal loads and stores, one cross-wave LDS step), with the lanes per row, the")
+    print("occupancy cap (resident workgroups per CU, through the dynamic LDS request; 0 = none),")
+    print("the XCD row run (0 = dispatch order) and the point where the weight is loaded chosen")
+    print("per variant. Variant 1 is the launch table's entry. Same data (x ~ 0.5 N(0,1), buffer")
+    print("sets rotated through >= 1 GiB), outputs checked against the library's; per round, in")
+    print("alternating order, the median of 40 launches timed by the kernels' own start and end;")
+    print("the median over 6 rounds; % of 8 TB/s on the algorithmic bytes.")
+    for M, N in sorted({(r["M"], r["N"]) for r in rows if "kernel" in r}):
+        print()
+        lib = next(r for r in rows if r.get("kernel") == "library" and r["M"] == M)
+        print(f"  x[{M}, {N}]")
+        print(f"  {'case':<58} {'median_us':>9} {'%':>6} {'vs library':>10} {'same bits':>9}")
+        print(f"  {'library rmsnorm_fwd':<58} {lib['median_us']:>9.2f} {lib['pct']:>6.2f} {1.0:>10.3f} {'':>9}")
+        for r in rows:
+            if r.get("kernel") in WIDE_ROW_VARIANTS and r["M"] == M:
+                lanes, cap, run, wt = WIDE_ROW_VARIANTS[r["kernel"]]
+                chk = next(c for c in rows if c.get("check") == r["kernel"] and c["M"] == M)
+                desc = f"{r['kernel']}: {lanes} lanes, cap {cap}, XCD run {run}, weight {wt}"
+                print(f"  {desc:<58} {r['median_us']:>9.2f} {r['pct']:>6.2f} {lib['median_us'] / r['median_us']:>10.3f} "
+                      f"{100 * chk['bit_identical']:>8.4f}%")
+
+
+# Cache-policy bits of the row copy's LDS-DMA loads (global_load_lds_dwordx4):
+# aux operand of __builtin_amdgcn_global_load_lds on gfx950 (sc0 1, nt 2, sc1 16).
+LOAD_POLICIES = {0: "none", 16: "sc1", 18: "nt sc1", 17: "sc0 sc1", 3: "nt sc0"}
+LOAD_POLICY_SHAPES = [(16384, 16384), (8192, 8192)]
+
+
+def lp_lib_path(pol: int) -> str:
+    return os.path.join(PROBE_CSRC, f"libmbn_lp{pol}.so")
+
+
+def build_load_policy(verbose: bool = False) -> None:
+    """Compile the whole library once per load policy into
+    probe_csrc/libmbn_lp<policy>.so, from a copy of its sources in
+    probe_csrc/gen/lp<policy>/ whose device.h gives the LDS-DMA loads that
+    policy (the library's is nt); always rebuilds."""
+    sys.path.insert(0, ROOT)
+    import shutil
+    from concurrent.futures import ThreadPoolExecutor
+
+    from memory_bound_normalization_amd.build import build
+
+    csrc = os.path.join(ROOT, "memory_bound_normalization_amd", "csrc")
+    gen = os.path.join(PROBE_CSRC, "gen")
+    os.makedirs(os.path.join(gen, "include"), exist_ok=True)  # csrc/abi.hip includes ../../include/mbn.h
+    shutil.copyfile(os.path.join(ROOT, "include", "mbn.h"), os.path.join(gen, "include", "mbn.h"))
+    line = "constexpr int kCachePolicyNT = 2;"
+    srcs = {}
+    for pol in LOAD_POLICIES:
+        d = os.path.join(gen, f"lp{pol}", "csrc")
+        if os.path.exists(d):
+            shutil.rmtree(d)
+        shutil.copytree(csrc, d)
+        text = open(os.path.join(d, "device.h")).read()
+        if text.count(line) != 1:
+            raise RuntimeError("device.h: the load policy constant is not where the probe expects it")
+        with open(os.path.join(d, "device.h"), "w") as f:
+            f.write(text.replace(line, f"constexpr int kCachePolicyNT = {pol};"))
+        srcs[pol] = sorted(os.path.join(d, n) for n in os.listdir(d) if n.endswith(".hip"))
+    with ThreadPoolExecutor(len(LOAD_POLICIES)) as ex:
+        list(ex.map(lambda p: build(verbose=verbose, out=lp_lib_path(p), sources_=srcs[p]), LOAD_POLICIES))
+
+
+def load_policy(rounds: int = 6, launches: int = 40) -> None:
+    """rmsnorm_fwd against the same library built with other cache policies on
+    its LDS-DMA row loads (libmbn_lp<policy>.so), at 16384 x 16384 and
+    8192 x 8192: outputs compared bit for bit, then per round, in alternating
+    order, the median of `launches` launches timed by the kernels' own start
+    and end (rmsnorm_fwd_timed of each library), buffer sets rotated through
+    >= 1 GiB. One JSON line per shape and case."""
+    sys.path.insert(0, ROOT)
+    import json
+    import statistics
+
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    if not all(os.path.exists(lp_lib_path(p)) for p in LOAD_POLICIES):
+        build_load_policy()
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    libs = {"nt (library)": mbn.lib()}
+    for p in LOAD_POLICIES:
+        h = ctypes.CDLL(lp_lib_path(p))
+        h.rmsnorm_fwd_timed.argtypes = [vp, vp, vp, i64, i64, f32, vp, vp, vp]
+        h.rmsnorm_fwd_timed.restype = ctypes.c_int
+        libs[LOAD_POLICIES[p]] = h
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    g = torch.Generator(device=dev).manual_seed(4)
+    for M, N in LOAD_POLICY_SHAPES:
+        spare = (timer.new(), timer.new())  # _timed_rounds destroys the timer's events
+        nrot = max(2, -(-(1 << 30) // (2 * M * N * 2)))
+        xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
+        ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        ref = mbn.rmsnorm_fwd(xs[0], w, eps=1e-6)
+
+        def mk(h):
+            def f(i, a, b):
+                rc = h.rmsnorm_fwd_timed(xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, N, 1e-6, sp, a, b)
+                if rc != 0:
+                    raise RuntimeError(f"rmsnorm_fwd_timed: status {rc}")
+            return f
+
+        cases = [(k, mk(h)) for k, h in libs.items()]
+        for k, f in cases[1:]:
+            f(0, *spare)
+            torch.cuda.synchronize()
+            if not torch.equal(ys[0].view(torch.int16), ref.view(torch.int16)):
+                raise RuntimeError(f"load policy {k}: outputs differ from the library's")
+        for i in range(2000 * (16384 * 16384) // (M * N)):
+            cases[0][1](i % nrot, *spare)
+        torch.cuda.synchronize()
+        res = _timed_rounds(cases, nrot, timer, rounds, launches)
+        nb = 2 * M * N * 2 + 2 * N
+        for k, _ in cases:
+            med = statistics.median(res[k])
+            print(json.dumps({"policy": k, "M": M, "N": N, "median_us": round(med, 2),
+                              "pct": round(nb / med / 1e3 / 80, 2), "rounds": [round(r, 2) for r in res[k]]}),
+                  flush=True)
+        del xs, ys
+        torch.cuda.empty_cache()
+
+
+def load_policy_summary(log: str) -> None:
+    import json
+
+    rows = [json.loads(x) for x in open(log) if x.startswith("{")]
+    print("rmsnorm_fwd with other cache policies on its LDS-DMA row loads, MI355X (gfx950), one GPU")
+    print("=" * 88)
+    print()
+    print("Commands (from the repository root; probe.py builds probe_csrc/libmbn_lp<policy>.so from")
+    print("copies of the library's sources in probe_csrc/gen/ on first use):")
+    print(f"  python -u probe.py load-policy > {log}")
+    print(f"  python probe.py load-policy-summary {log}")
+    print()
+    print("The whole library is rebuilt with another cache policy on global_load_lds_dwordx4 (the")
+    print("row copy HBM -> LDS); everything else is unchanged. Outputs are bit-identical to the")
+    print("library's. Per round, in alternating order, the median of 40 launches timed by the")
+    print("kernels' own start and end; the median over 6 rounds; buffer sets rotated through")
+    print(">= 1 GiB; % of 8 TB/s on the algorithmic bytes.")
+    for M, N in sorted({(r["M"], r["N"]) for r in rows}, reverse=True):
+        print()
+        lib = next(r for r in rows if r["policy"] == "nt (library)" and r["M"] == M)
+        print(f"  x[{M}, {N}]")
+        print(f"  {'load policy':<16} {'median_us':>9} {'%':>6} {'vs library':>10}")
+        for r in rows:
+            if r["M"] == M:
+                print(f"  {r['policy']:<16} {r['median_us']:>9.2f} {r['pct']:>6.2f} "
+                      f"{lib['median_us'] / r['median_us']:>10.3f}")
+
+
 PRIOR_ANY_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_prior_any.so")
 
 
@@ -2104,6 +2400,14 @@ if __name__ == "__main__":
         qk_pattern()
     elif len(sys.argv) == 3 and sys.argv[1] == "qk-pattern-summary":
         qk_pattern_summary(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "wide-rows":
+        wide_rows()
+    elif len(sys.argv) == 3 and sys.argv[1] == "wide-rows-summary":
+        wide_rows_summary(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "load-policy":
+        load_policy()
+    elif len(sys.argv) == 3 and sys.argv[1] == "load-policy-summary":
+        load_policy_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "late-weights":
         late_weights()
     elif len(sys.argv) == 3 and sys.argv[1] in ("staging-summary", "late-weights-summary"):

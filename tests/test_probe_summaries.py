@@ -224,3 +224,34 @@ def test_qk_ab_summary_table(tmp_path, capsys):
     probe.qk_ab_summary(str(log))
     out = capsys.readouterr().out
     assert "   65536  32   8     215.00   78.1    255.00   65.8   1.186" in out
+
+
+def test_wide_rows_summary(tmp_path, capsys):
+    """The wide-row table: one line per variant with its geometry, speed relative to
+    the library and the share of bit-identical outputs."""
+    import json
+
+    log = tmp_path / "wide.log"
+    lines = [{"check": v, "M": 4096, "N": 32768, "bit_identical": 1.0 if v < 5 else 0.99999, "max_bits": 0 if v < 5 else 1}
+             for v in probe.WIDE_ROW_VARIANTS]
+    lines.append({"kernel": "library", "M": 4096, "N": 32768, "median_us": 86.0, "pct": 78.0, "rounds": [86.0]})
+    lines += [{"kernel": v, "M": 4096, "N": 32768, "median_us": 86.0 + v, "pct": 70.0, "rounds": [86.0 + v]}
+              for v in probe.WIDE_ROW_VARIANTS]
+    log.write_text("\n".join(json.dumps(x) for x in lines) + "\n")
+    probe.wide_rows_summary(str(log))
+    out = capsys.readouterr().out
+    assert "1: 1024 lanes, cap 4, XCD run 4, weight with the row" in out
+    assert f"{86.0 / 88.0:.3f}" in out  # variant 2 against the library
+    assert "99.9990%" in out
+
+
+def test_load_policy_summary(tmp_path, capsys):
+    import json
+
+    log = tmp_path / "lp.log"
+    lines = [{"policy": k, "M": 16384, "N": 16384, "median_us": t, "pct": 80.0, "rounds": [t]}
+             for k, t in (("nt (library)", 166.0), ("none", 174.3), ("nt sc1", 166.5))]
+    log.write_text("\n".join(json.dumps(x) for x in lines) + "\n")
+    probe.load_policy_summary(str(log))
+    out = capsys.readouterr().out
+    assert "x[16384, 16384]" in out and f"{166.0 / 174.3:.3f}" in out and "nt sc1" in out
