@@ -1,8 +1,9 @@
 // Row-wise norms for gfx950 with each row staged in LDS: RMSNorm, residual add
 // + RMSNorm, LayerNorm and L2Norm, on bf16 or fp16 data (fp16 is among the
 // broadened inputs of "[Inductor] Codegen Gluon", section 3.2). RMSNorm rows
-// of exactly 32768 and 65536 elements are held in VGPRs instead
-// (rownorm_regs_kernel, below).
+// of exactly 32768 and 65536 elements, and small RMSNorm launches (up to a few
+// thousand rows) at exactly 2048, 4096, 8192 and 16384, are held in VGPRs
+// instead (rownorm_regs_kernel, below).
 //
 // The method ("[Inductor] Codegen Gluon", section 3.1, RMSNorm as the reference
 // workload; section 3.2 for the rest of the family): the input row is needed
@@ -816,6 +817,22 @@ constexpr RowNormKernel chunk_wait_kernel() {
         {nullptr, nullptr}, true                                                     \
   }
 
+// The _ROWS_R form: a row window with register-resident rows at one exact
+// width (rownorm_regs_kernel, RPL = 1) for small launches. On MI355X, at
+// N = 2048 ... 16384 and a few hundred to two thousand rows, the kernel-trace
+// medians of these geometries were 3-12% below the staged kernels' windows: a
+// small launch's time is mostly the latency of one row's trip, and the rows
+// go HBM -> VGPRs without the LDS write and read. Windows are listed before the
+// band's other windows (they serve only its top width), in increasing MAXROWS.
+#define MBN_CFG_ROWS_EXACT_R(MODE, MAXROWS, WPR, ROWS, MAXC, CAP, GROUP)                       \
+  RowNormCfg {                                                                                \
+    64 * (WPR) * (MAXC), 64 * (WPR) * (MAXC), true, MAXROWS, WPR, ROWS, 1, MAXC, CAP, GROUP,    \
+        {nullptr, nullptr},                                                                   \
+        {&rownorm_regs_kernel<MODE, Bf16, WPR, ROWS, MAXC, true>,                             \
+         &rownorm_regs_kernel<MODE, F16, WPR, ROWS, MAXC, true>},                             \
+        {nullptr, nullptr}, true                                                              \
+  }
+
 // Per-width launch tables, narrowest first: the first entry that serves the
 // row width is used. Every entry with WPR > 1 serves only widths of at least
 // 64 * WPR chunks, which the parked partial sums need (exact entries, or the
@@ -851,14 +868,19 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_ROWS(Norm::kRms, 2048, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 2048
     MBN_CFG_ROWS(Norm::kRms, 8192, 1, 4, 2, 2, 4, 0),  // N <= 1024, M <= 8192
     MBN_CFG(Norm::kRms, 1, 4, 1, 2, 0, 16),  // N <= 1024:  4 x 64 threads
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 2048, 1, 1, 4, 0, 0),  // N == 2048, M <= 2048: 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 256, 2, 2, 1, 2, 1, 0),  // N <= 2048, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 2048, 1, 4, 1, 4, 4, 0),  // N <= 2048, M <= 2048
     MBN_CFG_ROWS(Norm::kRms, 4096, 1, 4, 2, 4, 2, 0),  // N <= 2048, M <= 4096
     MBN_CFG(Norm::kRms, 2, 2, 2, 2, 4, 8),   // N <= 2048:  2 x 128 threads x 2 rows, 4 WGs/CU
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 512, 4, 1, 2, 0, 0),  // N == 4096, M <= 512: 256 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 2048, 1, 1, 8, 0, 0),  // N == 4096, M <= 2048: 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 2, 0, 0),  // N <= 4096, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 2, 1, 4, 3, 0),  // N <= 4096, M <= 1024
     MBN_CFG_ROWS(Norm::kRms, 4096, 2, 1, 2, 4, 0, 0),  // N <= 4096, M <= 4096
     MBN_CFG_W(Norm::kRms, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows, 4 WGs/CU
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 256, 4, 1, 4, 0, 0),  // N == 8192, M <= 256: 256 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 1024, 4, 2, 4, 0, 0),  // N == 8192, M <= 1024: 2 x 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 4, 0, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 1024
     MBN_CFG_ROWS(Norm::kRms, 2048, 2, 1, 2, 8, 0, 0),  // N <= 8192, M <= 2048
@@ -866,6 +888,8 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_UPTO(Norm::kRms, 6144, 6, 1, 2, 2, 4, 0),  // 4096 < N <= 6144: 384 threads x 2 rows
     MBN_CFG_EXACT_W(Norm::kRms, 7, 1, 2, 2, 3, 0),  // N == 7168: 448 threads x 2 rows
     MBN_CFG_LW(Norm::kRms, 8, 1, 1, 2, 0, 0),  // N <= 8192:  512 threads, weight after the reduction
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 256, 8, 1, 4, 0, 0),  // N == 16384, M <= 256: 512 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 512, 8, 2, 4, 0, 0),  // N == 16384, M <= 512: 2 x 512 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 1536, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1536
     MBN_CFG_ROWS_EXACT_W(Norm::kRms, 6144, 4, 1, 1, 8, 2, 8),  // N == 16384, M <= 6144

@@ -1452,6 +1452,153 @@ def wide_rows_summary(log: str) -> None:
                       f"{100 * chk['bit_identical']:>8.4f}%")
 
 
+SMALL_REGS_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_small_regs.so")
+SMALL_REGS_WIDTHS = (2048, 4096, 8192, 16384)
+SMALL_REGS_ROWS = (256, 384, 512, 768, 1024, 1536, 2048)
+
+
+def build_small_regs(verbose: bool = False) -> str:
+    """Compile probe_csrc/small_regs.hip into probe_csrc/libmbn_small_regs.so;
+    always rebuilds."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=SMALL_REGS_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "small_regs.hip")])
+
+
+def small_regs_lib():
+    if not os.path.exists(SMALL_REGS_LIB_PATH):
+        build_small_regs()
+    h = ctypes.CDLL(SMALL_REGS_LIB_PATH)
+    h.mbn_small_regs.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int] + [
+        ctypes.c_void_p] * 3
+    h.mbn_small_regs.restype = ctypes.c_int
+    h.mbn_small_regs_geometry.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    h.mbn_small_regs_geometry.restype = ctypes.c_int
+    return h
+
+
+def small_regs_geometries(h):
+    out = {}
+    g = (ctypes.c_int * 3)()
+    for v in range(h.mbn_small_regs_count()):
+        if h.mbn_small_regs_geometry(v, g) != 0:
+            raise RuntimeError("mbn_small_regs_geometry failed")
+        out[v] = (g[0], g[1], g[2])
+    return out
+
+
+def small_regs(rounds: int = 8, launches: int = 60) -> None:
+    """Small RMSNorm launches (N = 2048 ... 16384, M = 256 ... 2048) through
+    rmsnorm_fwd and through the register-row geometries of
+    probe_csrc/small_regs.hip of the same width, on the same data, buffer sets
+    rotated through >= 1 GiB. Meant to run under rocprofv3 --kernel-trace:
+    every group of back-to-back launches is announced by a JSON line
+    {"block": [N, M, case, launches]} in launch order, so that
+    small-regs-summary can attribute the traced kernels. Outputs are compared
+    with the library's first (one ulp; the sum order differs)."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    h = small_regs_lib()
+    geo = small_regs_geometries(h)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    g = torch.Generator(device=dev).manual_seed(17)
+    ev = (timer.new(), timer.new())
+
+    def block(N, M, case, n):
+        print(json.dumps({"block": [N, M, case, n]}), flush=True)
+
+    for N in SMALL_REGS_WIDTHS:
+        vs = [v for v, (wpr, _, maxc) in geo.items() if 64 * wpr * maxc * 8 == N]
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        for M in SMALL_REGS_ROWS:
+            nrot = max(2, -(-(1 << 30) // (2 * M * N * 2)))
+            xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
+            ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+
+            def run(case, i):
+                if case == "library":
+                    mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=1e-6)
+                elif h.mbn_small_regs(xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, N, 1e-6, case, sp,
+                                      *ev) != 0:
+                    raise RuntimeError(f"small-regs variant {case}: launch failed")
+
+            block(N, M, "library", 1)
+            ref = mbn.rmsnorm_fwd(xs[0], w, eps=1e-6)
+            for v in vs:
+                block(N, M, v, 1)
+                run(v, 0)
+                torch.cuda.synchronize()
+                d = (ys[0].view(torch.int16).int() - ref.view(torch.int16).int()).abs()
+                if int(d.max()) > 1:
+                    raise RuntimeError(f"small-regs variant {v}: outputs differ from the library's by more than one ulp")
+            cases = ["library"] + vs
+            for rnd in range(rounds):
+                for case in (cases if rnd % 2 == 0 else cases[::-1]):
+                    block(N, M, case, launches)
+                    for i in range(launches):
+                        run(case, (i * 7) % nrot)
+                    torch.cuda.synchronize()
+            del xs, ys
+            torch.cuda.empty_cache()
+    timer.close()
+
+
+def small_regs_summary(trace_dir: str, log: str) -> None:
+    """Per width and row count, the median kernel duration of the library and
+    of each register-row geometry, from the kernel trace (trace_dir) of
+    `python -u probe.py small-regs > log`."""
+    import json
+    import statistics
+
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ks = [r for r in rows if "rownorm" in r["Kernel_Name"]]
+    blocks = [json.loads(x)["block"] for x in open(log) if x.startswith('{"block"')]
+    if sum(b[3] for b in blocks) != len(ks):
+        raise SystemExit(f"{len(ks)} traced row-norm dispatches, {sum(b[3] for b in blocks)} announced")
+    dur = {}
+    kname = {}
+    i = 0
+    for N, M, case, n in blocks:
+        grp = ks[i:i + n]
+        i += n
+        if n > 1:  # timed groups (single launches are the output checks)
+            dur.setdefault((N, M, case), []).extend(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+            kname[(N, M, case)] = _short_kernel(grp[0]["Kernel_Name"])
+    print("Small RMSNorm launches: the library against register-row geometries, MI355X (gfx950), one GPU")
+    print("=" * 96)
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp; probe.py builds probe_csrc/libmbn_small_regs.so")
+    print("from probe_csrc/small_regs.hip on first use):")
+    print(f"  rocprofv3 --kernel-trace --output-format csv -d {trace_dir} -o run -- \\")
+    print(f"      python -u probe.py small-regs > {log}")
+    print(f"  python probe.py small-regs-summary {trace_dir} {log}")
+    print()
+    print("Kernel durations from the trace: median over 8 rounds x 60 launches per case (rounds in")
+    print("alternating order, buffer sets rotated through >= 1 GiB); every variant's output within")
+    print("one ulp of the library's. regs<W, R, C>: rownorm_regs_kernel with 64 * W lanes per row,")
+    print("R rows per workgroup, C chunks of 16 bytes per lane, rows held in VGPRs.")
+    for N in sorted({k[0] for k in dur}):
+        for M in sorted({k[1] for k in dur if k[0] == N}):
+            lib = statistics.median(dur[(N, M, "library")])
+            print()
+            print(f"  x[{M}, {N}]: library {kname[(N, M, 'library')]}: {lib:.2f} us")
+            cases = sorted((statistics.median(v), c) for (n_, m_, c), v in dur.items()
+                           if n_ == N and m_ == M and c != "library")
+            for med, c in cases:
+                print(f"    {kname[(N, M, c)][:52]:<52} {med:7.2f} us  {lib / med:6.3f} x library")
+
+
 # Cache-policy bits of the row copy's LDS-DMA loads (global_load_lds_dwordx4):
 # aux operand of __builtin_amdgcn_global_load_lds on gfx950 (sc0 1, nt 2, sc1 16).
 LOAD_POLICIES = {0: "none", 16: "sc1", 18: "nt sc1", 17: "sc0 sc1", 3: "nt sc0"}
@@ -2404,6 +2551,10 @@ if __name__ == "__main__":
         wide_rows()
     elif len(sys.argv) == 3 and sys.argv[1] == "wide-rows-summary":
         wide_rows_summary(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "small-regs":
+        small_regs()
+    elif len(sys.argv) == 4 and sys.argv[1] == "small-regs-summary":
+        small_regs_summary(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 2 and sys.argv[1] == "load-policy":
         load_policy()
     elif len(sys.argv) == 3 and sys.argv[1] == "load-policy-summary":

@@ -1,0 +1,76 @@
+// Register-row RMSNorm geometries for small launches, for the measurement
+// tools (not part of the library): the library's rownorm_regs_kernel at
+// widths 2048 ... 16384 with the lanes per row, rows per workgroup and chunks
+// per lane chosen per variant, launched with the kernel's own start and end
+// recorded in two events (hipExtLaunchKernel).
+#include <hip/hip_ext.h>
+
+#include "../memory_bound_normalization_amd/csrc/rownorm.hip"
+
+namespace mbn {
+namespace {
+
+template <int WPR, int ROWS, int MAXC>
+int small_launch(const void* x, const void* w, void* y, int64_t M, int64_t N, float eps, hipStream_t s,
+                 hipEvent_t e0, hipEvent_t e1) {
+  if (N != (int64_t)64 * WPR * MAXC * 8) return 1;
+  RowNormArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.nchunk = (int)(N / 8);
+  a.inv_n = 1.0f / (float)N;
+  a.eps = eps;
+  a.xcd_group = 0;
+  const int64_t blocks = (M + ROWS - 1) / ROWS;
+  hipExtLaunchKernelGGL((rownorm_regs_kernel<Norm::kRms, Bf16, WPR, ROWS, MAXC, true>), dim3((unsigned)blocks),
+                        dim3(64 * WPR * ROWS), 0u, s, e0, e1, 0u, a);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+typedef int (*SmallLaunch)(const void*, const void*, void*, int64_t, int64_t, float, hipStream_t, hipEvent_t,
+                           hipEvent_t);
+struct SmallVariant {
+  int wpr, rows, maxc;
+  SmallLaunch f;
+};
+#define MBN_SMALL(W, R, C) SmallVariant{W, R, C, &small_launch<W, R, C>}
+// Index order is the variant number; the width is 64 * wpr * maxc * 8.
+const SmallVariant kSmall[] = {
+    MBN_SMALL(1, 1, 4), MBN_SMALL(1, 2, 4), MBN_SMALL(1, 4, 4), MBN_SMALL(2, 1, 2), MBN_SMALL(2, 2, 2),
+    MBN_SMALL(4, 1, 1),                                                                              // 2048
+    MBN_SMALL(1, 1, 8), MBN_SMALL(1, 2, 8), MBN_SMALL(2, 1, 4), MBN_SMALL(2, 2, 4), MBN_SMALL(4, 1, 2),
+    MBN_SMALL(4, 2, 2), MBN_SMALL(8, 1, 1),                                                          // 4096
+    MBN_SMALL(2, 1, 8), MBN_SMALL(2, 2, 8), MBN_SMALL(4, 1, 4), MBN_SMALL(4, 2, 4), MBN_SMALL(8, 1, 2),
+    MBN_SMALL(16, 1, 1),                                                                             // 8192
+    MBN_SMALL(4, 1, 8), MBN_SMALL(8, 1, 4), MBN_SMALL(16, 1, 2), MBN_SMALL(4, 2, 8), MBN_SMALL(8, 2, 4),  // 16384
+};
+
+}  // namespace
+}  // namespace mbn
+
+extern "C" {
+
+__attribute__((visibility("default"))) int mbn_small_regs_count() {
+  return (int)(sizeof(mbn::kSmall) / sizeof(mbn::kSmall[0]));
+}
+
+// Geometry of variant v: {lanes per row / 64, rows per workgroup, chunks per lane}.
+__attribute__((visibility("default"))) int mbn_small_regs_geometry(int v, int* out) {
+  if (v < 0 || v >= mbn_small_regs_count() || !out) return 1;
+  out[0] = mbn::kSmall[v].wpr;
+  out[1] = mbn::kSmall[v].rows;
+  out[2] = mbn::kSmall[v].maxc;
+  return 0;
+}
+
+// RMSNorm of x[M, N] bf16 with variant v (N must be its width): 0 = ok,
+// 1 = invalid arguments, 3 = launch failed.
+__attribute__((visibility("default"))) int mbn_small_regs(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                                                          float eps, int v, void* stream, void* e0, void* e1) {
+  if (!x || !w || !y || M <= 0 || M > (1 << 20) || v < 0 || v >= mbn_small_regs_count() || !e0 || !e1) return 1;
+  return mbn::kSmall[v].f(x, w, y, M, N, eps, (hipStream_t)stream, (hipEvent_t)e0, (hipEvent_t)e1);
+}
+
+}  // extern "C"

@@ -11,6 +11,8 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 CFG = r"MBN_CFG(_EXACT|_ROWS_EXACT|_ROWS|_UPTO)?(_W|_LW)?\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\)"
 # exact-width entries with register-resident rows: WPR, ROWS, MAXC, CAP, GROUP (RPL = 1)
 CFG_R = r"MBN_CFG_EXACT_R\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
+# row windows with register-resident rows at one exact width: MAXROWS, WPR, ROWS, MAXC, CAP, GROUP
+CFG_ROWS_R = r"MBN_CFG_ROWS_EXACT_R\((?:MODE|Norm::\w+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
 
 
 class Entry(namedtuple("Entry", "exact max_rows wpr rows rpl maxc cap grp upto chunk_wait regs late_w",
@@ -49,7 +51,10 @@ def _tables():
             found = macros.get(line.split("(")[0], None) if line.startswith("MBN_FIRST_BAND") else None
             for wpr, rows, maxc, cap, grp in re.findall(CFG_R, line):
                 entries.append(Entry(True, 0, int(wpr), int(rows), 1, int(maxc), int(cap), int(grp), 0, False, True))
-            if re.search(CFG_R, line):
+            for max_rows, wpr, rows, maxc, cap, grp in re.findall(CFG_ROWS_R, line):
+                entries.append(Entry(True, int(max_rows), int(wpr), int(rows), 1, int(maxc), int(cap), int(grp), 0,
+                                     False, True))
+            if re.search(CFG_R, line) or re.search(CFG_ROWS_R, line):
                 continue
             for e in (found if found is not None else re.findall(CFG, line)):
                 kind, w, *nums = e

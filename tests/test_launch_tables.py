@@ -20,7 +20,8 @@ def test_all_four_tables_found():
 @pytest.mark.parametrize("name", sorted(TABLES))
 def test_table_invariants(name):
     prev = 0  # widest row of the previous band
-    window = None  # (band top, max_rows) of the last row window
+    band_top = None  # top width of the current band's row windows
+    windows = []  # (exact, max_rows) of the current band's row windows, in table order
     sub_top = 0  # widest row of the last sub-band of the current band
     for e in TABLES[name]:
         top = e.top
@@ -33,21 +34,27 @@ def test_table_invariants(name):
         if e.max_rows:
             assert not e.sub and top > prev, (name, e)  # exact windows serve the band's top width
             assert not sub_top, (name, e)  # windows precede the band's sub-bands
-            if window is not None and window[0] == top:
-                assert e.max_rows > window[1], (name, e)  # increasing windows
+            assert band_top is None or band_top == top, (name, top)  # the previous band closed
+            band_top = top
+            # first match wins: an exact window must be reached at the top width
+            # past every window before it, a window of the whole band at the
+            # widths below the top past the band's windows before it
+            if e.exact:
+                assert all(e.max_rows > m for _, m in windows), (name, e)
             else:
-                assert window is None or window[0] == prev, (name, top)  # the previous band closed
-            window = (top, e.max_rows)
+                assert all(e.max_rows > m for x, m in windows if not x), (name, e)
+            windows.append((e.exact, e.max_rows))
         elif e.sub:
             assert top > max(prev, sub_top), (name, e)  # increasing sub-bands
             sub_top = top
         elif not e.exact:
             assert top > max(prev, sub_top)
-            assert window is None or window[0] == top, (name, top)  # windows end in their band's entry
-            window = None
+            assert band_top is None or band_top == top, (name, top)  # windows end in their band's entry
+            band_top = None
+            windows = []
             sub_top = 0
             prev = top
-    assert window is None and not sub_top
+    assert band_top is None and not windows and not sub_top
     assert prev * 8 == 65536  # the widest band reaches MBN_RMSNORM_MAX_N
 
 
