@@ -1599,6 +1599,128 @@ def small_regs_summary(trace_dir: str, log: str) -> None:
                 print(f"    {kname[(N, M, c)][:52]:<52} {med:7.2f} us  {lib / med:6.3f} x library")
 
 
+QK_ANGLE_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_qk_angle.so")
+QK_ANGLE_MODES = {0: "library path: wave 0 forms the angles, LDS table, barrier",
+                  1: "every wave forms the angles, ds_bpermute, no barrier",
+                  2: "no angle work (timing only, outputs not the operator's)",
+                  3: "as 1, rotation products in fp32"}
+
+
+def build_qk_angle(verbose: bool = False) -> str:
+    """Compile probe_csrc/qk_angle_paths.hip into probe_csrc/libmbn_qk_angle.so;
+    always rebuilds."""
+    sys.path.insert(0, ROOT)
+    from memory_bound_normalization_amd.build import build
+
+    return build(verbose=verbose, out=QK_ANGLE_LIB_PATH, sources_=[os.path.join(PROBE_CSRC, "qk_angle_paths.hip")])
+
+
+def qk_angles(rounds: int = 8, launches: int = 100) -> None:
+    """qk_norm_rope_fwd on 256 tokens (32 q + 8 k heads, full rotary, theta
+    1e6) beside the angle-path variants of probe_csrc/qk_angle_paths.hip, in
+    rounds of `launches` back-to-back launches per case (alternating order),
+    qkv buffers rotated through >= 1 GiB. Meant to run under rocprofv3
+    --kernel-trace (qk-angles-summary reads the durations by kernel name).
+    Modes 0, 1 and 3 are checked against the library first (mode 3 to one
+    ulp, the others bit for bit)."""
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    if not os.path.exists(QK_ANGLE_LIB_PATH):
+        build_qk_angle()
+    h = ctypes.CDLL(QK_ANGLE_LIB_PATH)
+    vp = ctypes.c_void_p
+    h.mbn_qk_angle_path.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                    vp, vp]
+    h.mbn_qk_angle_path.restype = ctypes.c_int
+    T, hq, hk = 256, 32, 8
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    width = (hq + 2 * hk) * 128
+    n = max(2, -(-(1 << 30) // (T * width * 2)))
+    qkv = [torch.randn(T, width, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+    qw = (torch.rand(128, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    kw = (torch.rand(128, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    pos = torch.arange(T, device=dev, dtype=torch.int64)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = HipTimingEvents(stream)
+    ev = (timer.new(), timer.new())
+
+    def library(i):
+        mbn.qk_norm_rope_fwd(qkv[i], qw, kw, pos, hq, hk, eps=1e-6, theta=1e6)
+
+    def mode(m):
+        def f(i):
+            if h.mbn_qk_angle_path(qkv[i].data_ptr(), qw.data_ptr(), kw.data_ptr(), pos.data_ptr(), T, hq, hk, m,
+                                   sp, *ev) != 0:
+                raise RuntimeError(f"qk angle path {m}: launch failed")
+        return f
+
+    src = qkv[0].clone()
+    qkv[0].copy_(src)
+    library(0)
+    torch.cuda.synchronize()
+    ref = qkv[0].clone()
+    for m in (0, 1, 3):
+        qkv[0].copy_(src)
+        mode(m)(0)
+        torch.cuda.synchronize()
+        d = (qkv[0].view(torch.int16).int() - ref.view(torch.int16).int()).abs()
+        if int(d.max()) > (1 if m == 3 else 0):
+            raise RuntimeError(f"qk angle path {m}: outputs differ from the library's")
+    qkv[0].copy_(src)
+    cases = [library] + [mode(m) for m in QK_ANGLE_MODES]
+    for i in range(500):
+        library(i % n)
+    torch.cuda.synchronize()
+    for rnd in range(rounds):
+        for f in (cases if rnd % 2 == 0 else cases[::-1]):
+            for i in range(launches):
+                f((i * 7) % n)
+            torch.cuda.synchronize()
+    timer.close()
+
+
+def qk_angles_summary(trace_dir: str) -> None:
+    import statistics
+
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    lib, modes = [], {m: [] for m in QK_ANGLE_MODES}
+    for r in rows:
+        n, d = r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        m = re.search(r"qkx_kernel<[^,]+, (\d)>", n)
+        if m:
+            modes[int(m.group(1))].append(d)
+        elif "qk_norm_rope_kernel" in n:
+            lib.append(d)
+    lib = lib[-800:]  # the timed rounds (the warm-up launches come first)
+    print("qk_norm_rope_fwd on 256 tokens: what the angle work adds, MI355X (gfx950), one GPU")
+    print("==================================================================================")
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp; probe.py builds probe_csrc/libmbn_qk_angle.so")
+    print("from probe_csrc/qk_angle_paths.hip on first use):")
+    print(f"  rocprofv3 --kernel-trace --output-format csv -d {trace_dir} -o run -- python -u probe.py qk-angles")
+    print(f"  python probe.py qk-angles-summary {trace_dir}")
+    print()
+    print("qkv[256, 48 * 128] bf16 (32 q + 8 k heads of 128), full rotary, theta 1e6, positions 0..255,")
+    print("buffers rotated through >= 1 GiB; 8 rounds x 100 back-to-back launches per case in")
+    print("alternating order; kernel durations from the trace (median, 10th percentile). The")
+    print("variants are the library's kernel body for one head row per wave with the angle work")
+    print("done another way; modes 0 and 1 give the library's bits, mode 3 within one ulp.")
+    print()
+    print(f"  {'case':<64} {'median_us':>9} {'p10_us':>7}")
+
+    def line(name, d):
+        print(f"  {name:<64} {statistics.median(d):>9.2f} {sorted(d)[len(d) // 10]:>7.2f}")
+
+    line("library qk_norm_rope_fwd", lib)
+    for m, d in modes.items():
+        line(f"{m}: {QK_ANGLE_MODES[m]}", d)
+
+
 # Cache-policy bits of the row copy's LDS-DMA loads (global_load_lds_dwordx4):
 # aux operand of __builtin_amdgcn_global_load_lds on gfx950 (sc0 1, nt 2, sc1 16).
 LOAD_POLICIES = {0: "none", 16: "sc1", 18: "nt sc1", 17: "sc0 sc1", 3: "nt sc0"}
@@ -2555,6 +2677,10 @@ if __name__ == "__main__":
         small_regs()
     elif len(sys.argv) == 4 and sys.argv[1] == "small-regs-summary":
         small_regs_summary(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 2 and sys.argv[1] == "qk-angles":
+        qk_angles()
+    elif len(sys.argv) == 3 and sys.argv[1] == "qk-angles-summary":
+        qk_angles_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "load-policy":
         load_policy()
     elif len(sys.argv) == 3 and sys.argv[1] == "load-policy-summary":

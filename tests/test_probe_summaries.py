@@ -255,3 +255,24 @@ def test_load_policy_summary(tmp_path, capsys):
     probe.load_policy_summary(str(log))
     out = capsys.readouterr().out
     assert "x[16384, 16384]" in out and f"{166.0 / 174.3:.3f}" in out and "nt sc1" in out
+
+
+def test_qk_angles_summary(tmp_path, capsys):
+    """The angle-path table reads the library's and each mode's durations by kernel name."""
+    import csv
+
+    d = tmp_path / "t"
+    d.mkdir()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for name, dur in [("void mbn::(anonymous namespace)::qk_norm_rope_kernel<mbn::Bf16, 1>(x)", 3760)] * 5 + [
+                (f"void mbn::(anonymous namespace)::qkx_kernel<mbn::Bf16, {m}>(x)", 3400 + 100 * m)
+                for m in range(4) for _ in range(5)]:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += 10000
+    probe.qk_angles_summary(str(d))
+    out = capsys.readouterr().out
+    assert "library qk_norm_rope_fwd" in out and "3.76" in out
+    assert "2: no angle work" in out and "3.60" in out
