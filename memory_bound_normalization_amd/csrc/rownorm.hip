@@ -1,9 +1,10 @@
 // Row-wise norms for gfx950 with each row staged in LDS: RMSNorm, residual add
 // + RMSNorm, LayerNorm and L2Norm, on bf16 or fp16 data (fp16 is among the
 // broadened inputs of "[Inductor] Codegen Gluon", section 3.2). RMSNorm rows
-// of exactly 32768 and 65536 elements, and small RMSNorm launches (up to a few
-// thousand rows) at exactly 2048, 4096, 8192 and 16384, are held in VGPRs
-// instead (rownorm_regs_kernel, below).
+// of exactly 32768 and 65536 elements, and small launches (up to a few
+// thousand rows) at exactly 2048, 4096, 8192 and 16384 for the widths and
+// norms the launch tables list, are held in VGPRs instead
+// (rownorm_regs_kernel, below).
 //
 // The method ("[Inductor] Codegen Gluon", section 3.1, RMSNorm as the reference
 // workload; section 3.2 for the rest of the family): the input row is needed
@@ -820,9 +821,11 @@ constexpr RowNormKernel chunk_wait_kernel() {
 // The _ROWS_R form: a row window with register-resident rows at one exact
 // width (rownorm_regs_kernel, RPL = 1) for small launches. On MI355X, at
 // N = 2048 ... 16384 and a few hundred to two thousand rows, the kernel-trace
-// medians of these geometries were 3-12% below the staged kernels' windows: a
-// small launch's time is mostly the latency of one row's trip, and the rows
-// go HBM -> VGPRs without the LDS write and read. Windows are listed before the
+// medians of these geometries were 2-38% below the staged kernels' windows
+// (RMSNorm 3-12%, LayerNorm, L2Norm and the residual add per width and row
+// count, each window kept only where two runs agreed): a small launch's time
+// is mostly the latency of one row's trip, and the rows go HBM -> VGPRs
+// without the LDS write and read. Windows are listed before the
 // band's other windows (they serve only its top width), in increasing MAXROWS.
 #define MBN_CFG_ROWS_EXACT_R(MODE, MAXROWS, WPR, ROWS, MAXC, CAP, GROUP)                       \
   RowNormCfg {                                                                                \
@@ -909,19 +912,26 @@ const RowNormCfg kAddRmsTable[] = {
     MBN_CFG_ROWS(Norm::kAddRms, 4096, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 4096
     MBN_CFG_ROWS(Norm::kAddRms, 32768, 1, 4, 2, 2, 0, 0),  // N <= 1024, M <= 32768
     MBN_CFG(Norm::kAddRms, 1, 4, 1, 2, 4, 16),  // N <= 1024
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1536, 2, 1, 2, 0, 0),  // N == 2048, M <= 1536: 128 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 2048, 1, 4, 4, 0, 0),  // N == 2048, M <= 2048: 4 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 1024, 2, 2, 1, 2, 0, 0),  // N <= 2048, M <= 1024
     MBN_CFG_ROWS(Norm::kAddRms, 8192, 2, 2, 2, 2, 4, 0),  // N <= 2048, M <= 8192
     MBN_CFG(Norm::kAddRms, 1, 4, 1, 4, 2, 8),   // N <= 2048
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1024, 8, 1, 1, 0, 0),  // N == 4096, M <= 1024: 512 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1536, 1, 2, 8, 0, 0),  // N == 4096, M <= 1536: 2 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 256, 4, 1, 1, 2, 4, 0),  // N <= 4096, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 4, 2, 1, 2, 0, 16),  // N <= 4096, M <= 512
     MBN_CFG_ROWS(Norm::kAddRms, 1024, 4, 1, 1, 2, 4, 16),  // N <= 4096, M <= 1024 (the band's general entry)
     MBN_CFG_ROWS(Norm::kAddRms, 4096, 1, 4, 1, 8, 0, 0),  // N <= 4096, M <= 4096
     MBN_CFG(Norm::kAddRms, 4, 1, 1, 2, 4, 16),  // N <= 4096:  256 threads, 4 WGs/CU
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 256, 16, 1, 1, 0, 0),  // N == 8192, M <= 256: 1024 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 512, 4, 2, 4, 0, 0),  // N == 8192, M <= 512: 2 x 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 2, 1, 64),  // N <= 8192, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 2, 0, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kAddRms, 2048, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 2048
     MBN_CFG_EXACT(Norm::kAddRms, 2, 2, 1, 5, 2, 4),  // N == 5120: 2 x 128 threads
     MBN_CFG(Norm::kAddRms, 8, 1, 1, 2, 2, 8),   // N <= 8192:  512 threads, 2 WGs/CU
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 256, 4, 1, 8, 0, 0),  // N == 16384, M <= 256: 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 4, 4, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 4, 0, 0),  // N <= 16384, M <= 512
     MBN_CFG_ROWS(Norm::kAddRms, 1024, 16, 1, 4, 2, 0, 0),  // N <= 16384, M <= 1024
@@ -934,13 +944,19 @@ const RowNormCfg kLayerTable[] = {
     MBN_FIRST_BAND(Norm::kLayer),
     MBN_CFG_ROWS(Norm::kLayer, 2048, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 2048
     MBN_CFG(Norm::kLayer, 1, 4, 2, 2, 4, 0),   // N <= 1024
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 1536, 1, 1, 4, 0, 0),  // N == 2048, M <= 1536: 64 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 2048, 1, 2, 4, 0, 0),  // N == 2048, M <= 2048: 2 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kLayer, 2048, 2, 2, 1, 2, 0, 0),  // N <= 2048, M <= 2048
     MBN_CFG_ROWS(Norm::kLayer, 4096, 1, 4, 2, 4, 0, 0),  // N <= 2048, M <= 4096
     MBN_CFG(Norm::kLayer, 2, 2, 2, 2, 4, 8),   // N <= 2048
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 1024, 1, 1, 8, 0, 0),  // N == 4096, M <= 1024: 64 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 2048, 2, 2, 4, 0, 0),  // N == 4096, M <= 2048: 2 x 128 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kLayer, 512, 4, 1, 1, 2, 4, 2),  // N <= 4096, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 2, 1, 2, 2, 0),  // N <= 4096, M <= 1024
     MBN_CFG_ROWS(Norm::kLayer, 2048, 1, 4, 1, 8, 2, 0),  // N <= 4096, M <= 2048
     MBN_CFG_W(Norm::kLayer, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 512, 4, 1, 4, 0, 0),  // N == 8192, M <= 512: 256 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 1536, 2, 1, 8, 0, 0),  // N == 8192, M <= 1536: 128 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kLayer, 512, 8, 1, 1, 2, 3, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 4, 2, 0),  // N <= 8192, M <= 1024
     MBN_CFG_ROWS(Norm::kLayer, 2048, 8, 1, 4, 2, 2, 0),  // N <= 8192, M <= 2048
@@ -948,6 +964,8 @@ const RowNormCfg kLayerTable[] = {
     MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 3, 3, 0),  // N == 6144: 256 threads x 2 rows
     MBN_CFG_EXACT_W(Norm::kLayer, 2, 2, 2, 7, 2, 0),  // N == 7168: 2 x 128 threads x 2 rows
     MBN_CFG_W(Norm::kLayer, 8, 1, 2, 2, 4, 16),  // N <= 8192:  512 threads x 2 rows
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 256, 8, 1, 4, 0, 0),  // N == 16384, M <= 256: 512 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 768, 4, 1, 8, 0, 0),  // N == 16384, M <= 768: 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kLayer, 512, 16, 1, 1, 2, 2, 0),  // N <= 16384, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 1, 2, 8, 2, 0),  // N <= 16384, M <= 1024
     MBN_CFG_EXACT_W(Norm::kLayer, 4, 1, 2, 5, 3, 8),  // N == 10240: 256 threads x 2 rows
@@ -963,6 +981,8 @@ const RowNormCfg kL2Table[] = {
     MBN_FIRST_BAND(Norm::kL2),
     MBN_CFG_ROWS(Norm::kL2, 2048, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 2048
     MBN_CFG(Norm::kL2, 1, 4, 2, 2, 4, 0),   // N <= 1024
+    MBN_CFG_ROWS_EXACT_R(Norm::kL2, 768, 1, 1, 4, 0, 0),  // N == 2048, M <= 768: 64 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kL2, 1536, 2, 1, 2, 0, 0),  // N == 2048, M <= 1536: 128 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kL2, 1024, 1, 4, 1, 4, 4, 0),  // N <= 2048, M <= 1024
     MBN_CFG(Norm::kL2, 2, 2, 2, 2, 4, 0),   // N <= 2048
     MBN_CFG_ROWS(Norm::kL2, 768, 4, 1, 1, 2, 0, 0),  // N <= 4096, M <= 768

@@ -1470,8 +1470,9 @@ def small_regs_lib():
     if not os.path.exists(SMALL_REGS_LIB_PATH):
         build_small_regs()
     h = ctypes.CDLL(SMALL_REGS_LIB_PATH)
-    h.mbn_small_regs.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int] + [
-        ctypes.c_void_p] * 3
+    vp = ctypes.c_void_p
+    h.mbn_small_regs.argtypes = [ctypes.c_int] + [vp] * 6 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                                            ctypes.c_int] + [vp] * 3
     h.mbn_small_regs.restype = ctypes.c_int
     h.mbn_small_regs_geometry.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     h.mbn_small_regs_geometry.restype = ctypes.c_int
@@ -1488,15 +1489,21 @@ def small_regs_geometries(h):
     return out
 
 
-def small_regs(rounds: int = 8, launches: int = 60) -> None:
-    """Small RMSNorm launches (N = 2048 ... 16384, M = 256 ... 2048) through
-    rmsnorm_fwd and through the register-row geometries of
+# op: (kernel mode, eps)
+SMALL_REGS_OPS = {"rms": (0, 1e-6), "add": (1, 1e-6), "layer": (2, 1e-5), "l2": (3, 1e-12)}
+
+
+def small_regs(ops: str = "rms", rounds: int = 8, launches: int = 60) -> None:
+    """Small row-norm launches (N = 2048 ... 16384, M = 256 ... 2048) through
+    the library and through the register-row geometries of
     probe_csrc/small_regs.hip of the same width, on the same data, buffer sets
-    rotated through >= 1 GiB. Meant to run under rocprofv3 --kernel-trace:
-    every group of back-to-back launches is announced by a JSON line
-    {"block": [N, M, case, launches]} in launch order, so that
-    small-regs-summary can attribute the traced kernels. Outputs are compared
-    with the library's first (one ulp; the sum order differs)."""
+    rotated through >= 1 GiB, for each op of `ops` (comma-separated: rms, add,
+    layer, l2). Meant to run under rocprofv3 --kernel-trace: every group of
+    back-to-back launches is announced by a JSON line {"block": [op, N, M,
+    case, launches]} in launch order, so that small-regs-summary can attribute
+    the traced kernels. Outputs are compared with the library's first (within
+    twice the one-ulp tolerance, the sums being taken in another order; the
+    residual sum h bit for bit)."""
     sys.path.insert(0, ROOT)
     import json
 
@@ -1513,42 +1520,68 @@ def small_regs(rounds: int = 8, launches: int = 60) -> None:
     g = torch.Generator(device=dev).manual_seed(17)
     ev = (timer.new(), timer.new())
 
-    def block(N, M, case, n):
-        print(json.dumps({"block": [N, M, case, n]}), flush=True)
+    def block(op, N, M, case, n):
+        print(json.dumps({"block": [op, N, M, case, n]}), flush=True)
 
-    for N in SMALL_REGS_WIDTHS:
-        vs = [v for v, (wpr, _, maxc) in geo.items() if 64 * wpr * maxc * 8 == N]
-        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
-        for M in SMALL_REGS_ROWS:
-            nrot = max(2, -(-(1 << 30) // (2 * M * N * 2)))
-            xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
-            ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+    for op in ops.split(","):
+        mode, eps = SMALL_REGS_OPS[op]
+        for N in SMALL_REGS_WIDTHS:
+            vs = [v for v, (wpr, _, maxc) in geo.items() if 64 * wpr * maxc * 8 == N]
+            w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+            b = (torch.rand(N, device=dev, generator=g) - 0.5).to(torch.bfloat16)
+            for M in SMALL_REGS_ROWS:
+                nrot = max(2, -(-(1 << 30) // ((4 if op == "add" else 2) * M * N * 2)))
+                xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
+                rs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)] \
+                    if op == "add" else [None] * nrot
+                ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+                hs = [torch.empty_like(xs[0]) for _ in range(nrot)] if op == "add" else [None] * nrot
 
-            def run(case, i):
-                if case == "library":
-                    mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=1e-6)
-                elif h.mbn_small_regs(xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(), M, N, 1e-6, case, sp,
-                                      *ev) != 0:
-                    raise RuntimeError(f"small-regs variant {case}: launch failed")
+                def ptr(t):
+                    return None if t is None else t.data_ptr()
 
-            block(N, M, "library", 1)
-            ref = mbn.rmsnorm_fwd(xs[0], w, eps=1e-6)
-            for v in vs:
-                block(N, M, v, 1)
-                run(v, 0)
+                def run(case, i):
+                    if case == "library":
+                        if op == "rms":
+                            mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps)
+                        elif op == "add":
+                            mbn.add_rmsnorm_fwd(xs[i], rs[i], w, hs[i], ys[i], eps=eps)
+                        elif op == "layer":
+                            mbn.layernorm_fwd(xs[i], w, b, ys[i], eps=eps)
+                        else:
+                            mbn.l2norm_fwd(xs[i], ys[i], eps=eps)
+                    elif h.mbn_small_regs(mode, xs[i].data_ptr(), ptr(rs[i]), None if op == "l2" else w.data_ptr(),
+                                          b.data_ptr() if op == "layer" else None, ptr(hs[i]), ys[i].data_ptr(),
+                                          M, N, eps, case, sp, *ev) != 0:
+                        raise RuntimeError(f"small-regs {op} variant {case}: launch failed")
+
+                block(op, N, M, "library", 1)
+                run("library", 0)
                 torch.cuda.synchronize()
-                d = (ys[0].view(torch.int16).int() - ref.view(torch.int16).int()).abs()
-                if int(d.max()) > 1:
-                    raise RuntimeError(f"small-regs variant {v}: outputs differ from the library's by more than one ulp")
-            cases = ["library"] + vs
-            for rnd in range(rounds):
-                for case in (cases if rnd % 2 == 0 else cases[::-1]):
-                    block(N, M, case, launches)
-                    for i in range(launches):
-                        run(case, (i * 7) % nrot)
+                ref_y = ys[0].clone()
+                ref_h = hs[0].clone() if op == "add" else None
+                for v in vs:
+                    block(op, N, M, v, 1)
+                    run(v, 0)
                     torch.cuda.synchronize()
-            del xs, ys
-            torch.cuda.empty_cache()
+                    # each within one bf16 ulp + 1e-6 of the exact result, so
+                    # within twice that of each other (LayerNorm outputs near
+                    # zero may differ in more than their last bit)
+                    a_, b_ = ys[0].float(), ref_y.float()
+                    bad = not bool(((a_ - b_).abs() <= 2.0 ** -6 * b_.abs() + 2e-6).all())
+                    if op == "add":
+                        bad = bad or not torch.equal(hs[0].view(torch.int16), ref_h.view(torch.int16))
+                    if bad:
+                        raise RuntimeError(f"small-regs {op} variant {v}: outputs differ from the library's")
+                cases = ["library"] + vs
+                for rnd in range(rounds):
+                    for case in (cases if rnd % 2 == 0 else cases[::-1]):
+                        block(op, N, M, case, launches)
+                        for i in range(launches):
+                            run(case, (i * 7) % nrot)
+                        torch.cuda.synchronize()
+                del xs, rs, ys, hs
+                torch.cuda.empty_cache()
     timer.close()
 
 
@@ -1563,40 +1596,86 @@ def small_regs_summary(trace_dir: str, log: str) -> None:
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     ks = [r for r in rows if "rownorm" in r["Kernel_Name"]]
     blocks = [json.loads(x)["block"] for x in open(log) if x.startswith('{"block"')]
-    if sum(b[3] for b in blocks) != len(ks):
-        raise SystemExit(f"{len(ks)} traced row-norm dispatches, {sum(b[3] for b in blocks)} announced")
+    blocks = [b if len(b) == 5 else ["rms"] + b for b in blocks]  # logs without the op are RMSNorm
+    if sum(b[4] for b in blocks) != len(ks):
+        raise SystemExit(f"{len(ks)} traced row-norm dispatches, {sum(b[4] for b in blocks)} announced")
     dur = {}
     kname = {}
     i = 0
-    for N, M, case, n in blocks:
+    for op, N, M, case, n in blocks:
         grp = ks[i:i + n]
         i += n
         if n > 1:  # timed groups (single launches are the output checks)
-            dur.setdefault((N, M, case), []).extend(
+            dur.setdefault((op, N, M, case), []).extend(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
-            kname[(N, M, case)] = _short_kernel(grp[0]["Kernel_Name"])
-    print("Small RMSNorm launches: the library against register-row geometries, MI355X (gfx950), one GPU")
+            kname[(op, N, M, case)] = _short_kernel(grp[0]["Kernel_Name"])
+    ops = [o for o in SMALL_REGS_OPS if any(b[0] == o for b in blocks)]
+    arg = "" if ops == ["rms"] else " " + ",".join(ops)
+    print("Small row-norm launches: the library against register-row geometries, MI355X (gfx950), one GPU")
     print("=" * 96)
     print()
     print("Commands (from the repository root, TMPDIR=/tmp; probe.py builds probe_csrc/libmbn_small_regs.so")
     print("from probe_csrc/small_regs.hip on first use):")
     print(f"  rocprofv3 --kernel-trace --output-format csv -d {trace_dir} -o run -- \\")
-    print(f"      python -u probe.py small-regs > {log}")
+    print(f"      python -u probe.py small-regs{arg} > {log}")
     print(f"  python probe.py small-regs-summary {trace_dir} {log}")
     print()
     print("Kernel durations from the trace: median over 8 rounds x 60 launches per case (rounds in")
     print("alternating order, buffer sets rotated through >= 1 GiB); every variant's output within")
-    print("one ulp of the library's. regs<W, R, C>: rownorm_regs_kernel with 64 * W lanes per row,")
-    print("R rows per workgroup, C chunks of 16 bytes per lane, rows held in VGPRs.")
-    for N in sorted({k[0] for k in dur}):
-        for M in sorted({k[1] for k in dur if k[0] == N}):
-            lib = statistics.median(dur[(N, M, "library")])
-            print()
-            print(f"  x[{M}, {N}]: library {kname[(N, M, 'library')]}: {lib:.2f} us")
-            cases = sorted((statistics.median(v), c) for (n_, m_, c), v in dur.items()
-                           if n_ == N and m_ == M and c != "library")
-            for med, c in cases:
-                print(f"    {kname[(N, M, c)][:52]:<52} {med:7.2f} us  {lib / med:6.3f} x library")
+    print("twice the one-ulp tolerance of the library's (the residual sum h bit for bit).")
+    print("rownorm_regs_kernel<mode, W, R, C, true>: 64 * W lanes per row, R rows per workgroup,")
+    print("C chunks of 16 bytes per lane, rows held in VGPRs (mode 0 RMSNorm, 1 residual add +")
+    print("RMSNorm, 2 LayerNorm, 3 L2Norm).")
+    names = {"rms": "RMSNorm", "add": "residual add + RMSNorm", "layer": "LayerNorm", "l2": "L2Norm"}
+    for op in [o for o in SMALL_REGS_OPS if any(k[0] == o for k in dur)]:
+        for N in sorted({k[1] for k in dur if k[0] == op}):
+            for M in sorted({k[2] for k in dur if k[:2] == (op, N)}):
+                lib = statistics.median(dur[(op, N, M, "library")])
+                print()
+                print(f"  {names[op]} x[{M}, {N}]: library {kname[(op, N, M, 'library')]}: {lib:.2f} us")
+                cases = sorted((statistics.median(v), c) for (o_, n_, m_, c), v in dur.items()
+                               if (o_, n_, m_) == (op, N, M) and c != "library")
+                for med, c in cases:
+                    print(f"    {kname[(op, N, M, c)][:52]:<52} {med:7.2f} us  {lib / med:6.3f} x library")
+
+
+def _small_regs_table(path: str) -> dict:
+    """{(op name, N, M): (library us, library kernel, {variant kernel: us})}
+    from a small-regs-summary text."""
+    out, cur = {}, None
+    for line in open(path):
+        m = re.match(r"\s+(.+) x\[(\d+), (\d+)\]: library (.*): ([\d.]+) us", line)
+        if m:
+            cur = (m.group(1), int(m.group(3)), int(m.group(2)))
+            out[cur] = (float(m.group(5)), m.group(4), {})
+            continue
+        m = re.match(r"\s+(rownorm_regs_kernel<[^>]*>)\s+([\d.]+) us", line)
+        if m and cur:
+            out[cur][2][m.group(1)] = float(m.group(2))
+    return out
+
+
+def small_regs_compare(before: str, after: str) -> None:
+    """Per op, width and row count: the library's kernel time in two
+    small-regs-summary texts (before and after a change of the launch tables)
+    and the best register-row geometry of the second."""
+    import math
+
+    b, a = _small_regs_table(before), _small_regs_table(after)
+    print(f"  {'op':<24} {'N':>6} {'M':>5}  {'before_us':>9} {'after_us':>8} {'speedup':>7}  "
+          f"{'best_variant_us':>15}  after: kernel")
+    ratios = []
+    for k in sorted(a, key=lambda k: (k[0], k[1], k[2])):
+        if k not in b:
+            continue
+        t0, t1 = b[k][0], a[k][0]
+        best = min(a[k][2].values()) if a[k][2] else float("nan")
+        ratios.append(t0 / t1)
+        print(f"  {k[0]:<24} {k[1]:>6} {k[2]:>5}  {t0:>9.2f} {t1:>8.2f} {t0 / t1:>7.3f}  {best:>15.2f}  "
+              f"{a[k][1][:48]}")
+    if ratios:
+        print(f"  geometric mean speedup over {len(ratios)} launches: "
+              f"{math.exp(sum(map(math.log, ratios)) / len(ratios)):.3f}")
 
 
 QK_ANGLE_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_qk_angle.so")
@@ -2673,10 +2752,12 @@ if __name__ == "__main__":
         wide_rows()
     elif len(sys.argv) == 3 and sys.argv[1] == "wide-rows-summary":
         wide_rows_summary(sys.argv[2])
-    elif len(sys.argv) == 2 and sys.argv[1] == "small-regs":
-        small_regs()
+    elif len(sys.argv) in (2, 3) and sys.argv[1] == "small-regs":
+        small_regs(*sys.argv[2:])
     elif len(sys.argv) == 4 and sys.argv[1] == "small-regs-summary":
         small_regs_summary(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 4 and sys.argv[1] == "small-regs-compare":
+        small_regs_compare(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 2 and sys.argv[1] == "qk-angles":
         qk_angles()
     elif len(sys.argv) == 3 and sys.argv[1] == "qk-angles-summary":

@@ -276,3 +276,46 @@ def test_qk_angles_summary(tmp_path, capsys):
     out = capsys.readouterr().out
     assert "library qk_norm_rope_fwd" in out and "3.76" in out
     assert "2: no angle work" in out and "3.60" in out
+
+
+def test_small_regs_summary(tmp_path, capsys):
+    """Blocks of launches announced in the log are matched to the traced row-norm
+    kernels in order; output checks (single launches) are skipped."""
+    import csv
+    import json
+
+    d = tmp_path / "t"
+    d.mkdir()
+    blocks = [["layer", 4096, 512, "library", 1], ["layer", 4096, 512, 10, 1],
+              ["layer", 4096, 512, "library", 3], ["layer", 4096, 512, 10, 3]]
+    names = {"library": "void mbn::(anonymous namespace)::rownorm_kernel<(mbn::Norm)2, mbn::Bf16, 4, 1, 1, 2, true, "
+                        "false>(mbn::RowNormArgs)",
+             10: "void mbn::(anonymous namespace)::rownorm_regs_kernel<(mbn::Norm)2, mbn::Bf16, 4, 1, 2, true>"
+                 "(mbn::RowNormArgs)"}
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for op, N, M, case, n in blocks:
+            for _ in range(n):
+                w.writerow({"Kernel_Name": names[case], "Start_Timestamp": t,
+                            "End_Timestamp": t + (4000 if case == "library" else 3600)})
+                t += 10000
+    log = tmp_path / "small.log"
+    log.write_text("\n".join(json.dumps({"block": b}) for b in blocks) + "\n")
+    probe.small_regs_summary(str(d), str(log))
+    out = capsys.readouterr().out
+    assert "small-regs layer" in out and "LayerNorm x[512, 4096]" in out
+    assert "4.00 us" in out and "1.111 x library" in out
+
+
+def test_small_regs_compare(tmp_path, capsys):
+    text = ("  LayerNorm x[512, 4096]: library rownorm_kernel<2, 4, 1, 1, 2, true, false>: 4.66 us\n"
+            "    rownorm_regs_kernel<2, 1, 1, 8, true>                   4.36 us   1.069 x library\n")
+    after = ("  LayerNorm x[512, 4096]: library rownorm_regs_kernel<2, 1, 1, 8, true>: 4.36 us\n"
+             "    rownorm_regs_kernel<2, 1, 1, 8, true>                   4.30 us   1.014 x library\n")
+    (tmp_path / "b.txt").write_text(text)
+    (tmp_path / "a.txt").write_text(after)
+    probe.small_regs_compare(str(tmp_path / "b.txt"), str(tmp_path / "a.txt"))
+    out = capsys.readouterr().out
+    assert "4.66" in out and "4.36" in out and f"{4.66 / 4.36:.3f}" in out and "4.30" in out
