@@ -1681,7 +1681,6 @@ def small_regs_compare(before: str, after: str) -> None:
 QK_ANGLE_LIB_PATH = os.path.join(PROBE_CSRC, "libmbn_qk_angle.so")
 QK_ANGLE_MODES = {0: "library path: wave 0 forms the angles, LDS table, barrier",
                   1: "every wave forms the angles, ds_bpermute, no barrier",
-                  2: "no angle work (timing only, outputs not the operator's)",
                   3: "as 1, rotation products in fp32"}
 
 

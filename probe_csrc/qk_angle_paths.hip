@@ -1,13 +1,11 @@
 // Angle paths of the fused QK-norm + RoPE kernel, for the measurement tools
 // (not part of the library): the library's kernel body for one head row per
-// wave (few tokens) with the token's sine / cosine obtained in one of four
-// ways, to time what the angle work adds to a short launch:
+// wave (few tokens) with the token's sine / cosine obtained in one of three
+// ways, each giving the operator's outputs:
 //   MODE 0: the library's path: wave 0 forms the 64 angles (one per lane)
 //           and shares them through LDS behind a workgroup barrier;
 //   MODE 1: every wave forms the 64 angles itself and each lane fetches its 8
 //           with ds_bpermute (no LDS table, no barrier);
-//   MODE 2: no angle work at all (cos 1, sin 0): the outputs are NOT the
-//           operator's; timing only, never compared;
 //   MODE 3: MODE 1 with the rotation products in fp32 instead of fp64.
 #include <hip/hip_ext.h>
 
@@ -55,12 +53,6 @@ qkx_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_w, const u
       const double2 a = cs[i0 + e];
       hc[e] = a.x;
       hs[e] = sgn * a.y;
-    }
-  } else if constexpr (MODE == 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hc[e] = 1.0;
-      hs[e] = 0.0;
     }
   } else {
     const double inv_freq = rope_inv_freq(inv_pow, lane);
@@ -128,8 +120,8 @@ extern "C" __attribute__((visibility("default"))) int mbn_qk_angle_path(void* qk
   const int waves = (n_heads + 3) / 4;
   const int64_t row_stride = (int64_t)(hq + 2 * hk) * 128;
   const InvFreqPowers ip = rope_inv_freq_powers(1e6f, 128);
-  auto k = mode == 0 ? qkx_kernel<Bf16, 0> : mode == 1 ? qkx_kernel<Bf16, 1> : mode == 2 ? qkx_kernel<Bf16, 2>
-                                                                                          : qkx_kernel<Bf16, 3>;
+  if (mode != 0 && mode != 1 && mode != 3) return 1;
+  auto k = mode == 0 ? qkx_kernel<Bf16, 0> : mode == 1 ? qkx_kernel<Bf16, 1> : qkx_kernel<Bf16, 3>;
   hipExtLaunchKernelGGL(k, dim3((unsigned)T), dim3(64 * waves), 0u, (hipStream_t)stream, (hipEvent_t)e0,
                         (hipEvent_t)e1, 0u, static_cast<uint16_t*>(qkv), static_cast<const uint16_t*>(q_w),
                         static_cast<const uint16_t*>(k_w), pos, hq, n_heads, row_stride, 1e-6f, ip);
