@@ -872,18 +872,23 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_ROWS(Norm::kRms, 2048, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 2048
     MBN_CFG_ROWS(Norm::kRms, 8192, 1, 4, 2, 2, 4, 0),  // N <= 1024, M <= 8192
     MBN_CFG(Norm::kRms, 1, 4, 1, 2, 0, 16),  // N <= 1024:  4 x 64 threads
-    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 2048, 1, 1, 4, 0, 0),  // N == 2048, M <= 2048: 64 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 1024, 1, 1, 4, 0, 0),  // N == 2048, M <= 1024: 64 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 1536, 2, 1, 2, 0, 0),  // N == 2048, M <= 1536: 128 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 2048, 1, 4, 4, 0, 0),  // N == 2048, M <= 2048: 4 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 256, 2, 2, 1, 2, 1, 0),  // N <= 2048, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 2048, 1, 4, 1, 4, 4, 0),  // N <= 2048, M <= 2048
     MBN_CFG_ROWS(Norm::kRms, 4096, 1, 4, 2, 4, 2, 0),  // N <= 2048, M <= 4096
     MBN_CFG(Norm::kRms, 2, 2, 2, 2, 4, 8),   // N <= 2048:  2 x 128 threads x 2 rows, 4 WGs/CU
     MBN_CFG_ROWS_EXACT_R(Norm::kRms, 512, 4, 1, 2, 0, 0),  // N == 4096, M <= 512: 256 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kRms, 2048, 1, 1, 8, 0, 0),  // N == 4096, M <= 2048: 64 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 4096, 1, 2, 8, 0, 0),  // N == 4096, M <= 4096: 2 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 2, 0, 0),  // N <= 4096, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 2, 1, 4, 3, 0),  // N <= 4096, M <= 1024
     MBN_CFG_ROWS(Norm::kRms, 4096, 2, 1, 2, 4, 0, 0),  // N <= 4096, M <= 4096
     MBN_CFG_W(Norm::kRms, 4, 1, 2, 2, 4, 8),   // N <= 4096:  256 threads x 2 rows, 4 WGs/CU
     MBN_CFG_ROWS_EXACT_R(Norm::kRms, 256, 4, 1, 4, 0, 0),  // N == 8192, M <= 256: 256 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 512, 4, 2, 4, 0, 0),  // N == 8192, M <= 512: 2 x 256 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 768, 2, 1, 8, 0, 0),  // N == 8192, M <= 768: 128 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kRms, 1024, 4, 2, 4, 0, 0),  // N == 8192, M <= 1024: 2 x 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 512, 4, 1, 1, 4, 0, 0),  // N <= 8192, M <= 512
     MBN_CFG_ROWS(Norm::kRms, 1024, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 1024
@@ -894,6 +899,7 @@ const RowNormCfg kRmsTable[] = {
     MBN_CFG_LW(Norm::kRms, 8, 1, 1, 2, 0, 0),  // N <= 8192:  512 threads, weight after the reduction
     MBN_CFG_ROWS_EXACT_R(Norm::kRms, 256, 8, 1, 4, 0, 0),  // N == 16384, M <= 256: 512 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kRms, 512, 8, 2, 4, 0, 0),  // N == 16384, M <= 512: 2 x 512 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kRms, 768, 4, 1, 8, 0, 0),  // N == 16384, M <= 768: 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kRms, 256, 16, 1, 1, 2, 0, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kRms, 1536, 4, 1, 2, 8, 0, 0),  // N <= 16384, M <= 1536
     MBN_CFG_ROWS_EXACT_W(Norm::kRms, 6144, 4, 1, 1, 8, 2, 8),  // N == 16384, M <= 6144
@@ -952,6 +958,7 @@ const RowNormCfg kLayerTable[] = {
     MBN_CFG(Norm::kLayer, 2, 2, 2, 2, 4, 8),   // N <= 2048
     MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 1024, 1, 1, 8, 0, 0),  // N == 4096, M <= 1024: 64 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 2048, 2, 2, 4, 0, 0),  // N == 4096, M <= 2048: 2 x 128 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 3072, 1, 2, 8, 0, 0),  // N == 4096, M <= 3072: 2 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kLayer, 512, 4, 1, 1, 2, 4, 2),  // N <= 4096, M <= 512
     MBN_CFG_ROWS(Norm::kLayer, 1024, 4, 2, 1, 2, 2, 0),  // N <= 4096, M <= 1024
     MBN_CFG_ROWS(Norm::kLayer, 2048, 1, 4, 1, 8, 2, 0),  // N <= 4096, M <= 2048
@@ -1103,7 +1110,19 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
   args.inv_n = 1.0f / (float)N;
   args.xcd_group = 0;
 
-  if (path != RowNormPath::kOneShot) {
+  const RowNormCfg* cfg = nullptr;
+  switch (mode) {
+    case Norm::kRms: cfg = pick(kRmsTable, nchunk, args.M); break;
+    case Norm::kAddRms: cfg = pick(kAddRmsTable, nchunk, args.M); break;
+    case Norm::kLayer: cfg = pick(kLayerTable, nchunk, args.M); break;
+    case Norm::kL2: cfg = pick(kL2Table, nchunk, args.M); break;
+  }
+  // An exact-width register-row window serves its launches ahead of the
+  // persistent table: those windows were chosen against whatever served the
+  // launch before, the persistent kernel included.
+  const bool regs_window = cfg && cfg->regs && cfg->max_rows > 0;
+
+  if (path == RowNormPath::kPersistent || (path == RowNormPath::kAuto && !regs_window)) {
     const bool forced = path == RowNormPath::kPersistent;
     const PersistentCfg* pc = nullptr;
     switch (mode) {
@@ -1123,13 +1142,6 @@ hipError_t launch_rownorm(Norm mode, Storage dtype, RowNormArgs args, hipStream_
     }
   }
 
-  const RowNormCfg* cfg = nullptr;
-  switch (mode) {
-    case Norm::kRms: cfg = pick(kRmsTable, nchunk, args.M); break;
-    case Norm::kAddRms: cfg = pick(kAddRmsTable, nchunk, args.M); break;
-    case Norm::kLayer: cfg = pick(kLayerTable, nchunk, args.M); break;
-    case Norm::kL2: cfg = pick(kL2Table, nchunk, args.M); break;
-  }
   if (!cfg) return hipErrorInvalidValue;
   if (cfg->wpr > 1 && nchunk < 64 * cfg->wpr) return hipErrorInvalidValue;  // table invariant
   const int rows_per_wg = cfg->rows * cfg->rpl;

@@ -1493,9 +1493,10 @@ def small_regs_geometries(h):
 SMALL_REGS_OPS = {"rms": (0, 1e-6), "add": (1, 1e-6), "layer": (2, 1e-5), "l2": (3, 1e-12)}
 
 
-def small_regs(ops: str = "rms", rounds: int = 8, launches: int = 60) -> None:
-    """Small row-norm launches (N = 2048 ... 16384, M = 256 ... 2048) through
-    the library and through the register-row geometries of
+def small_regs(ops: str = "rms", width: str = "", rows: str = "", rounds: int = 8, launches: int = 60) -> None:
+    """Small row-norm launches (N = 2048 ... 16384, M = 256 ... 2048, or the
+    one width `width` at the comma-separated row counts `rows`) through the
+    library and through the register-row geometries of
     probe_csrc/small_regs.hip of the same width, on the same data, buffer sets
     rotated through >= 1 GiB, for each op of `ops` (comma-separated: rms, add,
     layer, l2). Meant to run under rocprofv3 --kernel-trace: every group of
@@ -1516,20 +1517,23 @@ def small_regs(ops: str = "rms", rounds: int = 8, launches: int = 60) -> None:
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    timer = HipTimingEvents(stream)
+    L = mbn.lib()
     g = torch.Generator(device=dev).manual_seed(17)
-    ev = (timer.new(), timer.new())
 
     def block(op, N, M, case, n):
         print(json.dumps({"block": [op, N, M, case, n]}), flush=True)
 
+    widths = (int(width),) if width else SMALL_REGS_WIDTHS
+    row_counts = tuple(int(m) for m in rows.split(",")) if rows else SMALL_REGS_ROWS
+    print(json.dumps({"small_regs": {"ops": ops, "width": width, "rows": rows, "rounds": rounds,
+                                     "launches": launches}}), flush=True)
     for op in ops.split(","):
         mode, eps = SMALL_REGS_OPS[op]
-        for N in SMALL_REGS_WIDTHS:
+        for N in widths:
             vs = [v for v, (wpr, _, maxc) in geo.items() if 64 * wpr * maxc * 8 == N]
             w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
             b = (torch.rand(N, device=dev, generator=g) - 0.5).to(torch.bfloat16)
-            for M in SMALL_REGS_ROWS:
+            for M in row_counts:
                 nrot = max(2, -(-(1 << 30) // ((4 if op == "add" else 2) * M * N * 2)))
                 xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
                 rs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)] \
@@ -1541,18 +1545,24 @@ def small_regs(ops: str = "rms", rounds: int = 8, launches: int = 60) -> None:
                     return None if t is None else t.data_ptr()
 
                 def run(case, i):
+                    # both through ctypes straight to C, so that the host paces
+                    # the library's launches and the variants' alike
                     if case == "library":
+                        x_, y_ = xs[i].data_ptr(), ys[i].data_ptr()
                         if op == "rms":
-                            mbn.rmsnorm_fwd(xs[i], w, ys[i], eps=eps)
+                            st = L.rmsnorm_fwd(x_, w.data_ptr(), y_, M, N, eps, sp)
                         elif op == "add":
-                            mbn.add_rmsnorm_fwd(xs[i], rs[i], w, hs[i], ys[i], eps=eps)
+                            st = L.add_rmsnorm_fwd(x_, rs[i].data_ptr(), w.data_ptr(), hs[i].data_ptr(), y_, M, N,
+                                                   eps, sp)
                         elif op == "layer":
-                            mbn.layernorm_fwd(xs[i], w, b, ys[i], eps=eps)
+                            st = L.layernorm_fwd(x_, w.data_ptr(), b.data_ptr(), y_, M, N, eps, sp)
                         else:
-                            mbn.l2norm_fwd(xs[i], ys[i], eps=eps)
+                            st = L.l2norm_fwd(x_, y_, M, N, eps, sp)
+                        if st != 0:
+                            raise RuntimeError(f"small-regs {op} library: {mbn.mbn_strerror(st)}")
                     elif h.mbn_small_regs(mode, xs[i].data_ptr(), ptr(rs[i]), None if op == "l2" else w.data_ptr(),
                                           b.data_ptr() if op == "layer" else None, ptr(hs[i]), ys[i].data_ptr(),
-                                          M, N, eps, case, sp, *ev) != 0:
+                                          M, N, eps, case, sp, None, None) != 0:
                         raise RuntimeError(f"small-regs {op} variant {case}: launch failed")
 
                 block(op, N, M, "library", 1)
@@ -1582,7 +1592,6 @@ def small_regs(ops: str = "rms", rounds: int = 8, launches: int = 60) -> None:
                         torch.cuda.synchronize()
                 del xs, rs, ys, hs
                 torch.cuda.empty_cache()
-    timer.close()
 
 
 def small_regs_summary(trace_dir: str, log: str) -> None:
@@ -1610,7 +1619,11 @@ def small_regs_summary(trace_dir: str, log: str) -> None:
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
             kname[(op, N, M, case)] = _short_kernel(grp[0]["Kernel_Name"])
     ops = [o for o in SMALL_REGS_OPS if any(b[0] == o for b in blocks)]
-    arg = "" if ops == ["rms"] else " " + ",".join(ops)
+    args = [json.loads(x)["small_regs"] for x in open(log) if x.startswith('{"small_regs"')]
+    args = args[0] if args else {"width": "", "rows": "", "rounds": 8, "launches": 60}
+    arg = "" if ops == ["rms"] and not args["width"] else " " + ",".join(ops)
+    if args["width"]:
+        arg += f" {args['width']} {args['rows']}"
     print("Small row-norm launches: the library against register-row geometries, MI355X (gfx950), one GPU")
     print("=" * 96)
     print()
@@ -1620,7 +1633,8 @@ def small_regs_summary(trace_dir: str, log: str) -> None:
     print(f"      python -u probe.py small-regs{arg} > {log}")
     print(f"  python probe.py small-regs-summary {trace_dir} {log}")
     print()
-    print("Kernel durations from the trace: median over 8 rounds x 60 launches per case (rounds in")
+    print(f"Kernel durations from the trace: median over {args['rounds']} rounds x {args['launches']} "
+          "launches per case (rounds in")
     print("alternating order, buffer sets rotated through >= 1 GiB); every variant's output within")
     print("twice the one-ulp tolerance of the library's (the residual sum h bit for bit).")
     print("rownorm_regs_kernel<mode, W, R, C, true>: 64 * W lanes per row, R rows per workgroup,")
@@ -1644,9 +1658,9 @@ def _small_regs_table(path: str) -> dict:
     from a small-regs-summary text."""
     out, cur = {}, None
     for line in open(path):
-        m = re.match(r"\s+(.+) x\[(\d+), (\d+)\]: library (.*): ([\d.]+) us", line)
-        if m:
-            cur = (m.group(1), int(m.group(3)), int(m.group(2)))
+        m = re.match(r"\s+(?:(\S.*?) )?x\[(\d+), (\d+)\]: library (.*): ([\d.]+) us", line)
+        if m:  # summaries of RMSNorm-only runs name no op
+            cur = (m.group(1) or "RMSNorm", int(m.group(3)), int(m.group(2)))
             out[cur] = (float(m.group(5)), m.group(4), {})
             continue
         m = re.match(r"\s+(rownorm_regs_kernel<[^>]*>)\s+([\d.]+) us", line)
@@ -2751,7 +2765,7 @@ if __name__ == "__main__":
         wide_rows()
     elif len(sys.argv) == 3 and sys.argv[1] == "wide-rows-summary":
         wide_rows_summary(sys.argv[2])
-    elif len(sys.argv) in (2, 3) and sys.argv[1] == "small-regs":
+    elif len(sys.argv) in (2, 3, 5) and sys.argv[1] == "small-regs":
         small_regs(*sys.argv[2:])
     elif len(sys.argv) == 4 and sys.argv[1] == "small-regs-summary":
         small_regs_summary(sys.argv[2], sys.argv[3])

@@ -2,8 +2,8 @@
 // tools (not part of the library): the library's rownorm_regs_kernel (RMSNorm,
 // residual add + RMSNorm, LayerNorm or L2Norm) at widths 2048 ... 16384 with
 // the lanes per row, rows per workgroup and chunks per lane chosen per
-// variant, launched with the kernel's own start and end recorded in two events
-// (hipExtLaunchKernel).
+// variant, launched plainly or, given two events, with the kernel's own start
+// and end recorded in them (hipExtLaunchKernel).
 #include <hip/hip_ext.h>
 
 #include "../memory_bound_normalization_amd/csrc/rownorm.hip"
@@ -19,8 +19,12 @@ int small_launch(const RowNormArgs& args, hipStream_t s, hipEvent_t e0, hipEvent
   a.inv_n = 1.0f / (float)N;
   a.xcd_group = 0;
   const int64_t blocks = (a.M + ROWS - 1) / ROWS;
-  hipExtLaunchKernelGGL((rownorm_regs_kernel<MODE, Bf16, WPR, ROWS, MAXC, true>), dim3((unsigned)blocks),
-                        dim3(64 * WPR * ROWS), 0u, s, e0, e1, 0u, a);
+  if (e0)
+    hipExtLaunchKernelGGL((rownorm_regs_kernel<MODE, Bf16, WPR, ROWS, MAXC, true>), dim3((unsigned)blocks),
+                          dim3(64 * WPR * ROWS), 0u, s, e0, e1, 0u, a);
+  else
+    hipLaunchKernelGGL((rownorm_regs_kernel<MODE, Bf16, WPR, ROWS, MAXC, true>), dim3((unsigned)blocks),
+                       dim3(64 * WPR * ROWS), 0u, s, a);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
@@ -65,13 +69,13 @@ __attribute__((visibility("default"))) int mbn_small_regs_geometry(int v, int* o
 
 // Row norm `mode` (0 RMSNorm, 1 residual add + RMSNorm, 2 LayerNorm, 3 L2Norm)
 // of bf16 rows [M, N] with variant v (N must be its width); r and h only for
-// mode 1, w for all but mode 3, b for mode 2 (else null). 0 = ok, 1 = invalid
-// arguments, 3 = launch failed.
+// mode 1, w for all but mode 3, b for mode 2 (else null); e0 and e1 both
+// events or both null. 0 = ok, 1 = invalid arguments, 3 = launch failed.
 __attribute__((visibility("default"))) int mbn_small_regs(int mode, const void* x, const void* r, const void* w,
                                                           const void* b, void* h, void* y, int64_t M, int64_t N,
                                                           float eps, int v, void* stream, void* e0, void* e1) {
   if (mode < 0 || mode > 3 || !x || !y || M <= 0 || M > (1 << 20) || N <= 0 || N % 8 != 0 || v < 0 ||
-      v >= mbn_small_regs_count() || !e0 || !e1)
+      v >= mbn_small_regs_count() || !e0 != !e1)
     return 1;
   if ((mode != 3 && !w) || (mode == 2 && !b) || (mode == 1 && (!r || !h))) return 1;
   mbn::RowNormArgs a{};

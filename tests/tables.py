@@ -95,3 +95,23 @@ def persistent_windows(op, nchunk):
     rows of `nchunk` 16-byte chunks."""
     return [(grid, lo_r, hi_r) for lo, hi, wpr, rpl, maxc, grid, lo_r, hi_r in PERSISTENT[PERSISTENT_TABLE[op]]
             if lo <= nchunk <= hi]
+
+
+def pick_entry(tname, nchunk, M):
+    """The one-shot table entry the launcher picks for rows of `nchunk`
+    16-byte chunks and M rows (the first that serves both), or None."""
+    for e in TABLES[tname]:
+        if (nchunk == e.top if e.exact else nchunk <= e.top) and (e.max_rows == 0 or M <= e.max_rows):
+            return e
+    return None
+
+
+def serves_persistent(tname, op, nchunk, M):
+    """Whether the launcher runs the persistent kernel for this launch: a
+    persistent entry covers it and no exact-width register-row window (which
+    takes precedence) does."""
+    e = pick_entry(tname, nchunk, M)
+    if e is not None and e.regs and e.max_rows:
+        return False
+    return op in PERSISTENT_TABLE and any(lo <= M <= hi for _, lo, hi in persistent_windows(op, nchunk))
+

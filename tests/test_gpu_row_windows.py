@@ -8,7 +8,7 @@ the top row count of its window where that launch stays within 16M elements; aga
 
 import pytest
 
-from tables import TABLES, persistent_windows
+from tables import TABLES, serves_persistent
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -54,10 +54,11 @@ def test_every_window_reached():
     assert len(CASES) >= 2 * 30
 
 
+_TABLE_OF = {op: t for t, op in OPS.items()}
+
+
 def _persistent_here(op, M, N):
-    if op == "add":
-        return False
-    return any(lo <= M <= hi for _, lo, hi in persistent_windows(op, N // 8))
+    return serves_persistent(_TABLE_OF[op], op, N // 8, M)
 
 
 @pytest.mark.parametrize("op,M,N", CASES)

@@ -119,3 +119,19 @@ def test_persistent_windows_do_not_overlap(name):
         windows.sort()
         for (_, a_max), (b_min, _) in zip(windows, windows[1:]):
             assert a_max < b_min
+
+
+def test_register_windows_precede_the_persistent_table():
+    """An exact-width register-row window serves its launches even where a
+    persistent entry covers the same width and row count; past the window the
+    persistent kernel serves them again."""
+    from tables import pick_entry, serves_persistent
+
+    assert pick_entry("kRmsTable", 512, 3000).regs and not serves_persistent("kRmsTable", "rms", 512, 3000)
+    assert serves_persistent("kRmsTable", "rms", 512, 5000)
+    assert pick_entry("kLayerTable", 512, 1000).regs and not serves_persistent("kLayerTable", "layer", 512, 1000)
+    assert serves_persistent("kLayerTable", "layer", 512, 4000)
+    # a ragged width of the same band has no exact window: persistent
+    assert serves_persistent("kRmsTable", "rms", 500, 3000)
+    # the residual add has no persistent kernel
+    assert not serves_persistent("kAddRmsTable", "add", 512, 3000)

@@ -319,3 +319,27 @@ def test_small_regs_compare(tmp_path, capsys):
     probe.small_regs_compare(str(tmp_path / "b.txt"), str(tmp_path / "a.txt"))
     out = capsys.readouterr().out
     assert "4.66" in out and "4.36" in out and f"{4.66 / 4.36:.3f}" in out and "4.30" in out
+
+
+def test_small_regs_summary_names_width_and_rows(tmp_path, capsys):
+    """A log that starts with the run's arguments gives the command back with its
+    width, row counts, rounds and launches."""
+    import csv
+    import json
+
+    d = tmp_path / "t"
+    d.mkdir()
+    blocks = [["rms", 4096, 2560, "library", 2], ["rms", 4096, 2560, 3, 2]]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i in range(4):
+            w.writerow({"Kernel_Name": "rownorm_regs_kernel<(mbn::Norm)0, mbn::Bf16, 1, 2, 8, true>",
+                        "Start_Timestamp": 10000 * i, "End_Timestamp": 10000 * i + 8000})
+    log = tmp_path / "small.log"
+    head = {"small_regs": {"ops": "rms", "width": "4096", "rows": "2560", "rounds": 6, "launches": 40}}
+    log.write_text(json.dumps(head) + "\n" + "\n".join(json.dumps({"block": b}) for b in blocks) + "\n")
+    probe.small_regs_summary(str(d), str(log))
+    out = capsys.readouterr().out
+    assert "probe.py small-regs rms 4096 2560 >" in out
+    assert "6 rounds x 40 launches" in out and "RMSNorm x[2560, 4096]" in out and "8.00 us" in out
