@@ -772,7 +772,11 @@ constexpr RowNormKernel chunk_wait_kernel() {
 #define MBN_CFG_ROWS(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
   MBN_CFG_(MODE, 64 * (WPR) * (MAXC), false, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP, false)
 // a row window that serves only the width 64 * WPR * MAXC chunks (the band's
-// top width), with per-chunk waits
+// top width); placed after other windows it holds their row counts for that
+// width only, so that a later exact window starts above them
+#define MBN_CFG_ROWS_EXACT(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
+  MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP, false)
+// the same with per-chunk waits
 #define MBN_CFG_ROWS_EXACT_W(MODE, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP) \
   MBN_CFG_(MODE, 64 * (WPR) * (MAXC), true, MAXROWS, WPR, ROWS, RPL, MAXC, CAP, GROUP, true)
 // sub-band: serves the widths from the band's lower edge (or the previous
@@ -919,12 +923,15 @@ const RowNormCfg kAddRmsTable[] = {
     MBN_CFG_ROWS(Norm::kAddRms, 4096, 1, 4, 1, 2, 0, 0),  // N <= 1024, M <= 4096
     MBN_CFG_ROWS(Norm::kAddRms, 32768, 1, 4, 2, 2, 0, 0),  // N <= 1024, M <= 32768
     MBN_CFG(Norm::kAddRms, 1, 4, 1, 2, 4, 16),  // N <= 1024
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 768, 2, 1, 2, 0, 0),  // N == 2048, M <= 768: 128 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1024, 4, 1, 1, 0, 0),  // N == 2048, M <= 1024: 256 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1536, 2, 1, 2, 0, 0),  // N == 2048, M <= 1536: 128 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 2048, 1, 4, 4, 0, 0),  // N == 2048, M <= 2048: 4 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 1024, 2, 2, 1, 2, 0, 0),  // N <= 2048, M <= 1024
     MBN_CFG_ROWS(Norm::kAddRms, 8192, 2, 2, 2, 2, 4, 0),  // N <= 2048, M <= 8192
     MBN_CFG(Norm::kAddRms, 1, 4, 1, 4, 2, 8),   // N <= 2048
-    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1024, 8, 1, 1, 0, 0),  // N == 4096, M <= 1024: 512 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 768, 8, 1, 1, 0, 0),  // N == 4096, M <= 768: 512 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1024, 4, 2, 2, 0, 0),  // N == 4096, M <= 1024: 2 x 256 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1536, 1, 2, 8, 0, 0),  // N == 4096, M <= 1536: 2 x 64 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 256, 4, 1, 1, 2, 4, 0),  // N <= 4096, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 4, 2, 1, 2, 0, 16),  // N <= 4096, M <= 512
@@ -935,6 +942,8 @@ const RowNormCfg kAddRmsTable[] = {
     MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 512, 4, 2, 4, 0, 0),  // N == 8192, M <= 512: 2 x 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 2, 1, 64),  // N <= 8192, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 2, 0, 0),  // N <= 8192, M <= 512
+    MBN_CFG_ROWS_EXACT(Norm::kAddRms, 1024, 2, 1, 1, 8, 0, 0),  // N == 8192, M <= 1024: the next window's kernel
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 1536, 2, 2, 8, 0, 0),  // N == 8192, M <= 1536: 2 x 128 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kAddRms, 2048, 2, 1, 1, 8, 0, 0),  // N <= 8192, M <= 2048
     MBN_CFG_EXACT(Norm::kAddRms, 2, 2, 1, 5, 2, 4),  // N == 5120: 2 x 128 threads
     MBN_CFG(Norm::kAddRms, 8, 1, 1, 2, 2, 8),   // N <= 8192:  512 threads, 2 WGs/CU
@@ -942,6 +951,7 @@ const RowNormCfg kAddRmsTable[] = {
     MBN_CFG_ROWS(Norm::kAddRms, 256, 8, 1, 1, 4, 4, 0),  // N <= 16384, M <= 256
     MBN_CFG_ROWS(Norm::kAddRms, 512, 8, 1, 2, 4, 0, 0),  // N <= 16384, M <= 512
     MBN_CFG_ROWS(Norm::kAddRms, 1024, 16, 1, 4, 2, 0, 0),  // N <= 16384, M <= 1024
+    MBN_CFG_ROWS_EXACT_R(Norm::kAddRms, 2048, 16, 1, 2, 0, 0),  // N == 16384, M <= 2048: 1024 lanes, rows in VGPRs
     MBN_CFG(Norm::kAddRms, 4, 1, 1, 8, 3, 4),   // N <= 16384: 256 threads, 3 WGs/CU
     MBN_CFG_ROWS(Norm::kAddRms, 512, 4, 1, 1, 16, 2, 0),  // N <= 32768, M <= 512
     MBN_CFG(Norm::kAddRms, 16, 1, 1, 4, 2, 2),  // N <= 32768: 1024 threads
@@ -956,6 +966,8 @@ const RowNormCfg kLayerTable[] = {
     MBN_CFG_ROWS(Norm::kLayer, 2048, 2, 2, 1, 2, 0, 0),  // N <= 2048, M <= 2048
     MBN_CFG_ROWS(Norm::kLayer, 4096, 1, 4, 2, 4, 0, 0),  // N <= 2048, M <= 4096
     MBN_CFG(Norm::kLayer, 2, 2, 2, 2, 4, 8),   // N <= 2048
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 256, 4, 1, 2, 0, 0),  // N == 4096, M <= 256: 256 lanes, rows in VGPRs
+    MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 384, 4, 2, 2, 0, 0),  // N == 4096, M <= 384: 2 x 256 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 1024, 1, 1, 8, 0, 0),  // N == 4096, M <= 1024: 64 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 2048, 2, 2, 4, 0, 0),  // N == 4096, M <= 2048: 2 x 128 lanes, rows in VGPRs
     MBN_CFG_ROWS_EXACT_R(Norm::kLayer, 3072, 1, 2, 8, 0, 0),  // N == 4096, M <= 3072: 2 x 64 lanes, rows in VGPRs
@@ -996,9 +1008,14 @@ const RowNormCfg kL2Table[] = {
     MBN_CFG_ROWS(Norm::kL2, 768, 4, 1, 1, 2, 0, 0),  // N <= 4096, M <= 768
     MBN_CFG(Norm::kL2, 2, 2, 1, 4, 4, 0),   // N <= 4096:  2 x 128 threads
     MBN_CFG_ROWS(Norm::kL2, 1024, 8, 1, 1, 2, 0, 0),  // N <= 8192, M <= 1024
+    MBN_CFG_ROWS_EXACT_R(Norm::kL2, 1536, 2, 2, 8, 0, 0),  // N == 8192, M <= 1536: 2 x 128 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kL2, 2048, 8, 1, 4, 2, 0, 0),  // N <= 8192, M <= 2048
     MBN_CFG(Norm::kL2, 8, 1, 1, 2, 0, 0),   // N <= 8192:  512 threads
+    MBN_CFG_ROWS_EXACT(Norm::kL2, 256, 8, 1, 1, 4, 2, 0),  // N == 16384, M <= 256: the M <= 512 window's kernel
+    MBN_CFG_ROWS_EXACT_R(Norm::kL2, 384, 8, 2, 4, 0, 0),  // N == 16384, M <= 384: 2 x 512 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kL2, 512, 8, 1, 1, 4, 2, 0),  // N <= 16384, M <= 512
+    MBN_CFG_ROWS_EXACT(Norm::kL2, 1024, 2, 2, 1, 16, 2, 0),  // N == 16384, M <= 1024: the M <= 2048 window's kernel
+    MBN_CFG_ROWS_EXACT_R(Norm::kL2, 2048, 4, 1, 8, 0, 0),  // N == 16384, M <= 2048: 256 lanes, rows in VGPRs
     MBN_CFG_ROWS(Norm::kL2, 2048, 2, 2, 1, 16, 2, 0),  // N <= 16384, M <= 2048
     MBN_CFG_UPTO(Norm::kL2, 12288, 12, 1, 1, 2, 3, 0),  // 8192 < N <= 12288: 768 threads
     MBN_CFG(Norm::kL2, 4, 1, 1, 8, 3, 4),   // N <= 16384: 256 threads, 3 WGs/CU

@@ -1813,6 +1813,128 @@ def qk_angles_summary(trace_dir: str) -> None:
         line(f"{m}: {QK_ANGLE_MODES[m]}", d)
 
 
+LAUNCH_MODE_SHAPES = [(2560, 4096), (768, 16384), (4096, 4096), (16384, 16384)]
+LAUNCH_MODES = {"plain": "rmsnorm_fwd",
+                "ev_nofence": "rmsnorm_fwd_timed, events created with hipEventDisableSystemFence",
+                "ev_default": "rmsnorm_fwd_timed, events created with default flags"}
+
+
+def launch_modes(rounds: int = 6, launches: int = 40) -> None:
+    """rmsnorm_fwd launched plainly and through rmsnorm_fwd_timed (two kinds of
+    events), in rounds of back-to-back launches per mode (alternating order),
+    for each shape of LAUNCH_MODE_SHAPES (10 launches per round at 16384 x
+    16384), buffer sets rotated through >= 1 GiB, all through ctypes. Prints a
+    JSON line {"block": [M, N, mode, launches]} before each group, so that
+    launch-modes-summary can attribute a kernel trace, and per shape the
+    median over rounds of (region events around the group) / launches."""
+    sys.path.insert(0, ROOT)
+    import json
+
+    import torch
+
+    import memory_bound_normalization_amd as mbn
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    L = mbn.lib()
+    timer = HipTimingEvents(stream)
+    hip = timer.hip
+    g = torch.Generator(device=dev).manual_seed(3)
+    for M, N in LAUNCH_MODE_SHAPES:
+        nrot = max(2, -(-(1 << 30) // (2 * M * N * 2)))
+        xs = [torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
+        ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+        w = (torch.rand(N, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+        n = launches if M * N < (1 << 26) else 10
+        nofence = [timer.new() for _ in range(2 * n)]
+        default = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreateWithFlags(ctypes.byref(e), 0) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            default.append(e)
+        r0, r1 = timer.new(), timer.new()
+        res = {}
+        modes = list(LAUNCH_MODES)
+        for rnd in range(rounds):
+            for mode in (modes if rnd % 2 == 0 else modes[::-1]):
+                print(json.dumps({"block": [M, N, mode, n]}), flush=True)
+                timer.record(r0)
+                for i in range(n):
+                    j = (i * 7) % nrot
+                    if mode == "plain":
+                        st = L.rmsnorm_fwd(xs[j].data_ptr(), w.data_ptr(), ys[j].data_ptr(), M, N, 1e-6, sp)
+                    else:
+                        ev = nofence if mode == "ev_nofence" else default
+                        st = L.rmsnorm_fwd_timed(xs[j].data_ptr(), w.data_ptr(), ys[j].data_ptr(), M, N, 1e-6, sp,
+                                                 ev[2 * i], ev[2 * i + 1])
+                    if st != 0:
+                        raise RuntimeError(f"launch-modes {mode}: {mbn.mbn_strerror(st)}")
+                timer.record(r1)
+                torch.cuda.synchronize()
+                res.setdefault(mode, []).append(timer.elapsed_ms(r0, r1) * 1e3 / n)
+        print(json.dumps({"region": [M, N, {k: sorted(v)[len(v) // 2] for k, v in res.items()}]}), flush=True)
+        for e in default:
+            hip.hipEventDestroy(e)
+        del xs, ys
+        torch.cuda.empty_cache()
+    timer.close()
+
+
+def launch_modes_summary(trace_dir: str, log: str, plain_log: str) -> None:
+    """Per shape and launch mode: the median kernel duration and the median
+    idle time between consecutive kernels of a group from the kernel trace
+    (trace_dir) of `python -u probe.py launch-modes > log`, the region time
+    per launch of that run, and of a run without the profiler (plain_log)."""
+    import json
+    import statistics
+
+    rows = sorted(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    ks = [r for r in rows if "rownorm" in r["Kernel_Name"]]
+    recs = [json.loads(x) for x in open(log) if x.startswith("{")]
+    blocks = [r["block"] for r in recs if "block" in r]
+    if sum(b[3] for b in blocks) != len(ks):
+        raise SystemExit(f"{len(ks)} traced row-norm dispatches, {sum(b[3] for b in blocks)} announced")
+    dur, gap, i = {}, {}, 0
+    for M, N, mode, n in blocks:
+        grp = ks[i:i + n]
+        i += n
+        dur.setdefault((M, N, mode), []).extend(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+        gap.setdefault((M, N, mode), []).extend(
+            (int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3 for a, b in zip(grp, grp[1:]))
+    region = {tuple(r["region"][:2]): r["region"][2] for r in recs if "region" in r}
+    plain = {tuple(r["region"][:2]): r["region"][2]
+             for r in (json.loads(x) for x in open(plain_log) if x.startswith('{"region"'))}
+    print("rmsnorm_fwd: what the timed entry point costs between launches, MI355X (gfx950), one GPU")
+    print("=========================================================================================")
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp):")
+    print(f"  rocprofv3 --kernel-trace --output-format csv -d {trace_dir} -o run -- \\")
+    print(f"      python -u probe.py launch-modes > {log}")
+    print(f"  python -u probe.py launch-modes > {plain_log}")
+    print(f"  python probe.py launch-modes-summary {trace_dir} {log} {plain_log}")
+    print()
+    print("Back-to-back launches of one mode per group (6 rounds, alternating order; 40 launches")
+    print("per group, 10 at 16384 x 16384), buffer sets rotated through >= 1 GiB, all through ctypes:")
+    for k, v in LAUNCH_MODES.items():
+        print(f"  {k:<11} {v}")
+    print("kernel: median trace duration; gap: median idle time between consecutive kernels of a")
+    print("group (trace); region / launch: events around each group / launches (median over rounds),")
+    print("under the profiler and in the run without it.")
+    print()
+    print(f"  {'x[M, N]':<16} {'mode':<11} {'kernel_us':>9} {'gap_us':>7} {'region/launch_us':>16} "
+          f"{'without_profiler_us':>19}")
+    for (M, N), reg in region.items():
+        for mode in LAUNCH_MODES:
+            k = (M, N, mode)
+            print(f"  {f'x[{M}, {N}]':<16} {mode:<11} {statistics.median(dur[k]):>9.2f} "
+                  f"{statistics.median(gap[k]):>7.2f} {reg[mode]:>16.2f} "
+                  f"{plain.get((M, N), {}).get(mode, float('nan')):>19.2f}")
+
+
 # Cache-policy bits of the row copy's LDS-DMA loads (global_load_lds_dwordx4):
 # aux operand of __builtin_amdgcn_global_load_lds on gfx950 (sc0 1, nt 2, sc1 16).
 LOAD_POLICIES = {0: "none", 16: "sc1", 18: "nt sc1", 17: "sc0 sc1", 3: "nt sc0"}
@@ -2773,6 +2895,10 @@ if __name__ == "__main__":
         small_regs_compare(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 2 and sys.argv[1] == "qk-angles":
         qk_angles()
+    elif len(sys.argv) == 2 and sys.argv[1] == "launch-modes":
+        launch_modes()
+    elif len(sys.argv) == 5 and sys.argv[1] == "launch-modes-summary":
+        launch_modes_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) == 3 and sys.argv[1] == "qk-angles-summary":
         qk_angles_summary(sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "load-policy":

@@ -343,3 +343,35 @@ def test_small_regs_summary_names_width_and_rows(tmp_path, capsys):
     out = capsys.readouterr().out
     assert "probe.py small-regs rms 4096 2560 >" in out
     assert "6 rounds x 40 launches" in out and "RMSNorm x[2560, 4096]" in out and "8.00 us" in out
+
+
+def test_launch_modes_summary(tmp_path, capsys):
+    """Traced kernels are attributed to the announced groups in order; the gap is
+    the idle time between consecutive kernels of a group."""
+    import csv
+    import json
+
+    d = tmp_path / "t"
+    d.mkdir()
+    blocks = [[4096, 4096, "plain", 3], [4096, 4096, "ev_nofence", 3], [4096, 4096, "ev_default", 2]]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for M, N, mode, n in blocks:
+            for _ in range(n):
+                w.writerow({"Kernel_Name": "rownorm_regs_kernel<0, 1, 2, 8, true>", "Start_Timestamp": t,
+                            "End_Timestamp": t + 11000})
+                t += 11000 + (1000 if mode == "plain" else 12000)
+    log = tmp_path / "lm.log"
+    reg = {"region": [4096, 4096, {"plain": 12.5, "ev_nofence": 25.0, "ev_default": 26.0}]}
+    log.write_text("\n".join(json.dumps({"block": b}) for b in blocks) + "\n" + json.dumps(reg) + "\n")
+    plain = tmp_path / "lm_plain.log"
+    plain.write_text(json.dumps({"region": [4096, 4096, {"plain": 11.5, "ev_nofence": 18.0,
+                                                          "ev_default": 18.5}]}) + "\n")
+    probe.launch_modes_summary(str(d), str(log), str(plain))
+    out = capsys.readouterr().out
+    rows = [line.split() for line in out.splitlines() if line.strip().startswith("x[4096, 4096]")]
+    assert [r[2] for r in rows] == ["plain", "ev_nofence", "ev_default"]
+    assert rows[0][3:] == ["11.00", "1.00", "12.50", "11.50"]
+    assert rows[1][3:] == ["11.00", "12.00", "25.00", "18.00"]
