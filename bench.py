@@ -9,12 +9,13 @@ One step is one pass of the whole hot path over resident synthetic inputs:
      (section 3.1) peaks at;
   2. qk_norm_rope_fwd on qkv[256, (32+8+8)*128] bf16 (full-rotary fused
      QK-norm + RoPE, "[pretuned] Optimize fused_qk_norm_rope on B200").
-Each launch is bracketed by HIP events on the stream it runs on; `value` is the
-RMSNorm's achieved HBM bandwidth, algorithmic bytes (2*M*N*2 + 2*N) divided by
-its mean event-timed duration, in GB/s (1e9 B/s). Prints one JSON line.
+Each launch records its own start and end in HIP events (hipExtLaunchKernel,
+on the stream it runs on); `value` is the RMSNorm's achieved HBM bandwidth,
+algorithmic bytes (2*M*N*2 + 2*N) divided by the mean of its durations, in
+GB/s (1e9 B/s). Prints one JSON line.
 
-The CPU baseline is the fp64 oracle run on the host over the same RMSNorm
-workload (row blocks of 1024), single-threaded.
+The CPU baseline is the fp64 oracle run on the host over row blocks of the
+same RMSNorm workload (512 rows each), on up to 16 threads and on one.
 """
 
 from __future__ import annotations
